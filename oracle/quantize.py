@@ -1,0 +1,57 @@
+"""FP8 (E4M3FN) quantisation of K/V (and per-tensor Q) -- oracle, test infrastructure.
+
+What the pages fix:
+  * symmetric per-tensor scales for Q/K/V (FlashMLA PR #54, "Functionality");
+  * a per-token-head FP8 KV cache, i.e. one scale per (token, KV head)
+    (FreeToken PR #900, end-to-end table row "fp8_per_token_head");
+  * scale = amax / 448 over the quantised group (the workloads' statement).
+Readings where the pages are silent: the scale is computed in float32 as
+fl32(amax / 448); a value is encoded as RNE_e4m3(clamp(fl32(x / scale), -448, 448))
+with an IEEE float32 division; a group whose amax is 0 gets scale 1 (all codes 0).
+
+Inputs are rows of d values (bf16 bit patterns, or float32); for per-token-head
+scales a row is one (token, KV head) vector, for per-tensor scales all rows share
+one scale.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import E4M3_MAX, bf16_bits_to_f64, f64_to_e4m3_rne
+
+
+def _as_f32(src: np.ndarray, src_dtype: str) -> np.ndarray:
+    if src_dtype == "bf16":
+        return bf16_bits_to_f64(src).astype(np.float32)      # exact
+    if src_dtype == "fp32":
+        return np.asarray(src, dtype=np.float32)
+    raise ValueError(src_dtype)
+
+
+def _encode(x32: np.ndarray, scale32: np.ndarray) -> np.ndarray:
+    q = (x32 / scale32).astype(np.float32)                     # IEEE fp32 divide, RNE
+    q = np.clip(q.astype(np.float64), -E4M3_MAX, E4M3_MAX)
+    return f64_to_e4m3_rne(q)
+
+
+def _scale_from_amax(amax32: np.ndarray) -> np.ndarray:
+    amax32 = np.asarray(amax32, dtype=np.float32)
+    s = (amax32 / np.float32(E4M3_MAX)).astype(np.float32)
+    return np.where(amax32 == 0, np.float32(1.0), s).astype(np.float32)
+
+
+def quantize_per_tensor(src: np.ndarray, src_dtype: str):
+    """Returns (codes uint8 with src's shape, scale float32 scalar)."""
+    x = _as_f32(src, src_dtype)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    scale = _scale_from_amax(amax)
+    return _encode(x, scale), np.float32(scale)
+
+
+def quantize_per_row(src: np.ndarray, src_dtype: str):
+    """Per-(token, KV head) scales: src [..., d]; one scale per leading index.
+    Returns (codes uint8 [..., d], scales float32 [...])."""
+    x = _as_f32(src, src_dtype)
+    amax = np.max(np.abs(x), axis=-1).astype(np.float32)
+    scale = _scale_from_amax(amax)
+    return _encode(x, scale[..., None]), scale
