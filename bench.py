@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark: stage 1 + merge of paged split-KV decode on one MI355X.
+
+Default workload: FP8 single-row decode, batch 128, 64 Q / 8 KV heads, head_dim 128,
+KV 2048 tokens per request in pages of 64, Q/K/V e4m3 with per-tensor scales, bf16
+output (the hpc-ops issue #4 benchmark shape).  A step is one stage-1 launch plus
+one merge launch over the whole batch, with inputs resident in HBM; a 512 MiB write
+before every step evicts L2 and the 256 MiB MALL (FreeToken PR #900 times its
+kernels with the cache flushed before each rep).  Each step is timed with HIP
+events on the stream the kernels run on.
+
+Prints one JSON line.  value = algorithmic HBM bytes per step / time per step (GB/s).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention µs/step + achieved HBM GB/s (% of MI355X peak), 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD_NAMES = {
+    "c1": "tiny decode B1 8/1 heads d128 ctx512 P16 bf16, fp32 out, 4 splits",
+    "c2": "fp8 single-row decode B128 64/8 heads d128 ctx2048 P64, e4m3 Q/K/V per-tensor, bf16 out",
+    "c3": "MTP verify R4 B16 16/2 heads d256 ctx32768 P16 bf16 KV",
+    "c3_b1": "MTP verify R4 B1 16/2 heads d256 ctx32768 P16 bf16 KV",
+    "c3_r1": "single-row decode B16 16/2 heads d256 ctx32768 P16 bf16 KV",
+    "c3_r8": "MTP verify R8 B16 16/2 heads d256 ctx32768 P16 bf16 KV",
+    "c4": "long-context R8 B16 16/2 heads d256 ctx131072 P16 e4m3 KV per-token-head",
+    "c4_b1": "long-context R8 B1 16/2 heads d256 ctx131072 P16 e4m3 KV per-token-head",
+    "c4_r1": "long-context R1 B16 16/2 heads d256 ctx131072 P16 e4m3 KV per-token-head",
+    "c4_b1_r1": "long-context R1 B1 16/2 heads d256 ctx131072 P16 e4m3 KV per-token-head",
+    "c5": "ragged R1..8 B64 48/2 heads (group 24) d128 ctx loguniform 1K-64K, half window 64, P32 e4m3 per-token-head",
+}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def cpu_baseline(w, out_gpu: np.ndarray, budget_s: float):
+    """Times the fp64 oracle on a bounded sample (whole requests, in order, until the
+    time budget is spent) and compares the GPU output of those requests with it."""
+    import torch
+
+    from oracle.attention import decode_attention
+    from paged_split_kv_stage1_amd.accounting import step_accounting
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from tests.oracle_inputs import max_rel_err, oracle_inputs
+
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    t_setup = time.perf_counter()
+    reqs = []
+    elapsed = 0.0
+    err = 0.0
+    oi_all = None
+    for b in range(w.batch):
+        if oi_all is None or w.kv_scale_mode == "per_token_head":
+            oi = oracle_inputs(w, requests=[b] if w.kv_scale_mode == "per_token_head" else None)
+            if w.kv_scale_mode != "per_token_head":
+                oi_all = oi
+        else:
+            oi = oi_all
+        t0 = time.perf_counter()
+        out, _ = decode_attention(oi["q64"], oi["k"], oi["v"], w.page_indices, w.kv_indptr, w.kv_len, w.qo_indptr,
+                                  w.window, w.sm_scale, requests=[b])
+        elapsed += time.perf_counter() - t0
+        rows = slice(int(w.qo_indptr[b]), int(w.qo_indptr[b + 1]))
+        err = max(err, max_rel_err(out_gpu[rows], out[rows]))
+        reqs.append(b)
+        if elapsed >= budget_s or time.perf_counter() - t_setup > 3 * budget_s:
+            break
+    sel = np.array(reqs)
+    qo = np.concatenate([[0], np.cumsum(np.diff(w.qo_indptr)[sel])])
+    acc = step_accounting(len(sel), qo, w.kv_len[sel], w.window[sel], w.page_size, w.num_q_heads, w.num_kv_heads,
+                          w.head_dim, w.q_dtype, w.kv_dtype, w.kv_scale_mode, w.out_dtype)
+    return {"value": round(acc["bytes"] / elapsed / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(sel)} of {w.batch} requests (all rows, heads and visible tokens of each), "
+                      f"{elapsed:.1f} s of fp64 numpy on {cores} threads, {_cpu_model()}",
+            "seconds": round(elapsed, 3)}, err
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting write between steps")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--force-splits", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    from paged_split_kv_stage1_amd.accounting import workload_accounting
+    from paged_split_kv_stage1_amd.decode import PagedDecode
+    from paged_split_kv_stage1_amd.device_inputs import to_device
+    from paged_split_kv_stage1_amd.inputs import make_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_workload(args.config)
+    di = to_device(w, dev)
+    acc = workload_accounting(w)
+    pd = PagedDecode(w.qo_indptr, w.kv_indptr, w.kv_len, w.window, w.max_q_len, w.page_size, w.num_q_heads,
+                     w.num_kv_heads, w.head_dim, w.q_dtype, w.kv_dtype, w.kv_scale_mode, dev,
+                     force_splits=w.forced_splits if args.force_splits is None else args.force_splits)
+    out = torch.empty(w.total_rows, w.num_q_heads, w.head_dim,
+                      dtype=torch.float32 if w.out_dtype == "fp32" else torch.bfloat16, device=dev)
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pd.stage1(di.q, di.q_scale, di.k, di.v, di.kv_layout, di.k_scale, di.v_scale, di.scale_layout,
+                  di.page_indices, w.sm_scale, out, w.out_dtype, stream=stream)
+
+    def merge():
+        pd.merge(out, w.out_dtype, stream=stream)
+
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush.fill_(1.0)
+        step()
+        merge()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.fill_(1.0)
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+        merge()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    s1 = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3      # us
+    mg = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    tot = s1 + mg
+
+    def iqm(x):
+        x = np.sort(x)
+        n = len(x)
+        return float(np.mean(x[n // 4: n - n // 4])) if n >= 4 else float(np.mean(x))
+
+    us_step = float(np.mean(tot))
+    gbps = acc["bytes"] / (us_step * 1e-6) / 1e9
+    s1_us = float(np.mean(s1))
+    s1_bytes = acc["bytes"]
+    roof_achieved = s1_bytes / (s1_us * 1e-6) / 1e9
+    result = {
+        "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us_step / 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {"c1": "bf16", "c3": "bf16"}.get(args.config.split("_")[0], "fp8-e4m3 (bf16 MFMA)" if w.q_dtype != "fp8" else "fp8-e4m3"),
+        "data": "synthetic (seeded N(0,1), random page permutation)",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "name": args.config, "batch": w.batch,
+                   "total_rows": w.total_rows, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "page_size": w.page_size, "kv_dtype": w.kv_dtype,
+                   "kv_scale_mode": w.kv_scale_mode, "work_items": pd.num_items, "max_splits": pd.max_splits,
+                   "cache_flush_between_steps": not args.no_flush},
+        "us_per_step": round(us_step, 3), "us_per_step_iqm": round(iqm(tot), 3),
+        "stage1_us": round(s1_us, 3), "merge_us": round(float(np.mean(mg)), 3),
+        "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "algorithmic_bytes_per_step": acc["bytes"], "algorithmic_flops_per_step": acc["flops"],
+        "tflops": round(acc["flops"] / (us_step * 1e-6) / 1e12, 3),
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "roofline": {"bound": "hbm", "achieved": round(roof_achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(roof_achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "stage1_kernel", "bytes_per_launch": s1_bytes},
+    }
+    if not args.no_cpu_baseline:
+        out_np = out.float().cpu().numpy().astype(np.float64)
+        cb, err = cpu_baseline(w, out_np, args.cpu_budget)
+        result["cpu_baseline"] = cb
+        result["sampled_parity_maxrel"] = err
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * pa.h -- C ABI of a gfx950 (MI355X) library for paged split-KV decode attention.
+ *
+ * The operation (FreeToken PR #900 "perf(attention): run up to 8 query rows per
+ * request in the triton decode kernel", section "Changes"): decode attention over a
+ * paged KV cache where each request carries up to 8 causal query rows described by
+ * qo_indptr / max_q_len; stage 1 keeps the KV split and packs query rows x GQA
+ * heads of one KV head into one matrix tile, limiting each row to its own position
+ * and window; stage 2 merges the splits of each row.  KV may be bf16 or FP8
+ * (OCP E4M3FN) with a per-tensor scale (FlashMLA PR #54 "Functionality") or one
+ * scale per (token, KV head) (FreeToken PR #900, "fp8_per_token_head").
+ * Dequantisation is folded into the score scale and the final normaliser
+ * (FlashInfer PR #869, item 3).  Requests with more rows than supported are
+ * rejected with an error rather than silently mishandled (hpc-ops issue #4: its
+ * FP8 decode entry point raises a runtime error for any q_len other than 1).
+ *
+ * Conventions for every entry point
+ *  - Every pointer is caller-owned.  Pointers documented as "device" must be
+ *    device memory of the current HIP device; "host" pointers are plain host
+ *    memory.  The library never allocates or frees memory, never synchronises,
+ *    and launches work only on the stream passed in (a hipStream_t; NULL = the
+ *    default stream).  stage1/merge launches are hipGraph-capturable.
+ *  - Every call returns a pa_status.  On failure nothing has been launched and
+ *    pa_last_error() returns a message (thread-local, valid until the next call
+ *    on the same thread).  Errors of kernels that already ran asynchronously
+ *    surface through the HIP runtime (hipStreamSynchronize), not here.
+ *  - FP8 means OCP E4M3FN: bias 7, max finite 448, S.1111.111 = NaN, no Inf.
+ *  - Q is [T, Hq, d] contiguous (T = total query rows = qo_indptr[B]); the output
+ *    is [T, Hq, d] contiguous.  Query head h reads KV head h / (Hq / Hkv).
+ *  - Row r (0-based) of request b sits at position p = kv_len[b] - n_b + r, with
+ *    n_b = qo_indptr[b+1] - qo_indptr[b]; kv_len counts the new rows' own keys.
+ *    It attends to keys j with lo <= j <= p, lo = max(0, p - W + 1) when the
+ *    request's window W > 0 (W keys including itself), lo = 0 otherwise.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1,     /* malformed input: the call can never succeed as given */
+  PA_ERR_UNSUPPORTED = 2,          /* well-formed but outside what the kernels implement   */
+  PA_ERR_INSUFFICIENT_WORKSPACE = 3,/* a caller buffer is smaller than required             */
+  PA_ERR_HIP = 4                   /* a HIP runtime call failed (message has the HIP error) */
+} pa_status;
+
+typedef enum { PA_DTYPE_BF16 = 0, PA_DTYPE_FP32 = 1, PA_DTYPE_FP8_E4M3 = 2 } pa_dtype;
+
+typedef enum {
+  PA_SCALE_NONE = 0,           /* bf16 KV                                               */
+  PA_SCALE_PER_TENSOR = 1,     /* one float32 scale for the whole K (and one for V)     */
+  PA_SCALE_PER_TOKEN_HEAD = 2  /* one float32 scale per (token slot, KV head)           */
+} pa_scale_mode;
+
+/* Element strides of a paged cache: element (page, kv_head, slot, c) lives at
+ * base[page*page + kv_head*head + slot*slot + c] (the head_dim axis is contiguous).
+ * [pages, Hkv, P, d] has {Hkv*P*d, P*d, d}; [pages, P, Hkv, d] has {P*Hkv*d, d, Hkv*d}.
+ * Every stride times the element size must be a multiple of 16 bytes. */
+typedef struct { int64_t page, head, slot; } pa_kv_layout;
+
+/* Element strides of per-(token, KV head) float32 scales: scale(page, kv_head, slot)
+ * = base[page*page + kv_head*head + slot*slot]. */
+typedef struct { int64_t page, head, slot; } pa_scale_layout;
+
+/* Planner input.  All array pointers are HOST memory. */
+typedef struct {
+  int32_t batch;               /* B >= 1 requests                                          */
+  const int32_t* qo_indptr;    /* [B+1] query-row CSR; 1 <= n_b <= max_q_len                */
+  const int32_t* kv_indptr;    /* [B+1] CSR into page_indices; must equal ceil(kv_len/P)    */
+  const int32_t* kv_len;       /* [B] tokens in the cache, including the new rows; >= n_b   */
+  const int32_t* window;       /* [B] sliding window in keys (0 = none), or NULL (none)      */
+  int32_t max_q_len;           /* upper bound of n_b; must be <= 8                          */
+  int32_t page_size;           /* tokens per page: 16, 32 or 64                             */
+  int32_t num_q_heads;         /* Hq                                                        */
+  int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0                                        */
+  int32_t head_dim;            /* 128 or 256                                                */
+  pa_dtype q_dtype;            /* BF16, or FP8_E4M3 (then kv must be FP8 with a per-tensor  */
+  pa_dtype kv_dtype;           /*   or per-token-head scale); kv: BF16 or FP8_E4M3          */
+  pa_scale_mode kv_scale_mode; /* NONE for bf16 KV; PER_TENSOR or PER_TOKEN_HEAD for FP8 KV  */
+  int32_t num_cus;             /* compute units to plan for; 0 = query the current device   */
+  int32_t max_splits;          /* cap on splits per request (fixes scratch size for graph   */
+                               /*   capture); 0 = no cap beyond the library's limit (1024)  */
+  int32_t force_splits;        /* > 0: every request gets exactly this many splits           */
+} pa_plan_args;
+
+/* Planner output, consumed by stage1/merge.  Sizes are in bytes. */
+typedef struct {
+  int32_t batch, total_rows, num_q_heads, num_kv_heads, head_dim, page_size, max_q_len;
+  int32_t q_dtype, kv_dtype, kv_scale_mode;
+  int32_t num_items;           /* stage-1 work items (one workgroup each)                   */
+  int32_t max_splits;          /* S_max: the split axis of the scratch buffers               */
+  int32_t needs_merge;         /* 0 when every request has a single split                   */
+  int32_t num_cus;
+  int32_t variant;             /* kernel tile configuration (library internal)              */
+  int32_t reserved0;
+  int64_t plan_bytes;          /* bytes of the plan buffer (host copy and device copy)       */
+  int64_t partial_o_bytes;     /* float32 [T, Hq, S_max, d]                                 */
+  int64_t partial_lse_bytes;   /* float32 [T, Hq, S_max]                                    */
+  int64_t reserved[4];
+} pa_plan_info;
+
+/* Split planner (host only; no device work, no allocation).
+ * Reads the host index arrays, validates them, chooses the number of KV splits of
+ * every request for the device's compute units, and writes the work list into
+ * plan_host (plan_capacity bytes).  With plan_host == NULL only *info is filled,
+ * which tells the caller how large the plan and scratch buffers must be.  The caller
+ * copies plan_host to a device buffer of info->plan_bytes bytes before stage 1.
+ * Errors: INVALID_ARGUMENT (non-monotone CSR, n_b > kv_len, kv_indptr inconsistent
+ * with kv_len, Hq % Hkv != 0, bad enum), UNSUPPORTED (max_q_len > 8, head_dim not
+ * 128/256, page size not 16/32/64, rows x group too large for one tile, dtype
+ * combination), INSUFFICIENT_WORKSPACE (plan_capacity < info->plan_bytes). */
+pa_status pa_plan_splits(const pa_plan_args* args, void* plan_host, size_t plan_capacity,
+                         pa_plan_info* info);
+
+/* Stage 1 (device): for every work item (request, KV head, split) stream the split's
+ * pages and write, for each of its query rows x heads, the split's normalised
+ * partial output and natural-log LSE; requests planned with a single split write
+ * the final output directly.
+ *   plan_dev     device copy of the plan (info->plan_bytes)
+ *   q            device [T, Hq, d]: bf16, or e4m3 codes with *q_scale (device float)
+ *   q_scale      device float32 scalar when q is FP8, else NULL
+ *   k_cache, v_cache  device paged caches (bf16 or e4m3 codes) with strides kv
+ *   k_scale, v_scale  device float32: a scalar (PER_TENSOR) or per-token-head array
+ *                with strides sc (PER_TOKEN_HEAD); NULL for bf16 KV
+ *   page_indices device int32, indexed through kv_indptr
+ *   sm_scale     softmax scale applied to q.k (typically 1/sqrt(d) in float32)
+ *   partial_o    device float32 [T, Hq, S_max, d] (unused if !info->needs_merge)
+ *   partial_lse  device float32 [T, Hq, S_max]
+ *   out          device [T, Hq, d] in out_dtype (BF16 or FP32)
+ * Tokens past kv_len (the tail of the last page) are never read. */
+pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev,
+                           const void* q, const float* q_scale,
+                           const void* k_cache, const void* v_cache, const pa_kv_layout* kv,
+                           const float* k_scale, const float* v_scale, const pa_scale_layout* sc,
+                           const int32_t* page_indices, float sm_scale,
+                           float* partial_o, float* partial_lse,
+                           void* out, pa_dtype out_dtype, void* stream);
+
+/* Stage 2 (device): per (row, query head) with more than one split,
+ * out = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M}, M = max_s lse_s, written
+ * in out_dtype; out_lse (device float32 [T, Hq], nullable) receives the merged
+ * natural-log LSE of those rows.  A no-op launch-free success when
+ * info->needs_merge == 0. */
+pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev,
+                          const float* partial_o, const float* partial_lse,
+                          void* out, pa_dtype out_dtype, float* out_lse, void* stream);
+
+/* FP8 quantiser (device): src holds n_rows rows of head_dim contiguous values
+ * (bf16 or float32; e.g. a [pages, Hkv, P, d] cache is pages*Hkv*P rows).
+ *   PER_TOKEN_HEAD: scale[i] = amax_i / 448 (1 if amax_i == 0) per row i;
+ *   PER_TENSOR:     one scale = amax / 448 over all rows, written to scale[0].
+ * dst[i, c] = RNE_e4m3(clamp(src[i, c] / scale, -448, 448)) with an IEEE float32
+ * divide.  dst: device uint8 [n_rows, head_dim]; scale: device float32 (n_rows, or 1).
+ * head_dim must be a multiple of 64 and <= 1024. */
+pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows, int32_t head_dim,
+                             pa_scale_mode mode, uint8_t* dst, float* scale, void* stream);
+
+/* Test hook (device): for every work item of KV head 0 and every token t of its
+ * split, writes the physical slot page*P + slot that stage 1 reads for token t of
+ * its request to phys_out[kv_tok_offset[b] + t] (int64), where kv_tok_offset[b] =
+ * sum of kv_len over requests < b.  Uses the same address code as stage 1.
+ * Entries of tokens no split covers are left untouched. */
+pa_status pa_debug_gather(const pa_plan_info* info, const void* plan_dev, const int32_t* page_indices,
+                          int64_t* phys_out, const int64_t* kv_tok_offset, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version string. */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,356 @@
+// Host side of the C ABI in include/pa.h: argument validation, the split planner,
+// and kernel dispatch.  Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.hpp"
+
+using namespace pa;
+
+namespace {
+
+thread_local std::string g_err;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+pa_status ok() {
+  g_err.clear();
+  return PA_OK;
+}
+pa_status hip_fail(int err, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString((hipError_t)err));
+}
+
+int ilog2_exact(int v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Tile configuration for the planned shape.
+bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int mq = a.max_q_len * G;
+  const int nqb = (mq + 15) / 16;
+  c->dh = a.head_dim;
+  c->qf8 = a.q_dtype == PA_DTYPE_FP8_E4M3;
+  c->kvf8 = a.kv_dtype == PA_DTYPE_FP8_E4M3;
+  c->pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD;
+  if (nqb <= 1) { c->wq = 1; c->nqb = 1; }
+  else if (nqb == 2) { c->wq = 2; c->nqb = 1; }
+  else if (nqb <= 4) { c->wq = 4; c->nqb = 1; }
+  else { c->wq = 4; c->nqb = (nqb + 3) / 4; }
+  return stage1_cfg_supported(*c);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+const char* pa_version(void) { return "paged_split_kv_stage1_amd 0.1 (gfx950)"; }
+
+pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_capacity, pa_plan_info* info) {
+  if (!a || !info) return fail(PA_ERR_INVALID_ARGUMENT, "pa_plan_splits: args and info must be non-NULL");
+  const int B = a->batch;
+  if (B < 1) return fail(PA_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", B);
+  if (!a->qo_indptr || !a->kv_indptr || !a->kv_len)
+    return fail(PA_ERR_INVALID_ARGUMENT, "qo_indptr, kv_indptr and kv_len must be non-NULL host arrays");
+  if (a->max_q_len < 1) return fail(PA_ERR_INVALID_ARGUMENT, "max_q_len must be >= 1 (got %d)", a->max_q_len);
+  if (a->max_q_len > 8)
+    return fail(PA_ERR_UNSUPPORTED, "max_q_len %d: at most 8 query rows per request are supported", a->max_q_len);
+  if (a->num_q_heads < 1 || a->num_kv_heads < 1 || a->num_q_heads % a->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                a->num_q_heads, a->num_kv_heads);
+  if (a->head_dim != 128 && a->head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d: only 128 and 256 are supported", a->head_dim);
+  const int page_shift = ilog2_exact(a->page_size);
+  if (page_shift < 0 || a->page_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "page_size %d: must be a power of two <= 1024", a->page_size);
+  if (a->q_dtype != PA_DTYPE_BF16 && a->q_dtype != PA_DTYPE_FP8_E4M3)
+    return fail(PA_ERR_INVALID_ARGUMENT, "q_dtype must be BF16 or FP8_E4M3");
+  if (a->kv_dtype != PA_DTYPE_BF16 && a->kv_dtype != PA_DTYPE_FP8_E4M3)
+    return fail(PA_ERR_INVALID_ARGUMENT, "kv_dtype must be BF16 or FP8_E4M3");
+  if (a->kv_dtype == PA_DTYPE_BF16 && a->kv_scale_mode != PA_SCALE_NONE)
+    return fail(PA_ERR_INVALID_ARGUMENT, "bf16 KV takes kv_scale_mode NONE");
+  if (a->kv_dtype == PA_DTYPE_FP8_E4M3 && a->kv_scale_mode != PA_SCALE_PER_TENSOR &&
+      a->kv_scale_mode != PA_SCALE_PER_TOKEN_HEAD)
+    return fail(PA_ERR_INVALID_ARGUMENT, "FP8 KV takes kv_scale_mode PER_TENSOR or PER_TOKEN_HEAD");
+  if (a->q_dtype == PA_DTYPE_FP8_E4M3 && a->kv_dtype != PA_DTYPE_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "FP8 queries need an FP8 KV cache");
+  if (a->max_splits < 0 || a->force_splits < 0 || a->num_cus < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_splits, force_splits and num_cus must be >= 0");
+  const int split_cap = a->max_splits > 0 ? std::min(a->max_splits, kMaxSplits) : kMaxSplits;
+  if (a->force_splits > split_cap)
+    return fail(PA_ERR_INVALID_ARGUMENT, "force_splits %d exceeds the split cap %d", a->force_splits, split_cap);
+
+  KernelCfg cfg;
+  if (!choose_cfg(*a, &cfg))
+    return fail(PA_ERR_UNSUPPORTED, "max_q_len x group = %d query rows per KV head is beyond the tile limit "
+                                    "for head_dim %d and this dtype combination",
+                a->max_q_len * (a->num_q_heads / a->num_kv_heads), a->head_dim);
+
+  // ---- validate the index arrays ------------------------------------------------
+  if (a->qo_indptr[0] != 0) return fail(PA_ERR_INVALID_ARGUMENT, "qo_indptr[0] must be 0");
+  for (int b = 0; b < B; ++b) {
+    const int n = a->qo_indptr[b + 1] - a->qo_indptr[b];
+    if (n < 1 || n > a->max_q_len)
+      return fail(PA_ERR_INVALID_ARGUMENT, "request %d has %d query rows (must be 1..max_q_len=%d)", b, n,
+                  a->max_q_len);
+    const int L = a->kv_len[b];
+    if (L < n) return fail(PA_ERR_INVALID_ARGUMENT, "request %d: kv_len %d < its %d query rows", b, L, n);
+    const int64_t pages = ((int64_t)L + a->page_size - 1) / a->page_size;
+    if ((int64_t)a->kv_indptr[b + 1] - a->kv_indptr[b] != pages)
+      return fail(PA_ERR_INVALID_ARGUMENT, "request %d: kv_indptr spans %d pages but kv_len %d needs %lld", b,
+                  a->kv_indptr[b + 1] - a->kv_indptr[b], L, (long long)pages);
+    if (a->kv_indptr[b] < 0) return fail(PA_ERR_INVALID_ARGUMENT, "kv_indptr[%d] is negative", b);
+    if (a->window && a->window[b] < 0)
+      return fail(PA_ERR_INVALID_ARGUMENT, "request %d: window %d is negative", b, a->window[b]);
+  }
+  const int T = a->qo_indptr[B];
+  const int Hkv = a->num_kv_heads;
+
+  int num_cus = a->num_cus;
+  if (num_cus == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "pa_plan_splits: hipGetDevice");
+    e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "pa_plan_splits: hipDeviceGetAttribute");
+  }
+
+  // ---- split plan -------------------------------------------------------------------
+  // Each request's visible token range [lo_b, L_b) (union over its rows) is aligned
+  // down to a multiple of 64 tokens and cut into S_b equal runs of 64-token blocks.
+  std::vector<int> begin(B), span(B), nsp(B);
+  int64_t total_tok = 0;
+  for (int b = 0; b < B; ++b) {
+    const int n = a->qo_indptr[b + 1] - a->qo_indptr[b];
+    const int L = a->kv_len[b];
+    const int W = a->window ? a->window[b] : 0;
+    const int lo = W > 0 ? std::max(0, L - n - W + 1) : 0;
+    begin[b] = (lo / kSplitAlign) * kSplitAlign;
+    span[b] = L - begin[b];
+    total_tok += (int64_t)span[b] * Hkv;
+  }
+  if (a->force_splits > 0) {
+    for (int b = 0; b < B; ++b) nsp[b] = a->force_splits;
+  } else {
+    // Enough work items to give every CU a few, but never splits so short that the
+    // partial-output traffic dominates (>= 256 tokens per split).
+    const int64_t target_items = 4LL * num_cus;
+    int64_t chunk = (total_tok + target_items - 1) / target_items;
+    chunk = std::max<int64_t>(chunk, 256);
+    chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+    for (int b = 0; b < B; ++b) {
+      int64_t s = (span[b] + chunk - 1) / chunk;
+      nsp[b] = (int)std::max<int64_t>(1, std::min<int64_t>(s, split_cap));
+    }
+  }
+  int s_max = 1;
+  int64_t n_items = 0;
+  for (int b = 0; b < B; ++b) {
+    s_max = std::max(s_max, nsp[b]);
+    n_items += (int64_t)nsp[b] * Hkv;
+  }
+  if (n_items > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "too many work items (%lld)", (long long)n_items);
+  const int64_t th_count = (int64_t)T * a->num_q_heads;
+
+  memset(info, 0, sizeof *info);
+  info->batch = B;
+  info->total_rows = T;
+  info->num_q_heads = a->num_q_heads;
+  info->num_kv_heads = Hkv;
+  info->head_dim = a->head_dim;
+  info->page_size = a->page_size;
+  info->max_q_len = a->max_q_len;
+  info->q_dtype = a->q_dtype;
+  info->kv_dtype = a->kv_dtype;
+  info->kv_scale_mode = a->kv_scale_mode;
+  info->num_items = (int32_t)n_items;
+  info->max_splits = s_max;
+  info->needs_merge = s_max > 1;
+  info->num_cus = num_cus;
+  info->variant = pack_cfg(cfg);
+  info->plan_bytes = plan_bytes_for(n_items, T);
+  info->partial_o_bytes = s_max > 1 ? th_count * s_max * a->head_dim * 4 : 0;
+  info->partial_lse_bytes = s_max > 1 ? th_count * s_max * 4 : 0;
+  if (!plan_host) return ok();
+  if ((int64_t)plan_capacity < info->plan_bytes)
+    return fail(PA_ERR_INSUFFICIENT_WORKSPACE, "plan buffer holds %zu bytes, %lld needed", plan_capacity,
+                (long long)info->plan_bytes);
+
+  // ---- emit work items, heaviest first ----------------------------------------------
+  std::vector<PaItem> items;
+  items.reserve((size_t)n_items);
+  for (int b = 0; b < B; ++b) {
+    const int n = a->qo_indptr[b + 1] - a->qo_indptr[b];
+    const int L = a->kv_len[b];
+    const int nblk = (span[b] + kSplitAlign - 1) / kSplitAlign;
+    for (int g = 0; g < Hkv; ++g) {
+      for (int s = 0; s < nsp[b]; ++s) {
+        PaItem it;
+        memset(&it, 0, sizeof it);
+        it.row0 = a->qo_indptr[b];
+        it.nrows = n;
+        it.kv_len = L;
+        it.page_base = a->kv_indptr[b];
+        it.window = a->window ? a->window[b] : 0;
+        it.kvh = g;
+        it.split = s;
+        it.nsplit = nsp[b];
+        const int64_t blk0 = (int64_t)s * nblk / nsp[b];
+        const int64_t blk1 = (int64_t)(s + 1) * nblk / nsp[b];
+        it.tok_begin = (int)std::min<int64_t>(begin[b] + blk0 * kSplitAlign, L);
+        it.tok_end = (int)std::min<int64_t>(begin[b] + blk1 * kSplitAlign, L);
+        it.req = b;
+        items.push_back(it);
+      }
+    }
+  }
+  const int G = a->num_q_heads / Hkv;
+  std::stable_sort(items.begin(), items.end(), [G](const PaItem& x, const PaItem& y) {
+    const int64_t cx = (int64_t)(x.tok_end - x.tok_begin) * (64 + x.nrows * G);
+    const int64_t cy = (int64_t)(y.tok_end - y.tok_begin) * (64 + y.nrows * G);
+    return cx > cy;
+  });
+  uint8_t* out = static_cast<uint8_t*>(plan_host);
+  memcpy(out, items.data(), items.size() * sizeof(PaItem));
+  int32_t* row_ns = reinterpret_cast<int32_t*>(out + items.size() * sizeof(PaItem));
+  for (int b = 0; b < B; ++b)
+    for (int t = a->qo_indptr[b]; t < a->qo_indptr[b + 1]; ++t) row_ns[t] = nsp[b];
+  return ok();
+}
+
+pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const void* q, const float* q_scale,
+                           const void* k_cache, const void* v_cache, const pa_kv_layout* kv, const float* k_scale,
+                           const float* v_scale, const pa_scale_layout* sc, const int32_t* page_indices,
+                           float sm_scale, float* partial_o, float* partial_lse, void* out, pa_dtype out_dtype,
+                           void* stream) {
+  if (!info || !plan_dev || !q || !k_cache || !v_cache || !kv || !page_indices || !out)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_stage1: a required pointer is NULL");
+  if (out_dtype != PA_DTYPE_BF16 && out_dtype != PA_DTYPE_FP32)
+    return fail(PA_ERR_INVALID_ARGUMENT, "out_dtype must be BF16 or FP32");
+  const KernelCfg cfg = unpack_cfg(info->variant);
+  if (!stage1_cfg_supported(cfg) || cfg.dh != info->head_dim)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_plan_info was not produced by pa_plan_splits");
+  if (info->needs_merge && (!partial_o || !partial_lse))
+    return fail(PA_ERR_INVALID_ARGUMENT, "this plan has several splits: partial_o and partial_lse are required");
+  if (cfg.qf8 && !q_scale) return fail(PA_ERR_INVALID_ARGUMENT, "FP8 queries need q_scale");
+  if (cfg.kvf8 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "FP8 KV needs k_scale and v_scale");
+  if (cfg.pt && !sc) return fail(PA_ERR_INVALID_ARGUMENT, "per-token-head scales need a scale layout");
+  const int esz = cfg.kvf8 ? 1 : 2;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out))
+    return fail(PA_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if ((kv->page * esz) % 16 || (kv->head * esz) % 16 || (kv->slot * esz) % 16 || kv->page < 0 || kv->head < 0 ||
+      kv->slot < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "KV strides must be non-negative multiples of 16 bytes");
+  if (info->needs_merge && (((uintptr_t)partial_o & 15u) != 0))
+    return fail(PA_ERR_INVALID_ARGUMENT, "partial_o must be 16-byte aligned");
+  const int ps = ilog2_exact(info->page_size);
+  Stage1Args s;
+  memset(&s, 0, sizeof s);
+  s.items = static_cast<const PaItem*>(plan_dev);
+  s.q = q;
+  s.q_scale = q_scale;
+  s.k = k_cache;
+  s.v = v_cache;
+  s.kv_sp = kv->page;
+  s.kv_sh = kv->head;
+  s.kv_ss = kv->slot;
+  s.k_scale = k_scale;
+  s.v_scale = v_scale;
+  if (sc) {
+    s.sc_sp = sc->page;
+    s.sc_sh = sc->head;
+    s.sc_ss = sc->slot;
+  }
+  s.page_indices = page_indices;
+  s.sm_scale = sm_scale;
+  s.partial_o = partial_o;
+  s.partial_lse = partial_lse;
+  s.out = out;
+  s.out_bf16 = out_dtype == PA_DTYPE_BF16;
+  s.hq = info->num_q_heads;
+  s.group = info->num_q_heads / info->num_kv_heads;
+  s.page_shift = ps;
+  s.s_max = info->max_splits;
+  const int e = launch_stage1(cfg, s, info->num_items, stream);
+  if (e) return hip_fail(e, "pa_decode_stage1 launch");
+  return ok();
+}
+
+pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev, const float* partial_o,
+                          const float* partial_lse, void* out, pa_dtype out_dtype, float* out_lse, void* stream) {
+  if (!info || !plan_dev || !out) return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_merge: a required pointer is NULL");
+  if (out_dtype != PA_DTYPE_BF16 && out_dtype != PA_DTYPE_FP32)
+    return fail(PA_ERR_INVALID_ARGUMENT, "out_dtype must be BF16 or FP32");
+  if (!info->needs_merge) return ok();
+  if (!partial_o || !partial_lse) return fail(PA_ERR_INVALID_ARGUMENT, "partial_o and partial_lse are required");
+  MergeArgs m;
+  m.row_nsplit = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(plan_dev) +
+                                                  (int64_t)info->num_items * sizeof(PaItem));
+  m.partial_o = partial_o;
+  m.partial_lse = partial_lse;
+  m.out = out;
+  m.out_bf16 = out_dtype == PA_DTYPE_BF16;
+  m.out_lse = out_lse;
+  m.total_rows = info->total_rows;
+  m.hq = info->num_q_heads;
+  m.dh = info->head_dim;
+  m.s_max = info->max_splits;
+  const int e = launch_merge(m, stream);
+  if (e) return hip_fail(e, "pa_decode_merge launch");
+  return ok();
+}
+
+pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows, int32_t head_dim,
+                             pa_scale_mode mode, uint8_t* dst, float* scale, void* stream) {
+  if (!src || !dst || !scale) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_quantize_fp8: NULL pointer");
+  if (src_dtype != PA_DTYPE_BF16 && src_dtype != PA_DTYPE_FP32)
+    return fail(PA_ERR_INVALID_ARGUMENT, "src_dtype must be BF16 or FP32");
+  if (mode != PA_SCALE_PER_TENSOR && mode != PA_SCALE_PER_TOKEN_HEAD)
+    return fail(PA_ERR_INVALID_ARGUMENT, "mode must be PER_TENSOR or PER_TOKEN_HEAD");
+  if (n_rows < 0) return fail(PA_ERR_INVALID_ARGUMENT, "n_rows must be >= 0");
+  if (head_dim < 64 || head_dim > 1024 || ilog2_exact(head_dim / 64) < 0 || head_dim % 64)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d: must be 64 times a power of two, at most 1024", head_dim);
+  const int e = launch_quant(src, src_dtype == PA_DTYPE_BF16, n_rows, head_dim, mode == PA_SCALE_PER_TENSOR, dst,
+                             scale, stream);
+  if (e) return hip_fail(e, "pa_kv_quantize_fp8 launch");
+  return ok();
+}
+
+pa_status pa_debug_gather(const pa_plan_info* info, const void* plan_dev, const int32_t* page_indices,
+                          int64_t* phys_out, const int64_t* kv_tok_offset, void* stream) {
+  if (!info || !plan_dev || !page_indices || !phys_out || !kv_tok_offset)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_debug_gather: NULL pointer");
+  GatherArgs g;
+  g.items = static_cast<const PaItem*>(plan_dev);
+  g.page_indices = page_indices;
+  g.phys_out = phys_out;
+  g.kv_tok_offset = kv_tok_offset;
+  g.page_shift = ilog2_exact(info->page_size);
+  const int e = launch_gather(g, info->num_items, stream);
+  if (e) return hip_fail(e, "pa_debug_gather launch");
+  return ok();
+}
+
+}  // extern "C"

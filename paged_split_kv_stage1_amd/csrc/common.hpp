@@ -1,0 +1,76 @@
+// Device helpers for the gfx950 kernels: vector types, FP8/bf16 conversions, MFMA
+// wrappers, wave shuffles, and the page-gather address code shared by stage 1 and
+// the gather test hook.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.hpp"
+
+namespace pa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((vector_size(8)));
+typedef int i32x2 __attribute__((vector_size(8)));
+
+#define PA_LDS __attribute__((address_space(3)))
+
+// ---- page gather ---------------------------------------------------------------
+// Logical token j of a request lives in page page_indices[page_base + j / P] at
+// slot j % P (P = 1 << page_shift).
+__device__ __forceinline__ int32_t token_page(const int32_t* __restrict__ page_indices, int32_t page_base,
+                                              int32_t j, int page_shift) {
+  return page_indices[page_base + (j >> page_shift)];
+}
+__device__ __forceinline__ int32_t token_slot(int32_t j, int page_shift) { return j & ((1 << page_shift) - 1); }
+
+// ---- MFMA ----------------------------------------------------------------------
+// 16x16x32: A lane l holds row l%16, K = 8*(l/16)..+7; B lane l holds column l%16,
+// same K; C lane l holds rows 4*(l/16)..+3 of column l%16.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_fp8(long a, long b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+// ---- conversions ------------------------------------------------------------------
+// 8 e4m3 codes (two dwords) -> 8 bf16, exactly (every e4m3 value is a bf16 value).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+// Four floats -> four e4m3 codes packed in a dword (RNE; inputs must be within +-448).
+__device__ __forceinline__ uint32_t f32x4_to_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+template <bool HI_WORD>
+__device__ __forceinline__ f32x2 fp8x2_to_f32x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI_WORD);
+}
+
+__device__ __forceinline__ float wave_max_xor_16_32(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_xor_16_32(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa

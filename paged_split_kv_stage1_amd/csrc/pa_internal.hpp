@@ -1,0 +1,84 @@
+// Internal definitions shared by the host planner/dispatcher and the gfx950 kernels.
+#pragma once
+#include <stdint.h>
+
+namespace pa {
+
+// One stage-1 work item: (request, KV head, split).  64 bytes, int32 fields.
+struct PaItem {
+  int32_t row0;       // first query row of the request (qo_indptr[b])
+  int32_t nrows;      // query rows of the request
+  int32_t kv_len;     // tokens of the request
+  int32_t page_base;  // kv_indptr[b]
+  int32_t window;     // sliding window (0 = none)
+  int32_t kvh;        // KV head
+  int32_t split;      // split index within the request
+  int32_t nsplit;     // splits of the request (1 => write the final output)
+  int32_t tok_begin;  // token range [tok_begin, tok_end) of this split
+  int32_t tok_end;
+  int32_t req;        // request index
+  int32_t pad[5];
+};
+static_assert(sizeof(PaItem) == 64, "PaItem must be 64 bytes");
+
+// Plan buffer layout: PaItem items[num_items]; int32 row_nsplit[total_rows].
+inline int64_t plan_bytes_for(int64_t items, int64_t rows) { return items * 64 + rows * 4; }
+
+// Tile configuration of a stage-1 launch (packed into pa_plan_info.variant).
+struct KernelCfg {
+  int dh;        // 128 or 256
+  int qf8;       // q is e4m3 (fp8 MFMA for q.k)
+  int kvf8;      // KV is e4m3
+  int pt;        // per-(token, KV head) scales
+  int wq;        // waves splitting the 16-row query blocks (1, 2, 4); 4/wq waves split tokens
+  int nqb;       // 16-row query blocks per wave
+};
+inline int32_t pack_cfg(const KernelCfg& c) {
+  return (c.dh == 256 ? 1 : 0) | (c.qf8 << 1) | (c.kvf8 << 2) | (c.pt << 3) | (c.wq << 4) | (c.nqb << 8);
+}
+inline KernelCfg unpack_cfg(int32_t v) {
+  KernelCfg c;
+  c.dh = (v & 1) ? 256 : 128; c.qf8 = (v >> 1) & 1; c.kvf8 = (v >> 2) & 1; c.pt = (v >> 3) & 1;
+  c.wq = (v >> 4) & 15; c.nqb = (v >> 8) & 15;
+  return c;
+}
+
+constexpr int kSplitAlign = 64;     // split boundaries are multiples of this many tokens
+constexpr int kMaxSplits = 1024;
+
+struct Stage1Args {
+  const PaItem* items;
+  const void* q; const float* q_scale;
+  const void* k; const void* v;
+  int64_t kv_sp, kv_sh, kv_ss;          // element strides (page, head, slot)
+  const float* k_scale; const float* v_scale;
+  int64_t sc_sp, sc_sh, sc_ss;
+  const int32_t* page_indices;
+  float sm_scale;
+  float* partial_o; float* partial_lse;
+  void* out; int out_bf16;
+  int hq, group, page_shift, s_max;
+};
+
+struct MergeArgs {
+  const int32_t* row_nsplit;
+  const float* partial_o; const float* partial_lse;
+  void* out; int out_bf16; float* out_lse;
+  int total_rows, hq, dh, s_max;
+};
+
+struct GatherArgs {
+  const PaItem* items; const int32_t* page_indices;
+  int64_t* phys_out; const int64_t* kv_tok_offset;
+  int page_shift;
+};
+
+// Launchers (defined in the .hip files); return a hipError_t as int.
+int launch_stage1(const KernelCfg& cfg, const Stage1Args& a, int num_items, void* stream);
+int launch_merge(const MergeArgs& a, void* stream);
+int launch_gather(const GatherArgs& a, int num_items, void* stream);
+int launch_quant(const void* src, int src_bf16, int64_t n_rows, int head_dim, int per_tensor,
+                 uint8_t* dst, float* scale, void* stream);
+bool stage1_cfg_supported(const KernelCfg& cfg);
+
+}  // namespace pa

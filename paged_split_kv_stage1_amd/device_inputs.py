@@ -1,0 +1,82 @@
+"""Puts a synthetic workload on the GPU in the layouts the kernels read.
+
+bf16 caches are uploaded as they are; FP8 caches and FP8 queries are produced on
+the device by the library's own quantiser (pa_kv_quantize_fp8).  Slots that hold no
+token (the tail of each request's last page) are then overwritten with NaN bit
+patterns, together with their per-token scales, so that any read of them shows.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+from ._lib import pa_kv_quantize_fp8
+from .inputs import BF16_NAN_BITS, E4M3_NAN_CODE, Workload
+
+
+@dataclasses.dataclass
+class DeviceInputs:
+    q: torch.Tensor                  # bf16 [T, Hq, d] or uint8 codes
+    q_scale: Optional[torch.Tensor]  # float32 [1] for FP8 queries
+    k: torch.Tensor                  # bf16 or uint8, layout HPD [pages, Hkv, P, d] or PHD [pages, P, Hkv, d]
+    v: torch.Tensor
+    k_scale: Optional[torch.Tensor]  # float32 [1] (per tensor) or [pages, Hkv, P] / [pages, P, Hkv]
+    v_scale: Optional[torch.Tensor]
+    page_indices: torch.Tensor       # int32
+    layout: str
+    kv_layout: tuple                 # element strides (page, head, slot)
+    scale_layout: Optional[tuple]
+
+
+def _strides(layout: str, Hkv: int, P: int, d: int):
+    if layout == "HPD":
+        return (Hkv * P * d, P * d, d), (Hkv * P, P, 1)
+    return (P * Hkv * d, d, Hkv * d), (P * Hkv, 1, Hkv)
+
+
+def _quantize(src_bf16: torch.Tensor, mode: str, d: int, device):
+    n_rows = src_bf16.numel() // d
+    codes = torch.empty(src_bf16.shape, dtype=torch.uint8, device=device)
+    scale = torch.empty(1 if mode == "per_tensor" else n_rows, dtype=torch.float32, device=device)
+    pa_kv_quantize_fp8(src_bf16, "bf16", n_rows, d, mode, codes, scale)
+    if mode == "per_token_head":
+        scale = scale.view(src_bf16.shape[:-1])
+    return codes, scale
+
+
+def to_device(w: Workload, device="cuda", layout: str = "HPD") -> DeviceInputs:
+    d, P, Hkv = w.head_dim, w.page_size, w.num_kv_heads
+    kv_layout, sc_layout = _strides(layout, Hkv, P, d)
+    k_src, v_src = w.k, w.v
+    if layout == "PHD":
+        k_src = k_src.permute(0, 2, 1, 3).contiguous()
+        v_src = v_src.permute(0, 2, 1, 3).contiguous()
+    unused = torch.from_numpy(w.unused_slots).to(device)
+    m4 = unused[:, None, :, None] if layout == "HPD" else unused[:, :, None, None]
+    m3 = unused[:, None, :] if layout == "HPD" else unused[:, :, None]
+    k_scale = v_scale = None
+    if w.kv_dtype == "bf16":
+        k = k_src.to(device)
+        v = v_src.to(device)
+        k.view(torch.int16).masked_fill_(m4.expand(k.shape), BF16_NAN_BITS)
+        v.view(torch.int16).masked_fill_(m4.expand(v.shape), BF16_NAN_BITS)
+    else:
+        k, k_scale = _quantize(k_src.to(device), w.kv_scale_mode, d, device)
+        v, v_scale = _quantize(v_src.to(device), w.kv_scale_mode, d, device)
+        k.masked_fill_(m4.expand(k.shape), E4M3_NAN_CODE)
+        v.masked_fill_(m4.expand(v.shape), E4M3_NAN_CODE)
+        if w.kv_scale_mode == "per_token_head":
+            k_scale.masked_fill_(m3.expand(k_scale.shape), float("nan"))
+            v_scale.masked_fill_(m3.expand(v_scale.shape), float("nan"))
+    q_scale = None
+    if w.q_dtype == "fp8":
+        q, q_scale = _quantize(w.q.to(device), "per_tensor", d, device)
+    else:
+        q = w.q.to(device)
+    return DeviceInputs(q=q, q_scale=q_scale, k=k, v=v, k_scale=k_scale, v_scale=v_scale,
+                        page_indices=torch.from_numpy(np.ascontiguousarray(w.page_indices)).to(device),
+                        layout=layout, kv_layout=kv_layout,
+                        scale_layout=sc_layout if w.kv_scale_mode == "per_token_head" else None)

@@ -1,0 +1,197 @@
+"""CPU tests of the C ABI: the library loads and exports every declared entry point,
+the planner's work list covers each request's visible tokens exactly once, and
+malformed or unsupported inputs return the documented status without launching."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from paged_split_kv_stage1_amd import _lib
+from paged_split_kv_stage1_amd._lib import (PA_ERR_INSUFFICIENT_WORKSPACE, PA_ERR_INVALID_ARGUMENT,
+                                            PA_ERR_UNSUPPORTED, PaError, pa_plan_splits)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "pa.h")).read()
+    declared = set(re.findall(r"^(?:pa_status|const char\*)\s+(pa_\w+)\(", header, flags=re.M))
+    assert {"pa_plan_splits", "pa_decode_stage1", "pa_decode_merge", "pa_kv_quantize_fp8",
+            "pa_debug_gather", "pa_last_error"} <= declared
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _plan(B=2, rows=(1, 4), kv=(100, 3000), window=None, R=8, P=16, Hq=16, Hkv=2, d=256, q="bf16", kvd="bf16",
+          mode="none", cus=256, max_splits=0, force=0):
+    rows = np.asarray(rows)
+    kv = np.asarray(kv)
+    qo = np.concatenate([[0], np.cumsum(rows)])
+    kvi = np.concatenate([[0], np.cumsum((kv + P - 1) // P)])
+    return pa_plan_splits(qo, kvi, kv, window, R, P, Hq, Hkv, d, q, kvd, mode, num_cus=cus, max_splits=max_splits,
+                          force_splits=force)
+
+
+def _items(info, plan):
+    n = info.num_items
+    return plan[: n * 64].view(np.int32).reshape(n, 16), plan[n * 64:].view(np.int32)
+
+
+def _check_cover(info, plan, rows, kv, window, Hkv):
+    it, row_ns = _items(info, plan)
+    qo = np.concatenate([[0], np.cumsum(rows)])
+    for b in range(len(kv)):
+        n, L = rows[b], kv[b]
+        W = 0 if window is None else window[b]
+        lo = max(0, L - n - W + 1) if W > 0 else 0
+        sel_b = it[it[:, 10] == b]
+        assert np.all(sel_b[:, 7] == sel_b[0, 7])                  # same nsplit for the request
+        assert np.all(row_ns[qo[b]:qo[b + 1]] == sel_b[0, 7])
+        for g in range(Hkv):
+            sel = sel_b[sel_b[:, 5] == g]
+            sel = sel[np.argsort(sel[:, 6])]
+            assert sel[:, 6].tolist() == list(range(len(sel)))
+            assert sel[0, 8] <= lo and sel[0, 8] % 64 == 0
+            assert np.all(sel[:-1, 9] == sel[1:, 8])                 # contiguous, no overlap
+            assert sel[-1, 9] == L
+            assert np.all(sel[:, 9] >= sel[:, 8])
+            assert np.all(sel[:, 0] == qo[b]) and np.all(sel[:, 1] == n) and np.all(sel[:, 2] == L)
+
+
+def test_plan_covers_visible_tokens_exactly_once():
+    rows, kv, win = [1, 4, 8, 2], [100, 3000, 8, 70000], [0, 64, 0, 5]
+    info, plan = _plan(B=4, rows=rows, kv=kv, window=win)
+    _check_cover(info, plan, np.array(rows), np.array(kv), win, 2)
+    assert info.total_rows == sum(rows)
+    assert info.plan_bytes == info.num_items * 64 + sum(rows) * 4
+    assert info.partial_o_bytes == (sum(rows) * 16 * info.max_splits * 256 * 4 if info.max_splits > 1 else 0)
+    info2, plan2 = _plan(B=4, rows=rows, kv=kv, window=[0, 0, 0, 0])
+    assert info2.max_splits > 1 and info2.needs_merge
+    assert info2.partial_o_bytes == sum(rows) * 16 * info2.max_splits * 256 * 4
+    _check_cover(info2, plan2, np.array(rows), np.array(kv), None, 2)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.data())
+def test_plan_properties(data):
+    B = data.draw(st.integers(1, 12))
+    rows = np.array(data.draw(st.lists(st.integers(1, 8), min_size=B, max_size=B)))
+    kv = np.array([r + data.draw(st.integers(0, 40000)) for r in rows])
+    win = data.draw(st.one_of(st.none(), st.lists(st.sampled_from([0, 1, 7, 64, 1000]), min_size=B, max_size=B)))
+    cus = data.draw(st.sampled_from([1, 8, 256, 304]))
+    cap = data.draw(st.sampled_from([0, 1, 3, 64]))
+    Hkv = data.draw(st.sampled_from([1, 2, 8]))
+    info, plan = _plan(B=B, rows=rows, kv=kv, window=win, cus=cus, max_splits=cap, Hq=Hkv * 8, Hkv=Hkv, d=128)
+    _check_cover(info, plan, rows, kv, win, Hkv)
+    if cap:
+        assert info.max_splits <= cap
+    it, _ = _items(info, plan)
+    cost = (it[:, 9] - it[:, 8]).astype(np.int64) * (64 + it[:, 1] * 8)
+    assert np.all(cost[:-1] >= cost[1:])                               # heaviest first
+
+
+def test_force_splits_gives_exact_count():
+    info, plan = _plan(rows=[1, 1], kv=[512, 70], force=4)
+    it, row_ns = _items(info, plan)
+    assert info.num_items == 2 * 2 * 4 and info.max_splits == 4
+    assert row_ns.tolist() == [4, 4]
+
+
+def test_single_split_plan_needs_no_merge():
+    info, _ = _plan(rows=[1], kv=[64], B=1)
+    assert info.max_splits == 1 and not info.needs_merge and info.partial_o_bytes == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(R=9, rows=[9, 1]), PA_ERR_UNSUPPORTED),
+    (dict(d=64), PA_ERR_UNSUPPORTED),
+    (dict(d=192), PA_ERR_UNSUPPORTED),
+    (dict(Hq=15), PA_ERR_INVALID_ARGUMENT),
+    (dict(rows=[5, 1], kv=[4, 100]), PA_ERR_INVALID_ARGUMENT),
+    (dict(rows=[0, 1]), PA_ERR_INVALID_ARGUMENT),
+    (dict(R=2, rows=[3, 1]), PA_ERR_INVALID_ARGUMENT),
+    (dict(window=[-1, 0]), PA_ERR_INVALID_ARGUMENT),
+    (dict(q="fp8"), PA_ERR_UNSUPPORTED),
+    (dict(mode="per_tensor"), PA_ERR_INVALID_ARGUMENT),
+    (dict(kvd="fp8"), PA_ERR_INVALID_ARGUMENT),
+    (dict(P=24), PA_ERR_UNSUPPORTED),
+    (dict(Hq=128, Hkv=1), PA_ERR_UNSUPPORTED),              # 8 rows x group 128 exceeds one tile
+    (dict(force=5, max_splits=4), PA_ERR_INVALID_ARGUMENT),
+])
+def test_plan_errors(kw, status):
+    with pytest.raises(PaError) as e:
+        _plan(**kw)
+    assert e.value.status == status
+
+
+def test_plan_rejects_inconsistent_page_counts():
+    with pytest.raises(PaError) as e:
+        pa_plan_splits([0, 1], [0, 3], [100], None, 1, 16, 8, 1, 128, "bf16", "bf16", "none", num_cus=8)
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT
+    with pytest.raises(PaError) as e:
+        pa_plan_splits([1, 2], [0, 7], [100], None, 1, 16, 8, 1, 128, "bf16", "bf16", "none", num_cus=8)
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT
+
+
+def test_plan_buffer_too_small():
+    L = _lib.lib()
+    qo = (ctypes.c_int32 * 2)(0, 1)
+    kvi = (ctypes.c_int32 * 2)(0, 4)
+    kvl = (ctypes.c_int32 * 1)(64)
+    a = _lib.PlanArgs(1, qo, kvi, kvl, None, 1, 16, 8, 1, 128, 0, 0, 0, 8, 0, 0)
+    info = _lib.PlanInfo()
+    buf = (ctypes.c_uint8 * 8)()
+    st_ = L.pa_plan_splits(ctypes.byref(a), ctypes.addressof(buf), 8, ctypes.byref(info))
+    assert st_ == PA_ERR_INSUFFICIENT_WORKSPACE and info.plan_bytes > 8
+    assert b"plan buffer" in L.pa_last_error()
+
+
+def test_stage1_validates_before_launch():
+    info, _ = _plan(rows=[1, 1], kv=[512, 70])
+    lay = (16 * 256 * 2, 16 * 256, 256)
+    fake = 1 << 20        # never dereferenced: validation fails first
+    with pytest.raises(PaError) as e:          # misaligned cache pointer
+        _lib.pa_decode_stage1(info, fake, fake, None, fake + 8, fake, lay, None, None, None, fake, 0.1, fake, fake,
+                              fake, "bf16")
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT
+    with pytest.raises(PaError) as e:          # stride not a multiple of 16 bytes
+        _lib.pa_decode_stage1(info, fake, fake, None, fake, fake, (1000, 8, 4), None, None, None, fake, 0.1, fake,
+                              fake, fake, "bf16")
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT
+    with pytest.raises(PaError) as e:          # missing output
+        _lib.pa_decode_stage1(info, fake, fake, None, fake, fake, lay, None, None, None, fake, 0.1, fake, fake, None,
+                              "bf16")
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT
+    with pytest.raises(PaError) as e:          # bad output dtype
+        _lib.pa_decode_stage1(info, fake, fake, None, fake, fake, lay, None, None, None, fake, 0.1, fake, fake, fake,
+                              "fp8")
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT
+
+
+def test_fp8_kv_needs_scales():
+    info, _ = _plan(rows=[1, 1], kv=[512, 70], kvd="fp8", mode="per_token_head")
+    fake = 1 << 20
+    with pytest.raises(PaError) as e:
+        _lib.pa_decode_stage1(info, fake, fake, None, fake, fake, (4096, 256, 256), None, None, (32, 16, 1), fake,
+                              0.1, fake, fake, fake, "bf16")
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT
+
+
+def test_quantize_validates():
+    fake = 1 << 20
+    with pytest.raises(PaError) as e:
+        _lib.pa_kv_quantize_fp8(fake, "bf16", 10, 96, "per_token_head", fake, fake)
+    assert e.value.status == PA_ERR_UNSUPPORTED
+    with pytest.raises(PaError) as e:
+        _lib.pa_kv_quantize_fp8(fake, "bf16", 10, 128, "none", fake, fake)
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT
+
+
+def test_merge_without_splits_is_a_noop():
+    info, _ = _plan(rows=[1], kv=[64], B=1)
+    fake = 1 << 20
+    _lib.pa_decode_merge(info, fake, None, None, fake, "bf16")      # launches nothing, returns OK
