@@ -158,7 +158,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     s1 = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3      # us
-    mg = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    if pd.info.needs_merge:
+        mg = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    else:                      # no merge launch: the second event pair brackets nothing
+        mg = np.zeros_like(s1)
     tot = s1 + mg
 
     def iqm(x):

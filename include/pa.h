@@ -76,7 +76,7 @@ typedef struct {
   const int32_t* kv_len;       /* [B] tokens in the cache, including the new rows; >= n_b   */
   const int32_t* window;       /* [B] sliding window in keys (0 = none), or NULL (none)      */
   int32_t max_q_len;           /* upper bound of n_b; must be <= 8                          */
-  int32_t page_size;           /* tokens per page: 16, 32 or 64                             */
+  int32_t page_size;           /* tokens per page: a power of two in [16, 1024]             */
   int32_t num_q_heads;         /* Hq                                                        */
   int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0                                        */
   int32_t head_dim;            /* 128 or 256                                                */
@@ -113,7 +113,7 @@ typedef struct {
  * copies plan_host to a device buffer of info->plan_bytes bytes before stage 1.
  * Errors: INVALID_ARGUMENT (non-monotone CSR, n_b > kv_len, kv_indptr inconsistent
  * with kv_len, Hq % Hkv != 0, bad enum), UNSUPPORTED (max_q_len > 8, head_dim not
- * 128/256, page size not 16/32/64, rows x group too large for one tile, dtype
+ * 128/256, page size not a power of two in [16, 1024], rows x group too large for one tile, dtype
  * combination), INSUFFICIENT_WORKSPACE (plan_capacity < info->plan_bytes). */
 pa_status pa_plan_splits(const pa_plan_args* args, void* plan_host, size_t plan_capacity,
                          pa_plan_info* info);

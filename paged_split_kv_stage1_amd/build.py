@@ -17,6 +17,9 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # keep hipcc from emitting packed fp32 ops (v_pk_*_f32)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # keep MFMA accumulators in VGPRs: the online-softmax rescale then multiplies
+         # them in place instead of copying AGPR <-> VGPR every tile
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <functional>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -53,11 +54,75 @@ bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
   c->qf8 = a.q_dtype == PA_DTYPE_FP8_E4M3;
   c->kvf8 = a.kv_dtype == PA_DTYPE_FP8_E4M3;
   c->pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD;
-  if (nqb <= 1) { c->wq = 1; c->nqb = 1; }
+  if (nqb <= 1) { c->wq = (c->dh == 256 && !c->kvf8) ? 2 : 1; c->nqb = 1; }
   else if (nqb == 2) { c->wq = 2; c->nqb = 1; }
   else if (nqb <= 4) { c->wq = 4; c->nqb = 1; }
   else { c->wq = 4; c->nqb = (nqb + 3) / 4; }
   return stage1_cfg_supported(*c);
+}
+
+// ---- split-count cost model --------------------------------------------------------
+// Stage 1 is HBM-bound: a work item costs its KV bytes (plus its partial-output
+// write when the request is split, plus a fixed prologue) at one CU's share of the
+// bandwidth; items are placed longest-first on the least loaded CU; the merge reads
+// every partial back.  The candidate split length with the smallest estimated step
+// time wins (ties go to fewer, longer splits).
+constexpr double kHbmBytesPerS = 8.0e12;     // MI355X HBM3E
+constexpr double kItemOverheadS = 1.5e-6;    // item prologue + pipeline fill
+constexpr double kMergeBytesPerS = 4.0e12;   // partials are re-read from the last-level cache
+constexpr double kMergeLaunchS = 3.0e-6;
+
+void choose_splits(const pa_plan_args& a, const std::vector<int>& begin, const std::vector<int>& span,
+                   int num_cus, int split_cap, std::vector<int>* nsp) {
+  const int B = a.batch;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const double kv_tok = 2.0 * a.head_dim * (a.kv_dtype == PA_DTYPE_FP8_E4M3 ? 1 : 2) +
+                        (a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD ? 8 : 0);
+  const double bw_cu = kHbmBytesPerS / num_cus;
+  int max_blk = 1;
+  for (int b = 0; b < B; ++b) max_blk = std::max(max_blk, (span[b] + kSplitAlign - 1) / kSplitAlign);
+  // candidate split lengths in 64-token blocks: geometric, plus the longest span
+  std::vector<int> cand;
+  for (double c = 1.0; c < max_blk; c *= 1.25) {
+    const int k = (int)c;
+    if (cand.empty() || cand.back() != k) cand.push_back(k);
+  }
+  cand.push_back(max_blk);
+  std::vector<int> best(B, 1), cur(B);
+  double best_t = 1e30;
+  std::vector<std::pair<double, int>> groups;       // (item cost, item count)
+  std::vector<double> heap;
+  for (int c : cand) {
+    groups.clear();
+    double merge_bytes = 0;
+    for (int b = 0; b < B; ++b) {
+      const int nblk = (span[b] + kSplitAlign - 1) / kSplitAlign;
+      int sb = (nblk + c - 1) / c;
+      sb = std::max(1, std::min(sb, split_cap));
+      cur[b] = sb;
+      const int n = a.qo_indptr[b + 1] - a.qo_indptr[b];
+      const double part = sb > 1 ? (double)n * G * (a.head_dim + 1) * 4.0 : 0.0;
+      const double tok = (double)span[b] / sb;
+      groups.push_back({(tok * kv_tok + part) / bw_cu + kItemOverheadS, sb * a.num_kv_heads});
+      merge_bytes += part * sb * a.num_kv_heads;
+    }
+    std::sort(groups.begin(), groups.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+    heap.assign(num_cus, 0.0);                       // min-heap of CU loads
+    for (const auto& gi : groups) {
+      for (int k = 0; k < gi.second; ++k) {
+        std::pop_heap(heap.begin(), heap.end(), std::greater<double>());
+        heap.back() += gi.first;
+        std::push_heap(heap.begin(), heap.end(), std::greater<double>());
+      }
+    }
+    const double makespan = *std::max_element(heap.begin(), heap.end());
+    const double t = makespan + (merge_bytes > 0 ? merge_bytes / kMergeBytesPerS + kMergeLaunchS : 0.0);
+    if (t <= best_t * (1 + 1e-9)) {
+      best_t = t;
+      best = cur;
+    }
+  }
+  *nsp = best;
 }
 
 }  // namespace
@@ -83,8 +148,8 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   if (a->head_dim != 128 && a->head_dim != 256)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d: only 128 and 256 are supported", a->head_dim);
   const int page_shift = ilog2_exact(a->page_size);
-  if (page_shift < 0 || a->page_size > 1024)
-    return fail(PA_ERR_UNSUPPORTED, "page_size %d: must be a power of two <= 1024", a->page_size);
+  if (page_shift < 4 || a->page_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "page_size %d: must be a power of two in [16, 1024]", a->page_size);
   if (a->q_dtype != PA_DTYPE_BF16 && a->q_dtype != PA_DTYPE_FP8_E4M3)
     return fail(PA_ERR_INVALID_ARGUMENT, "q_dtype must be BF16 or FP8_E4M3");
   if (a->kv_dtype != PA_DTYPE_BF16 && a->kv_dtype != PA_DTYPE_FP8_E4M3)
@@ -154,16 +219,7 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   if (a->force_splits > 0) {
     for (int b = 0; b < B; ++b) nsp[b] = a->force_splits;
   } else {
-    // Enough work items to give every CU a few, but never splits so short that the
-    // partial-output traffic dominates (>= 256 tokens per split).
-    const int64_t target_items = 4LL * num_cus;
-    int64_t chunk = (total_tok + target_items - 1) / target_items;
-    chunk = std::max<int64_t>(chunk, 256);
-    chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
-    for (int b = 0; b < B; ++b) {
-      int64_t s = (span[b] + chunk - 1) / chunk;
-      nsp[b] = (int)std::max<int64_t>(1, std::min<int64_t>(s, split_cap));
-    }
+    choose_splits(*a, begin, span, num_cus, split_cap, &nsp);
   }
   int s_max = 1;
   int64_t n_items = 0;

@@ -30,25 +30,84 @@ namespace pa {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB>
+template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB, int NS>
 struct S1Cfg {
   static constexpr int WT = 4 / WQ;                 // waves splitting the tokens of a tile
   static constexpr int BN = 32 * WT;                // tokens per tile
   static constexpr int KVB = KVF8 ? 1 : 2;          // bytes per cached element
-  static constexpr int ROWB = DH * KVB + 32;        // padded LDS row stride (bytes)
-  static constexpr int TILEB = BN * ROWB;
   static constexpr int CPR = DH * KVB / 16;         // 16-byte chunks per token row
-  static constexpr int CPT = BN * CPR / 256;        // chunks per thread per tile (K or V)
+  static constexpr int KTB = BN * DH * KVB;         // bytes of one K (or V) tile
+  static constexpr int NK = KTB / 4096;             // 1 KiB DMA instructions per wave per K (or V) tile
+  static constexpr int NSI = PT ? (2 * BN) / 64 : 0;// 256 B scale DMA instructions per tile (waves 0..NSI-1)
+  static constexpr int SCB = PT ? 2 * BN * 4 : 0;   // scale bytes per stage: k_scale[BN], v_scale[BN]
+  static constexpr int STAGEB = 2 * KTB + SCB;
+  static constexpr int NPMAX = BN / 16 + 1;         // pages a tile can touch (page size >= 16)
   static constexpr int KC = DH / 32;                // K-steps of q.k
   static constexpr int DB = DH / 16;                // 16-wide d blocks of P.V
   static constexpr bool PV_FP8 = KVF8 && !PT;       // per-tensor FP8 V: fp8 MFMA for P.V
-  static constexpr int SCALEB = PT ? 2 * BN * 4 : 0;
-  static constexpr int MAINB = 2 * TILEB + SCALEB;
+  static constexpr int QSZ = QF8 ? 1 : 2;           // bytes per query element
+  static constexpr int CPRQ = DH * QSZ / 16;         // 16-byte chunks per query row
+  static constexpr int QROWS = 16 * WQ * NQB;        // query rows (rows x heads) one item can hold
+  static constexpr int QB = QROWS * DH * QSZ;        // LDS bytes of the query block
   static constexpr int EPIB = (WT > 1) ? (4 * NQB * DB * 256 * 4 + 4 * NQB * 64 * 2 * 4) : 0;
+  static constexpr int MAINB = NS * STAGEB + QB;
   static constexpr int LDSB = MAINB > EPIB ? MAINB : EPIB;
-  static_assert(CPT >= 1, "tile too small for 256 threads");
+  static_assert(NK >= 1 && KTB % 4096 == 0, "tile must fill whole DMA instructions on all waves");
   static_assert(WT == 1 || NQB == 1, "query blocks per wave > 1 only without token split");
+  static_assert(NS >= 2, "at least double buffering");
 };
+
+// XOR swizzles of the 16-byte chunk index inside a token row, chosen so the MFMA
+// operand reads hit distinct LDS banks: K rows are read 16 tokens x one chunk; bf16
+// V rows by ds_read_b64_tr_b16 (4 tokens x 2 chunks per 16 lanes); fp8 V rows by
+// ds_read_b64_tr_b8 (tokens {0..7, 16..23} + 4g, one chunk).
+template <int CPR>
+__device__ __forceinline__ int swz_k(int t) {
+  if constexpr (CPR >= 16) return t & 15;
+  else return (t >> 1) & 7;
+}
+template <int CPR, bool FP8V>
+__device__ __forceinline__ int swz_v(int t) {
+  if constexpr (!FP8V) return 2 * (t & 7);
+  else if constexpr (CPR == 8) return ((t >> 1) + 4 * ((t >> 4) & 1)) & 7;
+  else return (t & 7) + 8 * ((t >> 4) & 1);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt/lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+template <int PER, int MAXK>
+__device__ __forceinline__ void wait_tiles_after(int k) {
+  // wait until at most k tiles' worth (PER instructions each) of this wave's loads are outstanding
+  if constexpr (MAXK >= 3) { if (k >= 3) { wait_vmcnt<3 * PER>(); return; } }
+  if constexpr (MAXK >= 2) { if (k == 2) { wait_vmcnt<2 * PER>(); return; } }
+  if constexpr (MAXK >= 1) { if (k == 1) { wait_vmcnt<PER>(); return; } }
+  wait_vmcnt<0>();
+}
+
+// Global -> LDS DMA: lane i's 16 (or 4) bytes land at lds + 16 i (or 4 i).  Written
+// as inline assembly on purpose: the compiler then does not order every later LDS
+// read behind all outstanding DMA (it would insert vmcnt(0) and serialise the
+// pipeline); the kernel waits for exactly the tiles it reads with wait_vmcnt.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(PA_LDS const uint8_t*)p;
+}
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+// saddr form: address = 64-bit scalar base + 32-bit per-lane offset
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
 
 template <bool QF8>
 struct QOperand;
@@ -57,20 +116,16 @@ struct QOperand<false> { using T = bf16x8; };
 template <>
 struct QOperand<true> { using T = long; };
 
-template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB>
+template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB, int NS>
 __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
-  using C = S1Cfg<DH, QF8, KVF8, PT, WQ, NQB>;
+  using C = S1Cfg<DH, QF8, KVF8, PT, WQ, NQB, NS>;
   using QT = typename QOperand<QF8>::T;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDSB];
-  uint8_t* Kl = smem;
-  uint8_t* Vl = smem + C::TILEB;
-  float* ksl = reinterpret_cast<float*>(smem + 2 * C::TILEB);
-  float* vsl = ksl + C::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDSB];
 
   const PaItem it = a.items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wq = wave % WQ;
   const int wt = wave / WQ;
   const int L16 = lane & 15;
@@ -80,9 +135,9 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
   const int Mq = it.nrows * G;
   const int tb0 = it.tok_begin;
   const int te = it.tok_end;
+  const int shift = a.page_shift;
 
-  // ---- query operand, per-row limits ------------------------------------------
-  QT qop[NQB][C::KC];
+  // ---- per-row limits ----------------------------------------------------------------
   int lim_lo[NQB], lim_hi[NQB];
   bool qvalid[NQB];
 #pragma unroll
@@ -92,25 +147,10 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
     const int m = 16 * qb + L16;
     const int mr = m < Mq ? m : Mq - 1;
     const int r = mr / G;
-    const int hl = mr - r * G;
     const int p = it.kv_len - it.nrows + r;
     const int lo = it.window > 0 ? max(0, p - it.window + 1) : 0;
     lim_lo[i] = max(lo, tb0);
     lim_hi[i] = min(p, te - 1);
-    const int64_t qrow = ((int64_t)(it.row0 + r) * Hq + (int64_t)it.kvh * G + hl) * DH;
-#pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) {
-      if constexpr (QF8) {
-        long v = 0;
-        if (m < Mq) v = *reinterpret_cast<const long*>(static_cast<const uint8_t*>(a.q) + qrow + kc * 32 + 8 * g);
-        qop[i][kc] = v;
-      } else {
-        bf16x8 v = {};
-        if (m < Mq)
-          v = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + qrow + kc * 32 + 8 * g);
-        qop[i][kc] = v;
-      }
-    }
   }
   // Tokens every real row of the item sees (fast path: no masking inside).
   const int p_first = it.kv_len - it.nrows;
@@ -122,7 +162,7 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
   if constexpr (QF8) qk_scale *= *a.q_scale;
   if constexpr (KVF8 && !PT) qk_scale *= *a.k_scale;
   float out_scale = 1.0f;
-  if constexpr (C::PV_FP8) out_scale = *a.v_scale * (1.0f / 448.0f);
+  if constexpr (C::PV_FP8) out_scale = *a.v_scale;   // P carried x448, and so does l
 
   f32x4 o[NQB][C::DB];
   f32x4 olo[C::PV_FP8 ? NQB : 1][C::PV_FP8 ? C::DB : 1];
@@ -141,130 +181,240 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
       for (int db = 0; db < C::DB; ++db) olo[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- tile staging ----------------------------------------------------------------
+  // ---- tile DMA: global -> LDS, 16 bytes per lane, no VGPR staging ------------------
+  // Position p (16-byte unit) of a stage's K tile holds chunk (p % CPR) ^ swz_k(t) of
+  // token t = p / CPR; V likewise with swz_v.  One DMA instruction covers TPI = 64/CPR
+  // consecutive tokens, which never straddle a page (pages hold >= 16 tokens and
+  // tiles start on 32-token boundaries), so its page and slot are wave-uniform: the
+  // address is a scalar base plus a per-lane offset that does not change between
+  // tiles.  A tile that reaches past the split end takes a per-lane path that clamps
+  // every token to the last valid one (finite data, masked later).
+  constexpr int TPI = 64 / C::CPR;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v);
-  uint4 kst[C::CPT], vst[C::CPT];
-  float ksc = 0.f, vsc = 0.f;
-  auto load_tile = [&](int tile0) {
+  // The page table is read-only for the kernel's lifetime: reading it through the
+  // constant address space lets the compiler use scalar loads, which do not share
+  // the vector-memory counter the DMA pipeline waits on.
+  typedef const int32_t __attribute__((address_space(4))) cint32;
+  const cint32* pidx = (const cint32*)(a.page_indices) + it.page_base;
+  const int64_t head_off = (int64_t)it.kvh * a.kv_sh;
+  const int pmask = (1 << shift) - 1;
+  uint32_t koff[C::NK], voff[C::NK];
 #pragma unroll
-    for (int c = 0; c < C::CPT; ++c) {
-      const int chunk = tid + 256 * c;
-      const int tok = chunk / C::CPR;
-      const int col = chunk % C::CPR;
-      const int j = tile0 + tok;
-      if (j < te) {
-        const int32_t pg = token_page(a.page_indices, it.page_base, j, a.page_shift);
-        const int32_t sl = token_slot(j, a.page_shift);
-        const int64_t off = ((int64_t)pg * a.kv_sp + (int64_t)it.kvh * a.kv_sh + (int64_t)sl * a.kv_ss) * C::KVB + col * 16;
-        kst[c] = *reinterpret_cast<const uint4*>(kbase + off);
-        vst[c] = *reinterpret_cast<const uint4*>(vbase + off);
-      } else {
-        kst[c] = uint4{0u, 0u, 0u, 0u};
-        vst[c] = uint4{0u, 0u, 0u, 0u};
-      }
-    }
+  for (int q = 0; q < C::NK; ++q) {
+    const int lt = lane / C::CPR;
+    const int cpos = lane % C::CPR;
+    const int t = (wave * C::NK + q) * TPI + lt;
+    koff[q] = (uint32_t)(lt * a.kv_ss * C::KVB) + ((cpos ^ swz_k<C::CPR>(t)) << 4);
+    voff[q] = (uint32_t)(lt * a.kv_ss * C::KVB) + ((cpos ^ swz_v<C::CPR, KVF8>(t)) << 4);
+  }
+  auto issue_scales = [&](int tile0, uint8_t* stage) {
     if constexpr (PT) {
-      if (tid < C::BN) {
-        const int j = tile0 + tid;
-        if (j < te) {
-          const int32_t pg = token_page(a.page_indices, it.page_base, j, a.page_shift);
-          const int32_t sl = token_slot(j, a.page_shift);
-          const int64_t so = (int64_t)pg * a.sc_sp + (int64_t)it.kvh * a.sc_sh + (int64_t)sl * a.sc_ss;
-          ksc = a.k_scale[so];
-          vsc = a.v_scale[so];
-        } else {
-          ksc = 0.f;
-          vsc = 0.f;
-        }
+      if (wave < C::NSI) {
+        // k_scale of the tile's BN tokens, then v_scale; pages loaded as scalars
+        int pages[C::NPMAX];
+        const int pg0 = tile0 >> shift;
+        const int pgl = (te - 1) >> shift;
+#pragma unroll
+        for (int k = 0; k < C::NPMAX; ++k) pages[k] = pidx[min(pg0 + k, pgl)];
+        const int f = wave * 64 + lane;
+        const bool is_v = f >= C::BN;
+        const int j = min(tile0 + (is_v ? f - C::BN : f), te - 1);
+        const int sel = (j >> shift) - pg0;
+        int page = pages[0];
+#pragma unroll
+        for (int k = 1; k < C::NPMAX; ++k) page = sel == k ? pages[k] : page;
+        const int64_t so = (int64_t)page * a.sc_sp + (int64_t)it.kvh * a.sc_sh + (int64_t)(j & pmask) * a.sc_ss;
+        lds_dma4((is_v ? a.v_scale : a.k_scale) + so, lds_addr(stage + 2 * C::KTB + wave * 256));
       }
     }
   };
-  auto store_tile = [&]() {
+  auto issue_tile = [&](int tile0, uint8_t* stage) {
+    const bool full = tile0 + C::BN <= te;
 #pragma unroll
-    for (int c = 0; c < C::CPT; ++c) {
-      const int chunk = tid + 256 * c;
-      const int tok = chunk / C::CPR;
-      const int col = chunk % C::CPR;
-      *reinterpret_cast<uint4*>(Kl + tok * C::ROWB + col * 16) = kst[c];
-      *reinterpret_cast<uint4*>(Vl + tok * C::ROWB + col * 16) = vst[c];
-    }
-    if constexpr (PT) {
-      if (tid < C::BN) {
-        ksl[tid] = ksc;
-        vsl[tid] = vsc;
+    for (int q = 0; q < C::NK; ++q) {
+      const int tq = (wave * C::NK + q) * TPI;          // first token of this instruction (in tile)
+      int jb = tile0 + tq;
+      uint32_t ko = koff[q], vo = voff[q];
+      if (!full) {
+        // past the split end: clamp each lane's token to te - 1 (same page as jb,
+        // because an instruction's tokens never straddle a page)
+        jb = min(jb, te - 1);
+        const int lt = lane / C::CPR;
+        const int ltc = min(lt, te - 1 - jb);
+        const uint32_t d = (uint32_t)((lt - ltc) * a.kv_ss * C::KVB);
+        ko -= d;
+        vo -= d;
       }
+      const int32_t page = pidx[jb >> shift];
+      const int64_t row = ((int64_t)page * a.kv_sp + head_off + (int64_t)(jb & pmask) * a.kv_ss) * C::KVB;
+      lds_dma16_s(kbase + row, ko, lds_addr(stage + (wave * C::NK + q) * 1024));
+      lds_dma16_s(vbase + row, vo, lds_addr(stage + C::KTB + (wave * C::NK + q) * 1024));
     }
+    issue_scales(tile0, stage);
   };
+  constexpr int PER_TILE = 2 * C::NK;   // this wave's DMA instructions per tile (+1 if it loads scales)
 
   const int ntiles = te > tb0 ? (te - tb0 + C::BN - 1) / C::BN : 0;
-  if (ntiles > 0) load_tile(tb0);
+
+  // ---- query block -> LDS (DMA, issued before any tile), then into registers --------
+  // Row m = r * G + h of the item is query row (row0 + r), head (kvh * G + h); rows
+  // past Mq repeat the last real row (their results are never stored).
+  uint8_t* qlds = smem + NS * C::STAGEB;
+  {
+    const int qrows = (Mq + 15) & ~15;
+    const int q_instr = qrows * C::CPRQ / 64;
+    const uint8_t* qbase = static_cast<const uint8_t*>(a.q);
+    for (int ins = wave; ins < q_instr; ins += 4) {
+      const int p = ins * 64 + lane;
+      const int m = p / C::CPRQ;
+      const int cpos = p % C::CPRQ;
+      const int mr = m < Mq ? m : Mq - 1;
+      const int r = mr / G;
+      const int hl = mr - r * G;
+      const int64_t qrow = ((int64_t)(it.row0 + r) * Hq + (int64_t)it.kvh * G + hl) * (DH * C::QSZ);
+      lds_dma16(qbase + qrow + ((cpos ^ swz_k<C::CPRQ>(m)) << 4), lds_addr(qlds + ins * 1024));
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < ntiles) issue_tile(tb0 + s * C::BN, smem + s * C::STAGEB);
+  {
+    const int issued = min(NS - 1, ntiles);               // tiles issued after the query block
+    if (PT && wave < C::NSI) wait_tiles_after<PER_TILE + 1, NS - 1>(issued);
+    else wait_tiles_after<PER_TILE, NS - 1>(issued);
+  }
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  QT qop[NQB][C::KC];
+#pragma unroll
+  for (int i = 0; i < NQB; ++i) {
+    const int m = 16 * (wq + WQ * i) + L16;
+    const uint8_t* qrow = qlds + m * (C::CPRQ * 16);
+    const int sq = swz_k<C::CPRQ>(m);
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) {
+      if constexpr (QF8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(qrow + (((2 * kc + (g >> 1)) ^ sq) << 4) + 8 * (g & 1));
+        qop[i][kc] = (long)v.x | ((long)v.y << 32);
+      } else {
+        qop[i][kc] = *reinterpret_cast<const bf16x8*>(qrow + (((4 * kc + g) ^ sq) << 4));
+      }
+    }
+  }
+
+  // Loop-invariant LDS offsets of this lane's operand reads.
+  const int tk0 = wt * 32 + L16;                         // K rows: tokens tk0 and tk0 + 16
+  uint32_t kro[2][C::KC];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) {
+      const int t = tk0 + 16 * tb;
+      if constexpr (!KVF8) kro[tb][kc] = t * (C::CPR * 16) + (((4 * kc + g) ^ swz_k<C::CPR>(t)) << 4);
+      else kro[tb][kc] = t * (C::CPR * 16) + (((2 * kc + (g >> 1)) ^ swz_k<C::CPR>(t)) << 4) + 8 * (g & 1);
+    }
+  // V rows read transposed: bf16 -> two 4-token reads (tokens 4g+j and 16+4g+j);
+  // fp8 -> one 8-token read (tokens {4g..4g+3, 16+4g..16+4g+3}).
+  uint32_t vro[2];
+  {
+    if constexpr (!KVF8) {
+      const int t1 = wt * 32 + 4 * g + (L16 >> 2);
+      vro[0] = t1 * (C::CPR * 16);
+      vro[1] = (t1 + 16) * (C::CPR * 16);
+    } else {
+      const int jr = L16 >> 1;
+      const int tv = wt * 32 + (jr < 4 ? 4 * g + jr : 16 + 4 * g + (jr - 4));
+      vro[0] = tv * (C::CPR * 16);
+      vro[1] = 0;
+    }
+  }
+  auto vaddr = [&](int db, int half) -> uint32_t {
+    if constexpr (!KVF8) {
+      const int t1 = wt * 32 + 4 * g + (L16 >> 2) + 16 * half;
+      const int c = 2 * db + ((L16 & 3) >> 1);
+      return vro[half] + ((c ^ swz_v<C::CPR, false>(t1)) << 4) + 8 * (L16 & 1);
+    } else {
+      const int jr = L16 >> 1;
+      const int tv = wt * 32 + (jr < 4 ? 4 * g + jr : 16 + 4 * g + (jr - 4));
+      return vro[0] + ((db ^ swz_v<C::CPR, true>(tv)) << 4) + 8 * (L16 & 1);
+    }
+  };
+  const bool wave_has_rows = qvalid[0];
+  // exponent offset: per-tensor FP8 V scales P into [0, 448] inside exp2 (the final
+  // normaliser divides the 448 out again because l accumulates the scaled P)
+  constexpr float kPoff = C::PV_FP8 ? 8.807354922057604f : 0.0f;   // log2(448)
 
   for (int ti = 0; ti < ntiles; ++ti) {
     const int tile0 = tb0 + ti * C::BN;
-    store_tile();
-    __syncthreads();
-    if (ti + 1 < ntiles) load_tile(tile0 + C::BN);
+    uint8_t* stage = smem + (ti % NS) * C::STAGEB;
+    {
+      const int later = min(NS - 2, ntiles - 1 - ti);   // tiles issued after this one
+      if (PT && wave < C::NSI) wait_tiles_after<PER_TILE + 1, NS - 2>(later);
+      else wait_tiles_after<PER_TILE, NS - 2>(later);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0): own LDS reads of the last tile done
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    if (ti + NS - 1 < ntiles) issue_tile(tile0 + (NS - 1) * C::BN, smem + ((ti + NS - 1) % NS) * C::STAGEB);
 
+    const uint8_t* Kl = stage;
+    const uint8_t* Vl = stage + C::KTB;
+    const float* ksl = reinterpret_cast<const float*>(stage + 2 * C::KTB);
+    const float* vsl = ksl + C::BN;
     const int c0 = tile0 + wt * 32;          // first token of this wave's 32-token chunk
-    if (c0 < te) {
-      // ---- S^T = K Q^T for 2 x 16 tokens ------------------------------------------
-      f32x4 s[NQB][2];
-#pragma unroll
-      for (int i = 0; i < NQB; ++i) s[i][0] = s[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const uint8_t* krow = Kl + (wt * 32 + tb * 16 + L16) * C::ROWB;
-#pragma unroll
-        for (int kc = 0; kc < C::KC; ++kc) {
-          if constexpr (!KVF8) {
-            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + (kc * 32 + 8 * g) * 2);
-#pragma unroll
-            for (int i = 0; i < NQB; ++i)
-              if (qvalid[i]) s[i][tb] = mfma_bf16(ka, qop[i][kc], s[i][tb]);
-          } else {
-            const uint2 raw = *reinterpret_cast<const uint2*>(krow + kc * 32 + 8 * g);
-            if constexpr (QF8) {
-              const long ka = (long)raw.x | ((long)raw.y << 32);
-#pragma unroll
-              for (int i = 0; i < NQB; ++i)
-                if (qvalid[i]) s[i][tb] = mfma_fp8(ka, qop[i][kc], s[i][tb]);
-            } else {
-              const bf16x8 ka = fp8x8_to_bf16x8(raw.x, raw.y);
-#pragma unroll
-              for (int i = 0; i < NQB; ++i)
-                if (qvalid[i]) s[i][tb] = mfma_bf16(ka, qop[i][kc], s[i][tb]);
-            }
-          }
-        }
-      }
-
-      // ---- scale, mask, online softmax, P operand ------------------------------------
+    if (c0 < te && wave_has_rows) {
       const bool need_mask = !(c0 >= vis_lo_all && c0 + 31 <= vis_hi_all);
       float ks[8], vs[8];
       if constexpr (PT) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          ks[k] = ksl[wt * 32 + 4 * g + k];
-          ks[4 + k] = ksl[wt * 32 + 16 + 4 * g + k];
+          ks[k] = ksl[wt * 32 + 4 * g + k] * qk_scale;
+          ks[4 + k] = ksl[wt * 32 + 16 + 4 * g + k] * qk_scale;
           vs[k] = vsl[wt * 32 + 4 * g + k];
           vs[4 + k] = vsl[wt * 32 + 16 + 4 * g + k];
         }
       }
-      bf16x8 phi[C::PV_FP8 ? 1 : NQB], plo[C::PV_FP8 ? 1 : NQB];
-      long phi8[C::PV_FP8 ? NQB : 1], plo8[C::PV_FP8 ? NQB : 1];
 #pragma unroll
       for (int i = 0; i < NQB; ++i) {
         if (!qvalid[i]) continue;
+        // ---- S^T = K Q^T for 2 x 16 tokens ----------------------------------------
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < C::KC; ++kc) {
+          if constexpr (!KVF8) {
+            const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Kl + kro[0][kc]);
+            const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Kl + kro[1][kc]);
+            s0 = mfma_bf16(k0, qop[i][kc], s0);
+            s1 = mfma_bf16(k1, qop[i][kc], s1);
+          } else {
+            const uint2 r0 = *reinterpret_cast<const uint2*>(Kl + kro[0][kc]);
+            const uint2 r1 = *reinterpret_cast<const uint2*>(Kl + kro[1][kc]);
+            if constexpr (QF8) {
+              s0 = mfma_fp8((long)r0.x | ((long)r0.y << 32), qop[i][kc], s0);
+              s1 = mfma_fp8((long)r1.x | ((long)r1.y << 32), qop[i][kc], s1);
+            } else {
+              s0 = mfma_bf16(fp8x8_to_bf16x8(r0.x, r0.y), qop[i][kc], s0);
+              s1 = mfma_bf16(fp8x8_to_bf16x8(r1.x, r1.y), qop[i][kc], s1);
+            }
+          }
+        }
+        // ---- scale, mask, online softmax -------------------------------------------
         float x[8];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          x[k] = s[i][0][k] * qk_scale;
-          x[4 + k] = s[i][1][k] * qk_scale;
+          x[k] = s0[k];
+          x[4 + k] = s1[k];
         }
+        float xs;                              // score scale still to apply (1 when folded)
         if constexpr (PT) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) x[k] *= ks[k];
+          xs = 1.0f;
+        } else {
+          xs = qk_scale;
         }
         if (need_mask) {
 #pragma unroll
@@ -273,40 +423,47 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
             x[k] = (j >= lim_lo[i] && j <= lim_hi[i]) ? x[k] : -INFINITY;
           }
         }
-        float mx = x[0];
-#pragma unroll
-        for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
-        mx = wave_max_xor_16_32(mx);
+        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        mx = wave_max_xor_16_32(mx) * xs;
         const float mnew = fmaxf(mrun[i], mx);
         const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = fast_exp2(mrun[i] - muse);
-        mrun[i] = mnew;
+        if (__builtin_amdgcn_ballot_w64(mnew != mrun[i]) != 0) {     // lazy rescale
+          const float alpha = fast_exp2(mrun[i] - muse);
+          lrun[i] *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) o[i][db] *= alpha;
+          if constexpr (C::PV_FP8) {
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) olo[i][db] *= alpha;
+          }
+          mrun[i] = mnew;
+        }
+        const float nb = kPoff - muse;
         float pv[8];
-        float ps = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          pv[k] = fast_exp2(x[k] - muse);
-          ps += pv[k];
+          pv[k] = fast_exp2(fmaf(x[k], xs, nb));
+          lrun[i] += pv[k];
         }
-        lrun[i] = lrun[i] * alpha + ps;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) o[i][db] *= alpha;
+        // ---- P operand and O^T += V^T P^T ------------------------------------------
         if constexpr (C::PV_FP8) {
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) olo[i][db] *= alpha;
-          float y[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) y[k] = pv[k] * 448.0f;
-          const uint32_t h0 = f32x4_to_fp8x4(y[0], y[1], y[2], y[3]);
-          const uint32_t h1 = f32x4_to_fp8x4(y[4], y[5], y[6], y[7]);
+          const uint32_t h0 = f32x4_to_fp8x4(pv[0], pv[1], pv[2], pv[3]);
+          const uint32_t h1 = f32x4_to_fp8x4(pv[4], pv[5], pv[6], pv[7]);
           const f32x2 d0 = fp8x2_to_f32x2<false>(h0), d1 = fp8x2_to_f32x2<true>(h0);
           const f32x2 d2 = fp8x2_to_f32x2<false>(h1), d3 = fp8x2_to_f32x2<true>(h1);
-          const uint32_t l0 = f32x4_to_fp8x4((y[0] - d0[0]) * 16.f, (y[1] - d0[1]) * 16.f,
-                                             (y[2] - d1[0]) * 16.f, (y[3] - d1[1]) * 16.f);
-          const uint32_t l1 = f32x4_to_fp8x4((y[4] - d2[0]) * 16.f, (y[5] - d2[1]) * 16.f,
-                                             (y[6] - d3[0]) * 16.f, (y[7] - d3[1]) * 16.f);
-          phi8[i] = (long)h0 | ((long)h1 << 32);
-          plo8[i] = (long)l0 | ((long)l1 << 32);
+          const uint32_t l0 = f32x4_to_fp8x4((pv[0] - d0[0]) * 16.f, (pv[1] - d0[1]) * 16.f,
+                                             (pv[2] - d1[0]) * 16.f, (pv[3] - d1[1]) * 16.f);
+          const uint32_t l1 = f32x4_to_fp8x4((pv[4] - d2[0]) * 16.f, (pv[5] - d2[1]) * 16.f,
+                                             (pv[6] - d3[0]) * 16.f, (pv[7] - d3[1]) * 16.f);
+          const long phi = (long)h0 | ((long)h1 << 32);
+          const long plo = (long)l0 | ((long)l1 << 32);
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
+            const long va = (long)(uint32_t)w[0] | ((long)(uint32_t)w[1] << 32);
+            o[i][db] = mfma_fp8(va, phi, o[i][db]);
+            olo[i][db] = mfma_fp8(va, plo, olo[i][db]);
+          }
         } else {
           bf16x8 hv, lv;
 #pragma unroll
@@ -316,59 +473,31 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
             hv[k] = h;
             lv[k] = (__bf16)(y - (float)h);
           }
-          phi[i] = hv;
-          plo[i] = lv;
-        }
-      }
-
-      // ---- O^T += V^T P^T --------------------------------------------------------------
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        if constexpr (!KVF8) {
-          const uint8_t* b1 = Vl + (wt * 32 + 4 * g + (L16 >> 2)) * C::ROWB + (16 * db + 4 * (L16 & 3)) * 2;
-          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(b1));
-          const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(b1 + 16 * C::ROWB));
-          bf16x8 va;
-          const __bf16* p1 = reinterpret_cast<const __bf16*>(&v1);
-          const __bf16* p2 = reinterpret_cast<const __bf16*>(&v2);
+          for (int db = 0; db < C::DB; ++db) {
+            bf16x8 va;
+            if constexpr (!KVF8) {
+              const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 0)));
+              const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 1)));
+              const __bf16* p1 = reinterpret_cast<const __bf16*>(&v1);
+              const __bf16* p2 = reinterpret_cast<const __bf16*>(&v2);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            va[k] = p1[k];
-            va[4 + k] = p2[k];
-          }
-#pragma unroll
-          for (int i = 0; i < NQB; ++i) {
-            if (!qvalid[i]) continue;
-            o[i][db] = mfma_bf16(va, phi[i], o[i][db]);
-            o[i][db] = mfma_bf16(va, plo[i], o[i][db]);
-          }
-        } else {
-          const int jr = L16 >> 1;
-          const int tok = jr < 4 ? 4 * g + jr : 16 + 4 * g + (jr - 4);
-          const uint8_t* b1 = Vl + (wt * 32 + tok) * C::ROWB + 16 * db + 8 * (L16 & 1);
-          const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(b1));
-          if constexpr (C::PV_FP8) {
-            const long va = (long)(uint32_t)w[0] | ((long)(uint32_t)w[1] << 32);
-#pragma unroll
-            for (int i = 0; i < NQB; ++i) {
-              if (!qvalid[i]) continue;
-              o[i][db] = mfma_fp8(va, phi8[i], o[i][db]);
-              olo[i][db] = mfma_fp8(va, plo8[i], olo[i][db]);
+              for (int k = 0; k < 4; ++k) {
+                va[k] = p1[k];
+                va[4 + k] = p2[k];
+              }
+            } else {
+              const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
+              va = fp8x8_to_bf16x8((uint32_t)w[0], (uint32_t)w[1]);
             }
-          } else {
-            const bf16x8 va = fp8x8_to_bf16x8((uint32_t)w[0], (uint32_t)w[1]);
-#pragma unroll
-            for (int i = 0; i < NQB; ++i) {
-              if (!qvalid[i]) continue;
-              o[i][db] = mfma_bf16(va, phi[i], o[i][db]);
-              o[i][db] = mfma_bf16(va, plo[i], o[i][db]);
-            }
+            o[i][db] = mfma_bf16(va, hv, o[i][db]);
+            o[i][db] = mfma_bf16(va, lv, o[i][db]);
           }
         }
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   // ---- epilogue ------------------------------------------------------------------------
   float ltot[NQB];
@@ -452,14 +581,27 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = o[i][db] * sc;
       if (g == 0)
-        a.partial_lse[th * a.s_max + it.split] = empty ? -INFINITY : (mrun[i] + __log2f(ltot[i])) * kLn2;
+        a.partial_lse[th * a.s_max + it.split] = empty ? -INFINITY : (mrun[i] + __log2f(ltot[i]) - kPoff) * kLn2;
     }
   }
 }
 
+// Pipeline depth: as many LDS stages as fit beside the query block in the CU's
+// 160 KiB, at most 4.
+template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB>
+constexpr int pick_stages() {
+  constexpr int WT = 4 / WQ;
+  constexpr int stage = 2 * 32 * WT * DH * (KVF8 ? 1 : 2) + (PT ? 2 * 32 * WT * 4 : 0);
+  constexpr int qb = 16 * WQ * NQB * DH * (QF8 ? 1 : 2);
+  constexpr int n = (160 * 1024 - qb) / stage;
+  return n > 4 ? 4 : n;
+}
+
 template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB>
 static int launch_one(const Stage1Args& a, int num_items, void* stream) {
-  hipLaunchKernelGGL((stage1_kernel<DH, QF8, KVF8, PT, WQ, NQB>), dim3(num_items), dim3(256), 0,
+  constexpr int NS = pick_stages<DH, QF8, KVF8, PT, WQ, NQB>();
+  static_assert(NS >= 2, "tile configuration does not fit in LDS");
+  hipLaunchKernelGGL((stage1_kernel<DH, QF8, KVF8, PT, WQ, NQB, NS>), dim3(num_items), dim3(256), 0,
                      (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
@@ -476,7 +618,9 @@ constexpr int max_nqb() {
 template <int DH, bool QF8, bool KVF8, bool PT>
 static int dispatch_tiles(const KernelCfg& c, const Stage1Args& a, int n, void* s) {
   constexpr int NMAX = max_nqb<DH, KVF8, PT>();
-  if (c.wq == 1 && c.nqb == 1) return launch_one<DH, QF8, KVF8, PT, 1, 1>(a, n, s);
+  if constexpr (DH == 128 || KVF8) {      // a 128-token bf16 d256 tile pair does not fit twice in LDS
+    if (c.wq == 1 && c.nqb == 1) return launch_one<DH, QF8, KVF8, PT, 1, 1>(a, n, s);
+  }
   if (c.wq == 2 && c.nqb == 1) return launch_one<DH, QF8, KVF8, PT, 2, 1>(a, n, s);
   if (c.wq == 4 && c.nqb == 1) return launch_one<DH, QF8, KVF8, PT, 4, 1>(a, n, s);
   if constexpr (NMAX >= 2) {
@@ -504,7 +648,7 @@ bool stage1_cfg_supported(const KernelCfg& c) {
   if (!c.kvf8 && c.pt) return false;
   const bool pv_fp8 = c.kvf8 && !c.pt;
   const int nmax = c.dh == 128 ? (pv_fp8 ? 2 : 3) : (pv_fp8 ? 1 : 2);
-  if (c.nqb == 1) return c.wq == 1 || c.wq == 2 || c.wq == 4;
+  if (c.nqb == 1) return (c.wq == 1 && (c.dh == 128 || c.kvf8)) || c.wq == 2 || c.wq == 4;
   return c.wq == 4 && c.nqb >= 2 && c.nqb <= nmax;
 }
 

@@ -119,6 +119,7 @@ def test_single_split_plan_needs_no_merge():
     (dict(mode="per_tensor"), PA_ERR_INVALID_ARGUMENT),
     (dict(kvd="fp8"), PA_ERR_INVALID_ARGUMENT),
     (dict(P=24), PA_ERR_UNSUPPORTED),
+    (dict(P=8), PA_ERR_UNSUPPORTED),
     (dict(Hq=128, Hkv=1), PA_ERR_UNSUPPORTED),              # 8 rows x group 128 exceeds one tile
     (dict(force=5, max_splits=4), PA_ERR_INVALID_ARGUMENT),
 ])
