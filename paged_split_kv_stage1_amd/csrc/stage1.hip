@@ -12,17 +12,24 @@
 // (ds_read_b64_tr_b16 / _tr_b8), the LDS-side counterpart of the in-kernel V
 // transpose FP8 tensor cores need (FlashInfer PR #869, item 1).
 //
+// KV tiles stream HBM -> VGPRs (16-byte loads, PD tiles ahead) -> LDS (NS stages);
+// the LDS footprint is kept small enough for two workgroups per CU, so that one
+// workgroup's prologue and tail overlap the other's streaming.
+//
 // Per tile, each wave owns 32 tokens x (its query blocks):
 //   QK:  bf16 MFMA 16x16x32 (bf16 Q; FP8 K upconverted exactly), or fp8 MFMA
 //        16x16x32 when Q is FP8 (exact products);
 //   softmax: scores scaled into the log2 domain with the dequant scales folded in
-//        (FlashInfer PR #869 item 3), per-row causal/window masks, online max/sum;
+//        (FlashInfer PR #869 item 3), per-row causal/window masks, online max/sum,
+//        the O rescale skipped while no row maximum moves;
 //   PV:  bf16 KV -> P split in two bf16 terms (hi + lo); per-token-head FP8 V ->
 //        v_scale folded into P, V upconverted, two bf16 terms; per-tensor FP8 V ->
 //        P requantised to e4m3 after scaling by the format maximum 448 (FlashInfer
 //        PR #869 item 2), as a hi term plus a lo term of the residual x16, with the
-//        per-tensor v_scale / 448 applied in the final normaliser.
+//        per-tensor v_scale applied in the final normaliser.
 // Waves that split the tokens of a tile merge their (max, sum, O) in LDS at the end.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace pa {
@@ -30,31 +37,29 @@ namespace pa {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB, int NS>
+template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB, int NS, int PD>
 struct S1Cfg {
   static constexpr int WT = 4 / WQ;                 // waves splitting the tokens of a tile
   static constexpr int BN = 32 * WT;                // tokens per tile
   static constexpr int KVB = KVF8 ? 1 : 2;          // bytes per cached element
   static constexpr int CPR = DH * KVB / 16;         // 16-byte chunks per token row
+  static constexpr int TPI = 64 / CPR;              // tokens one wave covers per load step
   static constexpr int KTB = BN * DH * KVB;         // bytes of one K (or V) tile
-  static constexpr int NK = KTB / 4096;             // 1 KiB DMA instructions per wave per K (or V) tile
-  static constexpr int NSI = PT ? (2 * BN) / 64 : 0;// 256 B scale DMA instructions per tile (waves 0..NSI-1)
+  static constexpr int CPT = BN * CPR / 256;        // 16-byte chunks per thread per K (or V) tile
   static constexpr int SCB = PT ? 2 * BN * 4 : 0;   // scale bytes per stage: k_scale[BN], v_scale[BN]
   static constexpr int STAGEB = 2 * KTB + SCB;
   static constexpr int NPMAX = BN / 16 + 1;         // pages a tile can touch (page size >= 16)
   static constexpr int KC = DH / 32;                // K-steps of q.k
   static constexpr int DB = DH / 16;                // 16-wide d blocks of P.V
   static constexpr bool PV_FP8 = KVF8 && !PT;       // per-tensor FP8 V: fp8 MFMA for P.V
-  static constexpr int QSZ = QF8 ? 1 : 2;           // bytes per query element
-  static constexpr int CPRQ = DH * QSZ / 16;         // 16-byte chunks per query row
-  static constexpr int QROWS = 16 * WQ * NQB;        // query rows (rows x heads) one item can hold
-  static constexpr int QB = QROWS * DH * QSZ;        // LDS bytes of the query block
   static constexpr int EPIB = (WT > 1) ? (4 * NQB * DB * 256 * 4 + 4 * NQB * 64 * 2 * 4) : 0;
-  static constexpr int MAINB = NS * STAGEB + QB;
+  static constexpr int MAINB = NS * STAGEB;
   static constexpr int LDSB = MAINB > EPIB ? MAINB : EPIB;
-  static_assert(NK >= 1 && KTB % 4096 == 0, "tile must fill whole DMA instructions on all waves");
+  static_assert(CPT >= 1 && (BN * CPR) % 256 == 0, "tile must split evenly over 256 threads");
   static_assert(WT == 1 || NQB == 1, "query blocks per wave > 1 only without token split");
-  static_assert(NS >= 2, "at least double buffering");
+  static_assert(NS == 1 || NS == 2, "one or two LDS stages");
+  static_assert(PD == 1 || PD == 2, "prefetch one or two tiles ahead");
+  static_assert(2 * BN <= 256, "scale loads use one thread per token");
 };
 
 // XOR swizzles of the 16-byte chunk index inside a token row, chosen so the MFMA
@@ -73,42 +78,6 @@ __device__ __forceinline__ int swz_v(int t) {
   else return (t & 7) + 8 * ((t >> 4) & 1);
 }
 
-// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt/lgkmcnt left unconstrained).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-template <int PER, int MAXK>
-__device__ __forceinline__ void wait_tiles_after(int k) {
-  // wait until at most k tiles' worth (PER instructions each) of this wave's loads are outstanding
-  if constexpr (MAXK >= 3) { if (k >= 3) { wait_vmcnt<3 * PER>(); return; } }
-  if constexpr (MAXK >= 2) { if (k == 2) { wait_vmcnt<2 * PER>(); return; } }
-  if constexpr (MAXK >= 1) { if (k == 1) { wait_vmcnt<PER>(); return; } }
-  wait_vmcnt<0>();
-}
-
-// Global -> LDS DMA: lane i's 16 (or 4) bytes land at lds + 16 i (or 4 i).  Written
-// as inline assembly on purpose: the compiler then does not order every later LDS
-// read behind all outstanding DMA (it would insert vmcnt(0) and serialise the
-// pipeline); the kernel waits for exactly the tiles it reads with wait_vmcnt.
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(PA_LDS const uint8_t*)p;
-}
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
-}
-// saddr form: address = 64-bit scalar base + 32-bit per-lane offset
-__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
-}
-
 template <bool QF8>
 struct QOperand;
 template <>
@@ -116,9 +85,12 @@ struct QOperand<false> { using T = bf16x8; };
 template <>
 struct QOperand<true> { using T = long; };
 
-template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB, int NS>
-__global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
-  using C = S1Cfg<DH, QF8, KVF8, PT, WQ, NQB, NS>;
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB, int NS, int PD>
+__global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
+  using C = S1Cfg<DH, QF8, KVF8, PT, WQ, NQB, NS, PD>;
   using QT = typename QOperand<QF8>::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDSB];
 
@@ -136,8 +108,10 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
   const int tb0 = it.tok_begin;
   const int te = it.tok_end;
   const int shift = a.page_shift;
+  const int pmask = (1 << shift) - 1;
 
-  // ---- per-row limits ----------------------------------------------------------------
+  // ---- query operand (registers), per-row limits ---------------------------------------
+  QT qop[NQB][C::KC];
   int lim_lo[NQB], lim_hi[NQB];
   bool qvalid[NQB];
 #pragma unroll
@@ -147,6 +121,7 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
     const int m = 16 * qb + L16;
     const int mr = m < Mq ? m : Mq - 1;
     const int r = mr / G;
+    const int hl = mr - r * G;
     const int p = it.kv_len - it.nrows + r;
     const int lo = it.window > 0 ? max(0, p - it.window + 1) : 0;
     lim_lo[i] = max(lo, tb0);
@@ -181,128 +156,81 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
       for (int db = 0; db < C::DB; ++db) olo[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- tile DMA: global -> LDS, 16 bytes per lane, no VGPR staging ------------------
-  // Position p (16-byte unit) of a stage's K tile holds chunk (p % CPR) ^ swz_k(t) of
-  // token t = p / CPR; V likewise with swz_v.  One DMA instruction covers TPI = 64/CPR
-  // consecutive tokens, which never straddle a page (pages hold >= 16 tokens and
-  // tiles start on 32-token boundaries), so its page and slot are wave-uniform: the
-  // address is a scalar base plus a per-lane offset that does not change between
-  // tiles.  A tile that reaches past the split end takes a per-lane path that clamps
-  // every token to the last valid one (finite data, masked later).
-  constexpr int TPI = 64 / C::CPR;
+  // ---- KV tile loads: HBM -> registers -> LDS ------------------------------------------
+  // Thread chunk i of a tile is 16-byte chunk cpos of token tb_i + lt, where one wave's
+  // 64 lanes cover TPI = 64/CPR consecutive tokens.  Those never straddle a page (pages
+  // hold >= 16 tokens, tiles start on 32-token boundaries), so each load's page and
+  // slot are wave-uniform: a scalar base plus a per-lane offset that does not change
+  // between tiles.  In LDS, position p (16-byte unit) of a K tile holds chunk
+  // (p % CPR) ^ swz_k(t) of token t = p / CPR; V likewise with swz_v.  Tokens past the
+  // split end are clamped to the last valid token (finite data, masked later).
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v);
   // The page table is read-only for the kernel's lifetime: reading it through the
-  // constant address space lets the compiler use scalar loads, which do not share
-  // the vector-memory counter the DMA pipeline waits on.
+  // constant address space lets the compiler use scalar loads.
   typedef const int32_t __attribute__((address_space(4))) cint32;
   const cint32* pidx = (const cint32*)(a.page_indices) + it.page_base;
   const int64_t head_off = (int64_t)it.kvh * a.kv_sh;
-  const int pmask = (1 << shift) - 1;
-  uint32_t koff[C::NK], voff[C::NK];
+  const int lt = lane / C::CPR;
+  const int cpos = lane % C::CPR;
+  const uint32_t goff = (uint32_t)(lt * a.kv_ss * C::KVB) + (cpos << 4);
+  uint32_t kpos[C::CPT], vpos[C::CPT];
 #pragma unroll
-  for (int q = 0; q < C::NK; ++q) {
-    const int lt = lane / C::CPR;
-    const int cpos = lane % C::CPR;
-    const int t = (wave * C::NK + q) * TPI + lt;
-    koff[q] = (uint32_t)(lt * a.kv_ss * C::KVB) + ((cpos ^ swz_k<C::CPR>(t)) << 4);
-    voff[q] = (uint32_t)(lt * a.kv_ss * C::KVB) + ((cpos ^ swz_v<C::CPR, KVF8>(t)) << 4);
+  for (int i = 0; i < C::CPT; ++i) {
+    const int t = (wave * 64 + 256 * i) / C::CPR + lt;
+    kpos[i] = (t * C::CPR + (cpos ^ swz_k<C::CPR>(t))) << 4;
+    vpos[i] = (t * C::CPR + (cpos ^ swz_v<C::CPR, KVF8>(t))) << 4;
   }
-  auto issue_scales = [&](int tile0, uint8_t* stage) {
+  u32x4 kreg[PD][C::CPT], vreg[PD][C::CPT];
+  float sreg[PD];
+  auto load_tile = [&](auto slot_c, int tile0) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    const bool full = tile0 + C::BN <= te;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      int jb = tile0 + (wave * 64 + 256 * i) / C::CPR;   // first token of this load (uniform)
+      uint32_t off = goff;
+      if (!full) {
+        jb = min(jb, te - 1);
+        const int ltc = min(lt, te - 1 - jb);
+        off -= (uint32_t)((lt - ltc) * a.kv_ss * C::KVB);
+      }
+      const int32_t page = pidx[jb >> shift];
+      const int64_t row = ((int64_t)page * a.kv_sp + head_off + (int64_t)(jb & pmask) * a.kv_ss) * C::KVB;
+      kreg[SL][i] = *reinterpret_cast<const u32x4*>(kbase + row + off);
+      vreg[SL][i] = *reinterpret_cast<const u32x4*>(vbase + row + off);
+    }
     if constexpr (PT) {
-      if (wave < C::NSI) {
-        // k_scale of the tile's BN tokens, then v_scale; pages loaded as scalars
+      if (tid < 2 * C::BN) {
         int pages[C::NPMAX];
         const int pg0 = tile0 >> shift;
         const int pgl = (te - 1) >> shift;
 #pragma unroll
         for (int k = 0; k < C::NPMAX; ++k) pages[k] = pidx[min(pg0 + k, pgl)];
-        const int f = wave * 64 + lane;
-        const bool is_v = f >= C::BN;
-        const int j = min(tile0 + (is_v ? f - C::BN : f), te - 1);
+        const bool is_v = tid >= C::BN;
+        const int j = min(tile0 + (is_v ? tid - C::BN : tid), te - 1);
         const int sel = (j >> shift) - pg0;
         int page = pages[0];
 #pragma unroll
         for (int k = 1; k < C::NPMAX; ++k) page = sel == k ? pages[k] : page;
         const int64_t so = (int64_t)page * a.sc_sp + (int64_t)it.kvh * a.sc_sh + (int64_t)(j & pmask) * a.sc_ss;
-        lds_dma4((is_v ? a.v_scale : a.k_scale) + so, lds_addr(stage + 2 * C::KTB + wave * 256));
+        sreg[SL] = (is_v ? a.v_scale : a.k_scale)[so];
       }
     }
   };
-  auto issue_tile = [&](int tile0, uint8_t* stage) {
-    const bool full = tile0 + C::BN <= te;
+  auto store_tile = [&](auto slot_c, uint8_t* stage) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
 #pragma unroll
-    for (int q = 0; q < C::NK; ++q) {
-      const int tq = (wave * C::NK + q) * TPI;          // first token of this instruction (in tile)
-      int jb = tile0 + tq;
-      uint32_t ko = koff[q], vo = voff[q];
-      if (!full) {
-        // past the split end: clamp each lane's token to te - 1 (same page as jb,
-        // because an instruction's tokens never straddle a page)
-        jb = min(jb, te - 1);
-        const int lt = lane / C::CPR;
-        const int ltc = min(lt, te - 1 - jb);
-        const uint32_t d = (uint32_t)((lt - ltc) * a.kv_ss * C::KVB);
-        ko -= d;
-        vo -= d;
-      }
-      const int32_t page = pidx[jb >> shift];
-      const int64_t row = ((int64_t)page * a.kv_sp + head_off + (int64_t)(jb & pmask) * a.kv_ss) * C::KVB;
-      lds_dma16_s(kbase + row, ko, lds_addr(stage + (wave * C::NK + q) * 1024));
-      lds_dma16_s(vbase + row, vo, lds_addr(stage + C::KTB + (wave * C::NK + q) * 1024));
+    for (int i = 0; i < C::CPT; ++i) {
+      *reinterpret_cast<u32x4*>(stage + kpos[i]) = kreg[SL][i];
+      *reinterpret_cast<u32x4*>(stage + C::KTB + vpos[i]) = vreg[SL][i];
     }
-    issue_scales(tile0, stage);
+    if constexpr (PT) {
+      if (tid < 2 * C::BN) reinterpret_cast<float*>(stage + 2 * C::KTB)[tid] = sreg[SL];
+    }
   };
-  constexpr int PER_TILE = 2 * C::NK;   // this wave's DMA instructions per tile (+1 if it loads scales)
 
   const int ntiles = te > tb0 ? (te - tb0 + C::BN - 1) / C::BN : 0;
-
-  // ---- query block -> LDS (DMA, issued before any tile), then into registers --------
-  // Row m = r * G + h of the item is query row (row0 + r), head (kvh * G + h); rows
-  // past Mq repeat the last real row (their results are never stored).
-  uint8_t* qlds = smem + NS * C::STAGEB;
-  {
-    const int qrows = (Mq + 15) & ~15;
-    const int q_instr = qrows * C::CPRQ / 64;
-    const uint8_t* qbase = static_cast<const uint8_t*>(a.q);
-    for (int ins = wave; ins < q_instr; ins += 4) {
-      const int p = ins * 64 + lane;
-      const int m = p / C::CPRQ;
-      const int cpos = p % C::CPRQ;
-      const int mr = m < Mq ? m : Mq - 1;
-      const int r = mr / G;
-      const int hl = mr - r * G;
-      const int64_t qrow = ((int64_t)(it.row0 + r) * Hq + (int64_t)it.kvh * G + hl) * (DH * C::QSZ);
-      lds_dma16(qbase + qrow + ((cpos ^ swz_k<C::CPRQ>(m)) << 4), lds_addr(qlds + ins * 1024));
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < ntiles) issue_tile(tb0 + s * C::BN, smem + s * C::STAGEB);
-  {
-    const int issued = min(NS - 1, ntiles);               // tiles issued after the query block
-    if (PT && wave < C::NSI) wait_tiles_after<PER_TILE + 1, NS - 1>(issued);
-    else wait_tiles_after<PER_TILE, NS - 1>(issued);
-  }
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-  QT qop[NQB][C::KC];
-#pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    const int m = 16 * (wq + WQ * i) + L16;
-    const uint8_t* qrow = qlds + m * (C::CPRQ * 16);
-    const int sq = swz_k<C::CPRQ>(m);
-#pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) {
-      if constexpr (QF8) {
-        const uint2 v = *reinterpret_cast<const uint2*>(qrow + (((2 * kc + (g >> 1)) ^ sq) << 4) + 8 * (g & 1));
-        qop[i][kc] = (long)v.x | ((long)v.y << 32);
-      } else {
-        qop[i][kc] = *reinterpret_cast<const bf16x8*>(qrow + (((4 * kc + g) ^ sq) << 4));
-      }
-    }
-  }
 
   // Loop-invariant LDS offsets of this lane's operand reads.
   const int tk0 = wt * 32 + L16;                         // K rows: tokens tk0 and tk0 + 16
@@ -317,28 +245,15 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
     }
   // V rows read transposed: bf16 -> two 4-token reads (tokens 4g+j and 16+4g+j);
   // fp8 -> one 8-token read (tokens {4g..4g+3, 16+4g..16+4g+3}).
-  uint32_t vro[2];
-  {
-    if constexpr (!KVF8) {
-      const int t1 = wt * 32 + 4 * g + (L16 >> 2);
-      vro[0] = t1 * (C::CPR * 16);
-      vro[1] = (t1 + 16) * (C::CPR * 16);
-    } else {
-      const int jr = L16 >> 1;
-      const int tv = wt * 32 + (jr < 4 ? 4 * g + jr : 16 + 4 * g + (jr - 4));
-      vro[0] = tv * (C::CPR * 16);
-      vro[1] = 0;
-    }
-  }
-  auto vaddr = [&](int db, int half) -> uint32_t {
+  auto vaddr = [&](int db, int half) __attribute__((always_inline)) -> uint32_t {
     if constexpr (!KVF8) {
       const int t1 = wt * 32 + 4 * g + (L16 >> 2) + 16 * half;
       const int c = 2 * db + ((L16 & 3) >> 1);
-      return vro[half] + ((c ^ swz_v<C::CPR, false>(t1)) << 4) + 8 * (L16 & 1);
+      return t1 * (C::CPR * 16) + ((c ^ swz_v<C::CPR, false>(t1)) << 4) + 8 * (L16 & 1);
     } else {
       const int jr = L16 >> 1;
       const int tv = wt * 32 + (jr < 4 ? 4 * g + jr : 16 + 4 * g + (jr - 4));
-      return vro[0] + ((db ^ swz_v<C::CPR, true>(tv)) << 4) + 8 * (L16 & 1);
+      return tv * (C::CPR * 16) + ((db ^ swz_v<C::CPR, true>(tv)) << 4) + 8 * (L16 & 1);
     }
   };
   const bool wave_has_rows = qvalid[0];
@@ -346,155 +261,200 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
   // normaliser divides the 448 out again because l accumulates the scaled P)
   constexpr float kPoff = C::PV_FP8 ? 8.807354922057604f : 0.0f;   // log2(448)
 
-  for (int ti = 0; ti < ntiles; ++ti) {
-    const int tile0 = tb0 + ti * C::BN;
-    uint8_t* stage = smem + (ti % NS) * C::STAGEB;
-    {
-      const int later = min(NS - 2, ntiles - 1 - ti);   // tiles issued after this one
-      if (PT && wave < C::NSI) wait_tiles_after<PER_TILE + 1, NS - 2>(later);
-      else wait_tiles_after<PER_TILE, NS - 2>(later);
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0): own LDS reads of the last tile done
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    if (ti + NS - 1 < ntiles) issue_tile(tile0 + (NS - 1) * C::BN, smem + ((ti + NS - 1) % NS) * C::STAGEB);
-
-    const uint8_t* Kl = stage;
-    const uint8_t* Vl = stage + C::KTB;
-    const float* ksl = reinterpret_cast<const float*>(stage + 2 * C::KTB);
-    const float* vsl = ksl + C::BN;
-    const int c0 = tile0 + wt * 32;          // first token of this wave's 32-token chunk
-    if (c0 < te && wave_has_rows) {
-      const bool need_mask = !(c0 >= vis_lo_all && c0 + 31 <= vis_hi_all);
-      float ks[8], vs[8];
-      if constexpr (PT) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          ks[k] = ksl[wt * 32 + 4 * g + k] * qk_scale;
-          ks[4 + k] = ksl[wt * 32 + 16 + 4 * g + k] * qk_scale;
-          vs[k] = vsl[wt * 32 + 4 * g + k];
-          vs[4 + k] = vsl[wt * 32 + 16 + 4 * g + k];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < NQB; ++i) {
-        if (!qvalid[i]) continue;
-        // ---- S^T = K Q^T for 2 x 16 tokens ----------------------------------------
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < C::KC; ++kc) {
-          if constexpr (!KVF8) {
-            const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Kl + kro[0][kc]);
-            const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Kl + kro[1][kc]);
-            s0 = mfma_bf16(k0, qop[i][kc], s0);
-            s1 = mfma_bf16(k1, qop[i][kc], s1);
-          } else {
-            const uint2 r0 = *reinterpret_cast<const uint2*>(Kl + kro[0][kc]);
-            const uint2 r1 = *reinterpret_cast<const uint2*>(Kl + kro[1][kc]);
-            if constexpr (QF8) {
-              s0 = mfma_fp8((long)r0.x | ((long)r0.y << 32), qop[i][kc], s0);
-              s1 = mfma_fp8((long)r1.x | ((long)r1.y << 32), qop[i][kc], s1);
-            } else {
-              s0 = mfma_bf16(fp8x8_to_bf16x8(r0.x, r0.y), qop[i][kc], s0);
-              s1 = mfma_bf16(fp8x8_to_bf16x8(r1.x, r1.y), qop[i][kc], s1);
-            }
-          }
-        }
-        // ---- scale, mask, online softmax -------------------------------------------
-        float x[8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          x[k] = s0[k];
-          x[4 + k] = s1[k];
-        }
-        float xs;                              // score scale still to apply (1 when folded)
+  auto compute_tile = [&](int tile0, const uint8_t* stage) __attribute__((always_inline)) {
+  const uint8_t* Kl = stage;
+      const uint8_t* Vl = stage + C::KTB;
+      const float* ksl = reinterpret_cast<const float*>(stage + 2 * C::KTB);
+      const float* vsl = ksl + C::BN;
+      const int c0 = tile0 + wt * 32;          // first token of this wave's 32-token chunk
+      if (c0 < te && wave_has_rows) {
+        const bool need_mask = !(c0 >= vis_lo_all && c0 + 31 <= vis_hi_all);
+        float ks[8], vs[8];
         if constexpr (PT) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) x[k] *= ks[k];
-          xs = 1.0f;
-        } else {
-          xs = qk_scale;
-        }
-        if (need_mask) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int j = c0 + (k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4));
-            x[k] = (j >= lim_lo[i] && j <= lim_hi[i]) ? x[k] : -INFINITY;
+  #pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            ks[k] = ksl[wt * 32 + 4 * g + k] * qk_scale;
+            ks[4 + k] = ksl[wt * 32 + 16 + 4 * g + k] * qk_scale;
+            vs[k] = vsl[wt * 32 + 4 * g + k];
+            vs[4 + k] = vsl[wt * 32 + 16 + 4 * g + k];
           }
         }
-        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        mx = wave_max_xor_16_32(mx) * xs;
-        const float mnew = fmaxf(mrun[i], mx);
-        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        if (__builtin_amdgcn_ballot_w64(mnew != mrun[i]) != 0) {     // lazy rescale
-          const float alpha = fast_exp2(mrun[i] - muse);
-          lrun[i] *= alpha;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) o[i][db] *= alpha;
-          if constexpr (C::PV_FP8) {
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) olo[i][db] *= alpha;
-          }
-          mrun[i] = mnew;
-        }
-        const float nb = kPoff - muse;
-        float pv[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          pv[k] = fast_exp2(fmaf(x[k], xs, nb));
-          lrun[i] += pv[k];
-        }
-        // ---- P operand and O^T += V^T P^T ------------------------------------------
-        if constexpr (C::PV_FP8) {
-          const uint32_t h0 = f32x4_to_fp8x4(pv[0], pv[1], pv[2], pv[3]);
-          const uint32_t h1 = f32x4_to_fp8x4(pv[4], pv[5], pv[6], pv[7]);
-          const f32x2 d0 = fp8x2_to_f32x2<false>(h0), d1 = fp8x2_to_f32x2<true>(h0);
-          const f32x2 d2 = fp8x2_to_f32x2<false>(h1), d3 = fp8x2_to_f32x2<true>(h1);
-          const uint32_t l0 = f32x4_to_fp8x4((pv[0] - d0[0]) * 16.f, (pv[1] - d0[1]) * 16.f,
-                                             (pv[2] - d1[0]) * 16.f, (pv[3] - d1[1]) * 16.f);
-          const uint32_t l1 = f32x4_to_fp8x4((pv[4] - d2[0]) * 16.f, (pv[5] - d2[1]) * 16.f,
-                                             (pv[6] - d3[0]) * 16.f, (pv[7] - d3[1]) * 16.f);
-          const long phi = (long)h0 | ((long)h1 << 32);
-          const long plo = (long)l0 | ((long)l1 << 32);
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
-            const long va = (long)(uint32_t)w[0] | ((long)(uint32_t)w[1] << 32);
-            o[i][db] = mfma_fp8(va, phi, o[i][db]);
-            olo[i][db] = mfma_fp8(va, plo, olo[i][db]);
-          }
-        } else {
-          bf16x8 hv, lv;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const float y = PT ? pv[k] * vs[k] : pv[k];
-            const __bf16 h = (__bf16)y;
-            hv[k] = h;
-            lv[k] = (__bf16)(y - (float)h);
-          }
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            bf16x8 va;
+  #pragma unroll
+        for (int i = 0; i < NQB; ++i) {
+          if (!qvalid[i]) continue;
+          // ---- S^T = K Q^T for 2 x 16 tokens ----------------------------------------
+          f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int kc = 0; kc < C::KC; ++kc) {
             if constexpr (!KVF8) {
-              const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 0)));
-              const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 1)));
-              const __bf16* p1 = reinterpret_cast<const __bf16*>(&v1);
-              const __bf16* p2 = reinterpret_cast<const __bf16*>(&v2);
-#pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                va[k] = p1[k];
-                va[4 + k] = p2[k];
-              }
+              const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Kl + kro[0][kc]);
+              const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Kl + kro[1][kc]);
+              s0 = mfma_bf16(k0, qop[i][kc], s0);
+              s1 = mfma_bf16(k1, qop[i][kc], s1);
             } else {
-              const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
-              va = fp8x8_to_bf16x8((uint32_t)w[0], (uint32_t)w[1]);
+              const uint2 r0 = *reinterpret_cast<const uint2*>(Kl + kro[0][kc]);
+              const uint2 r1 = *reinterpret_cast<const uint2*>(Kl + kro[1][kc]);
+              if constexpr (QF8) {
+                s0 = mfma_fp8((long)r0.x | ((long)r0.y << 32), qop[i][kc], s0);
+                s1 = mfma_fp8((long)r1.x | ((long)r1.y << 32), qop[i][kc], s1);
+              } else {
+                s0 = mfma_bf16(fp8x8_to_bf16x8(r0.x, r0.y), qop[i][kc], s0);
+                s1 = mfma_bf16(fp8x8_to_bf16x8(r1.x, r1.y), qop[i][kc], s1);
+              }
             }
-            o[i][db] = mfma_bf16(va, hv, o[i][db]);
-            o[i][db] = mfma_bf16(va, lv, o[i][db]);
+          }
+          // ---- scale, mask, online softmax -------------------------------------------
+          float x[8];
+  #pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            x[k] = s0[k];
+            x[4 + k] = s1[k];
+          }
+          float xs;                              // score scale still to apply (1 when folded)
+          if constexpr (PT) {
+  #pragma unroll
+            for (int k = 0; k < 8; ++k) x[k] *= ks[k];
+            xs = 1.0f;
+          } else {
+            xs = qk_scale;
+          }
+          if (need_mask) {
+  #pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int j = c0 + (k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4));
+              x[k] = (j >= lim_lo[i] && j <= lim_hi[i]) ? x[k] : -INFINITY;
+            }
+          }
+          float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+          mx = wave_max_xor_16_32(mx) * xs;
+          const float mnew = fmaxf(mrun[i], mx);
+          const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+          if (__builtin_amdgcn_ballot_w64(mnew != mrun[i]) != 0) {     // lazy rescale
+            const float alpha = fast_exp2(mrun[i] - muse);
+            lrun[i] *= alpha;
+  #pragma unroll
+            for (int db = 0; db < C::DB; ++db) o[i][db] *= alpha;
+            if constexpr (C::PV_FP8) {
+  #pragma unroll
+              for (int db = 0; db < C::DB; ++db) olo[i][db] *= alpha;
+            }
+            mrun[i] = mnew;
+          }
+          const float nb = kPoff - muse;
+          float pv[8];
+  #pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            pv[k] = fast_exp2(fmaf(x[k], xs, nb));
+            lrun[i] += pv[k];
+          }
+          // ---- P operand and O^T += V^T P^T ------------------------------------------
+          if constexpr (C::PV_FP8) {
+            const uint32_t h0 = f32x4_to_fp8x4(pv[0], pv[1], pv[2], pv[3]);
+            const uint32_t h1 = f32x4_to_fp8x4(pv[4], pv[5], pv[6], pv[7]);
+            const f32x2 d0 = fp8x2_to_f32x2<false>(h0), d1 = fp8x2_to_f32x2<true>(h0);
+            const f32x2 d2 = fp8x2_to_f32x2<false>(h1), d3 = fp8x2_to_f32x2<true>(h1);
+            const uint32_t l0 = f32x4_to_fp8x4((pv[0] - d0[0]) * 16.f, (pv[1] - d0[1]) * 16.f,
+                                               (pv[2] - d1[0]) * 16.f, (pv[3] - d1[1]) * 16.f);
+            const uint32_t l1 = f32x4_to_fp8x4((pv[4] - d2[0]) * 16.f, (pv[5] - d2[1]) * 16.f,
+                                               (pv[6] - d3[0]) * 16.f, (pv[7] - d3[1]) * 16.f);
+            const long phi = (long)h0 | ((long)h1 << 32);
+            const long plo = (long)l0 | ((long)l1 << 32);
+  #pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+              const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
+              const long va = (long)(uint32_t)w[0] | ((long)(uint32_t)w[1] << 32);
+              o[i][db] = mfma_fp8(va, phi, o[i][db]);
+              olo[i][db] = mfma_fp8(va, plo, olo[i][db]);
+            }
+          } else {
+            bf16x8 hv, lv;
+  #pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const float y = PT ? pv[k] * vs[k] : pv[k];
+              const __bf16 h = (__bf16)y;
+              hv[k] = h;
+              lv[k] = (__bf16)(y - (float)h);
+            }
+  #pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+              bf16x8 va;
+              if constexpr (!KVF8) {
+                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 0)));
+                const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 1)));
+                const __bf16* p1 = reinterpret_cast<const __bf16*>(&v1);
+                const __bf16* p2 = reinterpret_cast<const __bf16*>(&v2);
+  #pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  va[k] = p1[k];
+                  va[4 + k] = p2[k];
+                }
+              } else {
+                const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
+                va = fp8x8_to_bf16x8((uint32_t)w[0], (uint32_t)w[1]);
+              }
+              o[i][db] = mfma_bf16(va, hv, o[i][db]);
+              o[i][db] = mfma_bf16(va, lv, o[i][db]);
+            }
           }
         }
       }
+    };
+
+  // One tile: refill the register slot that held it PD tiles ahead, compute it, then
+  // move the next tile from registers to LDS.  FULL steps do this unconditionally,
+  // which keeps the compiler's load-counter bookkeeping exact in the steady state
+  // (a conditional load there makes it wait for every outstanding tile).
+  auto step = [&](auto slot_c, auto full_c, int ti) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    constexpr bool FULL = decltype(full_c)::value != 0;
+    const int tile0 = tb0 + ti * C::BN;
+    if (FULL || ti + PD < ntiles) load_tile(ic<SL>{}, tile0 + PD * C::BN);
+    compute_tile(tile0, smem + (ti % NS) * C::STAGEB);
+    if (FULL || ti + 1 < ntiles) {
+      if constexpr (NS == 1) __syncthreads();
+      store_tile(ic<(SL + 1) % PD>{}, smem + ((ti + 1) % NS) * C::STAGEB);
+      __syncthreads();
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(ic<0>{}, tb0);
+    if constexpr (PD == 2) {
+      if (ntiles > 1) load_tile(ic<1>{}, tb0 + C::BN);
+    }
+  }
+  // Query operand, loaded after the first tiles and waited for completely here: a
+  // load still pending at the loop entry would make every iteration wait for all
+  // outstanding tile loads before its first MFMA.
+#pragma unroll
+  for (int i = 0; i < NQB; ++i) {
+    const int m = 16 * (wq + WQ * i) + L16;
+    const int mr = m < Mq ? m : Mq - 1;                // rows past Mq repeat the last real row
+    const int r = mr / G;
+    const int hl = mr - r * G;
+    const int64_t qrow = ((int64_t)(it.row0 + r) * Hq + (int64_t)it.kvh * G + hl) * DH;
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) {
+      if constexpr (QF8)
+        qop[i][kc] = *reinterpret_cast<const long*>(static_cast<const uint8_t*>(a.q) + qrow + kc * 32 + 8 * g);
+      else
+        qop[i][kc] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + qrow + kc * 32 + 8 * g);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);          // vmcnt(0) lgkmcnt(0)
+  if (ntiles > 0) {
+    store_tile(ic<0>{}, smem);
+    __syncthreads();
+  }
+  int ti = 0;
+  for (; ti + 2 * PD - 1 < ntiles; ti += PD) {         // steady state
+    step(ic<0>{}, ic<1>{}, ti);
+    if constexpr (PD == 2) step(ic<1>{}, ic<1>{}, ti + 1);
+  }
+  for (; ti < ntiles; ti += PD) {                      // drain the last tiles
+    step(ic<0>{}, ic<0>{}, ti);
+    if constexpr (PD == 2) {
+      if (ti + 1 < ntiles) step(ic<1>{}, ic<0>{}, ti + 1);
     }
   }
   __syncthreads();
@@ -586,22 +546,22 @@ __global__ __launch_bounds__(256) void stage1_kernel(Stage1Args a) {
   }
 }
 
-// Pipeline depth: as many LDS stages as fit beside the query block in the CU's
-// 160 KiB, at most 4.
-template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB>
-constexpr int pick_stages() {
-  constexpr int WT = 4 / WQ;
-  constexpr int stage = 2 * 32 * WT * DH * (KVF8 ? 1 : 2) + (PT ? 2 * 32 * WT * 4 : 0);
-  constexpr int qb = 16 * WQ * NQB * DH * (QF8 ? 1 : 2);
-  constexpr int n = (160 * 1024 - qb) / stage;
-  return n > 4 ? 4 : n;
-}
+// LDS stages and register prefetch depth: two stages when two workgroups still fit
+// in the CU's 160 KiB of LDS, else one; two tiles of register prefetch when a tile
+// costs at most 32 VGPRs per thread, else one.
+template <int DH, bool KVF8, bool PT, int WQ>
+struct Pipe {
+  static constexpr int BN = 32 * (4 / WQ);
+  static constexpr int stage = 2 * BN * DH * (KVF8 ? 1 : 2) + (PT ? 2 * BN * 4 : 0);
+  static constexpr int NS = 2 * stage <= 80 * 1024 ? 2 : 1;
+  static constexpr int CPT = BN * DH * (KVF8 ? 1 : 2) / 16 / 256;
+  static constexpr int PD = CPT <= 4 ? 2 : 1;
+};
 
 template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB>
 static int launch_one(const Stage1Args& a, int num_items, void* stream) {
-  constexpr int NS = pick_stages<DH, QF8, KVF8, PT, WQ, NQB>();
-  static_assert(NS >= 2, "tile configuration does not fit in LDS");
-  hipLaunchKernelGGL((stage1_kernel<DH, QF8, KVF8, PT, WQ, NQB, NS>), dim3(num_items), dim3(256), 0,
+  using Pp = Pipe<DH, KVF8, PT, WQ>;
+  hipLaunchKernelGGL((stage1_kernel<DH, QF8, KVF8, PT, WQ, NQB, Pp::NS, Pp::PD>), dim3(num_items), dim3(256), 0,
                      (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
