@@ -52,6 +52,30 @@ def _cpu_model() -> str:
     return platform.processor()
 
 
+KERNEL_SOURCES = ("stage1.hip", "common.hpp", "pa_internal.hpp")
+
+
+def measured_traffic(config: str):
+    """HBM bytes per stage-1 launch from the committed FETCH_SIZE/WRITE_SIZE summary of this
+    workload, or None when there is none or the kernel sources changed since it was taken."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_split_kv_stage1_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    for path in glob.glob(os.path.join(ROOT, "profiles", f"stage1_kernel_{config}_*_hbm_traffic.txt")):
+        fields = {}
+        for line in open(path):
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        if fields.get("kernel_source_sha256") == h.hexdigest() and "traffic_bytes_per_launch" in fields:
+            return int(fields["traffic_bytes_per_launch"])
+    return None
+
+
 def cpu_baseline(w, out_gpu: np.ndarray, budget_s: float):
     """Times the fp64 oracle on a bounded sample (whole requests, in order, until the
     time budget is spent) and compares the GPU output of those requests with it."""
@@ -105,6 +129,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-splits", type=int, default=None)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 256 MiB device-to-device copy first, as a known-size reference for HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
@@ -136,6 +162,14 @@ def main():
 
     def merge():
         pd.merge(out, w.out_dtype, stream=stream)
+
+    if args.calibrate_copy:
+        src = torch.ones(256 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         if not args.no_flush:
@@ -191,7 +225,7 @@ def main():
         "tflops": round(acc["flops"] / (us_step * 1e-6) / 1e12, 3),
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "roofline": {"bound": "hbm", "achieved": round(roof_achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(roof_achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(roof_achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(args.config),
                      "kernel": "stage1_kernel", "bytes_per_launch": s1_bytes},
     }
     if not args.no_cpu_baseline:

@@ -92,9 +92,14 @@ void choose_splits(const pa_plan_args& a, const std::vector<int>& begin, const s
   double best_t = 1e30;
   std::vector<std::pair<double, int>> groups;       // (item cost, item count)
   std::vector<double> heap;
-  for (int c : cand) {
+  // Longest split length (fewest splits) first, so that an equal estimate keeps the
+  // plan with fewer splits.  A candidate whose lower bound -- its work spread evenly
+  // over the CUs, or its longest item, plus its merge -- cannot beat the best estimate
+  // so far is not scheduled at all.
+  for (auto ci = cand.rbegin(); ci != cand.rend(); ++ci) {
+    const int c = *ci;
     groups.clear();
-    double merge_bytes = 0;
+    double merge_bytes = 0, total = 0, longest = 0;
     for (int b = 0; b < B; ++b) {
       const int nblk = (span[b] + kSplitAlign - 1) / kSplitAlign;
       int sb = (nblk + c - 1) / c;
@@ -103,9 +108,14 @@ void choose_splits(const pa_plan_args& a, const std::vector<int>& begin, const s
       const int n = a.qo_indptr[b + 1] - a.qo_indptr[b];
       const double part = sb > 1 ? (double)n * G * (a.head_dim + 1) * 4.0 : 0.0;
       const double tok = (double)span[b] / sb;
-      groups.push_back({(tok * kv_tok + part) / bw_cu + kItemOverheadS, sb * a.num_kv_heads});
+      const double cost = (tok * kv_tok + part) / bw_cu + kItemOverheadS;
+      groups.push_back({cost, sb * a.num_kv_heads});
       merge_bytes += part * sb * a.num_kv_heads;
+      total += cost * sb * a.num_kv_heads;
+      longest = std::max(longest, cost);
     }
+    const double merge_t = merge_bytes > 0 ? merge_bytes / kMergeBytesPerS + kMergeLaunchS : 0.0;
+    if (std::max(total / num_cus, longest) + merge_t >= best_t * (1 - 1e-9)) continue;
     std::sort(groups.begin(), groups.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
     heap.assign(num_cus, 0.0);                       // min-heap of CU loads
     for (const auto& gi : groups) {
@@ -115,9 +125,8 @@ void choose_splits(const pa_plan_args& a, const std::vector<int>& begin, const s
         std::push_heap(heap.begin(), heap.end(), std::greater<double>());
       }
     }
-    const double makespan = *std::max_element(heap.begin(), heap.end());
-    const double t = makespan + (merge_bytes > 0 ? merge_bytes / kMergeBytesPerS + kMergeLaunchS : 0.0);
-    if (t <= best_t * (1 + 1e-9)) {
+    const double t = *std::max_element(heap.begin(), heap.end()) + merge_t;
+    if (t < best_t * (1 - 1e-9)) {
       best_t = t;
       best = cur;
     }
