@@ -62,32 +62,60 @@ bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
 }
 
 // ---- split-count cost model --------------------------------------------------------
-// Stage 1 is HBM-bound: a work item costs its KV bytes (plus its partial-output
-// write when the request is split, plus a fixed prologue) at one CU's share of the
-// bandwidth; items are placed longest-first on the least loaded CU; the merge reads
-// every partial back.  The candidate split length with the smallest estimated step
-// time wins (ties go to fewer, longer splits).
-constexpr double kHbmBytesPerS = 8.0e12;     // MI355X HBM3E
+// Every CU holds two stage-1 workgroups at once (the kernels' LDS and register
+// budgets are sized for that), and a CU running only one of them leaves its memory
+// pipeline half idle.  So the model schedules items onto 2 x num_cus slots, each with
+// half of a CU's share of the HBM bandwidth.  An item costs the larger of its KV
+// streaming time and its compute time (which grows with the number of 16-row query
+// blocks each wave runs per token), plus its partial-output write when the request is
+// split, plus a fixed prologue.  Items are placed longest-first on the least loaded
+// slot; the merge reads every partial back.  The candidate split length with the
+// smallest estimated step time wins (ties go to fewer, longer splits).
+constexpr double kHbmBytesPerS = 6.5e12;     // MI355X HBM3E, sustained streaming rate
+constexpr int kSlotsPerCu = 2;
 constexpr double kItemOverheadS = 1.5e-6;    // item prologue + pipeline fill
 constexpr double kMergeBytesPerS = 4.0e12;   // partials are re-read from the last-level cache
 constexpr double kMergeLaunchS = 3.0e-6;
 
-void choose_splits(const pa_plan_args& a, const std::vector<int>& begin, const std::vector<int>& span,
-                   int num_cus, int split_cap, std::vector<int>* nsp) {
+// Seconds of compute per KV token for one 16-row query block per wave, one workgroup
+// in a slot, by head_dim and KV format (measured with the KV loads switched off).
+double compute_s_per_token_block(const pa_plan_args& a) {
+  const bool f8 = a.kv_dtype == PA_DTYPE_FP8_E4M3;
+  const bool pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD;
+  const double d_scale = a.head_dim / 128.0;
+  double ns;
+  if (!f8) ns = 16.0;            // two-term bf16 P
+  else if (pt) ns = 14.0;        // fp8 -> bf16 upconversion of K and V
+  else ns = 8.0;                 // fp8 MFMA for both products
+  return ns * d_scale * 1e-9;
+}
+
+void choose_splits(const pa_plan_args& a, const KernelCfg& cfg, const std::vector<int>& begin,
+                   const std::vector<int>& span, int num_cus, int split_cap, std::vector<int>* nsp) {
   const int B = a.batch;
   const int G = a.num_q_heads / a.num_kv_heads;
   const double kv_tok = 2.0 * a.head_dim * (a.kv_dtype == PA_DTYPE_FP8_E4M3 ? 1 : 2) +
                         (a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD ? 8 : 0);
-  const double bw_cu = kHbmBytesPerS / num_cus;
+  const int slots = kSlotsPerCu * num_cus;
+  const double bw_slot = kHbmBytesPerS / slots;
+  const int wt = 4 / cfg.wq;                     // waves sharing the tokens of a tile
+  const double comp_blk = compute_s_per_token_block(a);
+  std::vector<double> comp_tok(B);               // compute seconds per token, per request
+  for (int b = 0; b < B; ++b) {
+    const int nb16 = ((a.qo_indptr[b + 1] - a.qo_indptr[b]) * G + 15) / 16;
+    const int rounds = (nb16 + cfg.wq - 1) / cfg.wq;
+    comp_tok[b] = comp_blk * rounds / wt;
+  }
   int max_blk = 1;
   for (int b = 0; b < B; ++b) max_blk = std::max(max_blk, (span[b] + kSplitAlign - 1) / kSplitAlign);
-  // candidate split lengths in 64-token blocks: geometric, plus the longest span
+  // candidate split lengths in 64-token blocks: every distinct ceil(max_blk / S), so
+  // that each split count of the longest request is reachable (about 2 sqrt(max_blk)
+  // values), in increasing order
   std::vector<int> cand;
-  for (double c = 1.0; c < max_blk; c *= 1.25) {
-    const int k = (int)c;
-    if (cand.empty() || cand.back() != k) cand.push_back(k);
+  for (int sc = std::min(max_blk, split_cap); sc >= 1; --sc) {
+    const int c = (max_blk + sc - 1) / sc;
+    if (cand.empty() || cand.back() != c) cand.push_back(c);
   }
-  cand.push_back(max_blk);
   std::vector<int> best(B, 1), cur(B);
   double best_t = 1e30;
   std::vector<std::pair<double, int>> groups;       // (item cost, item count)
@@ -108,16 +136,16 @@ void choose_splits(const pa_plan_args& a, const std::vector<int>& begin, const s
       const int n = a.qo_indptr[b + 1] - a.qo_indptr[b];
       const double part = sb > 1 ? (double)n * G * (a.head_dim + 1) * 4.0 : 0.0;
       const double tok = (double)span[b] / sb;
-      const double cost = (tok * kv_tok + part) / bw_cu + kItemOverheadS;
+      const double cost = std::max(tok * kv_tok / bw_slot, tok * comp_tok[b]) + part / bw_slot + kItemOverheadS;
       groups.push_back({cost, sb * a.num_kv_heads});
       merge_bytes += part * sb * a.num_kv_heads;
       total += cost * sb * a.num_kv_heads;
       longest = std::max(longest, cost);
     }
     const double merge_t = merge_bytes > 0 ? merge_bytes / kMergeBytesPerS + kMergeLaunchS : 0.0;
-    if (std::max(total / num_cus, longest) + merge_t >= best_t * (1 - 1e-9)) continue;
+    if (std::max(total / slots, longest) + merge_t >= best_t * (1 - 1e-9)) continue;
     std::sort(groups.begin(), groups.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
-    heap.assign(num_cus, 0.0);                       // min-heap of CU loads
+    heap.assign(slots, 0.0);                         // min-heap of slot loads
     for (const auto& gi : groups) {
       for (int k = 0; k < gi.second; ++k) {
         std::pop_heap(heap.begin(), heap.end(), std::greater<double>());
@@ -228,7 +256,7 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   if (a->force_splits > 0) {
     for (int b = 0; b < B; ++b) nsp[b] = a->force_splits;
   } else {
-    choose_splits(*a, begin, span, num_cus, split_cap, &nsp);
+    choose_splits(*a, cfg, begin, span, num_cus, split_cap, &nsp);
   }
   int s_max = 1;
   int64_t n_items = 0;

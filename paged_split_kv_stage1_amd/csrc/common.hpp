@@ -61,15 +61,25 @@ __device__ __forceinline__ f32x2 fp8x2_to_f32x2(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI_WORD);
 }
 
-__device__ __forceinline__ float wave_max_xor_16_32(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Reductions over lanes {l, l^16, l^32, l^48}: the gfx950 row-swap moves exchange
+// 32-lane halves and 16-lane rows of two registers in the VALU, with no LDS round trip.
+// permlane32_swap(x, x) yields {x[l mod 32], x[(l mod 32) + 32]}; permlane16_swap(x, x)
+// yields the even and the odd row of each row pair, so each step combines lane l with
+// lane l^32 (then l^16).
+__device__ __forceinline__ float swap32_combine_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float swap16_combine_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_max_xor_16_32(float x) { return swap16_combine_max(swap32_combine_max(x)); }
 __device__ __forceinline__ float wave_sum_xor_16_32(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

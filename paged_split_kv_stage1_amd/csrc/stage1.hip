@@ -22,8 +22,10 @@
 //   softmax: scores scaled into the log2 domain with the dequant scales folded in
 //        (FlashInfer PR #869 item 3), per-row causal/window masks, online max/sum,
 //        the O rescale skipped while no row maximum moves;
-//   PV:  bf16 KV -> P split in two bf16 terms (hi + lo); per-token-head FP8 V ->
-//        v_scale folded into P, V upconverted, two bf16 terms; per-tensor FP8 V ->
+//   PV:  bf16 KV -> P split in two bf16 terms (hi + lo), so that P carries ~16
+//        significant bits; per-token-head FP8 V -> v_scale folded into P, V
+//        upconverted, one bf16 term (its 2^-9 rounding is far below the e4m3
+//        resolution of V itself); per-tensor FP8 V ->
 //        P requantised to e4m3 after scaling by the format maximum 448 (FlashInfer
 //        PR #869 item 2), as a hi term plus a lo term of the residual x16, with the
 //        per-tensor v_scale applied in the final normaliser.
@@ -185,17 +187,22 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
   float sreg[PD];
   auto load_tile = [&](auto slot_c, int tile0) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot_c)::value;
-    const bool full = tile0 + C::BN <= te;
+    // Page numbers of all load groups first, so that their scalar loads share one wait.
+    // The clamps to the last token of the split are no-ops inside full tiles; keeping
+    // them unconditional leaves the whole load sequence in one basic block.
+    int jbs[C::CPT];
+    int32_t pages[C::CPT];
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      int jb = tile0 + (wave * 64 + 256 * i) / C::CPR;   // first token of this load (uniform)
-      uint32_t off = goff;
-      if (!full) {
-        jb = min(jb, te - 1);
-        const int ltc = min(lt, te - 1 - jb);
-        off -= (uint32_t)((lt - ltc) * a.kv_ss * C::KVB);
-      }
-      const int32_t page = pidx[jb >> shift];
+      jbs[i] = min(tile0 + (wave * 64 + 256 * i) / C::CPR, te - 1);   // first token of this load (uniform)
+      pages[i] = pidx[jbs[i] >> shift];
+    }
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int jb = jbs[i];
+      const int ltc = min(lt, te - 1 - jb);
+      const uint32_t off = goff - (uint32_t)((lt - ltc) * a.kv_ss * C::KVB);
+      const int32_t page = pages[i];
       const int64_t row = ((int64_t)page * a.kv_sp + head_off + (int64_t)(jb & pmask) * a.kv_ss) * C::KVB;
       // Streaming loads: every KV byte is read once, so keep it out of the caches;
       // normal loads must first evict (and write back) whatever dirty lines the
@@ -376,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
               const float y = PT ? pv[k] * vs[k] : pv[k];
               const __bf16 h = (__bf16)y;
               hv[k] = h;
-              lv[k] = (__bf16)(y - (float)h);
+              if constexpr (!KVF8) lv[k] = (__bf16)(y - (float)h);
             }
   #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
@@ -396,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
                 va = fp8x8_to_bf16x8((uint32_t)w[0], (uint32_t)w[1]);
               }
               o[i][db] = mfma_bf16(va, hv, o[i][db]);
-              o[i][db] = mfma_bf16(va, lv, o[i][db]);
+              if constexpr (!KVF8) o[i][db] = mfma_bf16(va, lv, o[i][db]);
             }
           }
         }

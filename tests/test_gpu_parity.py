@@ -121,11 +121,12 @@ def test_gather_bit_exact(name):
         assert np.array_equal(g[covered], ref[covered])
 
 
-# With bf16 two-term P (bf16 KV, per-token-head FP8 KV) the split count only moves
-# fp32 rounding.  With per-tensor FP8 V, P is requantised to e4m3 relative to each
-# split's running maximum, so the rounding of P itself changes with the splits: the
-# bound there is that requantisation error (about 1e-3 here), not fp32 noise.
-SPLIT_TOL = {"c3": 2e-5, "c4": 2e-5, "c2": 3e-3}
+# With bf16 two-term P (bf16 KV) the split count only moves fp32 rounding.  Where P
+# is rounded relative to each split's running maximum the rounding of P itself
+# changes with the splits: per-tensor FP8 V requantises P to two e4m3 terms (about
+# 1e-3 here), per-token-head FP8 KV carries P as one bf16 term (relative rounding
+# <= 2^-9 per probability; 4 x 2^-9 bounds the difference of two such sums).
+SPLIT_TOL = {"c3": 2e-5, "c4": 4 * 2.0 ** -9, "c2": 3e-3}
 
 
 @pytest.mark.parametrize("name", ["c3", "c4", "c2"])
