@@ -123,12 +123,15 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # compute-heavy workloads need ~50 back-to-back steps before the clocks settle
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting write between steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-splits", type=int, default=None)
+    ap.add_argument("--graph-reps", type=int, default=100,
+                    help="also time this many replays of stage 1 + merge captured in one hipGraph (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first, as a known-size reference for HBM counters")
     args = ap.parse_args()
@@ -162,6 +165,11 @@ def main():
 
     def merge():
         pd.merge(out, w.out_dtype, stream=stream)
+
+    def step_on(st):
+        pd.stage1(di.q, di.q_scale, di.k, di.v, di.kv_layout, di.k_scale, di.v_scale, di.scale_layout,
+                  di.page_indices, w.sm_scale, out, w.out_dtype, stream=st)
+        pd.merge(out, w.out_dtype, stream=st)
 
     if args.calibrate_copy:
         src = torch.ones(256 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
@@ -203,6 +211,32 @@ def main():
         n = len(x)
         return float(np.mean(x[n // 4: n - n // 4])) if n >= 4 else float(np.mean(x))
 
+    graph = None
+    if args.graph_reps > 0:
+        # the same two launches captured once and replayed; flush stays outside the graph
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_on(side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step_on(torch.cuda.current_stream())
+        for _ in range(3):
+            g.replay()
+        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.graph_reps)]
+        for i in range(args.graph_reps):
+            if not args.no_flush:
+                flush.fill_(1.0)
+            gev[i][0].record()
+            g.replay()
+            gev[i][1].record()
+        torch.cuda.synchronize()
+        gt = np.array([e[0].elapsed_time(e[1]) for e in gev]) * 1e3
+        graph = {"reps": args.graph_reps, "us_per_step_mean": round(float(np.mean(gt)), 3),
+                 "us_per_step_iqm": round(iqm(gt), 3)}
+
     us_step = float(np.mean(tot))
     gbps = acc["bytes"] / (us_step * 1e-6) / 1e9
     s1_us = float(np.mean(s1))
@@ -219,7 +253,7 @@ def main():
                    "kv_scale_mode": w.kv_scale_mode, "work_items": pd.num_items, "max_splits": pd.max_splits,
                    "cache_flush_between_steps": not args.no_flush},
         "us_per_step": round(us_step, 3), "us_per_step_iqm": round(iqm(tot), 3),
-        "stage1_us": round(s1_us, 3), "merge_us": round(float(np.mean(mg)), 3),
+        "stage1_us": round(s1_us, 3), "merge_us": round(float(np.mean(mg)), 3), "graph_replay": graph,
         "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_step": acc["bytes"], "algorithmic_flops_per_step": acc["flops"],
         "tflops": round(acc["flops"] / (us_step * 1e-6) / 1e12, 3),

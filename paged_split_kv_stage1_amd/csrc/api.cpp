@@ -54,7 +54,9 @@ bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
   c->qf8 = a.q_dtype == PA_DTYPE_FP8_E4M3;
   c->kvf8 = a.kv_dtype == PA_DTYPE_FP8_E4M3;
   c->pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD;
-  if (nqb <= 1) { c->wq = (c->dh == 256 && !c->kvf8) ? 2 : 1; c->nqb = 1; }
+  // head_dim 256 with one query block: 64-token tiles (two token groups of two waves)
+  // keep two LDS stages; 128-token tiles of d256 would fit only one
+  if (nqb <= 1) { c->wq = c->dh == 256 ? 2 : 1; c->nqb = 1; }
   else if (nqb == 2) { c->wq = 2; c->nqb = 1; }
   else if (nqb <= 4) { c->wq = 4; c->nqb = 1; }
   else { c->wq = 4; c->nqb = (nqb + 3) / 4; }

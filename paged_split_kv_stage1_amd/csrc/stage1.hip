@@ -43,13 +43,25 @@ template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB, int NS, int PD>
 struct S1Cfg {
   static constexpr int WT = 4 / WQ;                 // waves splitting the tokens of a tile
   static constexpr int BN = 32 * WT;                // tokens per tile
-  static constexpr int KVB = KVF8 ? 1 : 2;          // bytes per cached element
-  static constexpr int CPR = DH * KVB / 16;         // 16-byte chunks per token row
+  static constexpr int KVB = KVF8 ? 1 : 2;          // bytes per cached element in HBM
+  // LDS holds bf16 tiles for bf16 caches.  For per-token-head FP8 caches read with
+  // bf16 queries by four query-block waves, K is upconverted once when a tile is stored
+  // (instead of once by every wave that reads it) while V stays FP8, which halves the
+  // bytes of the transposing V reads that bound this shape.
+  static constexpr bool LBF = !KVF8 || (PT && !QF8 && WQ == 4);   // K tile in bf16
+  static constexpr bool LBFV = !KVF8;                               // V tile in bf16
+  static constexpr int LKB = LBF ? 2 : 1;           // bytes per K element in LDS
+  static constexpr int LVB = LBFV ? 2 : 1;          // bytes per V element in LDS
+  static constexpr int CPR = DH * KVB / 16;         // 16-byte chunks per token row in HBM
+  static constexpr int LCPR = DH * LKB / 16;        // 16-byte chunks per K token row in LDS
+  static constexpr int VCPR = DH * LVB / 16;        // 16-byte chunks per V token row in LDS
+  static constexpr int XPC = LKB / KVB;             // LDS K chunks stored per loaded chunk
   static constexpr int TPI = 64 / CPR;              // tokens one wave covers per load step
-  static constexpr int KTB = BN * DH * KVB;         // bytes of one K (or V) tile
+  static constexpr int KTB = BN * DH * LKB;         // LDS bytes of one K tile
+  static constexpr int VTB = BN * DH * LVB;         // LDS bytes of one V tile
   static constexpr int CPT = BN * CPR / 256;        // 16-byte chunks per thread per K (or V) tile
   static constexpr int SCB = PT ? 2 * BN * 4 : 0;   // scale bytes per stage: k_scale[BN], v_scale[BN]
-  static constexpr int STAGEB = 2 * KTB + SCB;
+  static constexpr int STAGEB = KTB + VTB + SCB;
   static constexpr int NPMAX = BN / 16 + 1;         // pages a tile can touch (page size >= 16)
   static constexpr int KC = DH / 32;                // K-steps of q.k
   static constexpr int DB = DH / 16;                // 16-wide d blocks of P.V
@@ -60,7 +72,7 @@ struct S1Cfg {
   static_assert(CPT >= 1 && (BN * CPR) % 256 == 0, "tile must split evenly over 256 threads");
   static_assert(WT == 1 || NQB == 1, "query blocks per wave > 1 only without token split");
   static_assert(NS == 1 || NS == 2, "one or two LDS stages");
-  static_assert(PD == 1 || PD == 2, "prefetch one or two tiles ahead");
+  static_assert(PD >= 1 && PD <= 3, "prefetch one to three tiles ahead");
   static_assert(2 * BN <= 256, "scale loads use one thread per token");
 };
 
@@ -176,12 +188,16 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
   const int lt = lane / C::CPR;
   const int cpos = lane % C::CPR;
   const uint32_t goff = (uint32_t)(lt * a.kv_ss * C::KVB) + (cpos << 4);
-  uint32_t kpos[C::CPT], vpos[C::CPT];
+  uint32_t kpos[C::CPT][C::XPC], vpos[C::CPT];
 #pragma unroll
   for (int i = 0; i < C::CPT; ++i) {
     const int t = (wave * 64 + 256 * i) / C::CPR + lt;
-    kpos[i] = (t * C::CPR + (cpos ^ swz_k<C::CPR>(t))) << 4;
-    vpos[i] = (t * C::CPR + (cpos ^ swz_v<C::CPR, KVF8>(t))) << 4;
+#pragma unroll
+    for (int x = 0; x < C::XPC; ++x) {
+      const int c = cpos * C::XPC + x;
+      kpos[i][x] = (t * C::LCPR + (c ^ swz_k<C::LCPR>(t))) << 4;
+    }
+    vpos[i] = (t * C::VCPR + (cpos ^ swz_v<C::VCPR, !C::LBFV>(t))) << 4;
   }
   u32x4 kreg[PD][C::CPT], vreg[PD][C::CPT];
   float sreg[PD];
@@ -232,11 +248,17 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
     constexpr int SL = decltype(slot_c)::value;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      *reinterpret_cast<u32x4*>(stage + kpos[i]) = kreg[SL][i];
+      if constexpr (C::XPC == 1) {
+        *reinterpret_cast<u32x4*>(stage + kpos[i][0]) = kreg[SL][i];
+      } else {                 // 16 FP8 values -> two chunks of 8 bf16 (exact)
+        const u32x4 kq = kreg[SL][i];
+        *reinterpret_cast<bf16x8*>(stage + kpos[i][0]) = fp8x8_to_bf16x8(kq[0], kq[1]);
+        *reinterpret_cast<bf16x8*>(stage + kpos[i][1]) = fp8x8_to_bf16x8(kq[2], kq[3]);
+      }
       *reinterpret_cast<u32x4*>(stage + C::KTB + vpos[i]) = vreg[SL][i];
     }
     if constexpr (PT) {
-      if (tid < 2 * C::BN) reinterpret_cast<float*>(stage + 2 * C::KTB)[tid] = sreg[SL];
+      if (tid < 2 * C::BN) reinterpret_cast<float*>(stage + C::KTB + C::VTB)[tid] = sreg[SL];
     }
   };
 
@@ -250,20 +272,20 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
       const int t = tk0 + 16 * tb;
-      if constexpr (!KVF8) kro[tb][kc] = t * (C::CPR * 16) + (((4 * kc + g) ^ swz_k<C::CPR>(t)) << 4);
-      else kro[tb][kc] = t * (C::CPR * 16) + (((2 * kc + (g >> 1)) ^ swz_k<C::CPR>(t)) << 4) + 8 * (g & 1);
+      if constexpr (C::LBF) kro[tb][kc] = t * (C::LCPR * 16) + (((4 * kc + g) ^ swz_k<C::LCPR>(t)) << 4);
+      else kro[tb][kc] = t * (C::LCPR * 16) + (((2 * kc + (g >> 1)) ^ swz_k<C::LCPR>(t)) << 4) + 8 * (g & 1);
     }
   // V rows read transposed: bf16 -> two 4-token reads (tokens 4g+j and 16+4g+j);
   // fp8 -> one 8-token read (tokens {4g..4g+3, 16+4g..16+4g+3}).
   auto vaddr = [&](int db, int half) __attribute__((always_inline)) -> uint32_t {
-    if constexpr (!KVF8) {
+    if constexpr (C::LBFV) {
       const int t1 = wt * 32 + 4 * g + (L16 >> 2) + 16 * half;
       const int c = 2 * db + ((L16 & 3) >> 1);
-      return t1 * (C::CPR * 16) + ((c ^ swz_v<C::CPR, false>(t1)) << 4) + 8 * (L16 & 1);
+      return t1 * (C::VCPR * 16) + ((c ^ swz_v<C::VCPR, false>(t1)) << 4) + 8 * (L16 & 1);
     } else {
       const int jr = L16 >> 1;
       const int tv = wt * 32 + (jr < 4 ? 4 * g + jr : 16 + 4 * g + (jr - 4));
-      return tv * (C::CPR * 16) + ((db ^ swz_v<C::CPR, true>(tv)) << 4) + 8 * (L16 & 1);
+      return tv * (C::VCPR * 16) + ((db ^ swz_v<C::VCPR, true>(tv)) << 4) + 8 * (L16 & 1);
     }
   };
   const bool wave_has_rows = qvalid[0];
@@ -271,144 +293,146 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
   // normaliser divides the 448 out again because l accumulates the scaled P)
   constexpr float kPoff = C::PV_FP8 ? 8.807354922057604f : 0.0f;   // log2(448)
 
+  // One tile of this wave, query block by query block: S^T, online softmax, O^T += V^T P^T.
+  // (The compiler overlaps one block's MFMAs with the previous block's softmax; reading
+  // each K/V fragment once for all blocks instead serialises those phases.)
   auto compute_tile = [&](int tile0, const uint8_t* stage) __attribute__((always_inline)) {
-  const uint8_t* Kl = stage;
-      const uint8_t* Vl = stage + C::KTB;
-      const float* ksl = reinterpret_cast<const float*>(stage + 2 * C::KTB);
-      const float* vsl = ksl + C::BN;
-      const int c0 = tile0 + wt * 32;          // first token of this wave's 32-token chunk
-      if (c0 < te && wave_has_rows) {
-        const bool need_mask = !(c0 >= vis_lo_all && c0 + 31 <= vis_hi_all);
-        float ks[8], vs[8];
-        if constexpr (PT) {
-  #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            ks[k] = ksl[wt * 32 + 4 * g + k] * qk_scale;
-            ks[4 + k] = ksl[wt * 32 + 16 + 4 * g + k] * qk_scale;
-            vs[k] = vsl[wt * 32 + 4 * g + k];
-            vs[4 + k] = vsl[wt * 32 + 16 + 4 * g + k];
-          }
-        }
-  #pragma unroll
-        for (int i = 0; i < NQB; ++i) {
-          if (!qvalid[i]) continue;
-          // ---- S^T = K Q^T for 2 x 16 tokens ----------------------------------------
-          f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-          for (int kc = 0; kc < C::KC; ++kc) {
-            if constexpr (!KVF8) {
-              const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Kl + kro[0][kc]);
-              const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Kl + kro[1][kc]);
-              s0 = mfma_bf16(k0, qop[i][kc], s0);
-              s1 = mfma_bf16(k1, qop[i][kc], s1);
-            } else {
-              const uint2 r0 = *reinterpret_cast<const uint2*>(Kl + kro[0][kc]);
-              const uint2 r1 = *reinterpret_cast<const uint2*>(Kl + kro[1][kc]);
-              if constexpr (QF8) {
-                s0 = mfma_fp8((long)r0.x | ((long)r0.y << 32), qop[i][kc], s0);
-                s1 = mfma_fp8((long)r1.x | ((long)r1.y << 32), qop[i][kc], s1);
-              } else {
-                s0 = mfma_bf16(fp8x8_to_bf16x8(r0.x, r0.y), qop[i][kc], s0);
-                s1 = mfma_bf16(fp8x8_to_bf16x8(r1.x, r1.y), qop[i][kc], s1);
-              }
-            }
-          }
-          // ---- scale, mask, online softmax -------------------------------------------
-          float x[8];
-  #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            x[k] = s0[k];
-            x[4 + k] = s1[k];
-          }
-          float xs;                              // score scale still to apply (1 when folded)
-          if constexpr (PT) {
-  #pragma unroll
-            for (int k = 0; k < 8; ++k) x[k] *= ks[k];
-            xs = 1.0f;
+    const uint8_t* Kl = stage;
+    const uint8_t* Vl = stage + C::KTB;
+    const float* ksl = reinterpret_cast<const float*>(stage + C::KTB + C::VTB);
+    const float* vsl = ksl + C::BN;
+    const int c0 = tile0 + wt * 32;          // first token of this wave's 32-token chunk
+    if (!(c0 < te && wave_has_rows)) return;
+    const bool need_mask = !(c0 >= vis_lo_all && c0 + 31 <= vis_hi_all);
+    float ks[8], vs[8];
+    if constexpr (PT) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        ks[k] = ksl[wt * 32 + 4 * g + k] * qk_scale;
+        ks[4 + k] = ksl[wt * 32 + 16 + 4 * g + k] * qk_scale;
+        vs[k] = vsl[wt * 32 + 4 * g + k];
+        vs[4 + k] = vsl[wt * 32 + 16 + 4 * g + k];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) {
+      if (!qvalid[i]) continue;
+      // ---- S^T = K Q^T for 2 x 16 tokens ----------------------------------------------
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < C::KC; ++kc) {
+        if constexpr (C::LBF) {
+          const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Kl + kro[0][kc]);
+          const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Kl + kro[1][kc]);
+          s0 = mfma_bf16(k0, qop[i][kc], s0);
+          s1 = mfma_bf16(k1, qop[i][kc], s1);
+        } else {
+          const uint2 r0 = *reinterpret_cast<const uint2*>(Kl + kro[0][kc]);
+          const uint2 r1 = *reinterpret_cast<const uint2*>(Kl + kro[1][kc]);
+          if constexpr (QF8) {
+            s0 = mfma_fp8((long)r0.x | ((long)r0.y << 32), qop[i][kc], s0);
+            s1 = mfma_fp8((long)r1.x | ((long)r1.y << 32), qop[i][kc], s1);
           } else {
-            xs = qk_scale;
-          }
-          if (need_mask) {
-  #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              const int j = c0 + (k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4));
-              x[k] = (j >= lim_lo[i] && j <= lim_hi[i]) ? x[k] : -INFINITY;
-            }
-          }
-          float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-          mx = wave_max_xor_16_32(mx) * xs;
-          const float mnew = fmaxf(mrun[i], mx);
-          const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-          if (__builtin_amdgcn_ballot_w64(mnew != mrun[i]) != 0) {     // lazy rescale
-            const float alpha = fast_exp2(mrun[i] - muse);
-            lrun[i] *= alpha;
-  #pragma unroll
-            for (int db = 0; db < C::DB; ++db) o[i][db] *= alpha;
-            if constexpr (C::PV_FP8) {
-  #pragma unroll
-              for (int db = 0; db < C::DB; ++db) olo[i][db] *= alpha;
-            }
-            mrun[i] = mnew;
-          }
-          const float nb = kPoff - muse;
-          float pv[8];
-  #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            pv[k] = fast_exp2(fmaf(x[k], xs, nb));
-            lrun[i] += pv[k];
-          }
-          // ---- P operand and O^T += V^T P^T ------------------------------------------
-          if constexpr (C::PV_FP8) {
-            const uint32_t h0 = f32x4_to_fp8x4(pv[0], pv[1], pv[2], pv[3]);
-            const uint32_t h1 = f32x4_to_fp8x4(pv[4], pv[5], pv[6], pv[7]);
-            const f32x2 d0 = fp8x2_to_f32x2<false>(h0), d1 = fp8x2_to_f32x2<true>(h0);
-            const f32x2 d2 = fp8x2_to_f32x2<false>(h1), d3 = fp8x2_to_f32x2<true>(h1);
-            const uint32_t l0 = f32x4_to_fp8x4((pv[0] - d0[0]) * 16.f, (pv[1] - d0[1]) * 16.f,
-                                               (pv[2] - d1[0]) * 16.f, (pv[3] - d1[1]) * 16.f);
-            const uint32_t l1 = f32x4_to_fp8x4((pv[4] - d2[0]) * 16.f, (pv[5] - d2[1]) * 16.f,
-                                               (pv[6] - d3[0]) * 16.f, (pv[7] - d3[1]) * 16.f);
-            const long phi = (long)h0 | ((long)h1 << 32);
-            const long plo = (long)l0 | ((long)l1 << 32);
-  #pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-              const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
-              const long va = (long)(uint32_t)w[0] | ((long)(uint32_t)w[1] << 32);
-              o[i][db] = mfma_fp8(va, phi, o[i][db]);
-              olo[i][db] = mfma_fp8(va, plo, olo[i][db]);
-            }
-          } else {
-            bf16x8 hv, lv;
-  #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              const float y = PT ? pv[k] * vs[k] : pv[k];
-              const __bf16 h = (__bf16)y;
-              hv[k] = h;
-              if constexpr (!KVF8) lv[k] = (__bf16)(y - (float)h);
-            }
-  #pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-              bf16x8 va;
-              if constexpr (!KVF8) {
-                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 0)));
-                const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 1)));
-                const __bf16* p1 = reinterpret_cast<const __bf16*>(&v1);
-                const __bf16* p2 = reinterpret_cast<const __bf16*>(&v2);
-  #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                  va[k] = p1[k];
-                  va[4 + k] = p2[k];
-                }
-              } else {
-                const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
-                va = fp8x8_to_bf16x8((uint32_t)w[0], (uint32_t)w[1]);
-              }
-              o[i][db] = mfma_bf16(va, hv, o[i][db]);
-              if constexpr (!KVF8) o[i][db] = mfma_bf16(va, lv, o[i][db]);
-            }
+            s0 = mfma_bf16(fp8x8_to_bf16x8(r0.x, r0.y), qop[i][kc], s0);
+            s1 = mfma_bf16(fp8x8_to_bf16x8(r1.x, r1.y), qop[i][kc], s1);
           }
         }
       }
-    };
+      // ---- scale, mask, online softmax -----------------------------------------------
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[k] = s0[k];
+        x[4 + k] = s1[k];
+      }
+      float xs;                              // score scale still to apply (1 when folded)
+      if constexpr (PT) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] *= ks[k];
+        xs = 1.0f;
+      } else {
+        xs = qk_scale;
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int j = c0 + (k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4));
+          x[k] = (j >= lim_lo[i] && j <= lim_hi[i]) ? x[k] : -INFINITY;
+        }
+      }
+      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mx = wave_max_xor_16_32(mx) * xs;
+      const float mnew = fmaxf(mrun[i], mx);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      if (__builtin_amdgcn_ballot_w64(mnew != mrun[i]) != 0) {     // lazy rescale
+        const float alpha = fast_exp2(mrun[i] - muse);
+        lrun[i] *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) o[i][db] *= alpha;
+        if constexpr (C::PV_FP8) {
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) olo[i][db] *= alpha;
+        }
+        mrun[i] = mnew;
+      }
+      const float nb = kPoff - muse;
+      float pv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        pv[k] = fast_exp2(fmaf(x[k], xs, nb));
+        lrun[i] += pv[k];
+      }
+      // ---- P operand and O^T += V^T P^T --------------------------------------------------
+      if constexpr (C::PV_FP8) {
+        const uint32_t h0 = f32x4_to_fp8x4(pv[0], pv[1], pv[2], pv[3]);
+        const uint32_t h1 = f32x4_to_fp8x4(pv[4], pv[5], pv[6], pv[7]);
+        const f32x2 d0 = fp8x2_to_f32x2<false>(h0), d1 = fp8x2_to_f32x2<true>(h0);
+        const f32x2 d2 = fp8x2_to_f32x2<false>(h1), d3 = fp8x2_to_f32x2<true>(h1);
+        const uint32_t l0 = f32x4_to_fp8x4((pv[0] - d0[0]) * 16.f, (pv[1] - d0[1]) * 16.f,
+                                           (pv[2] - d1[0]) * 16.f, (pv[3] - d1[1]) * 16.f);
+        const uint32_t l1 = f32x4_to_fp8x4((pv[4] - d2[0]) * 16.f, (pv[5] - d2[1]) * 16.f,
+                                           (pv[6] - d3[0]) * 16.f, (pv[7] - d3[1]) * 16.f);
+        const long phi = (long)h0 | ((long)h1 << 32);
+        const long plo = (long)l0 | ((long)l1 << 32);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
+          const long va = (long)(uint32_t)w[0] | ((long)(uint32_t)w[1] << 32);
+          o[i][db] = mfma_fp8(va, phi, o[i][db]);
+          olo[i][db] = mfma_fp8(va, plo, olo[i][db]);
+        }
+      } else {
+        bf16x8 hv, lv;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float y = PT ? pv[k] * vs[k] : pv[k];
+          const __bf16 h = (__bf16)y;
+          hv[k] = h;
+          if constexpr (!KVF8) lv[k] = (__bf16)(y - (float)h);
+        }
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          bf16x8 va;
+          if constexpr (C::LBFV) {
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 0)));
+            const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 1)));
+            const __bf16* p1 = reinterpret_cast<const __bf16*>(&v1);
+            const __bf16* p2 = reinterpret_cast<const __bf16*>(&v2);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              va[k] = p1[k];
+              va[4 + k] = p2[k];
+            }
+          } else {
+            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
+            va = fp8x8_to_bf16x8((uint32_t)w[0], (uint32_t)w[1]);
+          }
+          o[i][db] = mfma_bf16(va, hv, o[i][db]);
+          if constexpr (!KVF8) o[i][db] = mfma_bf16(va, lv, o[i][db]);
+        }
+      }
+    }
+  };
 
   // One tile: refill the register slot that held it PD tiles ahead, compute it, then
   // move the next tile from registers to LDS.  FULL steps do this unconditionally,
@@ -429,8 +453,11 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
 
   if (ntiles > 0) {
     load_tile(ic<0>{}, tb0);
-    if constexpr (PD == 2) {
+    if constexpr (PD >= 2) {
       if (ntiles > 1) load_tile(ic<1>{}, tb0 + C::BN);
+    }
+    if constexpr (PD >= 3) {
+      if (ntiles > 2) load_tile(ic<2>{}, tb0 + 2 * C::BN);
     }
   }
   // Query operand, loaded after the first tiles and waited for completely here: a
@@ -459,12 +486,16 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
   int ti = 0;
   for (; ti + 2 * PD - 1 < ntiles; ti += PD) {         // steady state
     step(ic<0>{}, ic<1>{}, ti);
-    if constexpr (PD == 2) step(ic<1>{}, ic<1>{}, ti + 1);
+    if constexpr (PD >= 2) step(ic<1>{}, ic<1>{}, ti + 1);
+    if constexpr (PD >= 3) step(ic<2>{}, ic<1>{}, ti + 2);
   }
   for (; ti < ntiles; ti += PD) {                      // drain the last tiles
     step(ic<0>{}, ic<0>{}, ti);
-    if constexpr (PD == 2) {
+    if constexpr (PD >= 2) {
       if (ti + 1 < ntiles) step(ic<1>{}, ic<0>{}, ti + 1);
+    }
+    if constexpr (PD >= 3) {
+      if (ti + 2 < ntiles) step(ic<2>{}, ic<0>{}, ti + 2);
     }
   }
   __syncthreads();
@@ -559,18 +590,24 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
 // LDS stages and register prefetch depth: two stages when two workgroups still fit
 // in the CU's 160 KiB of LDS, else one; two tiles of register prefetch when a tile
 // costs at most 32 VGPRs per thread, else one.
-template <int DH, bool KVF8, bool PT, int WQ>
+template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB>
 struct Pipe {
   static constexpr int BN = 32 * (4 / WQ);
-  static constexpr int stage = 2 * BN * DH * (KVF8 ? 1 : 2) + (PT ? 2 * BN * 4 : 0);
+  static constexpr bool LBF = !KVF8 || (PT && !QF8 && WQ == 4);   // as S1Cfg::LBF
+  static constexpr int stage = BN * DH * ((LBF ? 2 : 1) + (KVF8 ? 1 : 2)) + (PT ? 2 * BN * 4 : 0);
   static constexpr int NS = 2 * stage <= 80 * 1024 ? 2 : 1;
   static constexpr int CPT = BN * DH * (KVF8 ? 1 : 2) / 16 / 256;
+  // tiles in flight in registers (8 VGPRs per 16-byte chunk of K and V).  A third tile
+  // measured slower on the d256 per-token-head shape (register pressure), so at most two.
   static constexpr int PD = CPT <= 4 ? 2 : 1;
 };
 
 template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB>
 static int launch_one(const Stage1Args& a, int num_items, void* stream) {
-  using Pp = Pipe<DH, KVF8, PT, WQ>;
+  using Pp = Pipe<DH, QF8, KVF8, PT, WQ, NQB>;
+  using C = S1Cfg<DH, QF8, KVF8, PT, WQ, NQB, Pp::NS, Pp::PD>;
+  static_assert(Pp::stage == C::STAGEB, "host and kernel disagree on the LDS stage size");
+  static_assert(C::LDSB <= 80 * 1024, "two workgroups per CU must fit in 160 KB of LDS");
   hipLaunchKernelGGL((stage1_kernel<DH, QF8, KVF8, PT, WQ, NQB, Pp::NS, Pp::PD>), dim3(num_items), dim3(256), 0,
                      (hipStream_t)stream, a);
   return (int)hipGetLastError();
@@ -588,7 +625,7 @@ constexpr int max_nqb() {
 template <int DH, bool QF8, bool KVF8, bool PT>
 static int dispatch_tiles(const KernelCfg& c, const Stage1Args& a, int n, void* s) {
   constexpr int NMAX = max_nqb<DH, KVF8, PT>();
-  if constexpr (DH == 128 || KVF8) {      // a 128-token bf16 d256 tile pair does not fit twice in LDS
+  if constexpr (DH == 128) {      // d256 always runs >= 2 query-block waves (64-token tiles)
     if (c.wq == 1 && c.nqb == 1) return launch_one<DH, QF8, KVF8, PT, 1, 1>(a, n, s);
   }
   if (c.wq == 2 && c.nqb == 1) return launch_one<DH, QF8, KVF8, PT, 2, 1>(a, n, s);
@@ -618,7 +655,7 @@ bool stage1_cfg_supported(const KernelCfg& c) {
   if (!c.kvf8 && c.pt) return false;
   const bool pv_fp8 = c.kvf8 && !c.pt;
   const int nmax = c.dh == 128 ? (pv_fp8 ? 2 : 3) : (pv_fp8 ? 1 : 2);
-  if (c.nqb == 1) return (c.wq == 1 && (c.dh == 128 || c.kvf8)) || c.wq == 2 || c.wq == 4;
+  if (c.nqb == 1) return (c.wq == 1 && c.dh == 128) || c.wq == 2 || c.wq == 4;
   return c.wq == 4 && c.nqb >= 2 && c.nqb <= nmax;
 }
 
