@@ -224,6 +224,33 @@ def test_window_edges(window):
     assert max_rel_err(o, ref) <= BAR["fp8"]
 
 
+@pytest.mark.parametrize("fs", [64, 81])
+def test_many_splits_workgroup_merge(fs):
+    # 64 or more splits take the merge shape in which four waves share one
+    # (row, head, d slice); fewer take the one-wave-per-slice shape
+    print(f"[many-splits] {fs}", flush=True)
+    w = make_workload("c3", batch=2, ctx=[5300, 4100], out_dtype="fp32")
+    di = to_device(w)
+    o, pd, lse = run_decode(w, di, force_splits=fs, out_lse=True)
+    assert pd.max_splits >= 64
+    ref, ref_lse = _oracle(w)
+    assert max_rel_err(o, ref) <= BAR["bf16"]
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-3 * max(1.0, np.max(np.abs(ref_lse)))
+
+
+def test_head_permutation_within_group_permutes_outputs():
+    # heads of one KV group share the MFMA row blocks; every row's softmax and P.V are
+    # independent of the other rows, so permuting them permutes the outputs bit for bit
+    w = make_workload("c5", batch=3, ctx=[900, 130, 64], rows=[8, 3, 1], out_dtype="fp32")
+    di = to_device(w)
+    o, _, _ = run_decode(w, di)
+    G = w.num_q_heads // w.num_kv_heads
+    perm = np.concatenate([g * G + np.random.default_rng(g).permutation(G) for g in range(w.num_kv_heads)])
+    di.q = di.q[:, torch.as_tensor(perm, device=di.q.device)].contiguous()
+    o2, _, _ = run_decode(w, di)
+    assert np.array_equal(o2, o[:, perm])
+
+
 def test_more_splits_than_blocks_gives_empty_splits():
     w = make_workload("c1", ctx=100, out_dtype="fp32")
     di = to_device(w)
