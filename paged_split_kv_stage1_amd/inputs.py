@@ -109,8 +109,9 @@ def _seed_for(name: str) -> int:
 def make_workload(name: str, seed: Optional[int] = None, *, batch: Optional[int] = None,
                   ctx: Optional[int] = None, ctx_range: Optional[tuple] = None,
                   rows: Optional[object] = None, out_dtype: Optional[str] = None,
-                  kv_layout_note: str = "HPD") -> Workload:
-    """Build the named workload, optionally shrunk (batch/ctx/rows overrides).
+                  page: Optional[int] = None, kv_layout_note: str = "HPD") -> Workload:
+    """Build the named workload, optionally shrunk (batch/ctx/rows overrides) or with
+    another page size (``page``).
 
     ``rows`` may be an int (every request), a list (per request) or "ragged"
     (uniform 1..8).  ``ctx`` may be an int or a list; ``ctx_range`` replaces the
@@ -121,7 +122,7 @@ def make_workload(name: str, seed: Optional[int] = None, *, batch: Optional[int]
     gen = torch.Generator().manual_seed(seed)
     rng = np.random.default_rng(seed)
     B = cfg["batch"] if batch is None else batch
-    P = cfg["page"]
+    P = cfg["page"] if page is None else page
     hq, hkv, d = cfg["hq"], cfg["hkv"], cfg["d"]
 
     # rows per request

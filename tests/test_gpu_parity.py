@@ -251,6 +251,20 @@ def test_head_permutation_within_group_permutes_outputs():
     assert np.array_equal(o2, o[:, perm])
 
 
+@pytest.mark.parametrize("name,page", [("c2", 128), ("c2", 1024), ("c3", 256), ("c4", 1024), ("c5", 128)])
+@pytest.mark.parametrize("layout", ["HPD", "PHD"])
+def test_large_pages(name, page, layout):
+    # pages of 128..1024 tokens: several tiles (and whole splits) inside one page, and a
+    # split boundary inside a page
+    print(f"[large-pages] {name} P={page} {layout}", flush=True)
+    w = make_workload(name, **SMALL[name], page=page, out_dtype="fp32")
+    di = to_device(w, layout=layout)
+    for fs in (0, 3):
+        o, _, _ = run_decode(w, di, force_splits=fs)
+        ref, _ = _oracle(w, layout=layout)
+        assert max_rel_err(o, ref) <= _bar(w)
+
+
 def test_more_splits_than_blocks_gives_empty_splits():
     w = make_workload("c1", ctx=100, out_dtype="fp32")
     di = to_device(w)
