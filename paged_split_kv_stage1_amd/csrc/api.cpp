@@ -427,6 +427,8 @@ pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows
   if (n_rows < 0) return fail(PA_ERR_INVALID_ARGUMENT, "n_rows must be >= 0");
   if (head_dim < 64 || head_dim > 1024 || ilog2_exact(head_dim / 64) < 0 || head_dim % 64)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d: must be 64 times a power of two, at most 1024", head_dim);
+  if (!aligned16(src) || ((uintptr_t)dst & 7u) != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_quantize_fp8: src must be 16-byte and dst 8-byte aligned");
   const int e = launch_quant(src, src_dtype == PA_DTYPE_BF16, n_rows, head_dim, mode == PA_SCALE_PER_TENSOR, dst,
                              scale, stream);
   if (e) return hip_fail(e, "pa_kv_quantize_fp8 launch");

@@ -3,54 +3,113 @@
 // the whole tensor (FlashMLA PR #54, symmetric per-tensor), codes =
 // RNE(clamp(x / scale, -448, 448)).  The hardware fp32 -> e4m3 conversion rounds
 // to nearest even without saturating, hence the clamp first.
+//
+// The quotient x / scale must be the IEEE fp32 one (the codes are compared bit for bit
+// with a reference that divides).  Instead of a full division per element, each row's
+// reciprocal y = RN(1/scale) is divided once and every element takes Markstein's
+// correction step q = RN(q0 + RN(x - q0*scale)*y) with q0 = RN(x*y): for
+// round-to-nearest and a normal quotient this is the correctly rounded x / scale.  A
+// subnormal quotient is far below e4m3's smallest step and encodes to zero either
+// way; the sign is copied from x so that -0 keeps its code.
+//
+// Memory access: 8 consecutive elements per lane (16-byte loads of bf16, two of fp32)
+// and 8-byte code stores.
 #include "common.hpp"
 
 namespace pa {
 
 template <bool BF16SRC>
-__device__ __forceinline__ float load_src(const void* src, int64_t i) {
-  if constexpr (BF16SRC) return (float)static_cast<const __bf16*>(src)[i];
-  else return static_cast<const float*>(src)[i];
-}
-
-__device__ __forceinline__ uint8_t encode_e4m3(float x, float scale) {
-  float y = x / scale;                                     // IEEE fp32 divide
-  y = fminf(fmaxf(y, -448.0f), 448.0f);
-  return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFF);
+__device__ __forceinline__ void load8(const void* src, int64_t i, float* x) {
+  if constexpr (BF16SRC) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(src) + i);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + i);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + i + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[k] = a[k];
+      x[4 + k] = b[k];
+    }
+  }
 }
 
 __device__ __forceinline__ float scale_of(float amax) { return amax == 0.f ? 1.0f : amax / 448.0f; }
 
-// one wave per row; EPL elements per lane (head_dim = 64 * EPL)
-template <bool BF16SRC, int EPL>
+// RN(x / b) from y = RN(1 / b) (see above)
+__device__ __forceinline__ float div_rn(float x, float b, float y) {
+  const float q0 = x * y;
+  const float r = fmaf(-q0, b, x);
+  return __builtin_copysignf(fmaf(r, y, q0), x);
+}
+
+// 8 elements -> 8 e4m3 codes (byte k = element k)
+__device__ __forceinline__ uint2 encode8(const float* x, float sc, float inv) {
+  float q[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) q[k] = fminf(fmaxf(div_rn(x[k], sc, inv), -448.0f), 448.0f);
+  return uint2{f32x4_to_fp8x4(q[0], q[1], q[2], q[3]), f32x4_to_fp8x4(q[4], q[5], q[6], q[7])};
+}
+
+// Per-row scales.  A row of D elements is LPR lanes x EPL elements (EPL = 8, or D/64
+// for D >= 512); a wave holds 64 / LPR rows and a workgroup four waves' worth.
+template <bool BF16SRC, int D>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* src, int64_t n_rows, uint8_t* dst,
                                                          float* scale) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int EPL = D >= 512 ? D / 64 : 8;
+  constexpr int LPR = D / EPL;
+  constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
-  if (row >= n_rows) return;
-  constexpr int D = 64 * EPL;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const int part = lane % LPR;
+  const bool live = row < n_rows;
   float x[EPL];
   float amax = 0.f;
+  if (live) {
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    x[e] = load_src<BF16SRC>(src, row * D + lane * EPL + e);
-    amax = fmaxf(amax, fabsf(x[e]));
+    for (int c = 0; c < EPL / 8; ++c) load8<BF16SRC>(src, row * D + (int64_t)part * EPL + 8 * c, x + 8 * c);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  for (int off = LPR / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if (!live) return;
   const float sc = scale_of(amax);
+  const float inv = 1.0f / sc;                            // IEEE divide, once per row
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) dst[row * D + lane * EPL + e] = encode_e4m3(x[e], sc);
-  if (lane == 0) scale[row] = sc;
+  for (int c = 0; c < EPL / 8; ++c)
+    *reinterpret_cast<uint2*>(dst + row * D + (int64_t)part * EPL + 8 * c) = encode8(x + 8 * c, sc, inv);
+  if (part == 0) scale[row] = sc;
 }
 
 __global__ void zero_word_kernel(float* p) { *p = 0.f; }
 
+// Per-tensor amax over n elements (n a multiple of 8), four 8-element groups in flight.
 template <bool BF16SRC>
 __global__ __launch_bounds__(256) void amax_kernel(const void* src, int64_t n, float* amax_word) {
+  const int64_t groups = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * 256;
   float m = 0.f;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    m = fmaxf(m, fabsf(load_src<BF16SRC>(src, i)));
+  int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; gi + 3 * stride < groups; gi += 4 * stride) {
+    float x[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8<BF16SRC>(src, (gi + u * stride) * 8, x[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[u][e]));
+  }
+  for (; gi < groups; gi += stride) {
+    float x[8];
+    load8<BF16SRC>(src, gi * 8, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   // non-negative floats order like their bit patterns
@@ -61,21 +120,38 @@ template <bool BF16SRC>
 __global__ __launch_bounds__(256) void quant_tensor_kernel(const void* src, int64_t n, uint8_t* dst,
                                                            const float* amax_word) {
   const float sc = scale_of(*amax_word);
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    dst[i] = encode_e4m3(load_src<BF16SRC>(src, i), sc);
+  const float inv = 1.0f / sc;
+  const int64_t groups = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; gi + stride < groups; gi += 2 * stride) {
+    float x[2][8];
+    load8<BF16SRC>(src, gi * 8, x[0]);
+    load8<BF16SRC>(src, (gi + stride) * 8, x[1]);
+    *reinterpret_cast<uint2*>(dst + gi * 8) = encode8(x[0], sc, inv);
+    *reinterpret_cast<uint2*>(dst + (gi + stride) * 8) = encode8(x[1], sc, inv);
+  }
+  for (; gi < groups; gi += stride) {
+    float x[8];
+    load8<BF16SRC>(src, gi * 8, x);
+    *reinterpret_cast<uint2*>(dst + gi * 8) = encode8(x, sc, inv);
+  }
 }
 
 __global__ void finish_scale_kernel(float* scale) { scale[0] = scale_of(scale[0]); }
 
 template <bool BF16SRC>
 static int launch_rows(const void* src, int64_t n_rows, int head_dim, uint8_t* dst, float* scale, hipStream_t s) {
-  const unsigned blocks = (unsigned)((n_rows + 3) / 4);
-  switch (head_dim / 64) {
-    case 1: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 1>), dim3(blocks), dim3(256), 0, s, src, n_rows, dst, scale); break;
-    case 2: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 2>), dim3(blocks), dim3(256), 0, s, src, n_rows, dst, scale); break;
-    case 4: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 4>), dim3(blocks), dim3(256), 0, s, src, n_rows, dst, scale); break;
-    case 8: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 8>), dim3(blocks), dim3(256), 0, s, src, n_rows, dst, scale); break;
-    case 16: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 16>), dim3(blocks), dim3(256), 0, s, src, n_rows, dst, scale); break;
+  auto blocks = [&](int d) {
+    const int rpw = 64 / (d / (d >= 512 ? d / 64 : 8));
+    return (unsigned)((n_rows + 4 * rpw - 1) / (4 * rpw));
+  };
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 64>), dim3(blocks(64)), dim3(256), 0, s, src, n_rows, dst, scale); break;
+    case 128: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 128>), dim3(blocks(128)), dim3(256), 0, s, src, n_rows, dst, scale); break;
+    case 256: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 256>), dim3(blocks(256)), dim3(256), 0, s, src, n_rows, dst, scale); break;
+    case 512: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 512>), dim3(blocks(512)), dim3(256), 0, s, src, n_rows, dst, scale); break;
+    case 1024: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 1024>), dim3(blocks(1024)), dim3(256), 0, s, src, n_rows, dst, scale); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
@@ -83,8 +159,8 @@ static int launch_rows(const void* src, int64_t n_rows, int head_dim, uint8_t* d
 
 template <bool BF16SRC>
 static int launch_tensor(const void* src, int64_t n, uint8_t* dst, float* scale, hipStream_t s) {
-  const int64_t want = (n + 255) / 256;
-  const unsigned blocks = (unsigned)(want < 4096 ? (want > 0 ? want : 1) : 4096);
+  const int64_t want = (n / 8 + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 2048 ? (want > 0 ? want : 1) : 2048);
   hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, s, scale);
   hipLaunchKernelGGL((amax_kernel<BF16SRC>), dim3(blocks), dim3(256), 0, s, src, n, scale);
   hipLaunchKernelGGL((quant_tensor_kernel<BF16SRC>), dim3(blocks), dim3(256), 0, s, src, n, dst, scale);

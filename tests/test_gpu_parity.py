@@ -72,12 +72,13 @@ def test_parity_bf16_out(name):
 
 
 @pytest.mark.parametrize("mode", ["per_token_head", "per_tensor"])
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [64, 128, 256, 512, 1024])
 def test_quantizer_bit_exact(mode, d):
     g = torch.Generator().manual_seed(d)
     x = (torch.randn(333, d, generator=g) * torch.rand(333, 1, generator=g) * 5).to(torch.bfloat16)
     x[7] = 0
     x[11, :3] = torch.tensor([1e-30, 3e4, -2.0])
+    x[13, :4] = torch.tensor([-0.0, 9.2e-41, -9.2e-41, 0.0])          # signed zeros, bf16 subnormals
     xd = x.cuda()
     n = x.shape[0]
     codes = torch.empty(n, d, dtype=torch.uint8, device="cuda")
@@ -86,6 +87,25 @@ def test_quantizer_bit_exact(mode, d):
     torch.cuda.synchronize()
     bits = x.view(torch.int16).numpy().astype(np.uint16)
     rc, rs = quantize_per_row(bits, "bf16") if mode == "per_token_head" else quantize_per_tensor(bits, "bf16")
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scale.cpu().numpy().reshape(np.shape(rs)), rs)
+
+
+@pytest.mark.parametrize("mode", ["per_token_head", "per_tensor"])
+def test_quantizer_division_stress(mode):
+    # fp32 values with arbitrary mantissas over 2^-20..2^20: the quotient x / scale must
+    # be the IEEE fp32 one for every element (the kernel divides once per row and
+    # corrects each element's product with the reciprocal)
+    rng = np.random.default_rng(17)
+    n, d = 2048, 64
+    x = (rng.uniform(1.0, 2.0, (n, d)) * np.exp2(rng.integers(-20, 21, (n, d)))
+         * rng.choice([-1.0, 1.0], (n, d))).astype(np.float32)
+    x[::7, 5] = -0.0
+    codes = torch.empty(n, d, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(n if mode == "per_token_head" else 1, dtype=torch.float32, device="cuda")
+    pa_kv_quantize_fp8(torch.from_numpy(x).cuda(), "fp32", n, d, mode, codes, scale)
+    torch.cuda.synchronize()
+    rc, rs = quantize_per_row(x, "fp32") if mode == "per_token_head" else quantize_per_tensor(x, "fp32")
     assert np.array_equal(codes.cpu().numpy(), rc)
     assert np.array_equal(scale.cpu().numpy().reshape(np.shape(rs)), rs)
 
