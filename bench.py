@@ -55,6 +55,16 @@ def _cpu_model() -> str:
 KERNEL_SOURCES = ("stage1.hip", "common.hpp", "pa_internal.hpp")
 
 
+def kernel_code(text: str) -> str:
+    """Source text without comments and blank lines: what the digest of a kernel covers
+    (a comment edit does not change the kernel the counters measured)."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line.strip())
+
+
 def measured_traffic(config: str):
     """HBM bytes per stage-1 launch from the committed FETCH_SIZE/WRITE_SIZE summary of this
     workload, or None when there is none or the kernel sources changed since it was taken."""
@@ -63,8 +73,8 @@ def measured_traffic(config: str):
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_split_kv_stage1_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_split_kv_stage1_amd", "csrc", f)) as fh:
+            h.update(kernel_code(fh.read()).encode())
     for path in glob.glob(os.path.join(ROOT, "profiles", f"stage1_kernel_{config}_*_hbm_traffic.txt")):
         fields = {}
         for line in open(path):

@@ -12,12 +12,13 @@
 // (ds_read_b64_tr_b16 / _tr_b8), the LDS-side counterpart of the in-kernel V
 // transpose FP8 tensor cores need (FlashInfer PR #869, item 1).
 //
-// KV tiles stream HBM -> VGPRs (16-byte loads, PD tiles ahead) -> LDS (NS stages);
-// the LDS footprint is kept small enough for two workgroups per CU, so that one
-// workgroup's prologue and tail overlap the other's streaming.
+// KV tiles stream HBM -> VGPRs (16-byte non-temporal loads, PD tiles ahead) -> LDS
+// (NS stages); the LDS footprint is kept small enough for two workgroups per CU, so
+// that one workgroup's prologue and tail overlap the other's streaming.
 //
 // Per tile, each wave owns 32 tokens x (its query blocks):
-//   QK:  bf16 MFMA 16x16x32 (bf16 Q; FP8 K upconverted exactly), or fp8 MFMA
+//   QK:  bf16 MFMA 16x16x32 (bf16 Q; FP8 K upconverted exactly, once when the tile is
+//        stored if four query-block waves read it, else as it is read), or fp8 MFMA
 //        16x16x32 when Q is FP8 (exact products);
 //   softmax: scores scaled into the log2 domain with the dequant scales folded in
 //        (FlashInfer PR #869 item 3), per-row causal/window masks, online max/sum,
