@@ -63,3 +63,13 @@ def f64_to_e4m3_rne(x: np.ndarray) -> np.ndarray:
     code = np.where(_POS_VALS[hi] == a, _POS_CODES[hi], code)   # exact hits
     neg = np.signbit(x)
     return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def f32_to_bf16_bits_rne(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit pattern, round to nearest, ties to even (the upper 16
+    bits of the float32 after adding 0x7FFF plus the lowest kept bit); NaN stays a
+    quiet NaN."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    return np.where(nan, (u >> 16) | 0x40, rounded).astype(np.uint16)
