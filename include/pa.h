@@ -161,6 +161,31 @@ pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev,
 pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows, int32_t head_dim,
                              pa_scale_mode mode, uint8_t* dst, float* scale, void* stream);
 
+/* KV append (device): writes the keys and values of n_tokens new tokens into the paged
+ * caches, as a serving step does before decode attention reads them (the per-token-head
+ * FP8 KV cache of FreeToken PR #900, end-to-end table; per-tensor scales as in FlashMLA
+ * PR #54, "Functionality").  The row of token t for KV head h goes to cache element
+ * (page, h, slot, :) with page = slot_mapping[t] / page_size, slot = slot_mapping[t] %
+ * page_size, addressed through kv.
+ *   k_new, v_new   device [n_tokens, num_kv_heads, head_dim], src_dtype BF16 or FP32,
+ *                  contiguous, 16-byte aligned
+ *   slot_mapping   device int64 [n_tokens]; a negative entry skips the token (padding)
+ *   kv_dtype BF16, mode NONE: rows stored as bf16 (FP32 sources rounded to nearest even);
+ *   kv_dtype FP8_E4M3, mode PER_TENSOR: codes RNE_e4m3(clamp(x / s, -448, 448)) with the
+ *                  caches' scales s = *k_scale, *v_scale (device scalars, only read);
+ *   kv_dtype FP8_E4M3, mode PER_TOKEN_HEAD: each row's scale amax/448 (1 if amax == 0)
+ *                  is written to k_scale / v_scale at (page, h, slot) through sc and the
+ *                  codes are those of pa_kv_quantize_fp8.
+ * The caller owns every buffer; slots must be distinct and inside the caches.  Cache
+ * pointers and strides must be 16-byte aligned (as for stage 1).  Errors:
+ * INVALID_ARGUMENT (NULL pointer, misalignment, dtype/mode combination), UNSUPPORTED
+ * (head_dim not 64 times a power of two up to 1024, page_size not a power of two). */
+pa_status pa_kv_append(const void* k_new, const void* v_new, pa_dtype src_dtype, int64_t n_tokens,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size, const int64_t* slot_mapping,
+                       void* k_cache, void* v_cache, pa_dtype kv_dtype, pa_scale_mode mode,
+                       const pa_kv_layout* kv, float* k_scale, float* v_scale, const pa_scale_layout* sc,
+                       void* stream);
+
 /* Test hook (device): for every work item of KV head 0 and every token t of its
  * split, writes the physical slot page*P + slot that stage 1 reads for token t of
  * its request to phys_out[kv_tok_offset[b] + t] (int64), where kv_tok_offset[b] =

@@ -73,8 +73,12 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(ScaleLayout), _p, ctypes.c_float, _p, _p, _p, ctypes.c_int, _p]
         L.pa_decode_merge.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, ctypes.c_int, _p, _p]
         L.pa_kv_quantize_fp8.argtypes = [_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, _p, _p, _p]
+        L.pa_kv_append.argtypes = [_p, _p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, _p, _p, _p, ctypes.c_int, ctypes.c_int, ctypes.POINTER(KVLayout),
+                                   _p, _p, ctypes.POINTER(ScaleLayout), _p]
         L.pa_debug_gather.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, _p]
-        for f in ("pa_plan_splits", "pa_decode_stage1", "pa_decode_merge", "pa_kv_quantize_fp8", "pa_debug_gather"):
+        for f in ("pa_plan_splits", "pa_decode_stage1", "pa_decode_merge", "pa_kv_quantize_fp8", "pa_kv_append",
+                  "pa_debug_gather"):
             getattr(L, f).restype = ctypes.c_int
         L.pa_last_error.restype = ctypes.c_char_p
         L.pa_version.restype = ctypes.c_char_p
@@ -154,6 +158,16 @@ def pa_decode_merge(info, plan_dev, partial_o, partial_lse, out, out_dtype, out_
 def pa_kv_quantize_fp8(src, src_dtype, n_rows, head_dim, mode, dst, scale, stream=None):
     _check(lib().pa_kv_quantize_fp8(_ptr(src), _dt(src_dtype), int(n_rows), int(head_dim), _sm(mode), _ptr(dst),
                                     _ptr(scale), _stream(stream)))
+
+
+def pa_kv_append(k_new, v_new, src_dtype, n_tokens, num_kv_heads, head_dim, page_size, slot_mapping, k_cache,
+                 v_cache, kv_dtype, mode, kv_layout, k_scale=None, v_scale=None, scale_layout=None, stream=None):
+    kvl = KVLayout(*kv_layout)
+    scl = None if scale_layout is None else ScaleLayout(*scale_layout)
+    _check(lib().pa_kv_append(_ptr(k_new), _ptr(v_new), _dt(src_dtype), ctypes.c_int64(int(n_tokens)),
+                              int(num_kv_heads), int(head_dim), int(page_size), _ptr(slot_mapping), _ptr(k_cache),
+                              _ptr(v_cache), _dt(kv_dtype), _sm(mode), ctypes.byref(kvl), _ptr(k_scale),
+                              _ptr(v_scale), None if scl is None else ctypes.byref(scl), _stream(stream)))
 
 
 def pa_debug_gather(info, plan_dev, page_indices, phys_out, kv_tok_offset, stream=None):

@@ -435,6 +435,44 @@ pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows
   return ok();
 }
 
+pa_status pa_kv_append(const void* k_new, const void* v_new, pa_dtype src_dtype, int64_t n_tokens,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size, const int64_t* slot_mapping,
+                       void* k_cache, void* v_cache, pa_dtype kv_dtype, pa_scale_mode mode,
+                       const pa_kv_layout* kv, float* k_scale, float* v_scale, const pa_scale_layout* sc,
+                       void* stream) {
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !kv)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: NULL pointer");
+  if (src_dtype != PA_DTYPE_BF16 && src_dtype != PA_DTYPE_FP32)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: src_dtype must be BF16 or FP32");
+  int m;
+  if (kv_dtype == PA_DTYPE_BF16 && mode == PA_SCALE_NONE) m = 0;
+  else if (kv_dtype == PA_DTYPE_FP8_E4M3 && mode == PA_SCALE_PER_TENSOR) m = 1;
+  else if (kv_dtype == PA_DTYPE_FP8_E4M3 && mode == PA_SCALE_PER_TOKEN_HEAD) m = 2;
+  else return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: kv_dtype/mode must be BF16/NONE, FP8/PER_TENSOR or FP8/PER_TOKEN_HEAD");
+  if (m > 0 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: FP8 caches need k_scale and v_scale");
+  if (m == 2 && !sc) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: per-token-head scales need a scale layout");
+  if (n_tokens < 0 || num_kv_heads < 1) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: n_tokens >= 0, num_kv_heads >= 1");
+  if (head_dim < 64 || head_dim > 1024 || head_dim % 64 || ilog2_exact(head_dim / 64) < 0)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d: must be 64 times a power of two, at most 1024", head_dim);
+  const int shift = ilog2_exact(page_size);
+  if (shift < 0) return fail(PA_ERR_UNSUPPORTED, "page_size %d: must be a power of two", page_size);
+  const int esz = kv_dtype == PA_DTYPE_BF16 ? 2 : 1;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: sources and caches must be 16-byte aligned");
+  if ((kv->page * esz) % 16 || (kv->head * esz) % 16 || (kv->slot * esz) % 16 || kv->page < 0 || kv->head < 0 ||
+      kv->slot < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: cache strides must be non-negative and 16-byte multiples");
+  AppendArgs a;
+  a.k_new = k_new; a.v_new = v_new; a.slots = slot_mapping;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.n_tokens = n_tokens; a.hkv = num_kv_heads; a.page_shift = shift;
+  a.kv_sp = kv->page; a.kv_sh = kv->head; a.kv_ss = kv->slot;
+  a.sc_sp = m == 2 ? sc->page : 0; a.sc_sh = m == 2 ? sc->head : 0; a.sc_ss = m == 2 ? sc->slot : 0;
+  const int e = launch_append(a, src_dtype == PA_DTYPE_BF16, head_dim, m, stream);
+  if (e) return hip_fail(e, "pa_kv_append launch");
+  return ok();
+}
+
 pa_status pa_debug_gather(const pa_plan_info* info, const void* plan_dev, const int32_t* page_indices,
                           int64_t* phys_out, const int64_t* kv_tok_offset, void* stream) {
   if (!info || !plan_dev || !page_indices || !phys_out || !kv_tok_offset)

@@ -168,6 +168,99 @@ static int launch_tensor(const void* src, int64_t n, uint8_t* dst, float* scale,
   return (int)hipGetLastError();
 }
 
+// ---- KV append -------------------------------------------------------------------------
+// Rows of the new tokens' K (first n_tokens * hkv rows) then V, laid out like the
+// quantiser's rows, each written to its token's slot in the paged cache.  MODE: 0 bf16
+// cache, 1 FP8 with the caches' per-tensor scales, 2 FP8 with per-token-head scales.
+// Rows of skipped tokens (negative slot) and rows past the end take part in the row's
+// lane shuffles but store nothing.
+template <bool BF16SRC, int D, int MODE>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  constexpr int EPL = D >= 512 ? D / 64 : 8;
+  constexpr int LPR = D / EPL;
+  constexpr int RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63;
+  const int64_t per = a.n_tokens * a.hkv;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const int part = lane % LPR;
+  const bool is_v = row >= per;
+  const int64_t rr = is_v ? row - per : row;          // token * hkv + head
+  const int64_t t = rr / a.hkv;
+  const int h = (int)(rr - t * a.hkv);
+  const int64_t slot = row < 2 * per ? a.slots[t] : -1;
+  const bool live = slot >= 0;
+  const void* src = is_v ? a.v_new : a.k_new;
+  float x[EPL];
+  float amax = 0.f;
+  if (live) {
+#pragma unroll
+    for (int c = 0; c < EPL / 8; ++c) load8<BF16SRC>(src, rr * D + (int64_t)part * EPL + 8 * c, x + 8 * c);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  }
+  if constexpr (MODE == 2) {
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  }
+  if (!live) return;
+  const int64_t page = slot >> a.page_shift;
+  const int64_t s_in = slot & ((1 << a.page_shift) - 1);
+  const int64_t off = page * a.kv_sp + (int64_t)h * a.kv_sh + s_in * a.kv_ss + (int64_t)part * EPL;
+  if constexpr (MODE == 0) {
+    uint16_t* dst = static_cast<uint16_t*>(is_v ? a.v_cache : a.k_cache) + off;
+#pragma unroll
+    for (int c = 0; c < EPL / 8; ++c) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[8 * c + e];   // exact for bf16, RNE for fp32
+      *reinterpret_cast<bf16x8*>(dst + 8 * c) = v;
+    }
+  } else {
+    float sc;
+    if constexpr (MODE == 1) sc = *(is_v ? a.v_scale : a.k_scale);
+    else sc = scale_of(amax);
+    const float inv = 1.0f / sc;
+    uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) + off;
+#pragma unroll
+    for (int c = 0; c < EPL / 8; ++c) *reinterpret_cast<uint2*>(dst + 8 * c) = encode8(x + 8 * c, sc, inv);
+    if constexpr (MODE == 2) {
+      if (part == 0)
+        (is_v ? a.v_scale : a.k_scale)[page * a.sc_sp + (int64_t)h * a.sc_sh + s_in * a.sc_ss] = sc;
+    }
+  }
+}
+
+template <bool BF16SRC, int MODE>
+static int launch_append_mode(const AppendArgs& a, int head_dim, hipStream_t s) {
+  const int64_t rows = 2 * a.n_tokens * a.hkv;
+  auto blocks = [&](int d) {
+    const int rpw = 64 / (d / (d >= 512 ? d / 64 : 8));
+    return (unsigned)((rows + 4 * rpw - 1) / (4 * rpw));
+  };
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL((append_kernel<BF16SRC, 64, MODE>), dim3(blocks(64)), dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((append_kernel<BF16SRC, 128, MODE>), dim3(blocks(128)), dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL((append_kernel<BF16SRC, 256, MODE>), dim3(blocks(256)), dim3(256), 0, s, a); break;
+    case 512: hipLaunchKernelGGL((append_kernel<BF16SRC, 512, MODE>), dim3(blocks(512)), dim3(256), 0, s, a); break;
+    case 1024: hipLaunchKernelGGL((append_kernel<BF16SRC, 1024, MODE>), dim3(blocks(1024)), dim3(256), 0, s, a); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_append(const AppendArgs& a, int src_bf16, int head_dim, int mode, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (a.n_tokens <= 0) return 0;
+  if (src_bf16) {
+    if (mode == 0) return launch_append_mode<true, 0>(a, head_dim, s);
+    if (mode == 1) return launch_append_mode<true, 1>(a, head_dim, s);
+    return launch_append_mode<true, 2>(a, head_dim, s);
+  }
+  if (mode == 0) return launch_append_mode<false, 0>(a, head_dim, s);
+  if (mode == 1) return launch_append_mode<false, 1>(a, head_dim, s);
+  return launch_append_mode<false, 2>(a, head_dim, s);
+}
+
 int launch_quant(const void* src, int src_bf16, int64_t n_rows, int head_dim, int per_tensor, uint8_t* dst,
                  float* scale, void* stream) {
   hipStream_t s = (hipStream_t)stream;

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_library_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "pa.h")).read()
     declared = set(re.findall(r"^(?:pa_status|const char\*)\s+(pa_\w+)\(", header, flags=re.M))
-    assert {"pa_plan_splits", "pa_decode_stage1", "pa_decode_merge", "pa_kv_quantize_fp8",
+    assert {"pa_plan_splits", "pa_decode_stage1", "pa_decode_merge", "pa_kv_quantize_fp8", "pa_kv_append",
             "pa_debug_gather", "pa_last_error"} <= declared
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in declared:
@@ -190,6 +190,27 @@ def test_quantize_validates():
     with pytest.raises(PaError) as e:
         _lib.pa_kv_quantize_fp8(fake, "bf16", 10, 128, "none", fake, fake)
     assert e.value.status == PA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(kv_dtype="bf16", mode="per_tensor"), PA_ERR_INVALID_ARGUMENT),       # dtype/mode combination
+    (dict(kv_dtype="fp8", mode="none"), PA_ERR_INVALID_ARGUMENT),
+    (dict(head_dim=96), PA_ERR_UNSUPPORTED),
+    (dict(page_size=48), PA_ERR_UNSUPPORTED),
+    (dict(k_scale=None), PA_ERR_INVALID_ARGUMENT),                             # FP8 without scales
+    (dict(scale_layout=None), PA_ERR_INVALID_ARGUMENT),                        # per-token-head without layout
+    (dict(k_new=(1 << 20) + 8), PA_ERR_INVALID_ARGUMENT),                      # misaligned source
+    (dict(kv_layout=(4096, 256, 24)), PA_ERR_INVALID_ARGUMENT),                # slot stride not 16 B
+])
+def test_append_validates(case, status):
+    fake = 1 << 20
+    args = dict(k_new=fake, v_new=fake, src_dtype="bf16", n_tokens=4, num_kv_heads=2, head_dim=128, page_size=16,
+                slot_mapping=fake, k_cache=fake, v_cache=fake, kv_dtype="fp8", mode="per_token_head",
+                kv_layout=(4096, 2048, 128), k_scale=fake, v_scale=fake, scale_layout=(32, 16, 1))
+    args.update(case)
+    with pytest.raises(PaError) as e:
+        _lib.pa_kv_append(**args)
+    assert e.value.status == status
 
 
 def test_merge_without_splits_is_a_noop():
