@@ -12,6 +12,7 @@
 
 #include "pa.h"
 #include "pa_internal.hpp"
+#include "kv_append.hpp"
 
 using namespace pa;
 

@@ -15,6 +15,7 @@
 // Memory access: 8 consecutive elements per lane (16-byte loads of bf16, two of fp32)
 // and 8-byte code stores.
 #include "common.hpp"
+#include "kv_append.hpp"
 
 namespace pa {
 
