@@ -65,23 +65,32 @@ def kernel_code(text: str) -> str:
     return "\n".join(line for line in lines if line.strip())
 
 
-def measured_traffic(config: str):
-    """HBM bytes per stage-1 launch from the committed FETCH_SIZE/WRITE_SIZE summary of this
-    workload, or None when there is none or the kernel sources changed since it was taken."""
-    import glob
+CACHE_OP_SOURCES = ("quant.hip", "common.hpp", "kv_append.hpp")
+
+
+def source_digest(files) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "paged_split_kv_stage1_amd", "csrc", f)) as fh:
             h.update(kernel_code(fh.read()).encode())
-    for path in glob.glob(os.path.join(ROOT, "profiles", f"stage1_kernel_{config}_*_hbm_traffic.txt")):
+    return h.hexdigest()
+
+
+def measured_traffic(config: str, kernel: str = "stage1_kernel", sources=KERNEL_SOURCES):
+    """HBM bytes per launch of ``kernel`` from the committed FETCH_SIZE/WRITE_SIZE summary of
+    this workload, or None when there is none or the kernel sources changed since it was taken."""
+    import glob
+
+    digest = source_digest(sources)
+    for path in glob.glob(os.path.join(ROOT, "profiles", f"{kernel}_{config}_*_hbm_traffic.txt")):
         fields = {}
         for line in open(path):
             if ":" in line:
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-        if fields.get("kernel_source_sha256") == h.hexdigest() and "traffic_bytes_per_launch" in fields:
+        if fields.get("kernel_source_sha256") == digest and "traffic_bytes_per_launch" in fields:
             return int(fields["traffic_bytes_per_launch"])
     return None
 
@@ -136,6 +145,167 @@ def cpu_baseline(w, out_gpu: np.ndarray, budget_s: float, threads: int = 0):
             "seconds": round(elapsed, 3)}, err
 
 
+def cache_op_bytes(op: str, n: int, hkv: int, d: int, kv: str, mode: str) -> int:
+    """Algorithmic HBM bytes of one cache operation over n tokens of bf16 rows [n, Hkv, d].
+
+    kv_append: per K or V row, read the bf16 row (2d), write the cache row (d codes or 2d
+    bf16) and, per token and head, the fp32 scale; plus the int64 slot of each token.
+    kv_quantize (one tensor of n*Hkv rows): per-row mode reads 2d and writes d + 4 per
+    row; per-tensor mode reads the tensor twice (the amax must be known before encoding
+    and the tensor does not fit on chip) and writes d per row."""
+    cb = 1 if kv == "fp8" else 2
+    pt = mode == "per_token_head"
+    if op == "kv_append":
+        return n * 8 + 2 * n * hkv * (2 * d + cb * d + (4 if pt else 0))
+    rows = n * hkv
+    return rows * (3 * d + 4) if pt else rows * 5 * d
+
+
+def cache_op_cpu_baseline(op, hkv, d, P, kv, mode, budget_s):
+    """Times the oracle's append / quantiser on growing samples of tokens until the
+    budget is spent (single thread: the oracle loops over rows in Python)."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle.cache import append_kv
+    from oracle.quantize import quantize_per_row, quantize_per_tensor
+
+    kind = {"none": "bf16", "per_tensor": "fp8_per_tensor", "per_token_head": "fp8_per_token_head"}[mode]
+    gen = torch.Generator().manual_seed(11)
+    m, elapsed, done = 16, 0.0, 0
+    with threadpool_limits(limits=1):
+        while elapsed < budget_s:
+            bits = torch.randn(m, hkv, d, generator=gen).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            t0 = time.perf_counter()
+            if op == "kv_append":
+                pages = (m + P - 1) // P
+                cache = np.zeros((pages, hkv, P, d), dtype=np.uint8 if kv == "fp8" else np.uint16)
+                sc = np.zeros((pages, hkv, P), dtype=np.float32) if kind == "fp8_per_token_head" else None
+                for _ in range(2):                                  # K and V
+                    append_kv(cache, sc, bits, "bf16", np.arange(m), P, kind, tensor_scale=0.02)
+            elif mode == "per_token_head":
+                quantize_per_row(bits.reshape(m * hkv, d), "bf16")
+            else:
+                quantize_per_tensor(bits.reshape(m * hkv, d), "bf16")
+            elapsed += time.perf_counter() - t0
+            done += m
+            # double the batch, but not past what the rest of the budget can take
+            m = max(16, min(2 * m, int((budget_s - elapsed) * done / elapsed)))
+    return {"value": round(cache_op_bytes(op, done, hkv, d, kv, mode) / elapsed / 1e9, 5), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{done} tokens x {hkv} KV heads in growing batches, {elapsed:.1f} s of numpy on 1 thread, "
+                      f"{_cpu_model()}", "seconds": round(elapsed, 3)}
+
+
+def bench_cache_op(args):
+    """KV append (new tokens' bf16 K/V rows into random pages of the paged cache) or the
+    standalone quantiser, on one workload's cache geometry and dtypes."""
+    import torch
+
+    from paged_split_kv_stage1_amd import pa_kv_append, pa_kv_quantize_fp8
+    from paged_split_kv_stage1_amd.inputs import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    hkv, d, P, kv, mode = cfg["hkv"], cfg["d"], cfg["page"], cfg["kv"], cfg["scale"]
+    if args.op == "kv_quantize" and kv != "fp8":
+        raise SystemExit(f"{args.config} keeps a bf16 cache: nothing to quantise")
+    n = args.tokens
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator().manual_seed(7)
+    k_new = torch.randn(n, hkv, d, generator=gen).to(torch.bfloat16).to(dev)
+    v_new = (torch.randn(n, hkv, d, generator=gen) * 2).to(torch.bfloat16).to(dev)
+    stream = torch.cuda.current_stream()
+    pt = mode == "per_token_head"
+    if args.op == "kv_append":
+        pages = (n + P - 1) // P + 64
+        perm = np.random.default_rng(7).permutation(pages)
+        slots = torch.from_numpy((perm[np.arange(n) // P] * P + np.arange(n) % P).astype(np.int64)).to(dev)
+        dt = torch.uint8 if kv == "fp8" else torch.bfloat16
+        kc = torch.zeros(pages, hkv, P, d, dtype=dt, device=dev)
+        vc = torch.zeros_like(kc)
+        layout = (hkv * P * d, P * d, d)
+        ks = vs = sl = None
+        if pt:
+            ks = torch.zeros(pages, hkv, P, dtype=torch.float32, device=dev)
+            vs = torch.zeros_like(ks)
+            sl = (hkv * P, P, 1)
+        elif mode == "per_tensor":
+            ks = torch.full((1,), 0.02, dtype=torch.float32, device=dev)
+            vs = torch.full((1,), 0.04, dtype=torch.float32, device=dev)
+
+        def run():
+            pa_kv_append(k_new, v_new, "bf16", n, hkv, d, P, slots, kc, vc, kv, mode, layout, ks, vs, sl,
+                         stream=stream)
+        kernel = "append_kernel"
+    else:
+        codes = torch.empty(n, hkv, d, dtype=torch.uint8, device=dev)
+        scale = torch.empty(n * hkv if pt else 1, dtype=torch.float32, device=dev)
+
+        def run():
+            pa_kv_quantize_fp8(k_new, "bf16", n * hkv, d, mode, codes, scale, stream=stream)
+        kernel = "quant_rows_kernel" if pt else "quant_tensor_kernel"
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    _spin_up(flush)
+    for _ in range(args.warmup):
+        flush.fill_(1.0)
+        run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush.fill_(1.0)
+        ev[i][0].record(stream)
+        run()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    nbytes = cache_op_bytes(args.op, n, hkv, d, kv, mode)
+    gbps = nbytes / (us * 1e-6) / 1e9
+    what = {"kv_append": f"append {n} tokens into random pages", "kv_quantize": f"quantise {n * hkv} rows"}[args.op]
+    result = {
+        "metric": f"{args.op} achieved HBM GB/s, 1 GPU", "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 -> " + ("bf16" if kv == "bf16" else "fp8-e4m3"),
+        "data": "synthetic (seeded N(0,1) bf16 rows)",
+        "config": {"workload": f"{what}, {hkv} KV heads d{d} P{P} {kv} cache, scales {mode}", "op": args.op,
+                   "name": args.config, "tokens": n, "num_kv_heads": hkv, "head_dim": d, "page_size": P,
+                   "kv_dtype": kv, "kv_scale_mode": mode, "cache_flush_between_steps": True},
+        "us_per_step": round(us, 3), "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(f"{args.op}_{args.config}", kernel, CACHE_OP_SOURCES),
+                     "kernel": kernel, "bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cache_op_cpu_baseline(args.op, hkv, d, P, kv, mode, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def _spin_up(flush, seconds: float = 0.5):
+    """Streams the flush buffer for ``seconds`` before the warm-up steps: a few dozen steps
+    of tens of microseconds do not bring the clocks up, so without this the warm-up and the
+    first timed steps (and a profiler's per-call average over all of them) run slower."""
+    import torch
+
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            flush.fill_(1.0)
+        torch.cuda.synchronize()
+
+
+def _calibrate_copy():
+    """One 256 MiB device-to-device copy: a known-size reference for the HBM counters."""
+    import torch
+
+    src = torch.ones(256 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,12 +319,19 @@ def main():
     ap.add_argument("--force-splits", type=int, default=None)
     ap.add_argument("--graph-reps", type=int, default=100,
                     help="also time this many replays of stage 1 + merge captured in one hipGraph (0: skip)")
+    ap.add_argument("--op", default="decode", choices=["decode", "kv_append", "kv_quantize"],
+                    help="decode (stage 1 + merge), or the cache-side append / quantiser on the workload's geometry")
+    ap.add_argument("--tokens", type=int, default=131072, help="tokens appended or quantised per step (cache ops)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first, as a known-size reference for HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
+    if args.calibrate_copy:
+        _calibrate_copy()
+    if args.op != "decode":
+        return bench_cache_op(args)
 
     import torch
 
@@ -188,14 +365,7 @@ def main():
                   di.page_indices, w.sm_scale, out, w.out_dtype, stream=st)
         pd.merge(out, w.out_dtype, stream=st)
 
-    if args.calibrate_copy:
-        src = torch.ones(256 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
+    _spin_up(flush)
     for _ in range(args.warmup):
         if not args.no_flush:
             flush.fill_(1.0)

@@ -179,7 +179,8 @@ pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows
  * The caller owns every buffer; slots must be distinct and inside the caches.  Cache
  * pointers and strides must be 16-byte aligned (as for stage 1).  Errors:
  * INVALID_ARGUMENT (NULL pointer, misalignment, dtype/mode combination), UNSUPPORTED
- * (head_dim not 64 times a power of two up to 1024, page_size not a power of two). */
+ * (head_dim not 64 times a power of two up to 1024, page_size not a power of two,
+ * 2 * n_tokens * num_kv_heads >= 2^31). */
 pa_status pa_kv_append(const void* k_new, const void* v_new, pa_dtype src_dtype, int64_t n_tokens,
                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size, const int64_t* slot_mapping,
                        void* k_cache, void* v_cache, pa_dtype kv_dtype, pa_scale_mode mode,

@@ -453,6 +453,8 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, pa_dtype src_dtype,
   if (m > 0 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: FP8 caches need k_scale and v_scale");
   if (m == 2 && !sc) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: per-token-head scales need a scale layout");
   if (n_tokens < 0 || num_kv_heads < 1) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: n_tokens >= 0, num_kv_heads >= 1");
+  if (2 * n_tokens * num_kv_heads >= (int64_t(1) << 31))
+    return fail(PA_ERR_UNSUPPORTED, "pa_kv_append: 2 * n_tokens * num_kv_heads must be below 2^31");
   if (head_dim < 64 || head_dim > 1024 || head_dim % 64 || ilog2_exact(head_dim / 64) < 0)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d: must be 64 times a power of two, at most 1024", head_dim);
   const int shift = ilog2_exact(page_size);

@@ -12,8 +12,13 @@
 // subnormal quotient is far below e4m3's smallest step and encodes to zero either
 // way; the sign is copied from x so that -0 keeps its code.
 //
-// Memory access: 8 consecutive elements per lane (16-byte loads of bf16, two of fp32)
-// and 8-byte code stores.
+// Memory access: a row of D elements is LPR lanes x EPL consecutive elements (EPL = 8,
+// or D/64 for D >= 512): 16-byte loads of bf16 (two of fp32) and 8-byte code stores.  A
+// wave takes U groups of 64/LPR consecutive rows and issues the loads of all of them
+// before it encodes the first, so that enough bytes are in flight per CU to stream at
+// HBM rate.  Every row is read once and every code written once, so loads and stores
+// carry the non-temporal hint (with dirty lines left in L2 by earlier writes, plain
+// loads stream at about two thirds of the rate).
 #include "common.hpp"
 #include "kv_append.hpp"
 
@@ -22,15 +27,15 @@ namespace pa {
 template <bool BF16SRC>
 __device__ __forceinline__ void load8(const void* src, int64_t i, float* x) {
   if constexpr (BF16SRC) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(src) + i);
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(src) + i));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       x[2 * k] = __uint_as_float(w[k] << 16);
       x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
     }
   } else {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + i);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + i + 4);
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + i));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + i + 4));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       x[k] = a[k];
@@ -38,6 +43,17 @@ __device__ __forceinline__ void load8(const void* src, int64_t i, float* x) {
     }
   }
 }
+
+// BIG: U = 4 row groups per wave (2 for D = 1024) on inputs that fill the chip several
+// times over; otherwise U = 1, so that small inputs still spread over many workgroups.
+template <int D, bool BIG>
+struct RowShape {
+  static constexpr int EPL = D >= 512 ? D / 64 : 8;   // elements per lane
+  static constexpr int LPR = D / EPL;                 // lanes per row
+  static constexpr int RPW = 64 / LPR;                // rows per wave and group
+  static constexpr int U = BIG ? (EPL == 8 ? 4 : 2) : 1;
+  static constexpr int ROWS_PER_BLOCK = 4 * RPW * U;
+};
 
 __device__ __forceinline__ float scale_of(float amax) { return amax == 0.f ? 1.0f : amax / 448.0f; }
 
@@ -56,52 +72,69 @@ __device__ __forceinline__ uint2 encode8(const float* x, float sc, float inv) {
   return uint2{f32x4_to_fp8x4(q[0], q[1], q[2], q[3]), f32x4_to_fp8x4(q[4], q[5], q[6], q[7])};
 }
 
-// Per-row scales.  A row of D elements is LPR lanes x EPL elements (EPL = 8, or D/64
-// for D >= 512); a wave holds 64 / LPR rows and a workgroup four waves' worth.
-template <bool BF16SRC, int D>
+// Streaming stores: 8 codes, 8 bf16.
+__device__ __forceinline__ void store_codes(uint8_t* p, uint2 c) {
+  __builtin_nontemporal_store((uint64_t)c.x | ((uint64_t)c.y << 32), reinterpret_cast<uint64_t*>(p));
+}
+__device__ __forceinline__ void store_bf16x8(uint16_t* p, bf16x8 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(p));
+}
+
+// Per-row scales.  Rows past the end load the last row (branch-free loads) and store
+// nothing.
+template <bool BF16SRC, int D, bool BIG>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* src, int64_t n_rows, uint8_t* dst,
                                                          float* scale) {
-  constexpr int EPL = D >= 512 ? D / 64 : 8;
-  constexpr int LPR = D / EPL;
-  constexpr int RPW = 64 / LPR;
+  using S = RowShape<D, BIG>;
   const int lane = threadIdx.x & 63;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
-  const int part = lane % LPR;
-  const bool live = row < n_rows;
-  float x[EPL];
-  float amax = 0.f;
-  if (live) {
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (S::RPW * S::U) + lane / S::LPR;
+  const int part = lane % S::LPR;
+  float x[S::U][S::EPL];
 #pragma unroll
-    for (int c = 0; c < EPL / 8; ++c) load8<BF16SRC>(src, row * D + (int64_t)part * EPL + 8 * c, x + 8 * c);
+  for (int u = 0; u < S::U; ++u) {
+    const int64_t row = min(row0 + u * S::RPW, n_rows - 1);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    for (int c = 0; c < S::EPL / 8; ++c)
+      load8<BF16SRC>(src, row * D + (int64_t)part * S::EPL + 8 * c, x[u] + 8 * c);
   }
 #pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  if (!live) return;
-  const float sc = scale_of(amax);
-  const float inv = 1.0f / sc;                            // IEEE divide, once per row
+  for (int u = 0; u < S::U; ++u) {
+    float amax = 0.f;
 #pragma unroll
-  for (int c = 0; c < EPL / 8; ++c)
-    *reinterpret_cast<uint2*>(dst + row * D + (int64_t)part * EPL + 8 * c) = encode8(x + 8 * c, sc, inv);
-  if (part == 0) scale[row] = sc;
+    for (int e = 0; e < S::EPL; ++e) amax = fmaxf(amax, fabsf(x[u][e]));
+#pragma unroll
+    for (int off = S::LPR / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const int64_t row = row0 + u * S::RPW;
+    if (row >= n_rows) continue;
+    const float sc = scale_of(amax);
+    const float inv = 1.0f / sc;                          // IEEE divide, once per row
+#pragma unroll
+    for (int c = 0; c < S::EPL / 8; ++c)
+      store_codes(dst + row * D + (int64_t)part * S::EPL + 8 * c, encode8(x[u] + 8 * c, sc, inv));
+    if (part == 0) scale[row] = sc;
+  }
 }
 
 __global__ void zero_word_kernel(float* p) { *p = 0.f; }
 
-// Per-tensor amax over n elements (n a multiple of 8), four 8-element groups in flight.
+// Per-tensor amax over n elements (n a multiple of 8), TENSOR_U 8-element groups in flight
+// per lane over a grid-stride loop.  The four wave maxima of a workgroup meet in LDS and
+// one atomic max per workgroup goes to the word (atomics on one address serialise, so
+// one per wave would cost more than the streaming at the end of the pass).
+constexpr int TENSOR_U = 4;
+
 template <bool BF16SRC>
 __global__ __launch_bounds__(256) void amax_kernel(const void* src, int64_t n, float* amax_word) {
   const int64_t groups = n / 8;
   const int64_t stride = (int64_t)gridDim.x * 256;
   float m = 0.f;
   int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; gi + 3 * stride < groups; gi += 4 * stride) {
-    float x[4][8];
+  for (; gi + (TENSOR_U - 1) * stride < groups; gi += TENSOR_U * stride) {
+    float x[TENSOR_U][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) load8<BF16SRC>(src, (gi + u * stride) * 8, x[u]);
+    for (int u = 0; u < TENSOR_U; ++u) load8<BF16SRC>(src, (gi + u * stride) * 8, x[u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < TENSOR_U; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[u][e]));
   }
@@ -113,8 +146,14 @@ __global__ __launch_bounds__(256) void amax_kernel(const void* src, int64_t n, f
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  // non-negative floats order like their bit patterns
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(amax_word), __float_as_uint(m));
+  __shared__ float wave_max[4];
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+    // non-negative floats order like their bit patterns
+    atomicMax(reinterpret_cast<unsigned int*>(amax_word), __float_as_uint(m));
+  }
 }
 
 template <bool BF16SRC>
@@ -125,34 +164,48 @@ __global__ __launch_bounds__(256) void quant_tensor_kernel(const void* src, int6
   const int64_t groups = n / 8;
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; gi + stride < groups; gi += 2 * stride) {
-    float x[2][8];
-    load8<BF16SRC>(src, gi * 8, x[0]);
-    load8<BF16SRC>(src, (gi + stride) * 8, x[1]);
-    *reinterpret_cast<uint2*>(dst + gi * 8) = encode8(x[0], sc, inv);
-    *reinterpret_cast<uint2*>(dst + (gi + stride) * 8) = encode8(x[1], sc, inv);
+  for (; gi + (TENSOR_U - 1) * stride < groups; gi += TENSOR_U * stride) {
+    float x[TENSOR_U][8];
+#pragma unroll
+    for (int u = 0; u < TENSOR_U; ++u) load8<BF16SRC>(src, (gi + u * stride) * 8, x[u]);
+#pragma unroll
+    for (int u = 0; u < TENSOR_U; ++u) store_codes(dst + (gi + u * stride) * 8, encode8(x[u], sc, inv));
   }
   for (; gi < groups; gi += stride) {
     float x[8];
     load8<BF16SRC>(src, gi * 8, x);
-    *reinterpret_cast<uint2*>(dst + gi * 8) = encode8(x, sc, inv);
+    store_codes(dst + gi * 8, encode8(x, sc, inv));
   }
 }
 
 __global__ void finish_scale_kernel(float* scale) { scale[0] = scale_of(scale[0]); }
 
+constexpr unsigned kBigGrid = 2048;      // 8 workgroups per CU: enough to take U = 4
+
+template <int D, bool BIG>
+static unsigned grid_of(int64_t n_rows) {
+  constexpr int per = RowShape<D, BIG>::ROWS_PER_BLOCK;
+  return (unsigned)((n_rows + per - 1) / per);
+}
+
+template <bool BF16SRC, int D>
+static void launch_rows_d(const void* src, int64_t n_rows, uint8_t* dst, float* scale, hipStream_t s) {
+  const unsigned big = grid_of<D, true>(n_rows);
+  if (big >= kBigGrid)
+    hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, D, true>), dim3(big), dim3(256), 0, s, src, n_rows, dst, scale);
+  else
+    hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, D, false>), dim3(grid_of<D, false>(n_rows)), dim3(256), 0, s,
+                       src, n_rows, dst, scale);
+}
+
 template <bool BF16SRC>
 static int launch_rows(const void* src, int64_t n_rows, int head_dim, uint8_t* dst, float* scale, hipStream_t s) {
-  auto blocks = [&](int d) {
-    const int rpw = 64 / (d / (d >= 512 ? d / 64 : 8));
-    return (unsigned)((n_rows + 4 * rpw - 1) / (4 * rpw));
-  };
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 64>), dim3(blocks(64)), dim3(256), 0, s, src, n_rows, dst, scale); break;
-    case 128: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 128>), dim3(blocks(128)), dim3(256), 0, s, src, n_rows, dst, scale); break;
-    case 256: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 256>), dim3(blocks(256)), dim3(256), 0, s, src, n_rows, dst, scale); break;
-    case 512: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 512>), dim3(blocks(512)), dim3(256), 0, s, src, n_rows, dst, scale); break;
-    case 1024: hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, 1024>), dim3(blocks(1024)), dim3(256), 0, s, src, n_rows, dst, scale); break;
+    case 64: launch_rows_d<BF16SRC, 64>(src, n_rows, dst, scale, s); break;
+    case 128: launch_rows_d<BF16SRC, 128>(src, n_rows, dst, scale, s); break;
+    case 256: launch_rows_d<BF16SRC, 256>(src, n_rows, dst, scale, s); break;
+    case 512: launch_rows_d<BF16SRC, 512>(src, n_rows, dst, scale, s); break;
+    case 1024: launch_rows_d<BF16SRC, 1024>(src, n_rows, dst, scale, s); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
@@ -161,7 +214,7 @@ static int launch_rows(const void* src, int64_t n_rows, int head_dim, uint8_t* d
 template <bool BF16SRC>
 static int launch_tensor(const void* src, int64_t n, uint8_t* dst, float* scale, hipStream_t s) {
   const int64_t want = (n / 8 + 255) / 256;
-  const unsigned blocks = (unsigned)(want < 2048 ? (want > 0 ? want : 1) : 2048);
+  const unsigned blocks = (unsigned)(want < 1024 ? (want > 0 ? want : 1) : 1024);   // 4 per CU
   hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, s, scale);
   hipLaunchKernelGGL((amax_kernel<BF16SRC>), dim3(blocks), dim3(256), 0, s, src, n, scale);
   hipLaunchKernelGGL((quant_tensor_kernel<BF16SRC>), dim3(blocks), dim3(256), 0, s, src, n, dst, scale);
@@ -173,77 +226,90 @@ static int launch_tensor(const void* src, int64_t n, uint8_t* dst, float* scale,
 // Rows of the new tokens' K (first n_tokens * hkv rows) then V, laid out like the
 // quantiser's rows, each written to its token's slot in the paged cache.  MODE: 0 bf16
 // cache, 1 FP8 with the caches' per-tensor scales, 2 FP8 with per-token-head scales.
-// Rows of skipped tokens (negative slot) and rows past the end take part in the row's
-// lane shuffles but store nothing.
-template <bool BF16SRC, int D, int MODE>
+// Row indices fit in 32 bits (the host checks 2 * n_tokens * hkv < 2^31).  Rows of
+// skipped tokens (negative slot) and rows past the end still load a row (the last one,
+// past the end) so that the loads stay branch-free, and store nothing.
+template <bool BF16SRC, int D, int MODE, bool BIG>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  constexpr int EPL = D >= 512 ? D / 64 : 8;
-  constexpr int LPR = D / EPL;
-  constexpr int RPW = 64 / LPR;
+  using S = RowShape<D, BIG>;
   const int lane = threadIdx.x & 63;
-  const int64_t per = a.n_tokens * a.hkv;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
-  const int part = lane % LPR;
-  const bool is_v = row >= per;
-  const int64_t rr = is_v ? row - per : row;          // token * hkv + head
-  const int64_t t = rr / a.hkv;
-  const int h = (int)(rr - t * a.hkv);
-  const int64_t slot = row < 2 * per ? a.slots[t] : -1;
-  const bool live = slot >= 0;
-  const void* src = is_v ? a.v_new : a.k_new;
-  float x[EPL];
-  float amax = 0.f;
-  if (live) {
+  const uint32_t hkv = (uint32_t)a.hkv;
+  const uint32_t per = (uint32_t)a.n_tokens * hkv;
+  const uint32_t row0 = ((uint32_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (S::RPW * S::U) + lane / S::LPR;
+  const int part = lane % S::LPR;
+  float x[S::U][S::EPL];
+  int64_t slot[S::U];
 #pragma unroll
-    for (int c = 0; c < EPL / 8; ++c) load8<BF16SRC>(src, rr * D + (int64_t)part * EPL + 8 * c, x + 8 * c);
+  for (int u = 0; u < S::U; ++u) {
+    const uint32_t row = min(row0 + u * S::RPW, 2 * per - 1);
+    const bool is_v = row >= per;
+    const uint32_t rr = is_v ? row - per : row;          // token * hkv + head
+    slot[u] = row0 + u * S::RPW < 2 * per ? a.slots[rr / hkv] : -1;
+    const void* src = is_v ? a.v_new : a.k_new;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    for (int c = 0; c < S::EPL / 8; ++c)
+      load8<BF16SRC>(src, (int64_t)rr * D + part * S::EPL + 8 * c, x[u] + 8 * c);
   }
-  if constexpr (MODE == 2) {
 #pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  }
-  if (!live) return;
-  const int64_t page = slot >> a.page_shift;
-  const int64_t s_in = slot & ((1 << a.page_shift) - 1);
-  const int64_t off = page * a.kv_sp + (int64_t)h * a.kv_sh + s_in * a.kv_ss + (int64_t)part * EPL;
-  if constexpr (MODE == 0) {
-    uint16_t* dst = static_cast<uint16_t*>(is_v ? a.v_cache : a.k_cache) + off;
-#pragma unroll
-    for (int c = 0; c < EPL / 8; ++c) {
-      bf16x8 v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[8 * c + e];   // exact for bf16, RNE for fp32
-      *reinterpret_cast<bf16x8*>(dst + 8 * c) = v;
-    }
-  } else {
-    float sc;
-    if constexpr (MODE == 1) sc = *(is_v ? a.v_scale : a.k_scale);
-    else sc = scale_of(amax);
-    const float inv = 1.0f / sc;
-    uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) + off;
-#pragma unroll
-    for (int c = 0; c < EPL / 8; ++c) *reinterpret_cast<uint2*>(dst + 8 * c) = encode8(x + 8 * c, sc, inv);
+  for (int u = 0; u < S::U; ++u) {
+    float amax = 0.f;
     if constexpr (MODE == 2) {
-      if (part == 0)
-        (is_v ? a.v_scale : a.k_scale)[page * a.sc_sp + (int64_t)h * a.sc_sh + s_in * a.sc_ss] = sc;
+#pragma unroll
+      for (int e = 0; e < S::EPL; ++e) amax = fmaxf(amax, fabsf(x[u][e]));
+#pragma unroll
+      for (int off = S::LPR / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    }
+    if (slot[u] < 0) continue;
+    const uint32_t row = row0 + u * S::RPW;
+    const bool is_v = row >= per;
+    const uint32_t rr = is_v ? row - per : row;
+    const uint32_t h = rr % hkv;
+    const int64_t page = slot[u] >> a.page_shift;
+    const int64_t s_in = slot[u] & ((1 << a.page_shift) - 1);
+    const int64_t off = page * a.kv_sp + (int64_t)h * a.kv_sh + s_in * a.kv_ss + part * S::EPL;
+    if constexpr (MODE == 0) {
+      uint16_t* dst = static_cast<uint16_t*>(is_v ? a.v_cache : a.k_cache) + off;
+#pragma unroll
+      for (int c = 0; c < S::EPL / 8; ++c) {
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[u][8 * c + e];   // exact for bf16, RNE for fp32
+        store_bf16x8(dst + 8 * c, v);
+      }
+    } else {
+      float sc;
+      if constexpr (MODE == 1) sc = *(is_v ? a.v_scale : a.k_scale);
+      else sc = scale_of(amax);
+      const float inv = 1.0f / sc;
+      uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) + off;
+#pragma unroll
+      for (int c = 0; c < S::EPL / 8; ++c) store_codes(dst + 8 * c, encode8(x[u] + 8 * c, sc, inv));
+      if constexpr (MODE == 2) {
+        if (part == 0)
+          (is_v ? a.v_scale : a.k_scale)[page * a.sc_sp + (int64_t)h * a.sc_sh + s_in * a.sc_ss] = sc;
+      }
     }
   }
 }
 
+template <bool BF16SRC, int D, int MODE>
+static void launch_append_d(const AppendArgs& a, hipStream_t s) {
+  const int64_t rows = 2 * a.n_tokens * a.hkv;
+  const unsigned big = grid_of<D, true>(rows);
+  if (big >= kBigGrid)
+    hipLaunchKernelGGL((append_kernel<BF16SRC, D, MODE, true>), dim3(big), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((append_kernel<BF16SRC, D, MODE, false>), dim3(grid_of<D, false>(rows)), dim3(256), 0, s, a);
+}
+
 template <bool BF16SRC, int MODE>
 static int launch_append_mode(const AppendArgs& a, int head_dim, hipStream_t s) {
-  const int64_t rows = 2 * a.n_tokens * a.hkv;
-  auto blocks = [&](int d) {
-    const int rpw = 64 / (d / (d >= 512 ? d / 64 : 8));
-    return (unsigned)((rows + 4 * rpw - 1) / (4 * rpw));
-  };
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL((append_kernel<BF16SRC, 64, MODE>), dim3(blocks(64)), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((append_kernel<BF16SRC, 128, MODE>), dim3(blocks(128)), dim3(256), 0, s, a); break;
-    case 256: hipLaunchKernelGGL((append_kernel<BF16SRC, 256, MODE>), dim3(blocks(256)), dim3(256), 0, s, a); break;
-    case 512: hipLaunchKernelGGL((append_kernel<BF16SRC, 512, MODE>), dim3(blocks(512)), dim3(256), 0, s, a); break;
-    case 1024: hipLaunchKernelGGL((append_kernel<BF16SRC, 1024, MODE>), dim3(blocks(1024)), dim3(256), 0, s, a); break;
+    case 64: launch_append_d<BF16SRC, 64, MODE>(a, s); break;
+    case 128: launch_append_d<BF16SRC, 128, MODE>(a, s); break;
+    case 256: launch_append_d<BF16SRC, 256, MODE>(a, s); break;
+    case 512: launch_append_d<BF16SRC, 512, MODE>(a, s); break;
+    case 1024: launch_append_d<BF16SRC, 1024, MODE>(a, s); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

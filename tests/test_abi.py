@@ -201,6 +201,7 @@ def test_quantize_validates():
     (dict(scale_layout=None), PA_ERR_INVALID_ARGUMENT),                        # per-token-head without layout
     (dict(k_new=(1 << 20) + 8), PA_ERR_INVALID_ARGUMENT),                      # misaligned source
     (dict(kv_layout=(4096, 256, 24)), PA_ERR_INVALID_ARGUMENT),                # slot stride not 16 B
+    (dict(n_tokens=1 << 29, num_kv_heads=2), PA_ERR_UNSUPPORTED),              # row index past 32 bits
 ])
 def test_append_validates(case, status):
     fake = 1 << 20

@@ -108,3 +108,55 @@ def test_appended_tokens_are_what_decode_reads(name):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8))
     o, _, _ = run_decode(w, di)
     assert np.array_equal(o, o_ref)
+
+
+# Enough rows for the launch to take four row groups per wave (2048 workgroups and more),
+# with a ragged last workgroup: (kind, Hkv, d, P, tokens, source dtype).
+MANY = [
+    ("fp8_per_token_head", 2, 256, 16, 16384 + 11, "bf16"),
+    ("fp8_per_tensor", 8, 128, 64, 8192 + 5, "fp32"),
+    ("bf16", 2, 256, 16, 16384 + 11, "bf16"),
+]
+
+
+@pytest.mark.parametrize("kind,hkv,d,P,n,src", MANY)
+def test_append_many_rows_matches_oracle(kind, hkv, d, P, n, src):
+    print(f"[append many] {kind} Hkv={hkv} d={d} n={n} {src}", flush=True)
+    rng = np.random.default_rng(n + d)
+    pages = (n + P - 1) // P + 9
+    shape = (pages, hkv, P, d)
+    if kind == "bf16":
+        c0 = [rng.integers(0, 1 << 16, shape).astype(np.uint16) for _ in range(2)]
+    else:
+        c0 = [rng.integers(0, 256, shape).astype(np.uint8) for _ in range(2)]
+    pt = kind == "fp8_per_token_head"
+    s0 = [rng.random(shape[:3]).astype(np.float32) for _ in range(2)] if pt else [None, None]
+    slots = rng.permutation(pages * P)[:n].astype(np.int64)
+    slots[rng.choice(n, 40, replace=False)] = -1
+    new = [torch.randn(n, hkv, d) * 4, torch.randn(n, hkv, d) * torch.rand(n, hkv, 1) * 6]
+    if src == "bf16":
+        new = [t.to(torch.bfloat16) for t in new]
+        rows = [t.view(torch.int16).numpy().view(np.uint16) for t in new]
+    else:
+        rows = [t.numpy() for t in new]
+    ts = [np.float32(0.03), np.float32(0.05)]
+    as_t = (lambda a: torch.from_numpy(a.view(np.int16).copy())) if kind == "bf16" else \
+           (lambda a: torch.from_numpy(a.copy()))
+    caches = [as_t(c).cuda() for c in c0]
+    if pt:
+        scales = [torch.from_numpy(s.copy()).cuda() for s in s0]
+    elif kind == "fp8_per_tensor":
+        scales = [torch.tensor([t]).cuda() for t in ts]
+    else:
+        scales = [None, None]
+    pa_kv_append(new[0].cuda(), new[1].cuda(), src, n, hkv, d, P, torch.from_numpy(slots).cuda(), caches[0],
+                 caches[1], "bf16" if kind == "bf16" else "fp8",
+                 {"bf16": "none", "fp8_per_tensor": "per_tensor", "fp8_per_token_head": "per_token_head"}[kind],
+                 (hkv * P * d, P * d, d), scales[0], scales[1], (hkv * P, P, 1) if pt else None)
+    torch.cuda.synchronize()
+    for i in range(2):
+        rc, rs = append_kv(c0[i], s0[i], rows[i], src, slots, P, kind, "HPD", tensor_scale=ts[i])
+        got = caches[i].cpu().numpy()
+        assert np.array_equal(got.view(np.uint16) if kind == "bf16" else got, rc)
+        if pt:
+            assert np.array_equal(scales[i].cpu().numpy(), rs)

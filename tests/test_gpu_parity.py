@@ -110,6 +110,40 @@ def test_quantizer_division_stress(mode):
     assert np.array_equal(scale.cpu().numpy().reshape(np.shape(rs)), rs)
 
 
+# Row counts at which the launch takes four row groups per wave (two for d = 1024), plus a
+# ragged tail; and a per-tensor size whose grid-stride loop runs twice and then a tail.
+MANY_ROWS = {64: 262144 + 37, 128: 131072 + 37, 256: 65536 + 37, 512: 32768 + 37, 1024: 16384 + 37}
+
+
+@pytest.mark.parametrize("d", list(MANY_ROWS))
+def test_quantizer_many_rows_bit_exact(d):
+    n = MANY_ROWS[d]
+    print(f"[quant many] d={d} rows={n}", flush=True)
+    g = torch.Generator().manual_seed(d + 1)
+    x = (torch.randn(n, d, generator=g) * torch.rand(n, 1, generator=g) * 5).to(torch.bfloat16)
+    codes = torch.empty(n, d, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(n, dtype=torch.float32, device="cuda")
+    pa_kv_quantize_fp8(x.cuda(), "bf16", n, d, "per_token_head", codes, scale)
+    torch.cuda.synchronize()
+    rc, rs = quantize_per_row(x.view(torch.int16).numpy().view(np.uint16), "bf16")
+    assert np.array_equal(scale.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantizer_per_tensor_many_groups_bit_exact():
+    n, d = 133000, 128
+    g = torch.Generator().manual_seed(3)
+    x = (torch.randn(n, d, generator=g) * 2).to(torch.bfloat16)
+    x[n - 1, d - 1] = -37.5                                          # the amax sits in the tail
+    codes = torch.empty(n, d, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(1, dtype=torch.float32, device="cuda")
+    pa_kv_quantize_fp8(x.cuda(), "bf16", n, d, "per_tensor", codes, scale)
+    torch.cuda.synchronize()
+    rc, rs = quantize_per_tensor(x.view(torch.int16).numpy().view(np.uint16), "bf16")
+    assert scale.cpu().numpy()[0] == rs
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
 def test_quantizer_fp32_source_bit_exact():
     g = torch.Generator().manual_seed(5)
     x = torch.randn(100, 128, generator=g) * 3
