@@ -68,7 +68,14 @@ struct S1Cfg {
   static constexpr int DB = DH / 16;                // 16-wide d blocks of P.V
   static constexpr bool PV_FP8 = KVF8 && !PT;       // per-tensor FP8 V: fp8 MFMA for P.V
   static constexpr int EPIB = (WT > 1) ? (4 * NQB * DB * 256 * 4 + 4 * NQB * 64 * 2 * 4) : 0;
-  static constexpr int MAINB = NS * STAGEB;
+  // Query blocks whose operand stays in registers.  Three blocks of bf16 queries against
+  // per-token-head FP8 would need more than 256 VGPRs: the third block's operand lives in
+  // LDS instead (16 B per lane and K-step, re-read every tile).  A spilled register
+  // would be reloaded from scratch every tile, and the wait for that load also waits for
+  // every tile load still in flight, which undoes the prefetch.
+  static constexpr int QREG = (NQB == 3 && KVF8 && PT && !QF8) ? 2 : NQB;
+  static constexpr int QLB = (NQB - QREG) * KC * 1024;   // LDS bytes per wave
+  static constexpr int MAINB = NS * STAGEB + 4 * QLB;
   static constexpr int LDSB = MAINB > EPIB ? MAINB : EPIB;
   static_assert(CPT >= 1 && (BN * CPR) % 256 == 0, "tile must split evenly over 256 threads");
   static_assert(WT == 1 || NQB == 1, "query blocks per wave > 1 only without token split");
@@ -125,8 +132,13 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
   const int shift = a.page_shift;
   const int pmask = (1 << shift) - 1;
 
-  // ---- query operand (registers), per-row limits ---------------------------------------
-  QT qop[NQB][C::KC];
+  // ---- query operand (registers, or LDS past QREG blocks), per-row limits -----------------
+  QT qop[NQB][C::KC];                                    // blocks >= QREG are never touched
+  uint8_t* const qlds = smem + NS * C::STAGEB + wave * C::QLB + lane * 16;
+  auto qget = [&](int i, int kc) __attribute__((always_inline)) -> QT {
+    if (i < C::QREG) return qop[i][kc];
+    return *reinterpret_cast<const QT*>(qlds + ((i - C::QREG) * C::KC + kc) * 1024);
+  };
   int lim_lo[NQB], lim_hi[NQB];
   bool qvalid[NQB];
 #pragma unroll
@@ -325,8 +337,9 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
         if constexpr (C::LBF) {
           const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Kl + kro[0][kc]);
           const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Kl + kro[1][kc]);
-          s0 = mfma_bf16(k0, qop[i][kc], s0);
-          s1 = mfma_bf16(k1, qop[i][kc], s1);
+          const QT qv = qget(i, kc);
+          s0 = mfma_bf16(k0, qv, s0);
+          s1 = mfma_bf16(k1, qv, s1);
         } else {
           const uint2 r0 = *reinterpret_cast<const uint2*>(Kl + kro[0][kc]);
           const uint2 r1 = *reinterpret_cast<const uint2*>(Kl + kro[1][kc]);
@@ -473,10 +486,13 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
     const int64_t qrow = ((int64_t)(it.row0 + r) * Hq + (int64_t)it.kvh * G + hl) * DH;
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
+      QT v;
       if constexpr (QF8)
-        qop[i][kc] = *reinterpret_cast<const long*>(static_cast<const uint8_t*>(a.q) + qrow + kc * 32 + 8 * g);
+        v = *reinterpret_cast<const long*>(static_cast<const uint8_t*>(a.q) + qrow + kc * 32 + 8 * g);
       else
-        qop[i][kc] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + qrow + kc * 32 + 8 * g);
+        v = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + qrow + kc * 32 + 8 * g);
+      if (i < C::QREG) qop[i][kc] = v;
+      else *reinterpret_cast<QT*>(qlds + ((i - C::QREG) * C::KC + kc) * 1024) = v;   // read back by this lane only
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);          // vmcnt(0) lgkmcnt(0)
