@@ -55,8 +55,9 @@ class PagedKV:
 
     data: bf16 bit patterns (uint16) or e4m3 codes (uint8), shape
           [pages, Hkv, P, d] for layout "HPD" or [pages, P, Hkv, d] for "PHD".
-    scale: None; a float32 scalar (per tensor); or float32 [pages, Hkv, P] ("HPD")
-           / [pages, P, Hkv] ("PHD") for per-(token, KV head) scales.
+    scale: None; a float32 scalar (per tensor); float32 [Hkv] (per head); or float32
+           [pages, Hkv, P] ("HPD") / [pages, P, Hkv] ("PHD") for per-(token, KV head)
+           scales.
     """
     data: np.ndarray
     dtype: str
@@ -84,6 +85,8 @@ class PagedKV:
             raise ValueError(self.dtype)
         if self.scale_mode == "per_tensor":
             val = val * np.float64(np.float32(self.scale))
+        elif self.scale_mode == "per_head":
+            val = val * np.float64(np.asarray(self.scale, dtype=np.float32)[g])
         elif self.scale_mode == "per_token_head":
             sc = self.scale[page, g, slot] if self.layout == "HPD" else self.scale[page, slot, g]
             val = val * np.asarray(sc, dtype=np.float32).astype(np.float64)[:, None]
@@ -91,11 +94,15 @@ class PagedKV:
 
 
 def dequant_q(q_raw: np.ndarray, q_dtype: str, q_scale=None) -> np.ndarray:
-    """Query [T, Hq, d] -> float64: bf16 bits, or e4m3 codes times a per-tensor scale."""
+    """Query [T, Hq, d] -> float64: bf16 bits, or e4m3 codes times a per-tensor scale
+    (a scalar) or per-query-head scales ([Hq])."""
     if q_dtype == "bf16":
         return bf16_bits_to_f64(q_raw)
     if q_dtype == "fp8":
-        return e4m3_code_to_f64(q_raw) * np.float64(np.float32(q_scale))
+        qs = np.asarray(q_scale, dtype=np.float32).astype(np.float64)
+        if qs.ndim == 1:
+            qs = qs[None, :, None]
+        return e4m3_code_to_f64(q_raw) * qs
     raise ValueError(q_dtype)
 
 

@@ -5,7 +5,8 @@ into the paged cache before decode attention reads them.  With the per-token-hea
 FP8 KV cache (FreeToken PR #900, end-to-end table row "fp8_per_token_head") every
 (token, KV head) row is quantised with its own scale as it is written; with a
 per-tensor FP8 cache the rows are encoded with the cache's given scale (FlashMLA
-PR #54, symmetric per-tensor scales).
+PR #54, symmetric per-tensor scales) or with its head's given scale (per-head scales,
+FlashInfer PR #869).
 
 Readings where the pages are silent:
   * token t goes to physical slot slot_mapping[t] = page * P + slot, the slot that
@@ -36,8 +37,9 @@ def append_kv(cache: np.ndarray, scales, rows: np.ndarray, src_dtype: str, slot_
     and returns (cache, scales).
 
     kind: "bf16" (cache holds bf16 bit patterns), "fp8_per_tensor" (codes, encoded with
-    ``tensor_scale``), "fp8_per_token_head" (codes, and ``scales`` [pages, Hkv, P] or
-    [pages, P, Hkv] receives each row's scale)."""
+    ``tensor_scale``), "fp8_per_head" (codes, KV head h encoded with
+    ``tensor_scale[h]``), "fp8_per_token_head" (codes, and ``scales`` [pages, Hkv, P]
+    or [pages, P, Hkv] receives each row's scale)."""
     cache = cache.copy()
     scales = None if scales is None else scales.copy()
     n, hkv, _ = rows.shape
@@ -53,6 +55,8 @@ def append_kv(cache: np.ndarray, scales, rows: np.ndarray, src_dtype: str, slot_
                 cache[idx] = rows[t, h] if src_dtype == "bf16" else f32_to_bf16_bits_rne(x32[t, h])
             elif kind == "fp8_per_tensor":
                 cache[idx] = _encode(x32[t, h], np.float32(tensor_scale))
+            elif kind == "fp8_per_head":
+                cache[idx] = _encode(x32[t, h], np.float32(np.asarray(tensor_scale, dtype=np.float32)[h]))
             elif kind == "fp8_per_token_head":
                 codes, sc = quantize_per_row(rows[t, h][None], src_dtype)
                 cache[idx] = codes[0]

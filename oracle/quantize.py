@@ -4,6 +4,8 @@ What the pages fix:
   * symmetric per-tensor scales for Q/K/V (FlashMLA PR #54, "Functionality");
   * a per-token-head FP8 KV cache, i.e. one scale per (token, KV head)
     (FreeToken PR #900, end-to-end table row "fp8_per_token_head");
+  * per-head scales, one per head over all of that head's values (FlashInfer PR
+    #869, title: per-head quantization);
   * scale = amax / 448 over the quantised group (the workloads' statement).
 Readings where the pages are silent: the scale is computed in float32 as
 fl32(amax / 448); a value is encoded as RNE_e4m3(clamp(fl32(x / scale), -448, 448))
@@ -11,7 +13,7 @@ with an IEEE float32 division; a group whose amax is 0 gets scale 1 (all codes 0
 
 Inputs are rows of d values (bf16 bit patterns, or float32); for per-token-head
 scales a row is one (token, KV head) vector, for per-tensor scales all rows share
-one scale.
+one scale, for per-head scales all rows of one head share one.
 """
 from __future__ import annotations
 
@@ -55,3 +57,17 @@ def quantize_per_row(src: np.ndarray, src_dtype: str):
     amax = np.max(np.abs(x), axis=-1).astype(np.float32)
     scale = _scale_from_amax(amax)
     return _encode(x, scale[..., None]), scale
+
+
+def quantize_per_head(src: np.ndarray, src_dtype: str, head_axis: int):
+    """Per-head scales: one scale per index of ``head_axis`` over every value of that
+    head (all tokens and all d).  Returns (codes uint8 with src's shape, scales
+    float32 [H])."""
+    x = _as_f32(src, src_dtype)
+    xh = np.moveaxis(x, head_axis, 0)
+    amax = np.max(np.abs(xh.reshape(xh.shape[0], -1)), axis=1).astype(np.float32) if x.size else \
+        np.zeros(x.shape[head_axis], np.float32)
+    scale = _scale_from_amax(amax)
+    shape = [1] * x.ndim
+    shape[head_axis] = -1
+    return _encode(x, scale.reshape(shape)), scale

@@ -44,8 +44,10 @@ def step_accounting(batch, qo_indptr, kv_len, window, page_size, num_q_heads, nu
     out = {
         "kv": kv_tok * num_kv_heads * 2 * d * _SIZE[kv_dtype],
         "kv_scales": kv_tok * num_kv_heads * 8 if kv_scale_mode == "per_token_head" else
-                     (8 if kv_scale_mode == "per_tensor" else 0),
-        "q": T * num_q_heads * d * _SIZE[q_dtype] + (4 if q_dtype == "fp8" else 0),
+                     (8 if kv_scale_mode == "per_tensor" else
+                      (8 * num_kv_heads if kv_scale_mode == "per_head" else 0)),
+        "q": T * num_q_heads * d * _SIZE[q_dtype] +
+             ((4 * num_q_heads if kv_scale_mode == "per_head" else 4) if q_dtype == "fp8" else 0),
         "out": T * num_q_heads * d * _SIZE[out_dtype],
         "page_table": pages * 4,
         "flops": 4 * d * row_tokens * G * num_kv_heads,

@@ -53,7 +53,7 @@ class Workload:
     unused_slots: np.ndarray   # bool [num_pages, P]: slot holds no token
     q_dtype: str               # "bf16" | "fp8"   (fp8: quantise q per tensor)
     kv_dtype: str              # "bf16" | "fp8"
-    kv_scale_mode: str         # "none" | "per_tensor" | "per_token_head"
+    kv_scale_mode: str         # "none" | "per_tensor" | "per_head" | "per_token_head"
     out_dtype: str             # "fp32" | "bf16"
     sm_scale: float            # float32 value of 1/sqrt(d)
     forced_splits: int = 0     # 0 = planner decides
@@ -78,6 +78,8 @@ CONFIGS = {
                scale="none", out="fp32", splits=4),
     "c2": dict(batch=128, rows=1, hq=64, hkv=8, d=128, ctx=2048, page=64, q="fp8", kv="fp8",
                scale="per_tensor", out="bf16"),
+    "c2_ph": dict(batch=128, rows=1, hq=64, hkv=8, d=128, ctx=2048, page=64, q="fp8", kv="fp8",
+                  scale="per_head", out="bf16"),
     "c3": dict(batch=16, rows=4, hq=16, hkv=2, d=256, ctx=32768, page=16, q="bf16", kv="bf16",
                scale="none", out="bf16"),
     "c3_b1": dict(batch=1, rows=4, hq=16, hkv=2, d=256, ctx=32768, page=16, q="bf16", kv="bf16",

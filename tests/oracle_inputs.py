@@ -4,7 +4,7 @@ import numpy as np
 import torch
 
 from oracle.attention import PagedKV, dequant_q
-from oracle.quantize import quantize_per_row, quantize_per_tensor
+from oracle.quantize import quantize_per_head, quantize_per_row, quantize_per_tensor
 from paged_split_kv_stage1_amd.inputs import BF16_NAN_BITS, E4M3_NAN_CODE
 
 
@@ -36,6 +36,14 @@ def oracle_inputs(w, layout="HPD", requests=None):
         vc = np.where(np.broadcast_to(m4, vc.shape), np.uint8(E4M3_NAN_CODE), vc)
         out["k"] = PagedKV(kc, "fp8", layout, "per_tensor", ks)
         out["v"] = PagedKV(vc, "fp8", layout, "per_tensor", vs)
+    elif w.kv_scale_mode == "per_head":
+        axis = 1 if layout == "HPD" else 2
+        kc, ks = quantize_per_head(kb, "bf16", axis)
+        vc, vs = quantize_per_head(vb, "bf16", axis)
+        kc = np.where(np.broadcast_to(m4, kc.shape), np.uint8(E4M3_NAN_CODE), kc)
+        vc = np.where(np.broadcast_to(m4, vc.shape), np.uint8(E4M3_NAN_CODE), vc)
+        out["k"] = PagedKV(kc, "fp8", layout, "per_head", ks)
+        out["v"] = PagedKV(vc, "fp8", layout, "per_head", vs)
     else:
         if requests is not None:
             pages = np.concatenate([w.page_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]] for b in requests])
@@ -53,7 +61,10 @@ def oracle_inputs(w, layout="HPD", requests=None):
         out["v"] = PagedKV(vc, "fp8", layout, "per_token_head", vs)
     qb = _bits(w.q)
     if w.q_dtype == "fp8":
-        qc, qs = quantize_per_tensor(qb, "bf16")
+        if w.kv_scale_mode == "per_head":
+            qc, qs = quantize_per_head(qb, "bf16", 1)          # one scale per query head
+        else:
+            qc, qs = quantize_per_tensor(qb, "bf16")
         out["q_codes"], out["q_scale"] = qc, qs
         out["q64"] = dequant_q(qc, "fp8", qs)
     else:

@@ -74,3 +74,20 @@ def test_append_per_tensor_exact_multiples_and_fp32_to_bf16():
     new, _ = append_kv(cb, None, x, "fp32", [1], 4, "bf16")
     ref = torch.from_numpy(x.reshape(-1)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(new[0, 0, 1], ref)
+
+
+def test_append_per_head_uses_each_heads_scale():
+    # with per-head scales, head h's row encodes as the per-tensor encoding with scale[h]:
+    # exact multiples of that scale give back exactly the e4m3 values
+    scales = np.array([0.125, 2.0, 0.0078125], np.float32)
+    vals = np.array([0.0, 1.0, -1.5, 448.0, -448.0, 2.0 ** -9, 3.25, -240.0], dtype=np.float32)
+    rows = np.stack([vals * s for s in scales])[None].astype(np.float32)        # [1, 3, 8]
+    cache = np.full((2, 3, 4, 8), 0x55, np.uint8)
+    new, _ = append_kv(cache, None, rows, "fp32", [6], 4, "fp8_per_head", tensor_scale=scales)
+    for h in range(3):
+        assert np.array_equal(e4m3_code_to_f64(new[1, h, 2]), vals.astype(np.float64))
+        one, _ = append_kv(cache, None, rows, "fp32", [6], 4, "fp8_per_tensor", tensor_scale=scales[h])
+        assert np.array_equal(new[1, h, 2], one[1, h, 2])
+    untouched = np.ones(new.shape[:3], bool)
+    untouched[1, :, 2] = False
+    assert np.all(new[untouched] == 0x55)

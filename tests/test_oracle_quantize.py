@@ -4,7 +4,7 @@ import numpy as np
 import torch
 
 from oracle.formats import e4m3_code_to_f64
-from oracle.quantize import quantize_per_row, quantize_per_tensor
+from oracle.quantize import quantize_per_head, quantize_per_row, quantize_per_tensor
 
 
 def _torch_quant_rows(x32: torch.Tensor):
@@ -50,3 +50,55 @@ def test_amax_element_maps_to_largest_code_and_error_bound():
     err = np.abs(deq - x)
     bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[:, None]) * (1 + 1e-6)
     assert np.all(err <= bound)
+
+
+def test_per_head_matches_torch_cast_head_by_head():
+    # each head's scale is the amax over all of that head's values / 448, computed by
+    # torch on the head's slice; codes are torch's cast of the clamped fp32 quotient
+    g = torch.Generator().manual_seed(4)
+    x = torch.randn(37, 5, 64, generator=g) * torch.tensor([0.01, 1.0, 30.0, 0.5, 2.0])[None, :, None]
+    x[:, 3] = 0                                      # an all-zero head: scale 1, codes 0
+    codes, scale = quantize_per_head(x.numpy(), "fp32", head_axis=1)
+    assert scale.shape == (5,)
+    for h in range(5):
+        xs = x[:, h]
+        amax = xs.abs().max()
+        ref_scale = torch.where(amax == 0, torch.ones(()), amax / 448.0)
+        ref = (xs / ref_scale).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        assert np.float32(scale[h]) == ref_scale.item()
+        assert np.array_equal(codes[:, h], ref.numpy())
+    assert scale[3] == 1.0 and not codes[:, 3].any()
+
+
+def test_per_head_heads_are_independent_and_axis_follows_layout():
+    g = torch.Generator().manual_seed(6)
+    x = torch.randn(3, 4, 16, 32, generator=g).to(torch.bfloat16)      # [pages, H, P, d]
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    c1, s1 = quantize_per_head(bits, "bf16", head_axis=1)
+    y = x.clone()
+    y[:, 0] *= 64                                    # only head 0 changes
+    c2, s2 = quantize_per_head(y.view(torch.int16).numpy().view(np.uint16), "bf16", head_axis=1)
+    assert np.array_equal(c1[:, 1:], c2[:, 1:]) and np.array_equal(s1[1:], s2[1:]) and s2[0] == 64 * s1[0]
+    # the same data in [pages, P, H, d] gives the same scales and transposed codes
+    c3, s3 = quantize_per_head(np.ascontiguousarray(bits.transpose(0, 2, 1, 3)), "bf16", head_axis=2)
+    assert np.array_equal(s3, s1) and np.array_equal(c3.transpose(0, 2, 1, 3), c1)
+
+
+def test_per_head_dequantisation_in_the_attention_inputs():
+    # PagedKV multiplies KV head g's decoded codes by scale[g]; dequant_q multiplies query
+    # head h's codes by q_scale[h] (checked against torch's own float8 decode)
+    from oracle.attention import PagedKV, dequant_q
+    rng = np.random.default_rng(8)
+    codes = rng.integers(0, 256, (2, 3, 4, 8)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x12             # no NaN codes
+    sc = np.array([0.5, 0.03125, 3.0], np.float32)
+    kv = PagedKV(codes, "fp8", "HPD", "per_head", sc)
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    slots = np.array([0, 5, 6])                      # (page 0, slot 0), (1, 1), (1, 2)
+    for gh in range(3):
+        ref = dec[slots // 4, gh, slots % 4] * np.float64(sc[gh])
+        assert np.array_equal(kv.tokens(slots, gh), ref)
+    q = codes.reshape(4, 3, 16)
+    qs = np.array([2.0, 0.25, 1.5], np.float32)
+    ref = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy() * qs[None, :, None].astype(np.float64)
+    assert np.array_equal(dequant_q(q, "fp8", qs), ref)
