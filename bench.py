@@ -30,6 +30,7 @@ HBM_PEAK_GBPS = 8000.0
 WORKLOAD_NAMES = {
     "c1": "tiny decode B1 8/1 heads d128 ctx512 P16 bf16, fp32 out, 4 splits",
     "c2": "fp8 single-row decode B128 64/8 heads d128 ctx2048 P64, e4m3 Q/K/V per-tensor, bf16 out",
+    "c2_ph": "fp8 single-row decode B128 64/8 heads d128 ctx2048 P64, e4m3 Q/K/V per-head scales, bf16 out",
     "c3": "MTP verify R4 B16 16/2 heads d256 ctx32768 P16 bf16 KV",
     "c3_b1": "MTP verify R4 B1 16/2 heads d256 ctx32768 P16 bf16 KV",
     "c3_r1": "single-row decode B16 16/2 heads d256 ctx32768 P16 bf16 KV",

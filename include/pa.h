@@ -55,7 +55,10 @@ typedef enum { PA_DTYPE_BF16 = 0, PA_DTYPE_FP32 = 1, PA_DTYPE_FP8_E4M3 = 2 } pa_
 typedef enum {
   PA_SCALE_NONE = 0,           /* bf16 KV                                               */
   PA_SCALE_PER_TENSOR = 1,     /* one float32 scale for the whole K (and one for V)     */
-  PA_SCALE_PER_TOKEN_HEAD = 2  /* one float32 scale per (token slot, KV head)           */
+  PA_SCALE_PER_TOKEN_HEAD = 2, /* one float32 scale per (token slot, KV head)           */
+  PA_SCALE_PER_HEAD = 3        /* one float32 scale per KV head for K and for V, and per */
+                               /* query head for FP8 Q (FlashInfer PR #869, title:       */
+                               /* per-head quantization)                                 */
 } pa_scale_mode;
 
 /* Element strides of a paged cache: element (page, kv_head, slot, c) lives at
@@ -82,7 +85,8 @@ typedef struct {
   int32_t head_dim;            /* 128 or 256                                                */
   pa_dtype q_dtype;            /* BF16, or FP8_E4M3 (then kv must be FP8 with a per-tensor  */
   pa_dtype kv_dtype;           /*   or per-token-head scale); kv: BF16 or FP8_E4M3          */
-  pa_scale_mode kv_scale_mode; /* NONE for bf16 KV; PER_TENSOR or PER_TOKEN_HEAD for FP8 KV  */
+  pa_scale_mode kv_scale_mode; /* NONE for bf16 KV; PER_TENSOR, PER_HEAD or PER_TOKEN_HEAD   */
+                               /*   for FP8 KV                                              */
   int32_t num_cus;             /* compute units to plan for; 0 = query the current device   */
   int32_t max_splits;          /* cap on splits per request (fixes scratch size for graph   */
                                /*   capture); 0 = no cap beyond the library's limit (1024)  */
@@ -124,10 +128,11 @@ pa_status pa_plan_splits(const pa_plan_args* args, void* plan_host, size_t plan_
  * the final output directly.
  *   plan_dev     device copy of the plan (info->plan_bytes)
  *   q            device [T, Hq, d]: bf16, or e4m3 codes with *q_scale (device float)
- *   q_scale      device float32 scalar when q is FP8, else NULL
+ *   q_scale      device float32 when q is FP8 (a scalar, or [Hq] per query head with
+ *                PER_HEAD), else NULL
  *   k_cache, v_cache  device paged caches (bf16 or e4m3 codes) with strides kv
- *   k_scale, v_scale  device float32: a scalar (PER_TENSOR) or per-token-head array
- *                with strides sc (PER_TOKEN_HEAD); NULL for bf16 KV
+ *   k_scale, v_scale  device float32: a scalar (PER_TENSOR), [Hkv] (PER_HEAD), or a
+ *                per-token-head array with strides sc (PER_TOKEN_HEAD); NULL for bf16 KV
  *   page_indices device int32, indexed through kv_indptr
  *   sm_scale     softmax scale applied to q.k (typically 1/sqrt(d) in float32)
  *   partial_o    device float32 [T, Hq, S_max, d] (unused if !info->needs_merge)
@@ -157,9 +162,23 @@ pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev,
  *   PER_TENSOR:     one scale = amax / 448 over all rows, written to scale[0].
  * dst[i, c] = RNE_e4m3(clamp(src[i, c] / scale, -448, 448)) with an IEEE float32
  * divide.  dst: device uint8 [n_rows, head_dim]; scale: device float32 (n_rows, or 1).
- * head_dim must be a multiple of 64 and <= 1024. */
+ * head_dim must be a multiple of 64 and <= 1024.  (PER_HEAD scales need the head
+ * count: pa_kv_quantize_fp8_per_head.) */
 pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows, int32_t head_dim,
                              pa_scale_mode mode, uint8_t* dst, float* scale, void* stream);
+
+/* Per-head FP8 quantiser (device; FlashInfer PR #869, per-head quantization): src is
+ * [n_tokens, num_heads, head_dim] (bf16 or float32, contiguous); head h's scale is
+ * amax over all of its n_tokens * head_dim values / 448 (1 if that amax is 0), written
+ * to scale[h] (device float32 [num_heads]); dst[t, h, c] = RNE_e4m3(clamp(src[t, h, c] /
+ * scale[h], -448, 448)) with an IEEE float32 divide (device uint8, src's shape).  A
+ * paged cache [pages, P, Hkv, d] is n_tokens = pages * P tokens of Hkv heads; use it for
+ * FP8 queries [T, Hq, d] too.  The caller owns every buffer.  Errors: INVALID_ARGUMENT
+ * (NULL pointer, src not 16-byte or dst not 8-byte aligned, src dtype, n_tokens < 0),
+ * UNSUPPORTED (num_heads outside [1, 1024], head_dim not 64 times a power of two up to
+ * 1024). */
+pa_status pa_kv_quantize_fp8_per_head(const void* src, pa_dtype src_dtype, int64_t n_tokens, int32_t num_heads,
+                                      int32_t head_dim, uint8_t* dst, float* scale, void* stream);
 
 /* KV append (device): writes the keys and values of n_tokens new tokens into the paged
  * caches, as a serving step does before decode attention reads them (the per-token-head
@@ -173,6 +192,8 @@ pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows
  *   kv_dtype BF16, mode NONE: rows stored as bf16 (FP32 sources rounded to nearest even);
  *   kv_dtype FP8_E4M3, mode PER_TENSOR: codes RNE_e4m3(clamp(x / s, -448, 448)) with the
  *                  caches' scales s = *k_scale, *v_scale (device scalars, only read);
+ *   kv_dtype FP8_E4M3, mode PER_HEAD: the same with s = k_scale[h], v_scale[h] for KV
+ *                  head h (device float32 [num_kv_heads], only read);
  *   kv_dtype FP8_E4M3, mode PER_TOKEN_HEAD: each row's scale amax/448 (1 if amax == 0)
  *                  is written to k_scale / v_scale at (page, h, slot) through sc and the
  *                  codes are those of pa_kv_quantize_fp8.

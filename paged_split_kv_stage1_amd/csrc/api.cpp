@@ -197,8 +197,8 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   if (a->kv_dtype == PA_DTYPE_BF16 && a->kv_scale_mode != PA_SCALE_NONE)
     return fail(PA_ERR_INVALID_ARGUMENT, "bf16 KV takes kv_scale_mode NONE");
   if (a->kv_dtype == PA_DTYPE_FP8_E4M3 && a->kv_scale_mode != PA_SCALE_PER_TENSOR &&
-      a->kv_scale_mode != PA_SCALE_PER_TOKEN_HEAD)
-    return fail(PA_ERR_INVALID_ARGUMENT, "FP8 KV takes kv_scale_mode PER_TENSOR or PER_TOKEN_HEAD");
+      a->kv_scale_mode != PA_SCALE_PER_HEAD && a->kv_scale_mode != PA_SCALE_PER_TOKEN_HEAD)
+    return fail(PA_ERR_INVALID_ARGUMENT, "FP8 KV takes kv_scale_mode PER_TENSOR, PER_HEAD or PER_TOKEN_HEAD");
   if (a->q_dtype == PA_DTYPE_FP8_E4M3 && a->kv_dtype != PA_DTYPE_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "FP8 queries need an FP8 KV cache");
   if (a->max_splits < 0 || a->force_splits < 0 || a->num_cus < 0)
@@ -374,6 +374,7 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const
   s.kv_ss = kv->slot;
   s.k_scale = k_scale;
   s.v_scale = v_scale;
+  s.scale_per_head = info->kv_scale_mode == PA_SCALE_PER_HEAD;
   if (sc) {
     s.sc_sp = sc->page;
     s.sc_sh = sc->head;
@@ -423,7 +424,7 @@ pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows
   if (!src || !dst || !scale) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_quantize_fp8: NULL pointer");
   if (src_dtype != PA_DTYPE_BF16 && src_dtype != PA_DTYPE_FP32)
     return fail(PA_ERR_INVALID_ARGUMENT, "src_dtype must be BF16 or FP32");
-  if (mode != PA_SCALE_PER_TENSOR && mode != PA_SCALE_PER_TOKEN_HEAD)
+  if (mode != PA_SCALE_PER_TENSOR && mode != PA_SCALE_PER_TOKEN_HEAD)   // per-head: pa_kv_quantize_fp8_per_head
     return fail(PA_ERR_INVALID_ARGUMENT, "mode must be PER_TENSOR or PER_TOKEN_HEAD");
   if (n_rows < 0) return fail(PA_ERR_INVALID_ARGUMENT, "n_rows must be >= 0");
   if (head_dim < 64 || head_dim > 1024 || ilog2_exact(head_dim / 64) < 0 || head_dim % 64)
@@ -433,6 +434,23 @@ pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows
   const int e = launch_quant(src, src_dtype == PA_DTYPE_BF16, n_rows, head_dim, mode == PA_SCALE_PER_TENSOR, dst,
                              scale, stream);
   if (e) return hip_fail(e, "pa_kv_quantize_fp8 launch");
+  return ok();
+}
+
+pa_status pa_kv_quantize_fp8_per_head(const void* src, pa_dtype src_dtype, int64_t n_tokens, int32_t num_heads,
+                                      int32_t head_dim, uint8_t* dst, float* scale, void* stream) {
+  if (!src || !dst || !scale) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_quantize_fp8_per_head: NULL pointer");
+  if (src_dtype != PA_DTYPE_BF16 && src_dtype != PA_DTYPE_FP32)
+    return fail(PA_ERR_INVALID_ARGUMENT, "src_dtype must be BF16 or FP32");
+  if (n_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "n_tokens must be >= 0");
+  if (num_heads < 1 || num_heads > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "num_heads %d: must be in [1, 1024]", num_heads);
+  if (head_dim < 64 || head_dim > 1024 || ilog2_exact(head_dim / 64) < 0 || head_dim % 64)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d: must be 64 times a power of two, at most 1024", head_dim);
+  if (!aligned16(src) || ((uintptr_t)dst & 7u) != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_quantize_fp8_per_head: src must be 16-byte and dst 8-byte aligned");
+  const int e = launch_quant_heads(src, src_dtype == PA_DTYPE_BF16, n_tokens, num_heads, head_dim, dst, scale, stream);
+  if (e) return hip_fail(e, "pa_kv_quantize_fp8_per_head launch");
   return ok();
 }
 
@@ -447,9 +465,10 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, pa_dtype src_dtype,
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: src_dtype must be BF16 or FP32");
   int m;
   if (kv_dtype == PA_DTYPE_BF16 && mode == PA_SCALE_NONE) m = 0;
-  else if (kv_dtype == PA_DTYPE_FP8_E4M3 && mode == PA_SCALE_PER_TENSOR) m = 1;
+  else if (kv_dtype == PA_DTYPE_FP8_E4M3 && (mode == PA_SCALE_PER_TENSOR || mode == PA_SCALE_PER_HEAD)) m = 1;
   else if (kv_dtype == PA_DTYPE_FP8_E4M3 && mode == PA_SCALE_PER_TOKEN_HEAD) m = 2;
-  else return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: kv_dtype/mode must be BF16/NONE, FP8/PER_TENSOR or FP8/PER_TOKEN_HEAD");
+  else return fail(PA_ERR_INVALID_ARGUMENT,
+                   "pa_kv_append: kv_dtype/mode must be BF16/NONE or FP8 with PER_TENSOR, PER_HEAD or PER_TOKEN_HEAD");
   if (m > 0 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: FP8 caches need k_scale and v_scale");
   if (m == 2 && !sc) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: per-token-head scales need a scale layout");
   if (n_tokens < 0 || num_kv_heads < 1) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: n_tokens >= 0, num_kv_heads >= 1");
@@ -471,6 +490,7 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, pa_dtype src_dtype,
   a.n_tokens = n_tokens; a.hkv = num_kv_heads; a.page_shift = shift;
   a.kv_sp = kv->page; a.kv_sh = kv->head; a.kv_ss = kv->slot;
   a.sc_sp = m == 2 ? sc->page : 0; a.sc_sh = m == 2 ? sc->head : 0; a.sc_ss = m == 2 ? sc->slot : 0;
+  a.scale_hstride = mode == PA_SCALE_PER_HEAD ? 1 : 0;
   const int e = launch_append(a, src_dtype == PA_DTYPE_BF16, head_dim, m, stream);
   if (e) return hip_fail(e, "pa_kv_append launch");
   return ok();

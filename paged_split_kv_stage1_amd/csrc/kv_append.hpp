@@ -1,5 +1,6 @@
-// Device launch of the KV append (new tokens' K/V rows into their paged-cache slots),
-// shared by the host API and the kernel file.
+// Device launches of the cache-side operations that the host API and the kernel file
+// share: the KV append (new tokens' K/V rows into their paged-cache slots) and the
+// per-head quantiser.
 #pragma once
 
 #include <cstdint>
@@ -12,8 +13,12 @@ struct AppendArgs {
   int64_t n_tokens; int hkv; int page_shift;
   int64_t kv_sp, kv_sh, kv_ss;        // cache element strides (page, head, slot)
   int64_t sc_sp, sc_sh, sc_ss;        // scale element strides (per-token-head)
+  int scale_hstride;                  // mode 1: 1 = per-head scales [Hkv], 0 = one scale
 };
 // mode: 0 bf16 cache, 1 FP8 with per-tensor scales, 2 FP8 with per-token-head scales
 int launch_append(const AppendArgs& a, int src_bf16, int head_dim, int mode, void* stream);
+// Per-head FP8 quantiser: src [n_tokens, num_heads, head_dim] -> codes, scale[num_heads].
+int launch_quant_heads(const void* src, int src_bf16, int64_t n_tokens, int num_heads, int head_dim, uint8_t* dst,
+                       float* scale, void* stream);
 
 }  // namespace pa

@@ -53,6 +53,7 @@ struct Stage1Args {
   int64_t kv_sp, kv_sh, kv_ss;          // element strides (page, head, slot)
   const float* k_scale; const float* v_scale;
   int64_t sc_sp, sc_sh, sc_ss;
+  int scale_per_head;                   // 1: k/v_scale[Hkv] and, for FP8 Q, q_scale[Hq]; 0: scalars
   const int32_t* page_indices;
   float sm_scale;
   float* partial_o; float* partial_lse;

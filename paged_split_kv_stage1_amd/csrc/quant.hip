@@ -19,6 +19,9 @@
 // HBM rate.  Every row is read once and every code written once, so loads and stores
 // carry the non-temporal hint (with dirty lines left in L2 by earlier writes, plain
 // loads stream at about two thirds of the rate).
+#include <algorithm>
+#include <type_traits>
+
 #include "common.hpp"
 #include "kv_append.hpp"
 
@@ -222,10 +225,126 @@ static int launch_tensor(const void* src, int64_t n, uint8_t* dst, float* scale,
   return (int)hipGetLastError();
 }
 
+// ---- per-head scales ---------------------------------------------------------------------
+// Rows of [n_tokens, H, D]; row r belongs to head r % H, and head h's scale is the amax over
+// all of its rows / 448 (FlashInfer PR #869, per-head quantization).  Three launches: the
+// per-head amax (a fixed grid striding over the rows; row maxima meet per head in LDS and
+// one atomic per head and workgroup goes to global memory), the encode (the per-row
+// quantiser with the row's head scale), and the finish that turns the amax words into
+// scales.  H <= kMaxHeads.
+constexpr int kMaxHeads = 1024;
+
+__global__ void zero_words_kernel(float* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0.f;
+}
+
+template <bool BF16SRC, int D>
+__global__ __launch_bounds__(256) void amax_heads_kernel(const void* src, int64_t n_rows, int H, float* amax_words) {
+  using S = RowShape<D, true>;
+  __shared__ unsigned int hmax[kMaxHeads];
+  for (int t = threadIdx.x; t < H; t += 256) hmax[t] = 0u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int part = lane % S::LPR;
+  for (int64_t base = (int64_t)blockIdx.x * S::ROWS_PER_BLOCK; base < n_rows;
+       base += (int64_t)gridDim.x * S::ROWS_PER_BLOCK) {
+    const int64_t row0 = base + (threadIdx.x >> 6) * (S::RPW * S::U) + lane / S::LPR;
+    float x[S::U][S::EPL];
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      const int64_t row = min(row0 + u * S::RPW, n_rows - 1);
+#pragma unroll
+      for (int c = 0; c < S::EPL / 8; ++c)
+        load8<BF16SRC>(src, row * D + (int64_t)part * S::EPL + 8 * c, x[u] + 8 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < S::EPL; ++e) amax = fmaxf(amax, fabsf(x[u][e]));
+#pragma unroll
+      for (int off = S::LPR / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      const int64_t row = row0 + u * S::RPW;
+      // non-negative floats order like their bit patterns
+      if (part == 0 && row < n_rows) atomicMax(&hmax[row % H], __float_as_uint(amax));
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < H; t += 256)
+    if (hmax[t] != 0u) atomicMax(reinterpret_cast<unsigned int*>(amax_words) + t, hmax[t]);
+}
+
+template <bool BF16SRC, int D, bool BIG>
+__global__ __launch_bounds__(256) void encode_heads_kernel(const void* src, int64_t n_rows, int H, uint8_t* dst,
+                                                           const float* amax_words) {
+  using S = RowShape<D, BIG>;
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (S::RPW * S::U) + lane / S::LPR;
+  const int part = lane % S::LPR;
+  float x[S::U][S::EPL];
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) {
+    const int64_t row = min(row0 + u * S::RPW, n_rows - 1);
+#pragma unroll
+    for (int c = 0; c < S::EPL / 8; ++c)
+      load8<BF16SRC>(src, row * D + (int64_t)part * S::EPL + 8 * c, x[u] + 8 * c);
+  }
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) {
+    const int64_t row = row0 + u * S::RPW;
+    if (row >= n_rows) continue;
+    const float sc = scale_of(amax_words[row % H]);
+    const float inv = 1.0f / sc;
+#pragma unroll
+    for (int c = 0; c < S::EPL / 8; ++c)
+      store_codes(dst + row * D + (int64_t)part * S::EPL + 8 * c, encode8(x[u] + 8 * c, sc, inv));
+  }
+}
+
+__global__ void finish_scales_kernel(float* scale, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) scale[i] = scale_of(scale[i]);
+}
+
+template <bool BF16SRC, int D>
+static void launch_heads_d(const void* src, int64_t n_rows, int H, uint8_t* dst, float* scale, hipStream_t s) {
+  const unsigned amax_blocks = std::min(grid_of<D, true>(n_rows), 1024u);   // 4 per CU
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(1024), 0, s, scale, H);
+  hipLaunchKernelGGL((amax_heads_kernel<BF16SRC, D>), dim3(amax_blocks), dim3(256), 0, s, src, n_rows, H, scale);
+  const unsigned big = grid_of<D, true>(n_rows);
+  if (big >= kBigGrid)
+    hipLaunchKernelGGL((encode_heads_kernel<BF16SRC, D, true>), dim3(big), dim3(256), 0, s, src, n_rows, H, dst,
+                       scale);
+  else
+    hipLaunchKernelGGL((encode_heads_kernel<BF16SRC, D, false>), dim3(grid_of<D, false>(n_rows)), dim3(256), 0, s,
+                       src, n_rows, H, dst, scale);
+  hipLaunchKernelGGL(finish_scales_kernel, dim3(1), dim3(1024), 0, s, scale, H);
+}
+
+int launch_quant_heads(const void* src, int src_bf16, int64_t n_tokens, int num_heads, int head_dim, uint8_t* dst,
+                       float* scale, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (n_tokens <= 0) return 0;
+  const int64_t n_rows = n_tokens * num_heads;
+  auto go = [&](auto bf16_c) {
+    constexpr bool B = decltype(bf16_c)::value;
+    switch (head_dim) {
+      case 64: launch_heads_d<B, 64>(src, n_rows, num_heads, dst, scale, s); break;
+      case 128: launch_heads_d<B, 128>(src, n_rows, num_heads, dst, scale, s); break;
+      case 256: launch_heads_d<B, 256>(src, n_rows, num_heads, dst, scale, s); break;
+      case 512: launch_heads_d<B, 512>(src, n_rows, num_heads, dst, scale, s); break;
+      case 1024: launch_heads_d<B, 1024>(src, n_rows, num_heads, dst, scale, s); break;
+      default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+  };
+  return src_bf16 ? go(std::true_type{}) : go(std::false_type{});
+}
+
 // ---- KV append -------------------------------------------------------------------------
 // Rows of the new tokens' K (first n_tokens * hkv rows) then V, laid out like the
 // quantiser's rows, each written to its token's slot in the paged cache.  MODE: 0 bf16
-// cache, 1 FP8 with the caches' per-tensor scales, 2 FP8 with per-token-head scales.
+// cache, 1 FP8 with the caches' per-tensor scales (per-head: indexed by the KV head),
+// 2 FP8 with per-token-head scales.
 // Row indices fit in 32 bits (the host checks 2 * n_tokens * hkv < 2^31).  Rows of
 // skipped tokens (negative slot) and rows past the end still load a row (the last one,
 // past the end) so that the loads stay branch-free, and store nothing.
@@ -278,7 +397,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       }
     } else {
       float sc;
-      if constexpr (MODE == 1) sc = *(is_v ? a.v_scale : a.k_scale);
+      if constexpr (MODE == 1) sc = (is_v ? a.v_scale : a.k_scale)[h * a.scale_hstride];
       else sc = scale_of(amax);
       const float inv = 1.0f / sc;
       uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) + off;

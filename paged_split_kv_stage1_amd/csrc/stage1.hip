@@ -141,6 +141,8 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
   };
   int lim_lo[NQB], lim_hi[NQB];
   bool qvalid[NQB];
+  float qsc[NQB];                     // FP8 query scale of this lane's row (per tensor or per head)
+  const int hstep = a.scale_per_head; // 1: scales indexed by head, 0: one scale
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
     const int qb = wq + WQ * i;
@@ -153,6 +155,7 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
     const int lo = it.window > 0 ? max(0, p - it.window + 1) : 0;
     lim_lo[i] = max(lo, tb0);
     lim_hi[i] = min(p, te - 1);
+    qsc[i] = QF8 ? a.q_scale[(it.kvh * G + hl) * hstep] : 1.0f;
   }
   // Tokens every real row of the item sees (fast path: no masking inside).
   const int p_first = it.kv_len - it.nrows;
@@ -160,11 +163,16 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
   const int vis_lo_all = max(lo_last, tb0);
   const int vis_hi_all = min(p_first, te - 1);
 
+  // Score scale into the log2 domain.  Per-tensor / per-head K and Q scales are folded
+  // into xsb (one value per query block and lane: with per-head Q scales each row of the
+  // block has its head's); per-token-head K scales are applied per token in the tile.
   float qk_scale = a.sm_scale * kLog2e;
-  if constexpr (QF8) qk_scale *= *a.q_scale;
-  if constexpr (KVF8 && !PT) qk_scale *= *a.k_scale;
+  if constexpr (KVF8 && !PT) qk_scale *= a.k_scale[it.kvh * hstep];
+  float xsb[NQB];
+#pragma unroll
+  for (int i = 0; i < NQB; ++i) xsb[i] = PT ? qsc[i] : qk_scale * qsc[i];
   float out_scale = 1.0f;
-  if constexpr (C::PV_FP8) out_scale = *a.v_scale;   // P carried x448, and so does l
+  if constexpr (C::PV_FP8) out_scale = a.v_scale[it.kvh * hstep];   // P carried x448, and so does l
 
   f32x4 o[NQB][C::DB];
   f32x4 olo[C::PV_FP8 ? NQB : 1][C::PV_FP8 ? C::DB : 1];
@@ -359,13 +367,10 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
         x[k] = s0[k];
         x[4 + k] = s1[k];
       }
-      float xs;                              // score scale still to apply (1 when folded)
+      const float xs = xsb[i];               // score scale still to apply
       if constexpr (PT) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) x[k] *= ks[k];
-        xs = 1.0f;
-      } else {
-        xs = qk_scale;
       }
       if (need_mask) {
 #pragma unroll

@@ -13,17 +13,17 @@ from typing import Optional
 import numpy as np
 import torch
 
-from ._lib import pa_kv_quantize_fp8
+from ._lib import pa_kv_quantize_fp8, pa_kv_quantize_fp8_per_head
 from .inputs import BF16_NAN_BITS, E4M3_NAN_CODE, Workload
 
 
 @dataclasses.dataclass
 class DeviceInputs:
     q: torch.Tensor                  # bf16 [T, Hq, d] or uint8 codes
-    q_scale: Optional[torch.Tensor]  # float32 [1] for FP8 queries
+    q_scale: Optional[torch.Tensor]  # float32 [1] for FP8 queries ([Hq] with per-head scales)
     k: torch.Tensor                  # bf16 or uint8, layout HPD [pages, Hkv, P, d] or PHD [pages, P, Hkv, d]
     v: torch.Tensor
-    k_scale: Optional[torch.Tensor]  # float32 [1] (per tensor) or [pages, Hkv, P] / [pages, P, Hkv]
+    k_scale: Optional[torch.Tensor]  # float32 [1] (per tensor), [Hkv] (per head) or [pages, Hkv, P] / [pages, P, Hkv]
     v_scale: Optional[torch.Tensor]
     page_indices: torch.Tensor       # int32
     layout: str
@@ -35,6 +35,18 @@ def _strides(layout: str, Hkv: int, P: int, d: int):
     if layout == "HPD":
         return (Hkv * P * d, P * d, d), (Hkv * P, P, 1)
     return (P * Hkv * d, d, Hkv * d), (P * Hkv, 1, Hkv)
+
+
+def _quantize_heads(src_bf16: torch.Tensor, head_axis: int, device):
+    """Per-head codes and scales [H] of a tensor whose head axis is ``head_axis``: the
+    quantiser takes token-major rows [tokens, H, d], so other layouts go through a
+    transposed copy."""
+    x = src_bf16.movedim(head_axis, -2).contiguous()
+    H, d = x.shape[-2], x.shape[-1]
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=device)
+    scale = torch.empty(H, dtype=torch.float32, device=device)
+    pa_kv_quantize_fp8_per_head(x, "bf16", x.numel() // (H * d), H, d, codes, scale)
+    return codes.movedim(-2, head_axis).contiguous(), scale
 
 
 def _quantize(src_bf16: torch.Tensor, mode: str, d: int, device):
@@ -63,6 +75,12 @@ def to_device(w: Workload, device="cuda", layout: str = "HPD") -> DeviceInputs:
         v = v_src.to(device)
         k.view(torch.int16).masked_fill_(m4.expand(k.shape), BF16_NAN_BITS)
         v.view(torch.int16).masked_fill_(m4.expand(v.shape), BF16_NAN_BITS)
+    elif w.kv_scale_mode == "per_head":
+        axis = 1 if layout == "HPD" else 2
+        k, k_scale = _quantize_heads(k_src.to(device), axis, device)
+        v, v_scale = _quantize_heads(v_src.to(device), axis, device)
+        k.masked_fill_(m4.expand(k.shape), E4M3_NAN_CODE)
+        v.masked_fill_(m4.expand(v.shape), E4M3_NAN_CODE)
     else:
         k, k_scale = _quantize(k_src.to(device), w.kv_scale_mode, d, device)
         v, v_scale = _quantize(v_src.to(device), w.kv_scale_mode, d, device)
@@ -72,7 +90,9 @@ def to_device(w: Workload, device="cuda", layout: str = "HPD") -> DeviceInputs:
             k_scale.masked_fill_(m3.expand(k_scale.shape), float("nan"))
             v_scale.masked_fill_(m3.expand(v_scale.shape), float("nan"))
     q_scale = None
-    if w.q_dtype == "fp8":
+    if w.q_dtype == "fp8" and w.kv_scale_mode == "per_head":
+        q, q_scale = _quantize_heads(w.q.to(device), 1, device)     # one scale per query head
+    elif w.q_dtype == "fp8":
         q, q_scale = _quantize(w.q.to(device), "per_tensor", d, device)
     else:
         q = w.q.to(device)

@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "pa.h")).read()
     declared = set(re.findall(r"^(?:pa_status|const char\*)\s+(pa_\w+)\(", header, flags=re.M))
     assert {"pa_plan_splits", "pa_decode_stage1", "pa_decode_merge", "pa_kv_quantize_fp8", "pa_kv_append",
-            "pa_debug_gather", "pa_last_error"} <= declared
+            "pa_kv_quantize_fp8_per_head", "pa_debug_gather", "pa_last_error"} <= declared
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -212,6 +212,34 @@ def test_append_validates(case, status):
     with pytest.raises(PaError) as e:
         _lib.pa_kv_append(**args)
     assert e.value.status == status
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(num_heads=0), PA_ERR_UNSUPPORTED),
+    (dict(num_heads=1025), PA_ERR_UNSUPPORTED),
+    (dict(head_dim=96), PA_ERR_UNSUPPORTED),
+    (dict(src=(1 << 20) + 8), PA_ERR_INVALID_ARGUMENT),
+    (dict(dst=(1 << 20) + 4), PA_ERR_INVALID_ARGUMENT),
+    (dict(scale=None), PA_ERR_INVALID_ARGUMENT),
+    (dict(n_tokens=-1), PA_ERR_INVALID_ARGUMENT),
+    (dict(src_dtype="fp8"), PA_ERR_INVALID_ARGUMENT),
+])
+def test_quantize_per_head_validates(args, status):
+    fake = 1 << 20
+    kw = dict(src=fake, src_dtype="bf16", n_tokens=10, num_heads=8, head_dim=128, dst=fake, scale=fake)
+    kw.update(args)
+    with pytest.raises(PaError) as e:
+        _lib.pa_kv_quantize_fp8_per_head(**kw)
+    assert e.value.status == status
+
+
+def test_per_head_mode_needs_fp8_kv_and_plans_like_per_tensor():
+    with pytest.raises(PaError) as e:
+        _plan(kvd="bf16", mode="per_head")
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT
+    a, _ = _plan(kvd="fp8", mode="per_head")
+    b, _ = _plan(kvd="fp8", mode="per_tensor")
+    assert (a.num_items, a.max_splits, a.variant) == (b.num_items, b.max_splits, b.variant)
 
 
 def test_merge_without_splits_is_a_noop():

@@ -12,6 +12,10 @@ from tests.gpu_run import run_decode
 pytestmark = pytest.mark.gpu
 
 
+MODE = {"bf16": "none", "fp8_per_tensor": "per_tensor", "fp8_per_head": "per_head",
+        "fp8_per_token_head": "per_token_head"}
+
+
 def _strides(layout, P, hkv, d):
     return (hkv * P * d, P * d, d) if layout == "HPD" else (P * hkv * d, d, hkv * d)
 
@@ -20,7 +24,7 @@ def _scale_strides(layout, P, hkv):
     return (hkv * P, P, 1) if layout == "HPD" else (P * hkv, 1, hkv)
 
 
-@pytest.mark.parametrize("kind", ["bf16", "fp8_per_tensor", "fp8_per_token_head"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8_per_tensor", "fp8_per_head", "fp8_per_token_head"])
 @pytest.mark.parametrize("src", ["bf16", "fp32"])
 @pytest.mark.parametrize("layout", ["HPD", "PHD"])
 @pytest.mark.parametrize("d", [128, 256])
@@ -46,7 +50,11 @@ def test_append_matches_oracle(kind, src, layout, d):
         v_rows = vx.view(torch.int16).numpy().view(np.uint16)
     else:
         k_rows, v_rows = kx.numpy(), vx.numpy()
-    ts_k, ts_v = np.float32(0.021), np.float32(0.033)
+    if kind == "fp8_per_head":
+        ts_k = (np.float32(0.021) * (1 + np.arange(hkv))).astype(np.float32)
+        ts_v = (np.float32(0.033) / (1 + np.arange(hkv))).astype(np.float32)
+    else:
+        ts_k, ts_v = np.float32(0.021), np.float32(0.033)
 
     as_t = (lambda a: torch.from_numpy(a.view(np.int16).copy())) if kind == "bf16" else (lambda a: torch.from_numpy(a.copy()))
     kc, vc = as_t(k0).cuda(), as_t(v0).cuda()
@@ -54,11 +62,12 @@ def test_append_matches_oracle(kind, src, layout, d):
         ksc, vsc = torch.from_numpy(ks0.copy()).cuda(), torch.from_numpy(vs0.copy()).cuda()
     elif kind == "fp8_per_tensor":
         ksc, vsc = torch.tensor([ts_k]).cuda(), torch.tensor([ts_v]).cuda()
+    elif kind == "fp8_per_head":
+        ksc, vsc = torch.from_numpy(ts_k).cuda(), torch.from_numpy(ts_v).cuda()
     else:
         ksc = vsc = None
     pa_kv_append(kx.cuda(), vx.cuda(), src, n, hkv, d, P, torch.from_numpy(slots).cuda(), kc, vc,
-                 "bf16" if kind == "bf16" else "fp8", {"bf16": "none", "fp8_per_tensor": "per_tensor",
-                                                       "fp8_per_token_head": "per_token_head"}[kind],
+                 "bf16" if kind == "bf16" else "fp8", MODE[kind],
                  _strides(layout, P, hkv, d), ksc, vsc, _scale_strides(layout, P, hkv) if pt else None)
     torch.cuda.synchronize()
     rk, rks = append_kv(k0, ks0, k_rows, src, slots, P, kind, layout, tensor_scale=ts_k)
@@ -71,7 +80,7 @@ def test_append_matches_oracle(kind, src, layout, d):
         assert np.array_equal(ksc.cpu().numpy(), rks) and np.array_equal(vsc.cpu().numpy(), rvs)
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c2", "c2_ph", "c3", "c4"])
 def test_appended_tokens_are_what_decode_reads(name):
     # poison the slots of each request's last 8 tokens, then append those tokens back
     # through pa_kv_append from their bf16 rows: the cache must come back byte for byte
@@ -115,6 +124,7 @@ def test_appended_tokens_are_what_decode_reads(name):
 MANY = [
     ("fp8_per_token_head", 2, 256, 16, 16384 + 11, "bf16"),
     ("fp8_per_tensor", 8, 128, 64, 8192 + 5, "fp32"),
+    ("fp8_per_head", 8, 128, 64, 8192 + 5, "bf16"),
     ("bf16", 2, 256, 16, 16384 + 11, "bf16"),
 ]
 
@@ -139,7 +149,11 @@ def test_append_many_rows_matches_oracle(kind, hkv, d, P, n, src):
         rows = [t.view(torch.int16).numpy().view(np.uint16) for t in new]
     else:
         rows = [t.numpy() for t in new]
-    ts = [np.float32(0.03), np.float32(0.05)]
+    if kind == "fp8_per_head":
+        ts = [(np.float32(0.03) * (1 + np.arange(hkv))).astype(np.float32),
+              (np.float32(0.05) / (1 + np.arange(hkv))).astype(np.float32)]
+    else:
+        ts = [np.float32(0.03), np.float32(0.05)]
     as_t = (lambda a: torch.from_numpy(a.view(np.int16).copy())) if kind == "bf16" else \
            (lambda a: torch.from_numpy(a.copy()))
     caches = [as_t(c).cuda() for c in c0]
@@ -147,11 +161,12 @@ def test_append_many_rows_matches_oracle(kind, hkv, d, P, n, src):
         scales = [torch.from_numpy(s.copy()).cuda() for s in s0]
     elif kind == "fp8_per_tensor":
         scales = [torch.tensor([t]).cuda() for t in ts]
+    elif kind == "fp8_per_head":
+        scales = [torch.from_numpy(t).cuda() for t in ts]
     else:
         scales = [None, None]
     pa_kv_append(new[0].cuda(), new[1].cuda(), src, n, hkv, d, P, torch.from_numpy(slots).cuda(), caches[0],
-                 caches[1], "bf16" if kind == "bf16" else "fp8",
-                 {"bf16": "none", "fp8_per_tensor": "per_tensor", "fp8_per_token_head": "per_token_head"}[kind],
+                 caches[1], "bf16" if kind == "bf16" else "fp8", MODE[kind],
                  (hkv * P * d, P * d, d), scales[0], scales[1], (hkv * P, P, 1) if pt else None)
     torch.cuda.synchronize()
     for i in range(2):

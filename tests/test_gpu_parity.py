@@ -5,8 +5,8 @@ import pytest
 import torch
 
 from oracle.attention import decode_attention, gather_slots
-from oracle.quantize import quantize_per_row, quantize_per_tensor
-from paged_split_kv_stage1_amd import pa_debug_gather, pa_kv_quantize_fp8
+from oracle.quantize import quantize_per_head, quantize_per_row, quantize_per_tensor
+from paged_split_kv_stage1_amd import pa_debug_gather, pa_kv_quantize_fp8, pa_kv_quantize_fp8_per_head
 from paged_split_kv_stage1_amd.device_inputs import to_device
 from paged_split_kv_stage1_amd.inputs import make_workload
 from tests.gpu_run import run_decode
@@ -22,6 +22,7 @@ BF16_OUT_EXTRA = 2.0 ** -8              # bf16 output rounding on top of the bar
 SMALL = {
     "c1": dict(),
     "c2": dict(batch=6, ctx=[2048, 1000, 77, 1, 640, 1999]),
+    "c2_ph": dict(batch=6, ctx=[2048, 1000, 77, 1, 640, 1999]),
     "c3": dict(batch=3, ctx=[3001, 517, 4]),
     "c3_r1": dict(batch=3, ctx=[2500, 130, 1]),
     "c3_r8": dict(batch=2, ctx=[1500, 9]),
@@ -59,7 +60,7 @@ def test_parity_fp32_out(name):
         assert np.max(np.abs(got - ref_lse[rows])) <= 1e-3 * max(1.0, np.max(np.abs(ref_lse)))
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c2_ph", "c3", "c4", "c5"])
 def test_parity_bf16_out(name):
     print(f"[parity-bf16] {name}", flush=True)
     w = make_workload(name, **SMALL[name], out_dtype="bf16")
@@ -144,6 +145,44 @@ def test_quantizer_per_tensor_many_groups_bit_exact():
     assert np.array_equal(codes.cpu().numpy(), rc)
 
 
+# (tokens, heads, d): few tokens (one small launch), and enough rows for four row groups
+# per wave with a ragged tail; 64 query heads as in the per-head FP8 workload.
+PER_HEAD_SHAPES = [(37, 3, 64), (129, 8, 128), (5, 2, 256), (9, 1, 512), (3, 64, 128), (16384 + 7, 8, 128),
+                   (4101, 2, 1024)]
+
+
+@pytest.mark.parametrize("n,h,d", PER_HEAD_SHAPES)
+@pytest.mark.parametrize("src", ["bf16", "fp32"])
+def test_quantizer_per_head_bit_exact(n, h, d, src):
+    print(f"[quant per-head] n={n} H={h} d={d} {src}", flush=True)
+    g = torch.Generator().manual_seed(n + h + d)
+    x = torch.randn(n, h, d, generator=g) * (torch.rand(1, h, 1, generator=g) * 8)
+    x[0, 0, :4] = torch.tensor([-0.0, 9.2e-41, -9.2e-41, 0.0])        # signed zeros, bf16 subnormals
+    if h > 1:
+        x[:, h - 1] = 0                                                # an all-zero head: scale 1
+    x = x.to(torch.bfloat16) if src == "bf16" else x
+    codes = torch.empty(n, h, d, dtype=torch.uint8, device="cuda")
+    scale = torch.full((h,), float("nan"), dtype=torch.float32, device="cuda")
+    pa_kv_quantize_fp8_per_head(x.cuda(), src, n, h, d, codes, scale)
+    torch.cuda.synchronize()
+    xs = x.view(torch.int16).numpy().view(np.uint16) if src == "bf16" else x.numpy()
+    rc, rs = quantize_per_head(xs, src, 1)
+    assert np.array_equal(scale.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantizer_per_head_twice_in_a_row():
+    # the amax words are cleared by every call: a second, smaller call gives its own scales
+    for n, amp in ((500, 30.0), (20, 0.5)):
+        x = (torch.randn(n, 4, 128, generator=torch.Generator().manual_seed(n)) * amp).to(torch.bfloat16)
+        codes = torch.empty(n, 4, 128, dtype=torch.uint8, device="cuda")
+        scale = torch.empty(4, dtype=torch.float32, device="cuda")
+        pa_kv_quantize_fp8_per_head(x.cuda(), "bf16", n, 4, 128, codes, scale)
+        torch.cuda.synchronize()
+        rc, rs = quantize_per_head(x.view(torch.int16).numpy().view(np.uint16), "bf16", 1)
+        assert np.array_equal(scale.cpu().numpy(), rs) and np.array_equal(codes.cpu().numpy(), rc)
+
+
 def test_quantizer_fp32_source_bit_exact():
     g = torch.Generator().manual_seed(5)
     x = torch.randn(100, 128, generator=g) * 3
@@ -180,10 +219,10 @@ def test_gather_bit_exact(name):
 # changes with the splits: per-tensor FP8 V requantises P to two e4m3 terms (about
 # 1e-3 here), per-token-head FP8 KV carries P as one bf16 term (relative rounding
 # <= 2^-9 per probability; 4 x 2^-9 bounds the difference of two such sums).
-SPLIT_TOL = {"c3": 2e-5, "c4": 4 * 2.0 ** -9, "c2": 3e-3}
+SPLIT_TOL = {"c3": 2e-5, "c4": 4 * 2.0 ** -9, "c2": 3e-3, "c2_ph": 3e-3}
 
 
-@pytest.mark.parametrize("name", ["c3", "c4", "c2"])
+@pytest.mark.parametrize("name", ["c3", "c4", "c2", "c2_ph"])
 def test_split_count_invariance(name):
     w = make_workload(name, **SMALL[name], out_dtype="fp32")
     di = to_device(w)
@@ -305,7 +344,8 @@ def test_head_permutation_within_group_permutes_outputs():
     assert np.array_equal(o2, o[:, perm])
 
 
-@pytest.mark.parametrize("name,page", [("c2", 128), ("c2", 1024), ("c3", 256), ("c4", 1024), ("c5", 128)])
+@pytest.mark.parametrize("name,page", [("c2", 128), ("c2", 1024), ("c2_ph", 128), ("c3", 256), ("c4", 1024),
+                                       ("c5", 128)])
 @pytest.mark.parametrize("layout", ["HPD", "PHD"])
 def test_large_pages(name, page, layout):
     # pages of 128..1024 tokens: several tiles (and whole splits) inside one page, and a
