@@ -53,7 +53,8 @@ def visible_range(kv_len_b: int, n_rows_b: int, r: int, window_b: int):
 class PagedKV:
     """One paged cache (K or V) as the GPU stores it.
 
-    data: bf16 bit patterns (uint16) or e4m3 codes (uint8), shape
+    data: bf16 bit patterns (uint16), e4m3 codes (uint8) or int8 codes (int8 or their
+          bytes as uint8), shape
           [pages, Hkv, P, d] for layout "HPD" or [pages, P, Hkv, d] for "PHD".
     scale: None; a float32 scalar (per tensor); float32 [Hkv] (per head); or float32
            [pages, Hkv, P] ("HPD") / [pages, P, Hkv] ("PHD") for per-(token, KV head)
@@ -81,6 +82,8 @@ class PagedKV:
             val = bf16_bits_to_f64(raw)
         elif self.dtype == "fp8":
             val = e4m3_code_to_f64(raw)
+        elif self.dtype == "int8":
+            val = np.asarray(raw).view(np.int8).astype(np.float64)
         else:
             raise ValueError(self.dtype)
         if self.scale_mode == "per_tensor":

@@ -15,14 +15,14 @@ Readings where the pages are silent:
     token (padding);
   * a bf16 cache stores bf16 sources unchanged and float32 sources rounded to the
     nearest bf16 (ties to even);
-  * FP8 codes follow oracle.quantize (RNE of the clamped fp32 quotient).
+  * FP8 and INT8 codes follow oracle.quantize (RNE of the clamped fp32 quotient).
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .formats import f32_to_bf16_bits_rne
-from .quantize import _as_f32, _encode, quantize_per_row
+from .quantize import _as_f32, _encode, _encode_int8, quantize_int8_per_row, quantize_per_row
 
 
 def _row_view(cache: np.ndarray, layout: str, page: int, head: int, slot: int):
@@ -39,7 +39,8 @@ def append_kv(cache: np.ndarray, scales, rows: np.ndarray, src_dtype: str, slot_
     kind: "bf16" (cache holds bf16 bit patterns), "fp8_per_tensor" (codes, encoded with
     ``tensor_scale``), "fp8_per_head" (codes, KV head h encoded with
     ``tensor_scale[h]``), "fp8_per_token_head" (codes, and ``scales`` [pages, Hkv, P]
-    or [pages, P, Hkv] receives each row's scale)."""
+    or [pages, P, Hkv] receives each row's scale), "int8_per_tensor" and
+    "int8_per_token_head" (the same with int8 codes; the cache holds their bytes)."""
     cache = cache.copy()
     scales = None if scales is None else scales.copy()
     n, hkv, _ = rows.shape
@@ -57,6 +58,12 @@ def append_kv(cache: np.ndarray, scales, rows: np.ndarray, src_dtype: str, slot_
                 cache[idx] = _encode(x32[t, h], np.float32(tensor_scale))
             elif kind == "fp8_per_head":
                 cache[idx] = _encode(x32[t, h], np.float32(np.asarray(tensor_scale, dtype=np.float32)[h]))
+            elif kind == "int8_per_tensor":
+                cache[idx] = _encode_int8(x32[t, h], np.float32(tensor_scale)).view(cache.dtype)
+            elif kind == "int8_per_token_head":
+                codes, sc = quantize_int8_per_row(rows[t, h][None], src_dtype)
+                cache[idx] = codes[0].view(cache.dtype)
+                scales[idx] = sc[0]
             elif kind == "fp8_per_token_head":
                 codes, sc = quantize_per_row(rows[t, h][None], src_dtype)
                 cache[idx] = codes[0]

@@ -11,6 +11,12 @@ Readings where the pages are silent: the scale is computed in float32 as
 fl32(amax / 448); a value is encoded as RNE_e4m3(clamp(fl32(x / scale), -448, 448))
 with an IEEE float32 division; a group whose amax is 0 gets scale 1 (all codes 0).
 
+INT8 codes (the pages name int8 KV caches -- FreeToken PR #900, "Tested on", the
+register-spill check over bf16/fp8/int8 kernels -- but define no format): symmetric,
+scale = fl32(amax / 127) (1 when amax is 0), code = round-half-even(clamp(fl32(x /
+scale), -127, 127)) as a signed byte, value = code * scale; per (token, KV head) or per
+tensor, like the FP8 scales.
+
 Inputs are rows of d values (bf16 bit patterns, or float32); for per-token-head
 scales a row is one (token, KV head) vector, for per-tensor scales all rows share
 one scale, for per-head scales all rows of one head share one.
@@ -71,3 +77,34 @@ def quantize_per_head(src: np.ndarray, src_dtype: str, head_axis: int):
     shape = [1] * x.ndim
     shape[head_axis] = -1
     return _encode(x, scale.reshape(shape)), scale
+
+
+INT8_MAX = 127.0
+
+
+def _encode_int8(x32: np.ndarray, scale32: np.ndarray) -> np.ndarray:
+    q = (x32 / scale32).astype(np.float32)                     # IEEE fp32 divide, RNE
+    q = np.clip(q.astype(np.float64), -INT8_MAX, INT8_MAX)
+    return np.rint(q).astype(np.int8)                          # ties to even
+
+
+def _int8_scale_from_amax(amax32: np.ndarray) -> np.ndarray:
+    amax32 = np.asarray(amax32, dtype=np.float32)
+    s = (amax32 / np.float32(INT8_MAX)).astype(np.float32)
+    return np.where(amax32 == 0, np.float32(1.0), s).astype(np.float32)
+
+
+def quantize_int8_per_row(src: np.ndarray, src_dtype: str):
+    """INT8 with per-(token, KV head) scales: src [..., d]; one scale per leading index.
+    Returns (codes int8 [..., d], scales float32 [...])."""
+    x = _as_f32(src, src_dtype)
+    scale = _int8_scale_from_amax(np.max(np.abs(x), axis=-1).astype(np.float32))
+    return _encode_int8(x, scale[..., None]), scale
+
+
+def quantize_int8_per_tensor(src: np.ndarray, src_dtype: str):
+    """INT8 with one scale for the whole tensor.  Returns (codes int8, scale float32)."""
+    x = _as_f32(src, src_dtype)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    scale = _int8_scale_from_amax(amax)
+    return _encode_int8(x, scale), np.float32(scale)

@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import numpy as np
 
-_SIZE = {"bf16": 2, "fp8": 1, "fp32": 4}
+_SIZE = {"bf16": 2, "fp8": 1, "int8": 1, "fp32": 4}
 
 
 def step_accounting(batch, qo_indptr, kv_len, window, page_size, num_q_heads, num_kv_heads,

@@ -52,7 +52,7 @@ class Workload:
     v: torch.Tensor            # bf16 [num_pages, Hkv, P, d] (CPU)
     unused_slots: np.ndarray   # bool [num_pages, P]: slot holds no token
     q_dtype: str               # "bf16" | "fp8"   (fp8: quantise q per tensor)
-    kv_dtype: str              # "bf16" | "fp8"
+    kv_dtype: str              # "bf16" | "fp8" | "int8"
     kv_scale_mode: str         # "none" | "per_tensor" | "per_head" | "per_token_head"
     out_dtype: str             # "fp32" | "bf16"
     sm_scale: float            # float32 value of 1/sqrt(d)
@@ -90,6 +90,8 @@ CONFIGS = {
                   scale="none", out="bf16"),
     "c4": dict(batch=16, rows=8, hq=16, hkv=2, d=256, ctx=131072, page=16, q="bf16", kv="fp8",
                scale="per_token_head", out="bf16"),
+    "c4_i8": dict(batch=16, rows=8, hq=16, hkv=2, d=256, ctx=131072, page=16, q="bf16", kv="int8",
+                  scale="per_token_head", out="bf16"),
     "c4_b1": dict(batch=1, rows=8, hq=16, hkv=2, d=256, ctx=131072, page=16, q="bf16", kv="fp8",
                   scale="per_token_head", out="bf16"),
     "c4_r1": dict(batch=16, rows=1, hq=16, hkv=2, d=256, ctx=131072, page=16, q="bf16", kv="fp8",
@@ -189,9 +191,12 @@ def make_workload(name: str, seed: Optional[int] = None, *, batch: Optional[int]
         forced_splits=cfg.get("splits", 0))
 
 
-# Byte patterns used to poison slots that hold no token: a NaN in each format.
+# Byte patterns used to poison slots that hold no token: a NaN in each format, and for
+# INT8 codes (which have no NaN) -128, a code the quantiser never writes (the per-token
+# scales of those slots are NaN).
 BF16_NAN_BITS = 0x7FC1
 E4M3_NAN_CODE = 0x7F
+INT8_POISON_CODE = 0x80
 
 
 def poison_unused(cache: torch.Tensor, unused_slots: np.ndarray, layout: str = "HPD") -> torch.Tensor:

@@ -4,8 +4,9 @@ import numpy as np
 import torch
 
 from oracle.attention import PagedKV, dequant_q
-from oracle.quantize import quantize_per_head, quantize_per_row, quantize_per_tensor
-from paged_split_kv_stage1_amd.inputs import BF16_NAN_BITS, E4M3_NAN_CODE
+from oracle.quantize import (quantize_int8_per_row, quantize_int8_per_tensor, quantize_per_head, quantize_per_row,
+                             quantize_per_tensor)
+from paged_split_kv_stage1_amd.inputs import BF16_NAN_BITS, E4M3_NAN_CODE, INT8_POISON_CODE
 
 
 def _bits(t: torch.Tensor) -> np.ndarray:
@@ -36,6 +37,19 @@ def oracle_inputs(w, layout="HPD", requests=None):
         vc = np.where(np.broadcast_to(m4, vc.shape), np.uint8(E4M3_NAN_CODE), vc)
         out["k"] = PagedKV(kc, "fp8", layout, "per_tensor", ks)
         out["v"] = PagedKV(vc, "fp8", layout, "per_tensor", vs)
+    elif w.kv_dtype == "int8":
+        if w.kv_scale_mode == "per_tensor":
+            kc, ks = quantize_int8_per_tensor(kb, "bf16")
+            vc, vs = quantize_int8_per_tensor(vb, "bf16")
+        else:
+            kc, ks = quantize_int8_per_row(kb, "bf16")
+            vc, vs = quantize_int8_per_row(vb, "bf16")
+            ks = np.where(m3, np.float32(np.nan), ks)
+            vs = np.where(m3, np.float32(np.nan), vs)
+        kc = np.where(np.broadcast_to(m4, kc.shape), np.uint8(INT8_POISON_CODE), kc.view(np.uint8))
+        vc = np.where(np.broadcast_to(m4, vc.shape), np.uint8(INT8_POISON_CODE), vc.view(np.uint8))
+        out["k"] = PagedKV(kc, "int8", layout, w.kv_scale_mode, ks)
+        out["v"] = PagedKV(vc, "int8", layout, w.kv_scale_mode, vs)
     elif w.kv_scale_mode == "per_head":
         axis = 1 if layout == "HPD" else 2
         kc, ks = quantize_per_head(kb, "bf16", axis)

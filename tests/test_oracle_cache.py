@@ -91,3 +91,25 @@ def test_append_per_head_uses_each_heads_scale():
     untouched = np.ones(new.shape[:3], bool)
     untouched[1, :, 2] = False
     assert np.all(new[untouched] == 0x55)
+
+
+def test_append_int8_per_token_head_and_per_tensor():
+    from oracle.quantize import quantize_int8_per_row
+    rng = np.random.default_rng(13)
+    rows = (rng.standard_normal((3, 2, 16)) * 4).astype(np.float32)
+    cache = np.full((2, 2, 4, 16), 0x5A, np.uint8)
+    scales = np.full((2, 2, 4), -1.0, np.float32)
+    new, nsc = append_kv(cache, scales, rows, "fp32", [7, -1, 0], 4, "int8_per_token_head")
+    for t, (page, slot) in ((0, (1, 3)), (2, (0, 0))):
+        for h in range(2):
+            c, s = quantize_int8_per_row(rows[t, h][None], "fp32")
+            assert np.array_equal(new[page, h, slot].view(np.int8), c[0]) and nsc[page, h, slot] == s[0]
+    keep = np.ones((2, 2, 4), bool)
+    keep[1, :, 3] = keep[0, :, 0] = False
+    assert np.all(new[keep] == 0x5A) and np.all(nsc[keep] == -1.0)
+    # integers times the tensor scale encode to exactly those integers
+    ints = np.array([0, 1, -1, 127, -127, 64, -3, 2], np.float32)
+    scale = np.float32(0.0625)
+    new, _ = append_kv(np.zeros((1, 1, 4, 8), np.uint8), None, (ints * scale).reshape(1, 1, 8), "fp32", [1], 4,
+                       "int8_per_tensor", tensor_scale=scale)
+    assert np.array_equal(new[0, 0, 1].view(np.int8), ints.astype(np.int8))

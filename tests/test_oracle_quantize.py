@@ -4,7 +4,8 @@ import numpy as np
 import torch
 
 from oracle.formats import e4m3_code_to_f64
-from oracle.quantize import quantize_per_head, quantize_per_row, quantize_per_tensor
+from oracle.quantize import (quantize_int8_per_row, quantize_int8_per_tensor, quantize_per_head, quantize_per_row,
+                             quantize_per_tensor)
 
 
 def _torch_quant_rows(x32: torch.Tensor):
@@ -102,3 +103,46 @@ def test_per_head_dequantisation_in_the_attention_inputs():
     qs = np.array([2.0, 0.25, 1.5], np.float32)
     ref = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy() * qs[None, :, None].astype(np.float64)
     assert np.array_equal(dequant_q(q, "fp8", qs), ref)
+
+
+def test_int8_per_row_matches_torch_round_half_even():
+    # scale = amax/127 in fp32; codes = torch.round (ties to even) of the clamped quotient
+    g = torch.Generator().manual_seed(9)
+    x = torch.randn(50, 2, 128, generator=g) * 3
+    x[0, 0] = 0                                                  # all-zero row: scale 1, codes 0
+    x[1, 1, :6] = torch.tensor([127.0, 2.5, 3.5, -0.5, -1.5, 0.5])   # amax 127 -> scale 1: exact ties
+    x[1, 1, 6:] = 0.25
+    codes, scale = quantize_int8_per_row(x.numpy(), "fp32")
+    amax = x.abs().amax(dim=-1)
+    ref_scale = torch.where(amax == 0, torch.ones_like(amax), amax / 127.0)
+    ref = torch.round(x / ref_scale[..., None]).clamp(-127, 127).to(torch.int8)
+    assert np.array_equal(scale, ref_scale.numpy())
+    assert codes.dtype == np.int8 and np.array_equal(codes, ref.numpy())
+    assert list(codes[1, 1, :6]) == [127, 2, 4, 0, -2, 0]
+    assert scale[0, 0] == 1.0 and not codes[0, 0].any()
+
+
+def test_int8_per_tensor_matches_torch_and_error_bound():
+    g = torch.Generator().manual_seed(10)
+    x = (torch.randn(40, 4, 64, generator=g) * 5).to(torch.bfloat16)
+    codes, scale = quantize_int8_per_tensor(x.view(torch.int16).numpy().view(np.uint16), "bf16")
+    xf = x.float()
+    ref_scale = xf.abs().max() / 127.0
+    ref = torch.round(xf / ref_scale).clamp(-127, 127).to(torch.int8)
+    assert np.float32(scale) == ref_scale.item() and np.array_equal(codes, ref.numpy())
+    err = np.abs(codes.astype(np.float64) * np.float64(scale) - xf.numpy().astype(np.float64))
+    assert np.all(err <= np.float64(scale) / 2 * (1 + 1e-6))
+    assert np.abs(codes).max() == 127
+
+
+def test_int8_dequantisation_in_the_attention_inputs():
+    from oracle.attention import PagedKV
+    rng = np.random.default_rng(12)
+    codes = rng.integers(-127, 128, (2, 2, 4, 8)).astype(np.int8)
+    sc = rng.random((2, 2, 4)).astype(np.float32)
+    kv = PagedKV(codes.view(np.uint8), "int8", "HPD", "per_token_head", sc)     # bytes as stored
+    slots = np.array([1, 6])
+    for gh in range(2):
+        ref = torch.from_numpy(codes[slots // 4, gh, slots % 4]).double().numpy() * \
+            sc[slots // 4, gh, slots % 4].astype(np.float64)[:, None]
+        assert np.array_equal(kv.tokens(slots, gh), ref)
