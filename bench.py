@@ -36,6 +36,8 @@ WORKLOAD_NAMES = {
     "c3_r1": "single-row decode B16 16/2 heads d256 ctx32768 P16 bf16 KV",
     "c3_r8": "MTP verify R8 B16 16/2 heads d256 ctx32768 P16 bf16 KV",
     "c4": "long-context R8 B16 16/2 heads d256 ctx131072 P16 e4m3 KV per-token-head",
+    "c4_i8": "long-context R8 B16 16/2 heads d256 ctx131072 P16 int8 KV per-token-head",
+    "c4_i8t": "long-context R8 B16 16/2 heads d256 ctx131072 P16 int8 KV per-tensor",
     "c4_b1": "long-context R8 B1 16/2 heads d256 ctx131072 P16 e4m3 KV per-token-head",
     "c4_r1": "long-context R1 B16 16/2 heads d256 ctx131072 P16 e4m3 KV per-token-head",
     "c4_b1_r1": "long-context R1 B1 16/2 heads d256 ctx131072 P16 e4m3 KV per-token-head",
@@ -433,7 +435,8 @@ def main():
     result = {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(us_step / 1e3, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": {"c1": "bf16", "c3": "bf16"}.get(args.config.split("_")[0], "fp8-e4m3 (bf16 MFMA)" if w.q_dtype != "fp8" else "fp8-e4m3"),
+        "vs_baseline": None, "dtype": ("bf16" if w.kv_dtype == "bf16" else "int8 (bf16 MFMA)" if w.kv_dtype == "int8" else
+                  "fp8-e4m3 (bf16 MFMA)" if w.q_dtype != "fp8" else "fp8-e4m3"),
         "data": "synthetic (seeded N(0,1), random page permutation)",
         "config": {"workload": WORKLOAD_NAMES[args.config], "name": args.config, "batch": w.batch,
                    "total_rows": w.total_rows, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,

@@ -50,7 +50,10 @@ typedef enum {
   PA_ERR_HIP = 4                   /* a HIP runtime call failed (message has the HIP error) */
 } pa_status;
 
-typedef enum { PA_DTYPE_BF16 = 0, PA_DTYPE_FP32 = 1, PA_DTYPE_FP8_E4M3 = 2 } pa_dtype;
+/* INT8 (KV caches only): symmetric codes in [-127, 127], value = code * scale, scale =
+ * amax / 127 over the scaled group (FreeToken PR #900, "Tested on", names int8 KV
+ * kernels; the format is this library's reading). */
+typedef enum { PA_DTYPE_BF16 = 0, PA_DTYPE_FP32 = 1, PA_DTYPE_FP8_E4M3 = 2, PA_DTYPE_INT8 = 3 } pa_dtype;
 
 typedef enum {
   PA_SCALE_NONE = 0,           /* bf16 KV                                               */
@@ -83,8 +86,9 @@ typedef struct {
   int32_t num_q_heads;         /* Hq                                                        */
   int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0                                        */
   int32_t head_dim;            /* 128 or 256                                                */
-  pa_dtype q_dtype;            /* BF16, or FP8_E4M3 (then kv must be FP8 with a per-tensor  */
-  pa_dtype kv_dtype;           /*   or per-token-head scale); kv: BF16 or FP8_E4M3          */
+  pa_dtype q_dtype;            /* BF16, or FP8_E4M3 (then kv must be FP8 as well)           */
+  pa_dtype kv_dtype;           /* BF16, FP8_E4M3 or INT8 (INT8: PER_TENSOR or PER_TOKEN_HEAD */
+                               /*   scales, bf16 queries)                                   */
   pa_scale_mode kv_scale_mode; /* NONE for bf16 KV; PER_TENSOR, PER_HEAD or PER_TOKEN_HEAD   */
                                /*   for FP8 KV                                              */
   int32_t num_cus;             /* compute units to plan for; 0 = query the current device   */
@@ -180,6 +184,14 @@ pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows
 pa_status pa_kv_quantize_fp8_per_head(const void* src, pa_dtype src_dtype, int64_t n_tokens, int32_t num_heads,
                                       int32_t head_dim, uint8_t* dst, float* scale, void* stream);
 
+/* INT8 quantiser (device): as pa_kv_quantize_fp8 with int8 codes: scale = amax / 127
+ * (1 if amax == 0) per row (PER_TOKEN_HEAD) or over all rows (PER_TENSOR, scale[0]);
+ * dst[i, c] = round-half-even(clamp(src[i, c] / scale, -127, 127)) with an IEEE float32
+ * divide (-128 is never written).  dst: device int8 [n_rows, head_dim], 8-byte
+ * aligned; src 16-byte aligned.  Errors as pa_kv_quantize_fp8. */
+pa_status pa_kv_quantize_int8(const void* src, pa_dtype src_dtype, int64_t n_rows, int32_t head_dim,
+                              pa_scale_mode mode, int8_t* dst, float* scale, void* stream);
+
 /* KV append (device): writes the keys and values of n_tokens new tokens into the paged
  * caches, as a serving step does before decode attention reads them (the per-token-head
  * FP8 KV cache of FreeToken PR #900, end-to-end table; per-tensor scales as in FlashMLA
@@ -194,6 +206,8 @@ pa_status pa_kv_quantize_fp8_per_head(const void* src, pa_dtype src_dtype, int64
  *                  caches' scales s = *k_scale, *v_scale (device scalars, only read);
  *   kv_dtype FP8_E4M3, mode PER_HEAD: the same with s = k_scale[h], v_scale[h] for KV
  *                  head h (device float32 [num_kv_heads], only read);
+ *   kv_dtype INT8, mode PER_TENSOR or PER_TOKEN_HEAD: as FP8 with the codes and scales
+ *                  of pa_kv_quantize_int8;
  *   kv_dtype FP8_E4M3, mode PER_TOKEN_HEAD: each row's scale amax/448 (1 if amax == 0)
  *                  is written to k_scale / v_scale at (page, h, slot) through sc and the
  *                  codes are those of pa_kv_quantize_fp8.

@@ -17,10 +17,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa_gfx950.so")
 
 PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_INSUFFICIENT_WORKSPACE, PA_ERR_HIP = range(5)
-PA_DTYPE_BF16, PA_DTYPE_FP32, PA_DTYPE_FP8_E4M3 = 0, 1, 2
+PA_DTYPE_BF16, PA_DTYPE_FP32, PA_DTYPE_FP8_E4M3, PA_DTYPE_INT8 = 0, 1, 2, 3
 PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_TOKEN_HEAD, PA_SCALE_PER_HEAD = 0, 1, 2, 3
 
-DTYPES = {"bf16": PA_DTYPE_BF16, "fp32": PA_DTYPE_FP32, "fp8": PA_DTYPE_FP8_E4M3}
+DTYPES = {"bf16": PA_DTYPE_BF16, "fp32": PA_DTYPE_FP32, "fp8": PA_DTYPE_FP8_E4M3, "int8": PA_DTYPE_INT8}
 SCALE_MODES = {"none": PA_SCALE_NONE, "per_tensor": PA_SCALE_PER_TENSOR, "per_token_head": PA_SCALE_PER_TOKEN_HEAD,
                "per_head": PA_SCALE_PER_HEAD}
 
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(ScaleLayout), _p, ctypes.c_float, _p, _p, _p, ctypes.c_int, _p]
         L.pa_decode_merge.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, ctypes.c_int, _p, _p]
         L.pa_kv_quantize_fp8.argtypes = [_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, _p, _p, _p]
+        L.pa_kv_quantize_int8.argtypes = [_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, _p, _p, _p]
         L.pa_kv_quantize_fp8_per_head.argtypes = [_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                   _p, _p, _p]
         L.pa_kv_append.argtypes = [_p, _p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -81,7 +82,7 @@ def lib() -> ctypes.CDLL:
                                    _p, _p, ctypes.POINTER(ScaleLayout), _p]
         L.pa_debug_gather.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, _p]
         for f in ("pa_plan_splits", "pa_decode_stage1", "pa_decode_merge", "pa_kv_quantize_fp8",
-                  "pa_kv_quantize_fp8_per_head", "pa_kv_append", "pa_debug_gather"):
+                  "pa_kv_quantize_fp8_per_head", "pa_kv_quantize_int8", "pa_kv_append", "pa_debug_gather"):
             getattr(L, f).restype = ctypes.c_int
         L.pa_last_error.restype = ctypes.c_char_p
         L.pa_version.restype = ctypes.c_char_p
@@ -161,6 +162,11 @@ def pa_decode_merge(info, plan_dev, partial_o, partial_lse, out, out_dtype, out_
 def pa_kv_quantize_fp8(src, src_dtype, n_rows, head_dim, mode, dst, scale, stream=None):
     _check(lib().pa_kv_quantize_fp8(_ptr(src), _dt(src_dtype), int(n_rows), int(head_dim), _sm(mode), _ptr(dst),
                                     _ptr(scale), _stream(stream)))
+
+
+def pa_kv_quantize_int8(src, src_dtype, n_rows, head_dim, mode, dst, scale, stream=None):
+    _check(lib().pa_kv_quantize_int8(_ptr(src), _dt(src_dtype), int(n_rows), int(head_dim), _sm(mode), _ptr(dst),
+                                     _ptr(scale), _stream(stream)))
 
 
 def pa_kv_quantize_fp8_per_head(src, src_dtype, n_tokens, num_heads, head_dim, dst, scale, stream=None):

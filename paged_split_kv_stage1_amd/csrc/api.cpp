@@ -53,8 +53,11 @@ bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
   const int nqb = (mq + 15) / 16;
   c->dh = a.head_dim;
   c->qf8 = a.q_dtype == PA_DTYPE_FP8_E4M3;
-  c->kvf8 = a.kv_dtype == PA_DTYPE_FP8_E4M3;
-  c->pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD;
+  c->kvf8 = a.kv_dtype != PA_DTYPE_BF16;            // one-byte codes
+  c->i8 = a.kv_dtype == PA_DTYPE_INT8;
+  // INT8 KV always runs the per-token scale path (bf16 MFMA on upconverted K and V); a
+  // per-tensor INT8 scale is read through zero scale strides
+  c->pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD || c->i8;
   // head_dim 256 with one query block: 64-token tiles (two token groups of two waves)
   // keep two LDS stages; 128-token tiles of d256 would fit only one
   if (nqb <= 1) { c->wq = c->dh == 256 ? 2 : 1; c->nqb = 1; }
@@ -83,8 +86,8 @@ constexpr double kMergeLaunchS = 3.0e-6;
 // Seconds of compute per KV token for one 16-row query block per wave, one workgroup
 // in a slot, by head_dim and KV format (measured with the KV loads switched off).
 double compute_s_per_token_block(const pa_plan_args& a) {
-  const bool f8 = a.kv_dtype == PA_DTYPE_FP8_E4M3;
-  const bool pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD;
+  const bool f8 = a.kv_dtype != PA_DTYPE_BF16;
+  const bool pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD || a.kv_dtype == PA_DTYPE_INT8;
   const double d_scale = a.head_dim / 128.0;
   double ns;
   if (!f8) ns = 16.0;            // two-term bf16 P
@@ -97,7 +100,7 @@ void choose_splits(const pa_plan_args& a, const KernelCfg& cfg, const std::vecto
                    const std::vector<int>& span, int num_cus, int split_cap, std::vector<int>* nsp) {
   const int B = a.batch;
   const int G = a.num_q_heads / a.num_kv_heads;
-  const double kv_tok = 2.0 * a.head_dim * (a.kv_dtype == PA_DTYPE_FP8_E4M3 ? 1 : 2) +
+  const double kv_tok = 2.0 * a.head_dim * (a.kv_dtype != PA_DTYPE_BF16 ? 1 : 2) +
                         (a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD ? 8 : 0);
   const int slots = kSlotsPerCu * num_cus;
   const double bw_slot = kHbmBytesPerS / slots;
@@ -192,13 +195,16 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
     return fail(PA_ERR_UNSUPPORTED, "page_size %d: must be a power of two in [16, 1024]", a->page_size);
   if (a->q_dtype != PA_DTYPE_BF16 && a->q_dtype != PA_DTYPE_FP8_E4M3)
     return fail(PA_ERR_INVALID_ARGUMENT, "q_dtype must be BF16 or FP8_E4M3");
-  if (a->kv_dtype != PA_DTYPE_BF16 && a->kv_dtype != PA_DTYPE_FP8_E4M3)
-    return fail(PA_ERR_INVALID_ARGUMENT, "kv_dtype must be BF16 or FP8_E4M3");
+  if (a->kv_dtype != PA_DTYPE_BF16 && a->kv_dtype != PA_DTYPE_FP8_E4M3 && a->kv_dtype != PA_DTYPE_INT8)
+    return fail(PA_ERR_INVALID_ARGUMENT, "kv_dtype must be BF16, FP8_E4M3 or INT8");
   if (a->kv_dtype == PA_DTYPE_BF16 && a->kv_scale_mode != PA_SCALE_NONE)
     return fail(PA_ERR_INVALID_ARGUMENT, "bf16 KV takes kv_scale_mode NONE");
   if (a->kv_dtype == PA_DTYPE_FP8_E4M3 && a->kv_scale_mode != PA_SCALE_PER_TENSOR &&
       a->kv_scale_mode != PA_SCALE_PER_HEAD && a->kv_scale_mode != PA_SCALE_PER_TOKEN_HEAD)
     return fail(PA_ERR_INVALID_ARGUMENT, "FP8 KV takes kv_scale_mode PER_TENSOR, PER_HEAD or PER_TOKEN_HEAD");
+  if (a->kv_dtype == PA_DTYPE_INT8 && a->kv_scale_mode != PA_SCALE_PER_TENSOR &&
+      a->kv_scale_mode != PA_SCALE_PER_TOKEN_HEAD)
+    return fail(PA_ERR_INVALID_ARGUMENT, "INT8 KV takes kv_scale_mode PER_TENSOR or PER_TOKEN_HEAD");
   if (a->q_dtype == PA_DTYPE_FP8_E4M3 && a->kv_dtype != PA_DTYPE_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "FP8 queries need an FP8 KV cache");
   if (a->max_splits < 0 || a->force_splits < 0 || a->num_cus < 0)
@@ -351,8 +357,10 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const
   if (info->needs_merge && (!partial_o || !partial_lse))
     return fail(PA_ERR_INVALID_ARGUMENT, "this plan has several splits: partial_o and partial_lse are required");
   if (cfg.qf8 && !q_scale) return fail(PA_ERR_INVALID_ARGUMENT, "FP8 queries need q_scale");
-  if (cfg.kvf8 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "FP8 KV needs k_scale and v_scale");
-  if (cfg.pt && !sc) return fail(PA_ERR_INVALID_ARGUMENT, "per-token-head scales need a scale layout");
+  if (cfg.kvf8 && (!k_scale || !v_scale))
+    return fail(PA_ERR_INVALID_ARGUMENT, "FP8 and INT8 KV need k_scale and v_scale");
+  const bool per_token = info->kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD;
+  if (per_token && !sc) return fail(PA_ERR_INVALID_ARGUMENT, "per-token-head scales need a scale layout");
   const int esz = cfg.kvf8 ? 1 : 2;
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out))
     return fail(PA_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache and out must be 16-byte aligned");
@@ -375,7 +383,7 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const
   s.k_scale = k_scale;
   s.v_scale = v_scale;
   s.scale_per_head = info->kv_scale_mode == PA_SCALE_PER_HEAD;
-  if (sc) {
+  if (per_token) {          // (per-tensor INT8 runs the per-token path with all strides 0)
     s.sc_sp = sc->page;
     s.sc_sh = sc->head;
     s.sc_ss = sc->slot;
@@ -431,9 +439,27 @@ pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d: must be 64 times a power of two, at most 1024", head_dim);
   if (!aligned16(src) || ((uintptr_t)dst & 7u) != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_quantize_fp8: src must be 16-byte and dst 8-byte aligned");
-  const int e = launch_quant(src, src_dtype == PA_DTYPE_BF16, n_rows, head_dim, mode == PA_SCALE_PER_TENSOR, dst,
+  const int e = launch_quant(src, src_dtype == PA_DTYPE_BF16, n_rows, head_dim, mode == PA_SCALE_PER_TENSOR, 0, dst,
                              scale, stream);
   if (e) return hip_fail(e, "pa_kv_quantize_fp8 launch");
+  return ok();
+}
+
+pa_status pa_kv_quantize_int8(const void* src, pa_dtype src_dtype, int64_t n_rows, int32_t head_dim,
+                              pa_scale_mode mode, int8_t* dst, float* scale, void* stream) {
+  if (!src || !dst || !scale) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_quantize_int8: NULL pointer");
+  if (src_dtype != PA_DTYPE_BF16 && src_dtype != PA_DTYPE_FP32)
+    return fail(PA_ERR_INVALID_ARGUMENT, "src_dtype must be BF16 or FP32");
+  if (mode != PA_SCALE_PER_TENSOR && mode != PA_SCALE_PER_TOKEN_HEAD)
+    return fail(PA_ERR_INVALID_ARGUMENT, "mode must be PER_TENSOR or PER_TOKEN_HEAD");
+  if (n_rows < 0) return fail(PA_ERR_INVALID_ARGUMENT, "n_rows must be >= 0");
+  if (head_dim < 64 || head_dim > 1024 || ilog2_exact(head_dim / 64) < 0 || head_dim % 64)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d: must be 64 times a power of two, at most 1024", head_dim);
+  if (!aligned16(src) || ((uintptr_t)dst & 7u) != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_quantize_int8: src must be 16-byte and dst 8-byte aligned");
+  const int e = launch_quant(src, src_dtype == PA_DTYPE_BF16, n_rows, head_dim, mode == PA_SCALE_PER_TENSOR, 1,
+                             reinterpret_cast<uint8_t*>(dst), scale, stream);
+  if (e) return hip_fail(e, "pa_kv_quantize_int8 launch");
   return ok();
 }
 
@@ -467,9 +493,13 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, pa_dtype src_dtype,
   if (kv_dtype == PA_DTYPE_BF16 && mode == PA_SCALE_NONE) m = 0;
   else if (kv_dtype == PA_DTYPE_FP8_E4M3 && (mode == PA_SCALE_PER_TENSOR || mode == PA_SCALE_PER_HEAD)) m = 1;
   else if (kv_dtype == PA_DTYPE_FP8_E4M3 && mode == PA_SCALE_PER_TOKEN_HEAD) m = 2;
+  else if (kv_dtype == PA_DTYPE_INT8 && mode == PA_SCALE_PER_TENSOR) m = 1;
+  else if (kv_dtype == PA_DTYPE_INT8 && mode == PA_SCALE_PER_TOKEN_HEAD) m = 2;
   else return fail(PA_ERR_INVALID_ARGUMENT,
-                   "pa_kv_append: kv_dtype/mode must be BF16/NONE or FP8 with PER_TENSOR, PER_HEAD or PER_TOKEN_HEAD");
-  if (m > 0 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: FP8 caches need k_scale and v_scale");
+                   "pa_kv_append: kv_dtype/mode must be BF16/NONE, FP8 with PER_TENSOR, PER_HEAD or PER_TOKEN_HEAD, "
+                   "or INT8 with PER_TENSOR or PER_TOKEN_HEAD");
+  if (m > 0 && (!k_scale || !v_scale))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: FP8 and INT8 caches need k_scale and v_scale");
   if (m == 2 && !sc) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: per-token-head scales need a scale layout");
   if (n_tokens < 0 || num_kv_heads < 1) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: n_tokens >= 0, num_kv_heads >= 1");
   if (2 * n_tokens * num_kv_heads >= (int64_t(1) << 31))
@@ -491,6 +521,7 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, pa_dtype src_dtype,
   a.kv_sp = kv->page; a.kv_sh = kv->head; a.kv_ss = kv->slot;
   a.sc_sp = m == 2 ? sc->page : 0; a.sc_sh = m == 2 ? sc->head : 0; a.sc_ss = m == 2 ? sc->slot : 0;
   a.scale_hstride = mode == PA_SCALE_PER_HEAD ? 1 : 0;
+  a.i8 = kv_dtype == PA_DTYPE_INT8;
   const int e = launch_append(a, src_dtype == PA_DTYPE_BF16, head_dim, m, stream);
   if (e) return hip_fail(e, "pa_kv_append launch");
   return ok();

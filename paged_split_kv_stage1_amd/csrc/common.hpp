@@ -50,6 +50,22 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
 }
+// 8 int8 codes (two dwords, byte k = code k) -> 8 bf16, exactly (|code| <= 128 fits the
+// 8-bit significand of bf16).
+__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    r[k] = (__bf16)(float)(int8_t)(lo >> (8 * k));
+    r[4 + k] = (__bf16)(float)(int8_t)(hi >> (8 * k));
+  }
+  return r;
+}
+template <bool I8>
+__device__ __forceinline__ bf16x8 codes8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  if constexpr (I8) return i8x8_to_bf16x8(lo, hi);
+  else return fp8x8_to_bf16x8(lo, hi);
+}
 // Four floats -> four e4m3 codes packed in a dword (RNE; inputs must be within +-448).
 __device__ __forceinline__ uint32_t f32x4_to_fp8x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);

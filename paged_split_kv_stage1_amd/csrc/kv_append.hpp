@@ -14,6 +14,7 @@ struct AppendArgs {
   int64_t kv_sp, kv_sh, kv_ss;        // cache element strides (page, head, slot)
   int64_t sc_sp, sc_sh, sc_ss;        // scale element strides (per-token-head)
   int scale_hstride;                  // mode 1: 1 = per-head scales [Hkv], 0 = one scale
+  int i8;                             // modes 1, 2: INT8 codes instead of e4m3
 };
 // mode: 0 bf16 cache, 1 FP8 with per-tensor scales, 2 FP8 with per-token-head scales
 int launch_append(const AppendArgs& a, int src_bf16, int head_dim, int mode, void* stream);

@@ -28,18 +28,20 @@ inline int64_t plan_bytes_for(int64_t items, int64_t rows) { return items * 64 +
 struct KernelCfg {
   int dh;        // 128 or 256
   int qf8;       // q is e4m3 (fp8 MFMA for q.k)
-  int kvf8;      // KV is e4m3
+  int kvf8;      // KV holds one-byte codes (e4m3, or int8 with i8)
+  int i8;        // KV codes are int8
   int pt;        // per-(token, KV head) scales
   int wq;        // waves splitting the 16-row query blocks (1, 2, 4); 4/wq waves split tokens
   int nqb;       // 16-row query blocks per wave
 };
 inline int32_t pack_cfg(const KernelCfg& c) {
-  return (c.dh == 256 ? 1 : 0) | (c.qf8 << 1) | (c.kvf8 << 2) | (c.pt << 3) | (c.wq << 4) | (c.nqb << 8);
+  return (c.dh == 256 ? 1 : 0) | (c.qf8 << 1) | (c.kvf8 << 2) | (c.pt << 3) | (c.wq << 4) | (c.nqb << 8) |
+         (c.i8 << 12);
 }
 inline KernelCfg unpack_cfg(int32_t v) {
   KernelCfg c;
   c.dh = (v & 1) ? 256 : 128; c.qf8 = (v >> 1) & 1; c.kvf8 = (v >> 2) & 1; c.pt = (v >> 3) & 1;
-  c.wq = (v >> 4) & 15; c.nqb = (v >> 8) & 15;
+  c.wq = (v >> 4) & 15; c.nqb = (v >> 8) & 15; c.i8 = (v >> 12) & 1;
   return c;
 }
 
@@ -78,7 +80,7 @@ struct GatherArgs {
 int launch_stage1(const KernelCfg& cfg, const Stage1Args& a, int num_items, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_gather(const GatherArgs& a, int num_items, void* stream);
-int launch_quant(const void* src, int src_bf16, int64_t n_rows, int head_dim, int per_tensor,
+int launch_quant(const void* src, int src_bf16, int64_t n_rows, int head_dim, int per_tensor, int i8,
                  uint8_t* dst, float* scale, void* stream);
 bool stage1_cfg_supported(const KernelCfg& cfg);
 

@@ -75,6 +75,29 @@ __device__ __forceinline__ uint2 encode8(const float* x, float sc, float inv) {
   return uint2{f32x4_to_fp8x4(q[0], q[1], q[2], q[3]), f32x4_to_fp8x4(q[4], q[5], q[6], q[7])};
 }
 
+// INT8 codes: scale = amax / 127, code = round-half-even(clamp(x / scale, -127, 127))
+// with the same correctly rounded quotient.
+__device__ __forceinline__ float scale_of_i8(float amax) { return amax == 0.f ? 1.0f : amax / 127.0f; }
+__device__ __forceinline__ uint2 encode8_i8(const float* x, float sc, float inv) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float q = fminf(fmaxf(div_rn(x[k], sc, inv), -127.0f), 127.0f);
+    w[k >> 2] |= ((uint32_t)(int)__builtin_rintf(q) & 0xFFu) << (8 * (k & 3));
+  }
+  return uint2{w[0], w[1]};
+}
+template <bool I8>
+__device__ __forceinline__ float scale_fmt(float amax) {
+  if constexpr (I8) return scale_of_i8(amax);
+  else return scale_of(amax);
+}
+template <bool I8>
+__device__ __forceinline__ uint2 encode_fmt(const float* x, float sc, float inv) {
+  if constexpr (I8) return encode8_i8(x, sc, inv);
+  else return encode8(x, sc, inv);
+}
+
 // Streaming stores: 8 codes, 8 bf16.
 __device__ __forceinline__ void store_codes(uint8_t* p, uint2 c) {
   __builtin_nontemporal_store((uint64_t)c.x | ((uint64_t)c.y << 32), reinterpret_cast<uint64_t*>(p));
@@ -85,7 +108,7 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* p, bf16x8 v) {
 
 // Per-row scales.  Rows past the end load the last row (branch-free loads) and store
 // nothing.
-template <bool BF16SRC, int D, bool BIG>
+template <bool BF16SRC, int D, bool BIG, bool I8 = false>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* src, int64_t n_rows, uint8_t* dst,
                                                          float* scale) {
   using S = RowShape<D, BIG>;
@@ -109,11 +132,11 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* src, int64_
     for (int off = S::LPR / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     const int64_t row = row0 + u * S::RPW;
     if (row >= n_rows) continue;
-    const float sc = scale_of(amax);
+    const float sc = scale_fmt<I8>(amax);
     const float inv = 1.0f / sc;                          // IEEE divide, once per row
 #pragma unroll
     for (int c = 0; c < S::EPL / 8; ++c)
-      store_codes(dst + row * D + (int64_t)part * S::EPL + 8 * c, encode8(x[u] + 8 * c, sc, inv));
+      store_codes(dst + row * D + (int64_t)part * S::EPL + 8 * c, encode_fmt<I8>(x[u] + 8 * c, sc, inv));
     if (part == 0) scale[row] = sc;
   }
 }
@@ -159,10 +182,10 @@ __global__ __launch_bounds__(256) void amax_kernel(const void* src, int64_t n, f
   }
 }
 
-template <bool BF16SRC>
+template <bool BF16SRC, bool I8 = false>
 __global__ __launch_bounds__(256) void quant_tensor_kernel(const void* src, int64_t n, uint8_t* dst,
                                                            const float* amax_word) {
-  const float sc = scale_of(*amax_word);
+  const float sc = scale_fmt<I8>(*amax_word);
   const float inv = 1.0f / sc;
   const int64_t groups = n / 8;
   const int64_t stride = (int64_t)gridDim.x * 256;
@@ -172,16 +195,17 @@ __global__ __launch_bounds__(256) void quant_tensor_kernel(const void* src, int6
 #pragma unroll
     for (int u = 0; u < TENSOR_U; ++u) load8<BF16SRC>(src, (gi + u * stride) * 8, x[u]);
 #pragma unroll
-    for (int u = 0; u < TENSOR_U; ++u) store_codes(dst + (gi + u * stride) * 8, encode8(x[u], sc, inv));
+    for (int u = 0; u < TENSOR_U; ++u) store_codes(dst + (gi + u * stride) * 8, encode_fmt<I8>(x[u], sc, inv));
   }
   for (; gi < groups; gi += stride) {
     float x[8];
     load8<BF16SRC>(src, gi * 8, x);
-    store_codes(dst + gi * 8, encode8(x, sc, inv));
+    store_codes(dst + gi * 8, encode_fmt<I8>(x, sc, inv));
   }
 }
 
-__global__ void finish_scale_kernel(float* scale) { scale[0] = scale_of(scale[0]); }
+template <bool I8 = false>
+__global__ void finish_scale_kernel(float* scale) { scale[0] = scale_fmt<I8>(scale[0]); }
 
 constexpr unsigned kBigGrid = 2048;      // 8 workgroups per CU: enough to take U = 4
 
@@ -191,37 +215,37 @@ static unsigned grid_of(int64_t n_rows) {
   return (unsigned)((n_rows + per - 1) / per);
 }
 
-template <bool BF16SRC, int D>
+template <bool BF16SRC, int D, bool I8 = false>
 static void launch_rows_d(const void* src, int64_t n_rows, uint8_t* dst, float* scale, hipStream_t s) {
   const unsigned big = grid_of<D, true>(n_rows);
   if (big >= kBigGrid)
-    hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, D, true>), dim3(big), dim3(256), 0, s, src, n_rows, dst, scale);
+    hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, D, true, I8>), dim3(big), dim3(256), 0, s, src, n_rows, dst, scale);
   else
-    hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, D, false>), dim3(grid_of<D, false>(n_rows)), dim3(256), 0, s,
+    hipLaunchKernelGGL((quant_rows_kernel<BF16SRC, D, false, I8>), dim3(grid_of<D, false>(n_rows)), dim3(256), 0, s,
                        src, n_rows, dst, scale);
 }
 
-template <bool BF16SRC>
+template <bool BF16SRC, bool I8 = false>
 static int launch_rows(const void* src, int64_t n_rows, int head_dim, uint8_t* dst, float* scale, hipStream_t s) {
   switch (head_dim) {
-    case 64: launch_rows_d<BF16SRC, 64>(src, n_rows, dst, scale, s); break;
-    case 128: launch_rows_d<BF16SRC, 128>(src, n_rows, dst, scale, s); break;
-    case 256: launch_rows_d<BF16SRC, 256>(src, n_rows, dst, scale, s); break;
-    case 512: launch_rows_d<BF16SRC, 512>(src, n_rows, dst, scale, s); break;
-    case 1024: launch_rows_d<BF16SRC, 1024>(src, n_rows, dst, scale, s); break;
+    case 64: launch_rows_d<BF16SRC, 64, I8>(src, n_rows, dst, scale, s); break;
+    case 128: launch_rows_d<BF16SRC, 128, I8>(src, n_rows, dst, scale, s); break;
+    case 256: launch_rows_d<BF16SRC, 256, I8>(src, n_rows, dst, scale, s); break;
+    case 512: launch_rows_d<BF16SRC, 512, I8>(src, n_rows, dst, scale, s); break;
+    case 1024: launch_rows_d<BF16SRC, 1024, I8>(src, n_rows, dst, scale, s); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
 }
 
-template <bool BF16SRC>
+template <bool BF16SRC, bool I8 = false>
 static int launch_tensor(const void* src, int64_t n, uint8_t* dst, float* scale, hipStream_t s) {
   const int64_t want = (n / 8 + 255) / 256;
   const unsigned blocks = (unsigned)(want < 1024 ? (want > 0 ? want : 1) : 1024);   // 4 per CU
   hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, s, scale);
   hipLaunchKernelGGL((amax_kernel<BF16SRC>), dim3(blocks), dim3(256), 0, s, src, n, scale);
-  hipLaunchKernelGGL((quant_tensor_kernel<BF16SRC>), dim3(blocks), dim3(256), 0, s, src, n, dst, scale);
-  hipLaunchKernelGGL(finish_scale_kernel, dim3(1), dim3(1), 0, s, scale);
+  hipLaunchKernelGGL((quant_tensor_kernel<BF16SRC, I8>), dim3(blocks), dim3(256), 0, s, src, n, dst, scale);
+  hipLaunchKernelGGL(finish_scale_kernel<I8>, dim3(1), dim3(1), 0, s, scale);
   return (int)hipGetLastError();
 }
 
@@ -348,7 +372,7 @@ int launch_quant_heads(const void* src, int src_bf16, int64_t n_tokens, int num_
 // Row indices fit in 32 bits (the host checks 2 * n_tokens * hkv < 2^31).  Rows of
 // skipped tokens (negative slot) and rows past the end still load a row (the last one,
 // past the end) so that the loads stay branch-free, and store nothing.
-template <bool BF16SRC, int D, int MODE, bool BIG>
+template <bool BF16SRC, int D, int MODE, bool BIG, bool I8 = false>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   using S = RowShape<D, BIG>;
   const int lane = threadIdx.x & 63;
@@ -398,11 +422,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     } else {
       float sc;
       if constexpr (MODE == 1) sc = (is_v ? a.v_scale : a.k_scale)[h * a.scale_hstride];
-      else sc = scale_of(amax);
+      else sc = scale_fmt<I8>(amax);
       const float inv = 1.0f / sc;
       uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) + off;
 #pragma unroll
-      for (int c = 0; c < S::EPL / 8; ++c) store_codes(dst + 8 * c, encode8(x[u] + 8 * c, sc, inv));
+      for (int c = 0; c < S::EPL / 8; ++c) store_codes(dst + 8 * c, encode_fmt<I8>(x[u] + 8 * c, sc, inv));
       if constexpr (MODE == 2) {
         if (part == 0)
           (is_v ? a.v_scale : a.k_scale)[page * a.sc_sp + (int64_t)h * a.sc_sh + s_in * a.sc_ss] = sc;
@@ -411,24 +435,24 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
-template <bool BF16SRC, int D, int MODE>
+template <bool BF16SRC, int D, int MODE, bool I8>
 static void launch_append_d(const AppendArgs& a, hipStream_t s) {
   const int64_t rows = 2 * a.n_tokens * a.hkv;
   const unsigned big = grid_of<D, true>(rows);
   if (big >= kBigGrid)
-    hipLaunchKernelGGL((append_kernel<BF16SRC, D, MODE, true>), dim3(big), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((append_kernel<BF16SRC, D, MODE, true, I8>), dim3(big), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((append_kernel<BF16SRC, D, MODE, false>), dim3(grid_of<D, false>(rows)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((append_kernel<BF16SRC, D, MODE, false, I8>), dim3(grid_of<D, false>(rows)), dim3(256), 0, s, a);
 }
 
-template <bool BF16SRC, int MODE>
+template <bool BF16SRC, int MODE, bool I8>
 static int launch_append_mode(const AppendArgs& a, int head_dim, hipStream_t s) {
   switch (head_dim) {
-    case 64: launch_append_d<BF16SRC, 64, MODE>(a, s); break;
-    case 128: launch_append_d<BF16SRC, 128, MODE>(a, s); break;
-    case 256: launch_append_d<BF16SRC, 256, MODE>(a, s); break;
-    case 512: launch_append_d<BF16SRC, 512, MODE>(a, s); break;
-    case 1024: launch_append_d<BF16SRC, 1024, MODE>(a, s); break;
+    case 64: launch_append_d<BF16SRC, 64, MODE, I8>(a, s); break;
+    case 128: launch_append_d<BF16SRC, 128, MODE, I8>(a, s); break;
+    case 256: launch_append_d<BF16SRC, 256, MODE, I8>(a, s); break;
+    case 512: launch_append_d<BF16SRC, 512, MODE, I8>(a, s); break;
+    case 1024: launch_append_d<BF16SRC, 1024, MODE, I8>(a, s); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
@@ -437,26 +461,27 @@ static int launch_append_mode(const AppendArgs& a, int head_dim, hipStream_t s) 
 int launch_append(const AppendArgs& a, int src_bf16, int head_dim, int mode, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (a.n_tokens <= 0) return 0;
-  if (src_bf16) {
-    if (mode == 0) return launch_append_mode<true, 0>(a, head_dim, s);
-    if (mode == 1) return launch_append_mode<true, 1>(a, head_dim, s);
-    return launch_append_mode<true, 2>(a, head_dim, s);
-  }
-  if (mode == 0) return launch_append_mode<false, 0>(a, head_dim, s);
-  if (mode == 1) return launch_append_mode<false, 1>(a, head_dim, s);
-  return launch_append_mode<false, 2>(a, head_dim, s);
+  auto go = [&](auto bf16_c, auto i8_c) {
+    constexpr bool B = decltype(bf16_c)::value, I = decltype(i8_c)::value;
+    if (mode == 0) return launch_append_mode<B, 0, false>(a, head_dim, s);
+    if (mode == 1) return launch_append_mode<B, 1, I>(a, head_dim, s);
+    return launch_append_mode<B, 2, I>(a, head_dim, s);
+  };
+  if (src_bf16) return a.i8 ? go(std::true_type{}, std::true_type{}) : go(std::true_type{}, std::false_type{});
+  return a.i8 ? go(std::false_type{}, std::true_type{}) : go(std::false_type{}, std::false_type{});
 }
 
-int launch_quant(const void* src, int src_bf16, int64_t n_rows, int head_dim, int per_tensor, uint8_t* dst,
+int launch_quant(const void* src, int src_bf16, int64_t n_rows, int head_dim, int per_tensor, int i8, uint8_t* dst,
                  float* scale, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (n_rows <= 0) return 0;
-  if (per_tensor) {
-    const int64_t n = n_rows * head_dim;
-    return src_bf16 ? launch_tensor<true>(src, n, dst, scale, s) : launch_tensor<false>(src, n, dst, scale, s);
-  }
-  return src_bf16 ? launch_rows<true>(src, n_rows, head_dim, dst, scale, s)
-                  : launch_rows<false>(src, n_rows, head_dim, dst, scale, s);
+  auto go = [&](auto bf16_c, auto i8_c) {
+    constexpr bool B = decltype(bf16_c)::value, I = decltype(i8_c)::value;
+    if (per_tensor) return launch_tensor<B, I>(src, n_rows * head_dim, dst, scale, s);
+    return launch_rows<B, I>(src, n_rows, head_dim, dst, scale, s);
+  };
+  if (src_bf16) return i8 ? go(std::true_type{}, std::true_type{}) : go(std::true_type{}, std::false_type{});
+  return i8 ? go(std::false_type{}, std::true_type{}) : go(std::false_type{}, std::false_type{});
 }
 
 }  // namespace pa

@@ -40,23 +40,29 @@ namespace pa {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB, int NS, int PD>
+// KV: 0 bf16 cache, 1 e4m3 codes, 2 int8 codes (both one byte per element).
+template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB, int NS, int PD>
 struct S1Cfg {
+  static constexpr bool KVF8 = KV != 0;             // one-byte codes (e4m3 or int8)
+  static constexpr bool I8 = KV == 2;
   static constexpr int WT = 4 / WQ;                 // waves splitting the tokens of a tile
   static constexpr int BN = 32 * WT;                // tokens per tile
   static constexpr int KVB = KVF8 ? 1 : 2;          // bytes per cached element in HBM
   // LDS holds bf16 tiles for bf16 caches.  For per-token-head FP8 caches read with
   // bf16 queries by four query-block waves, K is upconverted once when a tile is stored
   // (instead of once by every wave that reads it) while V stays FP8, which halves the
-  // bytes of the transposing V reads that bound this shape.
-  static constexpr bool LBF = !KVF8 || (PT && !QF8 && WQ == 4);   // K tile in bf16
-  static constexpr bool LBFV = !KVF8;                               // V tile in bf16
+  // bytes of the transposing V reads that bound this shape.  INT8 codes have no packed
+  // conversion to bf16 (two to three VALU operations per value), so both K and V are
+  // converted once, when the tile is stored.
+  static constexpr bool LBF = !KVF8 || I8 || (PT && !QF8 && WQ == 4);   // K tile in bf16
+  static constexpr bool LBFV = !KVF8 || I8;                               // V tile in bf16
   static constexpr int LKB = LBF ? 2 : 1;           // bytes per K element in LDS
   static constexpr int LVB = LBFV ? 2 : 1;          // bytes per V element in LDS
   static constexpr int CPR = DH * KVB / 16;         // 16-byte chunks per token row in HBM
   static constexpr int LCPR = DH * LKB / 16;        // 16-byte chunks per K token row in LDS
   static constexpr int VCPR = DH * LVB / 16;        // 16-byte chunks per V token row in LDS
   static constexpr int XPC = LKB / KVB;             // LDS K chunks stored per loaded chunk
+  static constexpr int VXPC = LVB / KVB;            // LDS V chunks stored per loaded chunk
   static constexpr int TPI = 64 / CPR;              // tokens one wave covers per load step
   static constexpr int KTB = BN * DH * LKB;         // LDS bytes of one K tile
   static constexpr int VTB = BN * DH * LVB;         // LDS bytes of one V tile
@@ -110,9 +116,10 @@ struct QOperand<true> { using T = long; };
 template <int V>
 using ic = std::integral_constant<int, V>;
 
-template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB, int NS, int PD>
+template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB, int NS, int PD>
 __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
-  using C = S1Cfg<DH, QF8, KVF8, PT, WQ, NQB, NS, PD>;
+  using C = S1Cfg<DH, QF8, KV, PT, WQ, NQB, NS, PD>;
+  constexpr bool KVF8 = C::KVF8;
   using QT = typename QOperand<QF8>::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDSB];
 
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
   const int lt = lane / C::CPR;
   const int cpos = lane % C::CPR;
   const uint32_t goff = (uint32_t)(lt * a.kv_ss * C::KVB) + (cpos << 4);
-  uint32_t kpos[C::CPT][C::XPC], vpos[C::CPT];
+  uint32_t kpos[C::CPT][C::XPC], vpos[C::CPT][C::VXPC];
 #pragma unroll
   for (int i = 0; i < C::CPT; ++i) {
     const int t = (wave * 64 + 256 * i) / C::CPR + lt;
@@ -218,7 +225,11 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
       const int c = cpos * C::XPC + x;
       kpos[i][x] = (t * C::LCPR + (c ^ swz_k<C::LCPR>(t))) << 4;
     }
-    vpos[i] = (t * C::VCPR + (cpos ^ swz_v<C::VCPR, !C::LBFV>(t))) << 4;
+#pragma unroll
+    for (int x = 0; x < C::VXPC; ++x) {
+      const int c = cpos * C::VXPC + x;
+      vpos[i][x] = (t * C::VCPR + (c ^ swz_v<C::VCPR, !C::LBFV>(t))) << 4;
+    }
   }
   u32x4 kreg[PD][C::CPT], vreg[PD][C::CPT];
   float sreg[PD];
@@ -271,12 +282,18 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
     for (int i = 0; i < C::CPT; ++i) {
       if constexpr (C::XPC == 1) {
         *reinterpret_cast<u32x4*>(stage + kpos[i][0]) = kreg[SL][i];
-      } else {                 // 16 FP8 values -> two chunks of 8 bf16 (exact)
+      } else {                 // 16 one-byte codes -> two chunks of 8 bf16 (exact)
         const u32x4 kq = kreg[SL][i];
-        *reinterpret_cast<bf16x8*>(stage + kpos[i][0]) = fp8x8_to_bf16x8(kq[0], kq[1]);
-        *reinterpret_cast<bf16x8*>(stage + kpos[i][1]) = fp8x8_to_bf16x8(kq[2], kq[3]);
+        *reinterpret_cast<bf16x8*>(stage + kpos[i][0]) = codes8_to_bf16x8<C::I8>(kq[0], kq[1]);
+        *reinterpret_cast<bf16x8*>(stage + kpos[i][1]) = codes8_to_bf16x8<C::I8>(kq[2], kq[3]);
       }
-      *reinterpret_cast<u32x4*>(stage + C::KTB + vpos[i]) = vreg[SL][i];
+      if constexpr (C::VXPC == 1) {
+        *reinterpret_cast<u32x4*>(stage + C::KTB + vpos[i][0]) = vreg[SL][i];
+      } else {
+        const u32x4 vq = vreg[SL][i];
+        *reinterpret_cast<bf16x8*>(stage + C::KTB + vpos[i][0]) = codes8_to_bf16x8<C::I8>(vq[0], vq[1]);
+        *reinterpret_cast<bf16x8*>(stage + C::KTB + vpos[i][1]) = codes8_to_bf16x8<C::I8>(vq[2], vq[3]);
+      }
     }
     if constexpr (PT) {
       if (tid < 2 * C::BN) reinterpret_cast<float*>(stage + C::KTB + C::VTB)[tid] = sreg[SL];
@@ -612,11 +629,13 @@ __global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
 // LDS stages and register prefetch depth: two stages when two workgroups still fit
 // in the CU's 160 KiB of LDS, else one; two tiles of register prefetch when a tile
 // costs at most 32 VGPRs per thread, else one.
-template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB>
+template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB>
 struct Pipe {
+  static constexpr bool KVF8 = KV != 0;
   static constexpr int BN = 32 * (4 / WQ);
-  static constexpr bool LBF = !KVF8 || (PT && !QF8 && WQ == 4);   // as S1Cfg::LBF
-  static constexpr int stage = BN * DH * ((LBF ? 2 : 1) + (KVF8 ? 1 : 2)) + (PT ? 2 * BN * 4 : 0);
+  static constexpr bool LBF = !KVF8 || KV == 2 || (PT && !QF8 && WQ == 4);   // as S1Cfg::LBF
+  static constexpr bool LBFV = !KVF8 || KV == 2;                              // as S1Cfg::LBFV
+  static constexpr int stage = BN * DH * ((LBF ? 2 : 1) + (LBFV ? 2 : 1)) + (PT ? 2 * BN * 4 : 0);
   static constexpr int NS = 2 * stage <= 80 * 1024 ? 2 : 1;
   static constexpr int CPT = BN * DH * (KVF8 ? 1 : 2) / 16 / 256;
   // tiles in flight in registers (8 VGPRs per 16-byte chunk of K and V).  A third tile
@@ -624,50 +643,51 @@ struct Pipe {
   static constexpr int PD = CPT <= 4 ? 2 : 1;
 };
 
-template <int DH, bool QF8, bool KVF8, bool PT, int WQ, int NQB>
+template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB>
 static int launch_one(const Stage1Args& a, int num_items, void* stream) {
-  using Pp = Pipe<DH, QF8, KVF8, PT, WQ, NQB>;
-  using C = S1Cfg<DH, QF8, KVF8, PT, WQ, NQB, Pp::NS, Pp::PD>;
+  using Pp = Pipe<DH, QF8, KV, PT, WQ, NQB>;
+  using C = S1Cfg<DH, QF8, KV, PT, WQ, NQB, Pp::NS, Pp::PD>;
   static_assert(Pp::stage == C::STAGEB, "host and kernel disagree on the LDS stage size");
   static_assert(C::LDSB <= 80 * 1024, "two workgroups per CU must fit in 160 KB of LDS");
-  hipLaunchKernelGGL((stage1_kernel<DH, QF8, KVF8, PT, WQ, NQB, Pp::NS, Pp::PD>), dim3(num_items), dim3(256), 0,
+  hipLaunchKernelGGL((stage1_kernel<DH, QF8, KV, PT, WQ, NQB, Pp::NS, Pp::PD>), dim3(num_items), dim3(256), 0,
                      (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
 // Largest query-block count per wave instantiated for a mode: per-tensor FP8 V keeps
 // a second (lo) accumulator, which does not fit in registers for more blocks.
-template <int DH, bool KVF8, bool PT>
+template <int DH, int KV, bool PT>
 constexpr int max_nqb() {
-  constexpr bool pv_fp8 = KVF8 && !PT;
+  constexpr bool pv_fp8 = KV == 1 && !PT;
   if constexpr (DH == 128) return pv_fp8 ? 2 : 3;
   else return pv_fp8 ? 1 : 2;
 }
 
-template <int DH, bool QF8, bool KVF8, bool PT>
+template <int DH, bool QF8, int KV, bool PT>
 static int dispatch_tiles(const KernelCfg& c, const Stage1Args& a, int n, void* s) {
-  constexpr int NMAX = max_nqb<DH, KVF8, PT>();
+  constexpr int NMAX = max_nqb<DH, KV, PT>();
   if constexpr (DH == 128) {      // d256 always runs >= 2 query-block waves (64-token tiles)
-    if (c.wq == 1 && c.nqb == 1) return launch_one<DH, QF8, KVF8, PT, 1, 1>(a, n, s);
+    if (c.wq == 1 && c.nqb == 1) return launch_one<DH, QF8, KV, PT, 1, 1>(a, n, s);
   }
-  if (c.wq == 2 && c.nqb == 1) return launch_one<DH, QF8, KVF8, PT, 2, 1>(a, n, s);
-  if (c.wq == 4 && c.nqb == 1) return launch_one<DH, QF8, KVF8, PT, 4, 1>(a, n, s);
+  if (c.wq == 2 && c.nqb == 1) return launch_one<DH, QF8, KV, PT, 2, 1>(a, n, s);
+  if (c.wq == 4 && c.nqb == 1) return launch_one<DH, QF8, KV, PT, 4, 1>(a, n, s);
   if constexpr (NMAX >= 2) {
-    if (c.wq == 4 && c.nqb == 2) return launch_one<DH, QF8, KVF8, PT, 4, 2>(a, n, s);
+    if (c.wq == 4 && c.nqb == 2) return launch_one<DH, QF8, KV, PT, 4, 2>(a, n, s);
   }
   if constexpr (NMAX >= 3) {
-    if (c.wq == 4 && c.nqb == 3) return launch_one<DH, QF8, KVF8, PT, 4, 3>(a, n, s);
+    if (c.wq == 4 && c.nqb == 3) return launch_one<DH, QF8, KV, PT, 4, 3>(a, n, s);
   }
   return (int)hipErrorInvalidValue;
 }
 
 template <int DH>
 static int dispatch_modes(const KernelCfg& c, const Stage1Args& a, int n, void* s) {
-  if (!c.qf8 && !c.kvf8) return dispatch_tiles<DH, false, false, false>(c, a, n, s);
-  if (c.qf8 && c.kvf8 && !c.pt) return dispatch_tiles<DH, true, true, false>(c, a, n, s);
-  if (c.qf8 && c.kvf8 && c.pt) return dispatch_tiles<DH, true, true, true>(c, a, n, s);
-  if (!c.qf8 && c.kvf8 && !c.pt) return dispatch_tiles<DH, false, true, false>(c, a, n, s);
-  if (!c.qf8 && c.kvf8 && c.pt) return dispatch_tiles<DH, false, true, true>(c, a, n, s);
+  if (c.i8) return !c.qf8 && c.pt ? dispatch_tiles<DH, false, 2, true>(c, a, n, s) : (int)hipErrorInvalidValue;
+  if (!c.qf8 && !c.kvf8) return dispatch_tiles<DH, false, 0, false>(c, a, n, s);
+  if (c.qf8 && c.kvf8 && !c.pt) return dispatch_tiles<DH, true, 1, false>(c, a, n, s);
+  if (c.qf8 && c.kvf8 && c.pt) return dispatch_tiles<DH, true, 1, true>(c, a, n, s);
+  if (!c.qf8 && c.kvf8 && !c.pt) return dispatch_tiles<DH, false, 1, false>(c, a, n, s);
+  if (!c.qf8 && c.kvf8 && c.pt) return dispatch_tiles<DH, false, 1, true>(c, a, n, s);
   return (int)hipErrorInvalidValue;
 }
 
@@ -675,6 +695,7 @@ bool stage1_cfg_supported(const KernelCfg& c) {
   if (c.dh != 128 && c.dh != 256) return false;
   if (c.qf8 && !c.kvf8) return false;
   if (!c.kvf8 && c.pt) return false;
+  if (c.i8 && (!c.kvf8 || !c.pt || c.qf8)) return false;    // INT8 KV: bf16 queries, per-token scale path
   const bool pv_fp8 = c.kvf8 && !c.pt;
   const int nmax = c.dh == 128 ? (pv_fp8 ? 2 : 3) : (pv_fp8 ? 1 : 2);
   if (c.nqb == 1) return (c.wq == 1 && c.dh == 128) || c.wq == 2 || c.wq == 4;

@@ -1,7 +1,7 @@
 """Puts a synthetic workload on the GPU in the layouts the kernels read.
 
-bf16 caches are uploaded as they are; FP8 caches and FP8 queries are produced on
-the device by the library's own quantiser (pa_kv_quantize_fp8).  Slots that hold no
+bf16 caches are uploaded as they are; FP8 / INT8 caches and FP8 queries are produced
+on the device by the library's own quantisers.  Slots that hold no
 token (the tail of each request's last page) are then overwritten with NaN bit
 patterns, together with their per-token scales, so that any read of them shows.
 """
@@ -13,8 +13,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from ._lib import pa_kv_quantize_fp8, pa_kv_quantize_fp8_per_head
-from .inputs import BF16_NAN_BITS, E4M3_NAN_CODE, Workload
+from ._lib import pa_kv_quantize_fp8, pa_kv_quantize_fp8_per_head, pa_kv_quantize_int8
+from .inputs import BF16_NAN_BITS, E4M3_NAN_CODE, INT8_POISON_CODE, Workload
 
 
 @dataclasses.dataclass
@@ -49,11 +49,12 @@ def _quantize_heads(src_bf16: torch.Tensor, head_axis: int, device):
     return codes.movedim(-2, head_axis).contiguous(), scale
 
 
-def _quantize(src_bf16: torch.Tensor, mode: str, d: int, device):
+def _quantize(src_bf16: torch.Tensor, mode: str, d: int, device, int8: bool = False):
+    """FP8 (or INT8) codes, as bytes, and the scales of a bf16 tensor of rows of d."""
     n_rows = src_bf16.numel() // d
     codes = torch.empty(src_bf16.shape, dtype=torch.uint8, device=device)
     scale = torch.empty(1 if mode == "per_tensor" else n_rows, dtype=torch.float32, device=device)
-    pa_kv_quantize_fp8(src_bf16, "bf16", n_rows, d, mode, codes, scale)
+    (pa_kv_quantize_int8 if int8 else pa_kv_quantize_fp8)(src_bf16, "bf16", n_rows, d, mode, codes, scale)
     if mode == "per_token_head":
         scale = scale.view(src_bf16.shape[:-1])
     return codes, scale
@@ -75,6 +76,14 @@ def to_device(w: Workload, device="cuda", layout: str = "HPD") -> DeviceInputs:
         v = v_src.to(device)
         k.view(torch.int16).masked_fill_(m4.expand(k.shape), BF16_NAN_BITS)
         v.view(torch.int16).masked_fill_(m4.expand(v.shape), BF16_NAN_BITS)
+    elif w.kv_dtype == "int8":
+        k, k_scale = _quantize(k_src.to(device), w.kv_scale_mode, d, device, int8=True)
+        v, v_scale = _quantize(v_src.to(device), w.kv_scale_mode, d, device, int8=True)
+        k.masked_fill_(m4.expand(k.shape), INT8_POISON_CODE)
+        v.masked_fill_(m4.expand(v.shape), INT8_POISON_CODE)
+        if w.kv_scale_mode == "per_token_head":
+            k_scale.masked_fill_(m3.expand(k_scale.shape), float("nan"))
+            v_scale.masked_fill_(m3.expand(v_scale.shape), float("nan"))
     elif w.kv_scale_mode == "per_head":
         axis = 1 if layout == "HPD" else 2
         k, k_scale = _quantize_heads(k_src.to(device), axis, device)

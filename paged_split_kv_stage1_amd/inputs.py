@@ -92,6 +92,8 @@ CONFIGS = {
                scale="per_token_head", out="bf16"),
     "c4_i8": dict(batch=16, rows=8, hq=16, hkv=2, d=256, ctx=131072, page=16, q="bf16", kv="int8",
                   scale="per_token_head", out="bf16"),
+    "c4_i8t": dict(batch=16, rows=8, hq=16, hkv=2, d=256, ctx=131072, page=16, q="bf16", kv="int8",
+                   scale="per_tensor", out="bf16"),
     "c4_b1": dict(batch=1, rows=8, hq=16, hkv=2, d=256, ctx=131072, page=16, q="bf16", kv="fp8",
                   scale="per_token_head", out="bf16"),
     "c4_r1": dict(batch=16, rows=1, hq=16, hkv=2, d=256, ctx=131072, page=16, q="bf16", kv="fp8",

@@ -15,7 +15,7 @@ def _bits(t: torch.Tensor) -> np.ndarray:
 
 def oracle_inputs(w, layout="HPD", requests=None):
     """Returns dict(q64, k, v, q_codes, q_scale) for the oracle.  With ``requests``
-    given (per-token-head only), only those requests' pages are quantised."""
+    given (per-token-head scales only), only those requests' pages are quantised."""
     k_src, v_src = w.k, w.v
     unused = w.unused_slots
     if layout == "PHD":
@@ -30,6 +30,23 @@ def oracle_inputs(w, layout="HPD", requests=None):
         vb = np.where(np.broadcast_to(m4, vb.shape), np.uint16(BF16_NAN_BITS), vb)
         out["k"] = PagedKV(kb, "bf16", layout)
         out["v"] = PagedKV(vb, "bf16", layout)
+    elif w.kv_dtype == "int8":
+        if w.kv_scale_mode == "per_tensor":
+            kc, ks = quantize_int8_per_tensor(kb, "bf16")
+            vc, vs = quantize_int8_per_tensor(vb, "bf16")
+        else:
+            pages = (np.concatenate([w.page_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]] for b in requests])
+                     if requests is not None else np.arange(kb.shape[0]))
+            kc = np.zeros(kb.shape, np.int8); vc = np.zeros(vb.shape, np.int8)
+            ks = np.zeros(kb.shape[:-1], np.float32); vs = np.zeros(vb.shape[:-1], np.float32)
+            kc[pages], ks[pages] = quantize_int8_per_row(kb[pages], "bf16")
+            vc[pages], vs[pages] = quantize_int8_per_row(vb[pages], "bf16")
+            ks = np.where(m3, np.float32(np.nan), ks)
+            vs = np.where(m3, np.float32(np.nan), vs)
+        kc = np.where(np.broadcast_to(m4, kc.shape), np.uint8(INT8_POISON_CODE), kc.view(np.uint8))
+        vc = np.where(np.broadcast_to(m4, vc.shape), np.uint8(INT8_POISON_CODE), vc.view(np.uint8))
+        out["k"] = PagedKV(kc, "int8", layout, w.kv_scale_mode, ks)
+        out["v"] = PagedKV(vc, "int8", layout, w.kv_scale_mode, vs)
     elif w.kv_scale_mode == "per_tensor":
         kc, ks = quantize_per_tensor(kb, "bf16")
         vc, vs = quantize_per_tensor(vb, "bf16")
@@ -37,19 +54,6 @@ def oracle_inputs(w, layout="HPD", requests=None):
         vc = np.where(np.broadcast_to(m4, vc.shape), np.uint8(E4M3_NAN_CODE), vc)
         out["k"] = PagedKV(kc, "fp8", layout, "per_tensor", ks)
         out["v"] = PagedKV(vc, "fp8", layout, "per_tensor", vs)
-    elif w.kv_dtype == "int8":
-        if w.kv_scale_mode == "per_tensor":
-            kc, ks = quantize_int8_per_tensor(kb, "bf16")
-            vc, vs = quantize_int8_per_tensor(vb, "bf16")
-        else:
-            kc, ks = quantize_int8_per_row(kb, "bf16")
-            vc, vs = quantize_int8_per_row(vb, "bf16")
-            ks = np.where(m3, np.float32(np.nan), ks)
-            vs = np.where(m3, np.float32(np.nan), vs)
-        kc = np.where(np.broadcast_to(m4, kc.shape), np.uint8(INT8_POISON_CODE), kc.view(np.uint8))
-        vc = np.where(np.broadcast_to(m4, vc.shape), np.uint8(INT8_POISON_CODE), vc.view(np.uint8))
-        out["k"] = PagedKV(kc, "int8", layout, w.kv_scale_mode, ks)
-        out["v"] = PagedKV(vc, "int8", layout, w.kv_scale_mode, vs)
     elif w.kv_scale_mode == "per_head":
         axis = 1 if layout == "HPD" else 2
         kc, ks = quantize_per_head(kb, "bf16", axis)

@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "pa.h")).read()
     declared = set(re.findall(r"^(?:pa_status|const char\*)\s+(pa_\w+)\(", header, flags=re.M))
     assert {"pa_plan_splits", "pa_decode_stage1", "pa_decode_merge", "pa_kv_quantize_fp8", "pa_kv_append",
-            "pa_kv_quantize_fp8_per_head", "pa_debug_gather", "pa_last_error"} <= declared
+            "pa_kv_quantize_fp8_per_head", "pa_kv_quantize_int8", "pa_debug_gather", "pa_last_error"} <= declared
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -240,6 +240,30 @@ def test_per_head_mode_needs_fp8_kv_and_plans_like_per_tensor():
     a, _ = _plan(kvd="fp8", mode="per_head")
     b, _ = _plan(kvd="fp8", mode="per_tensor")
     assert (a.num_items, a.max_splits, a.variant) == (b.num_items, b.max_splits, b.variant)
+
+
+def test_int8_kv_modes_and_queries():
+    # INT8 KV: bf16 queries, per-tensor or per-token-head scales; it plans on the
+    # per-token kernel path
+    a, _ = _plan(kvd="int8", mode="per_token_head")
+    b, _ = _plan(kvd="int8", mode="per_tensor")
+    assert a.variant == b.variant and (a.variant >> 12) & 1 and (a.variant >> 3) & 1
+    for kw in (dict(kvd="int8", mode="per_head"), dict(kvd="int8", mode="none"), dict(kvd="int8", q="fp8",
+                                                                                      mode="per_tensor")):
+        with pytest.raises(PaError) as e:
+            _plan(**kw)
+        assert e.value.status in (PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED)
+    fake = 1 << 20
+    with pytest.raises(PaError) as e:
+        _lib.pa_kv_quantize_int8(fake, "bf16", 10, 128, "per_head", fake, fake)
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT
+    with pytest.raises(PaError) as e:
+        _lib.pa_kv_quantize_int8(fake, "bf16", 10, 96, "per_tensor", fake, fake)
+    assert e.value.status == PA_ERR_UNSUPPORTED
+    with pytest.raises(PaError) as e:
+        _lib.pa_kv_append(fake, fake, "bf16", 4, 2, 128, 16, fake, fake, fake, "int8", "per_head",
+                          (4096, 2048, 128), fake, fake)
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT
 
 
 def test_merge_without_splits_is_a_noop():

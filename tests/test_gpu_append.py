@@ -6,14 +6,18 @@ import torch
 from oracle.cache import append_kv
 from paged_split_kv_stage1_amd import pa_kv_append
 from paged_split_kv_stage1_amd.device_inputs import to_device
-from paged_split_kv_stage1_amd.inputs import BF16_NAN_BITS, E4M3_NAN_CODE, make_workload
+from paged_split_kv_stage1_amd.inputs import BF16_NAN_BITS, E4M3_NAN_CODE, INT8_POISON_CODE, make_workload
 from tests.gpu_run import run_decode
 
 pytestmark = pytest.mark.gpu
 
 
 MODE = {"bf16": "none", "fp8_per_tensor": "per_tensor", "fp8_per_head": "per_head",
-        "fp8_per_token_head": "per_token_head"}
+        "fp8_per_token_head": "per_token_head", "int8_per_tensor": "per_tensor", "int8_per_token_head": "per_token_head"}
+
+
+def _kvd(kind):
+    return kind.split("_")[0]
 
 
 def _strides(layout, P, hkv, d):
@@ -24,7 +28,8 @@ def _scale_strides(layout, P, hkv):
     return (hkv * P, P, 1) if layout == "HPD" else (P * hkv, 1, hkv)
 
 
-@pytest.mark.parametrize("kind", ["bf16", "fp8_per_tensor", "fp8_per_head", "fp8_per_token_head"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8_per_tensor", "fp8_per_head", "fp8_per_token_head", "int8_per_tensor",
+                                  "int8_per_token_head"])
 @pytest.mark.parametrize("src", ["bf16", "fp32"])
 @pytest.mark.parametrize("layout", ["HPD", "PHD"])
 @pytest.mark.parametrize("d", [128, 256])
@@ -38,7 +43,7 @@ def test_append_matches_oracle(kind, src, layout, d):
         k0, v0 = (rng.integers(0, 1 << 16, shape).astype(np.uint16) for _ in range(2))
     else:
         k0, v0 = (rng.integers(0, 256, shape).astype(np.uint8) for _ in range(2))
-    pt = kind == "fp8_per_token_head"
+    pt = kind.endswith("per_token_head")
     ks0, vs0 = (rng.random(shape[:3]).astype(np.float32) for _ in range(2)) if pt else (None, None)
     slots = rng.permutation(pages * P)[:n].astype(np.int64)
     slots[[3, 20]] = -1                                          # padding tokens
@@ -60,14 +65,14 @@ def test_append_matches_oracle(kind, src, layout, d):
     kc, vc = as_t(k0).cuda(), as_t(v0).cuda()
     if pt:
         ksc, vsc = torch.from_numpy(ks0.copy()).cuda(), torch.from_numpy(vs0.copy()).cuda()
-    elif kind == "fp8_per_tensor":
+    elif kind.endswith("per_tensor"):
         ksc, vsc = torch.tensor([ts_k]).cuda(), torch.tensor([ts_v]).cuda()
     elif kind == "fp8_per_head":
         ksc, vsc = torch.from_numpy(ts_k).cuda(), torch.from_numpy(ts_v).cuda()
     else:
         ksc = vsc = None
     pa_kv_append(kx.cuda(), vx.cuda(), src, n, hkv, d, P, torch.from_numpy(slots).cuda(), kc, vc,
-                 "bf16" if kind == "bf16" else "fp8", MODE[kind],
+                 _kvd(kind), MODE[kind],
                  _strides(layout, P, hkv, d), ksc, vsc, _scale_strides(layout, P, hkv) if pt else None)
     torch.cuda.synchronize()
     rk, rks = append_kv(k0, ks0, k_rows, src, slots, P, kind, layout, tensor_scale=ts_k)
@@ -80,7 +85,7 @@ def test_append_matches_oracle(kind, src, layout, d):
         assert np.array_equal(ksc.cpu().numpy(), rks) and np.array_equal(vsc.cpu().numpy(), rvs)
 
 
-@pytest.mark.parametrize("name", ["c2", "c2_ph", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c2", "c2_ph", "c3", "c4", "c4_i8", "c4_i8t"])
 def test_appended_tokens_are_what_decode_reads(name):
     # poison the slots of each request's last 8 tokens, then append those tokens back
     # through pa_kv_append from their bf16 rows: the cache must come back byte for byte
@@ -104,8 +109,9 @@ def test_appended_tokens_are_what_decode_reads(name):
             di.k.view(torch.int16)[p, :, s] = BF16_NAN_BITS
             di.v.view(torch.int16)[p, :, s] = BF16_NAN_BITS
         else:
-            di.k[p, :, s] = E4M3_NAN_CODE
-            di.v[p, :, s] = E4M3_NAN_CODE
+            code = INT8_POISON_CODE if w.kv_dtype == "int8" else E4M3_NAN_CODE
+            di.k[p, :, s] = code
+            di.v[p, :, s] = code
         if w.kv_scale_mode == "per_token_head":
             di.k_scale[p, :, s] = float("nan")
             di.v_scale[p, :, s] = float("nan")
@@ -125,6 +131,7 @@ MANY = [
     ("fp8_per_token_head", 2, 256, 16, 16384 + 11, "bf16"),
     ("fp8_per_tensor", 8, 128, 64, 8192 + 5, "fp32"),
     ("fp8_per_head", 8, 128, 64, 8192 + 5, "bf16"),
+    ("int8_per_token_head", 2, 256, 16, 16384 + 11, "fp32"),
     ("bf16", 2, 256, 16, 16384 + 11, "bf16"),
 ]
 
@@ -139,7 +146,7 @@ def test_append_many_rows_matches_oracle(kind, hkv, d, P, n, src):
         c0 = [rng.integers(0, 1 << 16, shape).astype(np.uint16) for _ in range(2)]
     else:
         c0 = [rng.integers(0, 256, shape).astype(np.uint8) for _ in range(2)]
-    pt = kind == "fp8_per_token_head"
+    pt = kind.endswith("per_token_head")
     s0 = [rng.random(shape[:3]).astype(np.float32) for _ in range(2)] if pt else [None, None]
     slots = rng.permutation(pages * P)[:n].astype(np.int64)
     slots[rng.choice(n, 40, replace=False)] = -1
@@ -159,14 +166,14 @@ def test_append_many_rows_matches_oracle(kind, hkv, d, P, n, src):
     caches = [as_t(c).cuda() for c in c0]
     if pt:
         scales = [torch.from_numpy(s.copy()).cuda() for s in s0]
-    elif kind == "fp8_per_tensor":
+    elif kind.endswith("per_tensor"):
         scales = [torch.tensor([t]).cuda() for t in ts]
     elif kind == "fp8_per_head":
         scales = [torch.from_numpy(t).cuda() for t in ts]
     else:
         scales = [None, None]
     pa_kv_append(new[0].cuda(), new[1].cuda(), src, n, hkv, d, P, torch.from_numpy(slots).cuda(), caches[0],
-                 caches[1], "bf16" if kind == "bf16" else "fp8", MODE[kind],
+                 caches[1], _kvd(kind), MODE[kind],
                  (hkv * P * d, P * d, d), scales[0], scales[1], (hkv * P, P, 1) if pt else None)
     torch.cuda.synchronize()
     for i in range(2):

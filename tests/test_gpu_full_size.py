@@ -13,7 +13,7 @@ from tests.oracle_inputs import max_rel_err, oracle_inputs
 
 pytestmark = pytest.mark.gpu
 
-BAR = {"bf16": 2e-3, "fp8": 2e-2}
+BAR = {"bf16": 2e-3, "fp8": 2e-2, "int8": 2e-2}
 OUT_EXTRA = {"bf16": 2.0 ** -8, "fp32": 0.0}      # bf16 output rounding on top of the bar
 
 
@@ -28,7 +28,7 @@ def _samples(w, rng, n=6):
     return picks
 
 
-@pytest.mark.parametrize("name", ["c2", "c2_ph", "c3", "c3_b1", "c4", "c4_b1", "c5"])
+@pytest.mark.parametrize("name", ["c2", "c2_ph", "c3", "c3_b1", "c4", "c4_b1", "c4_i8", "c5"])
 def test_full_size_sampled_outputs(name):
     print(f"[full-size] {name}", flush=True)
     w = make_workload(name)

@@ -5,8 +5,10 @@ import pytest
 import torch
 
 from oracle.attention import decode_attention, gather_slots
-from oracle.quantize import quantize_per_head, quantize_per_row, quantize_per_tensor
-from paged_split_kv_stage1_amd import pa_debug_gather, pa_kv_quantize_fp8, pa_kv_quantize_fp8_per_head
+from oracle.quantize import (quantize_int8_per_row, quantize_int8_per_tensor, quantize_per_head, quantize_per_row,
+                             quantize_per_tensor)
+from paged_split_kv_stage1_amd import (pa_debug_gather, pa_kv_quantize_fp8, pa_kv_quantize_fp8_per_head,
+                                       pa_kv_quantize_int8)
 from paged_split_kv_stage1_amd.device_inputs import to_device
 from paged_split_kv_stage1_amd.inputs import make_workload
 from tests.gpu_run import run_decode
@@ -14,7 +16,9 @@ from tests.oracle_inputs import max_rel_err, oracle_inputs
 
 pytestmark = pytest.mark.gpu
 
-BAR = {"bf16": 2e-3, "fp8": 2e-2}       # max relative error (per row-head, inf-norm)
+# max relative error (per row-head, inf-norm); INT8 KV (not among the pages' bars) is held
+# to the FP8 one
+BAR = {"bf16": 2e-3, "fp8": 2e-2, "int8": 2e-2}
 BF16_OUT_EXTRA = 2.0 ** -8              # bf16 output rounding on top of the bar
 
 # Shapes of the five workloads at sizes the oracle finishes in seconds; contexts are
@@ -27,6 +31,8 @@ SMALL = {
     "c3_r1": dict(batch=3, ctx=[2500, 130, 1]),
     "c3_r8": dict(batch=2, ctx=[1500, 9]),
     "c4": dict(batch=2, ctx=[2500, 700]),
+    "c4_i8": dict(batch=2, ctx=[2500, 700]),
+    "c4_i8t": dict(batch=2, ctx=[1300, 45]),
     "c4_r1": dict(batch=2, ctx=[1800, 33]),
     "c5": dict(batch=10, ctx_range=(60, 2500)),
 }
@@ -60,7 +66,7 @@ def test_parity_fp32_out(name):
         assert np.max(np.abs(got - ref_lse[rows])) <= 1e-3 * max(1.0, np.max(np.abs(ref_lse)))
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c2_ph", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c2_ph", "c3", "c4", "c4_i8", "c5"])
 def test_parity_bf16_out(name):
     print(f"[parity-bf16] {name}", flush=True)
     w = make_workload(name, **SMALL[name], out_dtype="bf16")
@@ -183,6 +189,29 @@ def test_quantizer_per_head_twice_in_a_row():
         assert np.array_equal(scale.cpu().numpy(), rs) and np.array_equal(codes.cpu().numpy(), rc)
 
 
+@pytest.mark.parametrize("mode", ["per_token_head", "per_tensor"])
+@pytest.mark.parametrize("d,n", [(64, 333), (128, 131072 + 37), (256, 45), (512, 32768 + 37), (1024, 16384 + 37)])
+def test_quantizer_int8_bit_exact(mode, d, n):
+    # ties: rows whose amax is 127 (scale 1) hold exact halves, which round to even
+    print(f"[quant int8] {mode} d={d} n={n}", flush=True)
+    g = torch.Generator().manual_seed(d + n)
+    x = torch.randn(n, d, generator=g) * torch.rand(n, 1, generator=g) * 4
+    x[3] = 0
+    x[5, :6] = torch.tensor([127.0, 2.5, 3.5, -0.5, -1.5, 0.5])
+    x[5, 6:] = 0.25
+    x[7, :4] = torch.tensor([-0.0, 9.2e-41, -9.2e-41, 0.0])
+    for src in ("bf16", "fp32"):
+        xs = x.to(torch.bfloat16) if src == "bf16" else x
+        codes = torch.empty(n, d, dtype=torch.int8, device="cuda")
+        scale = torch.empty(n if mode == "per_token_head" else 1, dtype=torch.float32, device="cuda")
+        pa_kv_quantize_int8(xs.cuda(), src, n, d, mode, codes, scale)
+        torch.cuda.synchronize()
+        host = xs.view(torch.int16).numpy().view(np.uint16) if src == "bf16" else xs.numpy()
+        rc, rs = quantize_int8_per_row(host, src) if mode == "per_token_head" else quantize_int8_per_tensor(host, src)
+        assert np.array_equal(scale.cpu().numpy().reshape(np.shape(rs)), rs)
+        assert np.array_equal(codes.cpu().numpy(), rc)
+
+
 def test_quantizer_fp32_source_bit_exact():
     g = torch.Generator().manual_seed(5)
     x = torch.randn(100, 128, generator=g) * 3
@@ -219,10 +248,10 @@ def test_gather_bit_exact(name):
 # changes with the splits: per-tensor FP8 V requantises P to two e4m3 terms (about
 # 1e-3 here), per-token-head FP8 KV carries P as one bf16 term (relative rounding
 # <= 2^-9 per probability; 4 x 2^-9 bounds the difference of two such sums).
-SPLIT_TOL = {"c3": 2e-5, "c4": 4 * 2.0 ** -9, "c2": 3e-3, "c2_ph": 3e-3}
+SPLIT_TOL = {"c3": 2e-5, "c4": 4 * 2.0 ** -9, "c4_i8": 4 * 2.0 ** -9, "c2": 3e-3, "c2_ph": 3e-3}
 
 
-@pytest.mark.parametrize("name", ["c3", "c4", "c2", "c2_ph"])
+@pytest.mark.parametrize("name", ["c3", "c4", "c4_i8", "c2", "c2_ph"])
 def test_split_count_invariance(name):
     w = make_workload(name, **SMALL[name], out_dtype="fp32")
     di = to_device(w)
@@ -345,7 +374,7 @@ def test_head_permutation_within_group_permutes_outputs():
 
 
 @pytest.mark.parametrize("name,page", [("c2", 128), ("c2", 1024), ("c2_ph", 128), ("c3", 256), ("c4", 1024),
-                                       ("c5", 128)])
+                                       ("c4_i8", 128), ("c5", 128)])
 @pytest.mark.parametrize("layout", ["HPD", "PHD"])
 def test_large_pages(name, page, layout):
     # pages of 128..1024 tokens: several tiles (and whole splits) inside one page, and a

@@ -146,3 +146,17 @@ def test_int8_dequantisation_in_the_attention_inputs():
         ref = torch.from_numpy(codes[slots // 4, gh, slots % 4]).double().numpy() * \
             sc[slots // 4, gh, slots % 4].astype(np.float64)[:, None]
         assert np.array_equal(kv.tokens(slots, gh), ref)
+
+
+def test_oracle_inputs_use_each_workloads_own_format():
+    # the oracle's view of every named workload is quantised in that workload's format:
+    # INT8 scales are amax/127 and FP8 scales amax/448 of the same bf16 values
+    from paged_split_kv_stage1_amd.inputs import CONFIGS, make_workload
+    from tests.oracle_inputs import oracle_inputs
+    for name, cfg in CONFIGS.items():
+        w = make_workload(name, batch=1, ctx=[40], rows=1)
+        k = oracle_inputs(w)["k"]
+        assert k.dtype == cfg["kv"] and k.scale_mode == cfg["scale"], name
+        if cfg["scale"] == "per_tensor":
+            amax = np.float32(w.k.float().abs().max().item())
+            assert np.float32(k.scale) == np.float32(amax / np.float32(127.0 if cfg["kv"] == "int8" else 448.0)), name
