@@ -93,7 +93,8 @@ def measured_traffic(config: str, kernel: str = "stage1_kernel", sources=KERNEL_
             if ":" in line:
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-        if fields.get("kernel_source_sha256") == digest and "traffic_bytes_per_launch" in fields:
+        if (fields.get("workload_name") == config and fields.get("kernel_source_sha256") == digest
+                and "traffic_bytes_per_launch" in fields):
             return int(fields["traffic_bytes_per_launch"])
     return None
 
