@@ -85,7 +85,8 @@ typedef struct {
   int32_t page_size;           /* tokens per page: a power of two in [16, 1024]             */
   int32_t num_q_heads;         /* Hq                                                        */
   int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0                                        */
-  int32_t head_dim;            /* 128 or 256                                                */
+  int32_t head_dim;            /* 128 or 256; 512 with bf16 KV and at most 64 query rows x  */
+                               /*   heads per KV head (max_q_len * Hq / Hkv <= 64)          */
   pa_dtype q_dtype;            /* BF16, or FP8_E4M3 (then kv must be FP8 as well)           */
   pa_dtype kv_dtype;           /* BF16, FP8_E4M3 or INT8 (INT8: PER_TENSOR or PER_TOKEN_HEAD */
                                /*   scales, bf16 queries)                                   */
@@ -121,8 +122,8 @@ typedef struct {
  * copies plan_host to a device buffer of info->plan_bytes bytes before stage 1.
  * Errors: INVALID_ARGUMENT (non-monotone CSR, n_b > kv_len, kv_indptr inconsistent
  * with kv_len, Hq % Hkv != 0, bad enum), UNSUPPORTED (max_q_len > 8, head_dim not
- * 128/256, page size not a power of two in [16, 1024], rows x group too large for one tile, dtype
- * combination), INSUFFICIENT_WORKSPACE (plan_capacity < info->plan_bytes). */
+ * 128/256/512, page size not a power of two in [16, 1024], rows x group too large for one
+ * tile, dtype combination), INSUFFICIENT_WORKSPACE (plan_capacity < info->plan_bytes). */
 pa_status pa_plan_splits(const pa_plan_args* args, void* plan_host, size_t plan_capacity,
                          pa_plan_info* info);
 

@@ -60,7 +60,8 @@ bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
   c->pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD || c->i8;
   // head_dim 256 with one query block: 64-token tiles (two token groups of two waves)
   // keep two LDS stages; 128-token tiles of d256 would fit only one
-  if (nqb <= 1) { c->wq = c->dh == 256 ? 2 : 1; c->nqb = 1; }
+  if (c->dh == 512) { c->wq = 4; c->nqb = nqb <= 4 ? 1 : (nqb + 3) / 4; }   // one block per wave
+  else if (nqb <= 1) { c->wq = c->dh == 256 ? 2 : 1; c->nqb = 1; }
   else if (nqb == 2) { c->wq = 2; c->nqb = 1; }
   else if (nqb <= 4) { c->wq = 4; c->nqb = 1; }
   else { c->wq = 4; c->nqb = (nqb + 3) / 4; }
@@ -102,7 +103,7 @@ void choose_splits(const pa_plan_args& a, const KernelCfg& cfg, const std::vecto
   const int G = a.num_q_heads / a.num_kv_heads;
   const double kv_tok = 2.0 * a.head_dim * (a.kv_dtype != PA_DTYPE_BF16 ? 1 : 2) +
                         (a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD ? 8 : 0);
-  const int slots = kSlotsPerCu * num_cus;
+  const int slots = (cfg.dh == 512 ? 1 : kSlotsPerCu) * num_cus;   // head_dim 512: one workgroup per CU
   const double bw_slot = kHbmBytesPerS / slots;
   const int wt = 4 / cfg.wq;                     // waves sharing the tokens of a tile
   const double comp_blk = compute_s_per_token_block(a);
@@ -188,8 +189,8 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   if (a->num_q_heads < 1 || a->num_kv_heads < 1 || a->num_q_heads % a->num_kv_heads != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 a->num_q_heads, a->num_kv_heads);
-  if (a->head_dim != 128 && a->head_dim != 256)
-    return fail(PA_ERR_UNSUPPORTED, "head_dim %d: only 128 and 256 are supported", a->head_dim);
+  if (a->head_dim != 128 && a->head_dim != 256 && a->head_dim != 512)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d: only 128, 256 and 512 are supported", a->head_dim);
   const int page_shift = ilog2_exact(a->page_size);
   if (page_shift < 4 || a->page_size > 1024)
     return fail(PA_ERR_UNSUPPORTED, "page_size %d: must be a power of two in [16, 1024]", a->page_size);

@@ -26,7 +26,7 @@ inline int64_t plan_bytes_for(int64_t items, int64_t rows) { return items * 64 +
 
 // Tile configuration of a stage-1 launch (packed into pa_plan_info.variant).
 struct KernelCfg {
-  int dh;        // 128 or 256
+  int dh;        // 128, 256 or 512
   int qf8;       // q is e4m3 (fp8 MFMA for q.k)
   int kvf8;      // KV holds one-byte codes (e4m3, or int8 with i8)
   int i8;        // KV codes are int8
@@ -36,11 +36,11 @@ struct KernelCfg {
 };
 inline int32_t pack_cfg(const KernelCfg& c) {
   return (c.dh == 256 ? 1 : 0) | (c.qf8 << 1) | (c.kvf8 << 2) | (c.pt << 3) | (c.wq << 4) | (c.nqb << 8) |
-         (c.i8 << 12);
+         (c.i8 << 12) | ((c.dh == 512 ? 1 : 0) << 13);
 }
 inline KernelCfg unpack_cfg(int32_t v) {
   KernelCfg c;
-  c.dh = (v & 1) ? 256 : 128; c.qf8 = (v >> 1) & 1; c.kvf8 = (v >> 2) & 1; c.pt = (v >> 3) & 1;
+  c.dh = ((v >> 13) & 1) ? 512 : ((v & 1) ? 256 : 128); c.qf8 = (v >> 1) & 1; c.kvf8 = (v >> 2) & 1; c.pt = (v >> 3) & 1;
   c.wq = (v >> 4) & 15; c.nqb = (v >> 8) & 15; c.i8 = (v >> 12) & 1;
   return c;
 }

@@ -117,7 +117,7 @@ template <int V>
 using ic = std::integral_constant<int, V>;
 
 template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB, int NS, int PD>
-__global__ __launch_bounds__(256, 2) void stage1_kernel(Stage1Args a) {
+__global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Args a) {
   using C = S1Cfg<DH, QF8, KV, PT, WQ, NQB, NS, PD>;
   constexpr bool KVF8 = C::KVF8;
   using QT = typename QOperand<QF8>::T;
@@ -636,7 +636,9 @@ struct Pipe {
   static constexpr bool LBF = !KVF8 || KV == 2 || (PT && !QF8 && WQ == 4);   // as S1Cfg::LBF
   static constexpr bool LBFV = !KVF8 || KV == 2;                              // as S1Cfg::LBFV
   static constexpr int stage = BN * DH * ((LBF ? 2 : 1) + (LBFV ? 2 : 1)) + (PT ? 2 * BN * 4 : 0);
-  static constexpr int NS = 2 * stage <= 80 * 1024 ? 2 : 1;
+  // LDS per workgroup: 80 KB (two workgroups per CU), 160 KB for head_dim 512 (one)
+  static constexpr int LDS_CAP = (DH == 512 ? 160 : 80) * 1024;
+  static constexpr int NS = 2 * stage <= LDS_CAP ? 2 : 1;
   static constexpr int CPT = BN * DH * (KVF8 ? 1 : 2) / 16 / 256;
   // tiles in flight in registers (8 VGPRs per 16-byte chunk of K and V).  A third tile
   // measured slower on the d256 per-token-head shape (register pressure), so at most two.
@@ -648,7 +650,7 @@ static int launch_one(const Stage1Args& a, int num_items, void* stream) {
   using Pp = Pipe<DH, QF8, KV, PT, WQ, NQB>;
   using C = S1Cfg<DH, QF8, KV, PT, WQ, NQB, Pp::NS, Pp::PD>;
   static_assert(Pp::stage == C::STAGEB, "host and kernel disagree on the LDS stage size");
-  static_assert(C::LDSB <= 80 * 1024, "two workgroups per CU must fit in 160 KB of LDS");
+  static_assert(C::LDSB <= Pp::LDS_CAP, "the workgroups of a CU must fit in its 160 KB of LDS");
   hipLaunchKernelGGL((stage1_kernel<DH, QF8, KV, PT, WQ, NQB, Pp::NS, Pp::PD>), dim3(num_items), dim3(256), 0,
                      (hipStream_t)stream, a);
   return (int)hipGetLastError();
@@ -692,6 +694,9 @@ static int dispatch_modes(const KernelCfg& c, const Stage1Args& a, int n, void* 
 }
 
 bool stage1_cfg_supported(const KernelCfg& c) {
+  // head_dim 512: bf16 KV, up to four 16-row query blocks (one per wave), one workgroup
+  // per CU (its accumulators and query operand need the whole register file of a SIMD)
+  if (c.dh == 512) return !c.qf8 && !c.kvf8 && !c.pt && c.wq == 4 && c.nqb == 1;
   if (c.dh != 128 && c.dh != 256) return false;
   if (c.qf8 && !c.kvf8) return false;
   if (!c.kvf8 && c.pt) return false;
@@ -706,6 +711,8 @@ int launch_stage1(const KernelCfg& c, const Stage1Args& a, int num_items, void* 
   if (num_items <= 0) return 0;
   if (c.dh == 128) return dispatch_modes<128>(c, a, num_items, stream);
   if (c.dh == 256) return dispatch_modes<256>(c, a, num_items, stream);
+  if (c.dh == 512 && !c.qf8 && !c.kvf8 && c.wq == 4 && c.nqb == 1)
+    return launch_one<512, false, 0, false, 4, 1>(a, num_items, stream);
   return (int)hipErrorInvalidValue;
 }
 

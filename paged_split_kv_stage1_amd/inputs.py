@@ -100,11 +100,18 @@ CONFIGS = {
                   scale="per_token_head", out="bf16"),
     "c4_b1_r1": dict(batch=1, rows=1, hq=16, hkv=2, d=256, ctx=131072, page=16, q="bf16", kv="fp8",
                      scale="per_token_head", out="bf16"),
+    # head_dim 512 with one KV head (the Gemma-4 full-attention layers of FreeToken PR #900,
+    # "Gemma-4 MTP at long context": batch 1, k+1 = 4 or 8 verify rows, 128K context, bf16);
+    # the page gives no query-head count: 8 query heads, so that 8 rows fill one 64-row tile
+    "c6": dict(batch=1, rows=8, hq=8, hkv=1, d=512, ctx=131072, page=16, q="bf16", kv="bf16",
+               scale="none", out="bf16"),
+    "c6_r4": dict(batch=1, rows=4, hq=8, hkv=1, d=512, ctx=131072, page=16, q="bf16", kv="bf16",
+                  scale="none", out="bf16"),
     "c5": dict(batch=64, rows="ragged", hq=48, hkv=2, d=128, ctx="loguniform", page=32, q="bf16",
                kv="fp8", scale="per_token_head", out="bf16", windowed=True, window=64),
 }
 
-SEEDS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
+SEEDS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "c6": 6}
 
 
 def _seed_for(name: str) -> int:

@@ -270,3 +270,16 @@ def test_merge_without_splits_is_a_noop():
     info, _ = _plan(rows=[1], kv=[64], B=1)
     fake = 1 << 20
     _lib.pa_decode_merge(info, fake, None, None, fake, "bf16")      # launches nothing, returns OK
+
+
+def test_head_dim_512_plans_and_round_trips_its_variant():
+    # head_dim 512 (bf16 KV, <= 64 rows x heads per KV head) plans one item per CU slot and
+    # its tile variant names head_dim 512; more rows, or an FP8 cache, are refused
+    info, _ = _plan(B=1, rows=[8], kv=[131072], R=8, P=16, Hq=8, Hkv=1, d=512)
+    assert info.head_dim == 512 and (info.variant >> 13) & 1 and info.num_items == 256
+    for kw in (dict(Hq=16), dict(kvd="fp8", mode="per_tensor")):
+        args = dict(B=1, rows=[8], kv=[131072], R=8, P=16, Hq=8, Hkv=1, d=512)
+        args.update(kw)
+        with pytest.raises(PaError) as e:
+            _plan(**args)
+        assert e.value.status == PA_ERR_UNSUPPORTED
