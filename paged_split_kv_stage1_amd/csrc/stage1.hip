@@ -641,8 +641,9 @@ struct Pipe {
   static constexpr int NS = 2 * stage <= LDS_CAP ? 2 : 1;
   static constexpr int CPT = BN * DH * (KVF8 ? 1 : 2) / 16 / 256;
   // tiles in flight in registers (8 VGPRs per 16-byte chunk of K and V).  A third tile
-  // measured slower on the d256 per-token-head shape (register pressure), so at most two.
-  static constexpr int PD = CPT <= 4 ? 2 : 1;
+  // measured slower on the d256 per-token-head shape (register pressure), so at most two;
+  // head_dim 512 runs one wave per SIMD, whose register file holds two of its 64 KB tiles.
+  static constexpr int PD = (CPT <= 4 || DH == 512) ? 2 : 1;
 };
 
 template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB>
