@@ -122,15 +122,18 @@ def _seed_for(name: str) -> int:
 def make_workload(name: str, seed: Optional[int] = None, *, batch: Optional[int] = None,
                   ctx: Optional[int] = None, ctx_range: Optional[tuple] = None,
                   rows: Optional[object] = None, out_dtype: Optional[str] = None,
-                  page: Optional[int] = None, kv_layout_note: str = "HPD") -> Workload:
-    """Build the named workload, optionally shrunk (batch/ctx/rows overrides) or with
-    another page size (``page``).
+                  page: Optional[int] = None, kv_layout_note: str = "HPD",
+                  overrides: Optional[dict] = None) -> Workload:
+    """Build the named workload, optionally shrunk (batch/ctx/rows overrides), with
+    another page size (``page``), or with other configuration keys (``overrides``, the
+    keys of CONFIGS: hq, hkv, d, q, kv, scale, ...).
 
     ``rows`` may be an int (every request), a list (per request) or "ragged"
     (uniform 1..8).  ``ctx`` may be an int or a list; ``ctx_range`` replaces the
     log-uniform range of the ragged workload.
     """
     cfg = dict(CONFIGS[name])
+    cfg.update(overrides or {})          # e.g. other head counts, head_dim or dtypes
     seed = _seed_for(name) if seed is None else seed
     gen = torch.Generator().manual_seed(seed)
     rng = np.random.default_rng(seed)
