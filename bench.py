@@ -43,6 +43,7 @@ WORKLOAD_NAMES = {
     "c4_b1_r1": "long-context R1 B1 16/2 heads d256 ctx131072 P16 e4m3 KV per-token-head",
     "c6": "head_dim 512 verify R8 B1 8/1 heads ctx131072 P16 bf16 KV",
     "c6_r4": "head_dim 512 verify R4 B1 8/1 heads ctx131072 P16 bf16 KV",
+    "c6_f8": "head_dim 512 verify R8 B1 8/1 heads ctx131072 P16 e4m3 KV per-token-head",
     "c5": "ragged R1..8 B64 48/2 heads (group 24) d128 ctx loguniform 1K-64K, half window 64, P32 e4m3 per-token-head",
 }
 

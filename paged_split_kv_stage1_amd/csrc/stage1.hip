@@ -18,8 +18,10 @@
 //
 // Per tile, each wave owns 32 tokens x (its query blocks):
 //   QK:  bf16 MFMA 16x16x32 (bf16 Q; FP8 K upconverted exactly, once when the tile is
-//        stored if four query-block waves read it, else as it is read), or fp8 MFMA
-//        16x16x32 when Q is FP8 (exact products);
+//        stored if several query blocks per wave read it, else as it is read), or fp8
+//        MFMA 16x16x32 when Q is FP8 (exact products), or -- per-token-head FP8 K read
+//        by four one-block waves -- the 16x16x128 FP8 MFMA on the raw K codes with the
+//        bf16 query split into two e4m3 terms under a per-row scale;
 //   softmax: scores scaled into the log2 domain with the dequant scales folded in
 //        (FlashInfer PR #869 item 3), per-row causal/window masks, online max/sum,
 //        the O rescale skipped while no row maximum moves;
@@ -54,7 +56,15 @@ struct S1Cfg {
   // bytes of the transposing V reads that bound this shape.  INT8 codes have no packed
   // conversion to bf16 (two to three VALU operations per value), so both K and V are
   // converted once, when the tile is stored.
-  static constexpr bool LBF = !KVF8 || I8 || (PT && !QF8 && WQ == 4);   // K tile in bf16
+  // With four query-block waves reading every per-token-head FP8 tile (one block each),
+  // bf16 queries are carried as two e4m3 terms with a per-row scale,
+  // q ~ s_r (hi + lo / 16), so that q.k runs on the double-rate 16x16x128 FP8 MFMA
+  // straight from the e4m3 K tile: no K upconversion, and K occupies half the LDS
+  // bytes (and read instructions) of a bf16 tile.  Measured 4% faster there; with one
+  // or two query-block waves (K upconverted as it is read) and with three blocks per
+  // wave it measured 2-5% slower, so those keep bf16 MFMA on upconverted K.
+  static constexpr bool QX2 = KV == 1 && !QF8 && PT && WQ == 4 && NQB == 1;
+  static constexpr bool LBF = !KVF8 || I8 || (PT && !QF8 && WQ == 4 && !QX2);   // K tile in bf16
   static constexpr bool LBFV = !KVF8 || I8;                               // V tile in bf16
   static constexpr int LKB = LBF ? 2 : 1;           // bytes per K element in LDS
   static constexpr int LVB = LBFV ? 2 : 1;          // bytes per V element in LDS
@@ -70,7 +80,8 @@ struct S1Cfg {
   static constexpr int SCB = PT ? 2 * BN * 4 : 0;   // scale bytes per stage: k_scale[BN], v_scale[BN]
   static constexpr int STAGEB = KTB + VTB + SCB;
   static constexpr int NPMAX = BN / 16 + 1;         // pages a tile can touch (page size >= 16)
-  static constexpr int KC = DH / 32;                // K-steps of q.k
+  static constexpr int KC = DH / 32;                // K-steps of q.k (16x16x32 MFMA)
+  static constexpr int KC2 = DH / 128;              // K-steps of q.k (16x16x128 FP8 MFMA, QX2)
   static constexpr int DB = DH / 16;                // 16-wide d blocks of P.V
   static constexpr bool PV_FP8 = KVF8 && !PT;       // per-tensor FP8 V: fp8 MFMA for P.V
   static constexpr int EPIB = (WT > 1) ? (4 * NQB * DB * 256 * 4 + 4 * NQB * 64 * 2 * 4) : 0;
@@ -313,6 +324,17 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
       if constexpr (C::LBF) kro[tb][kc] = t * (C::LCPR * 16) + (((4 * kc + g) ^ swz_k<C::LCPR>(t)) << 4);
       else kro[tb][kc] = t * (C::LCPR * 16) + (((2 * kc + (g >> 1)) ^ swz_k<C::LCPR>(t)) << 4) + 8 * (g & 1);
     }
+  // QX2: lane group g reads the two 16-byte chunks 8*ks + 2g, +1 of tokens tk0, tk0 + 16.
+  uint32_t kro2[2][C::KC2][2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int ks = 0; ks < C::KC2; ++ks)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = tk0 + 16 * tb;
+        kro2[tb][ks][h] = t * (C::LCPR * 16) + (((8 * ks + 2 * g + h) ^ swz_k<C::LCPR>(t)) << 4);
+      }
   // V rows read transposed: bf16 -> two 4-token reads (tokens 4g+j and 16+4g+j);
   // fp8 -> one 8-token read (tokens {4g..4g+3, 16+4g..16+4g+3}).
   auto vaddr = [&](int db, int half) __attribute__((always_inline)) -> uint32_t {
@@ -357,8 +379,28 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
       if (!qvalid[i]) continue;
       // ---- S^T = K Q^T for 2 x 16 tokens ----------------------------------------------
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (C::QX2) {
 #pragma unroll
-      for (int kc = 0; kc < C::KC; ++kc) {
+        for (int ks = 0; ks < C::KC2; ++ks) {
+          auto kld = [&](int tb) __attribute__((always_inline)) -> i32x8 {
+            const i32x4 c0 = *reinterpret_cast<const i32x4*>(Kl + kro2[tb][ks][0]);
+            const i32x4 c1 = *reinterpret_cast<const i32x4*>(Kl + kro2[tb][ks][1]);
+            return __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+          };
+          auto qld = [&](int u) __attribute__((always_inline)) -> i32x4 {
+            return __builtin_bit_cast(i32x4, qget(i, 4 * ks + u));
+          };
+          const i32x8 qh = __builtin_shufflevector(qld(0), qld(1), 0, 1, 2, 3, 4, 5, 6, 7);
+          const i32x8 ql = __builtin_shufflevector(qld(2), qld(3), 0, 1, 2, 3, 4, 5, 6, 7);
+          const i32x8 k0 = kld(0), k1 = kld(1);
+          s0 = mfma_fp8_k128<127>(k0, qh, s0);
+          s1 = mfma_fp8_k128<127>(k1, qh, s1);
+          s0 = mfma_fp8_k128<123>(k0, ql, s0);     // lo term carries x16: scale 2^-4
+          s1 = mfma_fp8_k128<123>(k1, ql, s1);
+        }
+      }
+#pragma unroll
+      for (int kc = 0; kc < (C::QX2 ? 0 : C::KC); ++kc) {
         if constexpr (C::LBF) {
           const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Kl + kro[0][kc]);
           const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Kl + kro[1][kc]);
@@ -508,6 +550,7 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
     const int64_t qrow = ((int64_t)(it.row0 + r) * Hq + (int64_t)it.kvh * G + hl) * DH;
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
+      if constexpr (C::QX2) break;
       QT v;
       if constexpr (QF8)
         v = *reinterpret_cast<const long*>(static_cast<const uint8_t*>(a.q) + qrow + kc * 32 + 8 * g);
@@ -515,6 +558,51 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
         v = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + qrow + kc * 32 + 8 * g);
       if (i < C::QREG) qop[i][kc] = v;
       else *reinterpret_cast<QT*>(qlds + ((i - C::QREG) * C::KC + kc) * 1024) = v;   // read back by this lane only
+    }
+    if constexpr (C::QX2) {
+      // Lane group g holds d = 128*ks + 32*g .. +31 of its row for every K-step ks.  The
+      // row is scaled so that its largest magnitude maps to 448, rounded to e4m3 (hi),
+      // and the residual, x16, rounded again (lo): q = s_r (hi + lo/16) to ~2^-8
+      // relative, and s_r joins the row's score scale.  16-byte unit 4*ks + 2*term + half
+      // of the operand store holds 16 codes of term (0 hi, 1 lo).
+      const __bf16* qp = static_cast<const __bf16*>(a.q) + qrow;
+      bf16x8 raw[C::KC2][4];
+      float amax = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KC2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          raw[ks][j] = *reinterpret_cast<const bf16x8*>(qp + 128 * ks + 32 * g + 8 * j);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)raw[ks][j][e]));
+        }
+      amax = wave_max_xor_16_32(amax);
+      const float inv = amax > 0.f ? 448.f / amax : 1.f;
+      xsb[i] *= amax > 0.f ? amax * (1.f / 448.f) : 1.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KC2; ++ks) {
+        u32x4 hi[2], lo[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (float)raw[ks][j][4 * w + e] * inv;
+            const uint32_t h = f32x4_to_fp8x4(x[0], x[1], x[2], x[3]);
+            const f32x2 d0 = fp8x2_to_f32x2<false>(h), d1 = fp8x2_to_f32x2<true>(h);
+            hi[j >> 1][2 * (j & 1) + w] = h;
+            lo[j >> 1][2 * (j & 1) + w] = f32x4_to_fp8x4((x[0] - d0[0]) * 16.f, (x[1] - d0[1]) * 16.f,
+                                                         (x[2] - d1[0]) * 16.f, (x[3] - d1[1]) * 16.f);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const QT v = __builtin_bit_cast(QT, u < 2 ? hi[u] : lo[u - 2]);
+          if (i < C::QREG) qop[i][4 * ks + u] = v;
+          else *reinterpret_cast<QT*>(qlds + ((i - C::QREG) * C::KC + 4 * ks + u) * 1024) = v;
+        }
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);          // vmcnt(0) lgkmcnt(0)
@@ -633,7 +721,8 @@ template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB>
 struct Pipe {
   static constexpr bool KVF8 = KV != 0;
   static constexpr int BN = 32 * (4 / WQ);
-  static constexpr bool LBF = !KVF8 || KV == 2 || (PT && !QF8 && WQ == 4);   // as S1Cfg::LBF
+  static constexpr bool QX2 = KV == 1 && !QF8 && PT && WQ == 4 && NQB == 1;   // as S1Cfg::QX2
+  static constexpr bool LBF = !KVF8 || KV == 2 || (PT && !QF8 && WQ == 4 && !QX2);   // as S1Cfg::LBF
   static constexpr bool LBFV = !KVF8 || KV == 2;                              // as S1Cfg::LBFV
   static constexpr int stage = BN * DH * ((LBF ? 2 : 1) + (LBFV ? 2 : 1)) + (PT ? 2 * BN * 4 : 0);
   // LDS per workgroup: 80 KB (two workgroups per CU), 160 KB for head_dim 512 (one)
@@ -695,9 +784,11 @@ static int dispatch_modes(const KernelCfg& c, const Stage1Args& a, int n, void* 
 }
 
 bool stage1_cfg_supported(const KernelCfg& c) {
-  // head_dim 512: bf16 KV, up to four 16-row query blocks (one per wave), one workgroup
-  // per CU (its accumulators and query operand need the whole register file of a SIMD)
-  if (c.dh == 512) return !c.qf8 && !c.kvf8 && !c.pt && c.wq == 4 && c.nqb == 1;
+  // head_dim 512: bf16 KV, or per-token-head FP8 KV with bf16 queries; up to four 16-row
+  // query blocks (one per wave), one workgroup per CU (its accumulators and query
+  // operand need the whole register file of a SIMD)
+  if (c.dh == 512)
+    return !c.qf8 && !c.i8 && (c.kvf8 ? c.pt : !c.pt) && c.wq == 4 && c.nqb == 1;
   if (c.dh != 128 && c.dh != 256) return false;
   if (c.qf8 && !c.kvf8) return false;
   if (!c.kvf8 && c.pt) return false;
@@ -712,8 +803,10 @@ int launch_stage1(const KernelCfg& c, const Stage1Args& a, int num_items, void* 
   if (num_items <= 0) return 0;
   if (c.dh == 128) return dispatch_modes<128>(c, a, num_items, stream);
   if (c.dh == 256) return dispatch_modes<256>(c, a, num_items, stream);
-  if (c.dh == 512 && !c.qf8 && !c.kvf8 && c.wq == 4 && c.nqb == 1)
-    return launch_one<512, false, 0, false, 4, 1>(a, num_items, stream);
+  if (c.dh == 512 && stage1_cfg_supported(c)) {
+    if (!c.kvf8) return launch_one<512, false, 0, false, 4, 1>(a, num_items, stream);
+    return launch_one<512, false, 1, true, 4, 1>(a, num_items, stream);
+  }
   return (int)hipErrorInvalidValue;
 }
 

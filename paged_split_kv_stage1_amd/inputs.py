@@ -107,6 +107,10 @@ CONFIGS = {
                scale="none", out="bf16"),
     "c6_r4": dict(batch=1, rows=4, hq=8, hkv=1, d=512, ctx=131072, page=16, q="bf16", kv="bf16",
                   scale="none", out="bf16"),
+    # the same shape with an FP8 cache ("quantized head_dim 512" in the same PR's launch
+    # notes): per-token-head e4m3 K/V, bf16 queries
+    "c6_f8": dict(batch=1, rows=8, hq=8, hkv=1, d=512, ctx=131072, page=16, q="bf16", kv="fp8",
+                  scale="per_token_head", out="bf16"),
     "c5": dict(batch=64, rows="ragged", hq=48, hkv=2, d=128, ctx="loguniform", page=32, q="bf16",
                kv="fp8", scale="per_token_head", out="bf16", windowed=True, window=64),
 }

@@ -273,11 +273,14 @@ def test_merge_without_splits_is_a_noop():
 
 
 def test_head_dim_512_plans_and_round_trips_its_variant():
-    # head_dim 512 (bf16 KV, <= 64 rows x heads per KV head) plans one item per CU slot and
-    # its tile variant names head_dim 512; more rows, or an FP8 cache, are refused
-    info, _ = _plan(B=1, rows=[8], kv=[131072], R=8, P=16, Hq=8, Hkv=1, d=512)
-    assert info.head_dim == 512 and (info.variant >> 13) & 1 and info.num_items == 256
-    for kw in (dict(Hq=16), dict(kvd="fp8", mode="per_tensor")):
+    # head_dim 512 (bf16 KV or per-token-head FP8 KV, <= 64 rows x heads per KV head) plans
+    # one item per CU slot and its tile variant names head_dim 512; more rows, a per-tensor
+    # FP8 cache, INT8 or FP8 queries are refused
+    for kw in (dict(), dict(kvd="fp8", mode="per_token_head")):
+        info, _ = _plan(B=1, rows=[8], kv=[131072], R=8, P=16, Hq=8, Hkv=1, d=512, **kw)
+        assert info.head_dim == 512 and (info.variant >> 13) & 1 and info.num_items == 256
+    for kw in (dict(Hq=16), dict(kvd="fp8", mode="per_tensor"), dict(kvd="int8", mode="per_token_head"),
+               dict(kvd="fp8", mode="per_token_head", q="fp8")):
         args = dict(B=1, rows=[8], kv=[131072], R=8, P=16, Hq=8, Hkv=1, d=512)
         args.update(kw)
         with pytest.raises(PaError) as e:

@@ -30,8 +30,8 @@ SHAPES = {16: (8, 2), 32: (8, 4), 64: (8, 8), 128: (16, 8), 192: (24, 8)}   # ro
 
 def _supported(d, mode, m):
     q, kv, scale = MODES[mode]
-    if d == 512:                                                  # bf16 KV, one block per wave
-        return kv == "bf16" and m <= 64
+    if d == 512:                  # bf16 or per-token-head FP8 KV, bf16 queries, one block per wave
+        return (kv == "bf16" or (kv == "fp8" and scale == "per_token_head" and q == "bf16")) and m <= 64
     per_tensor_v = kv == "fp8" and scale != "per_token_head"    # fp8 P.V keeps a second accumulator
     if d == 128:
         return m <= (128 if per_tensor_v else 192)

@@ -28,7 +28,7 @@ def _samples(w, rng, n=6):
     return picks
 
 
-@pytest.mark.parametrize("name", ["c2", "c2_ph", "c3", "c3_b1", "c4", "c4_b1", "c4_i8", "c5", "c6"])
+@pytest.mark.parametrize("name", ["c2", "c2_ph", "c3", "c3_b1", "c4", "c4_b1", "c4_i8", "c5", "c6", "c6_f8"])
 def test_full_size_sampled_outputs(name):
     print(f"[full-size] {name}", flush=True)
     w = make_workload(name)

@@ -37,6 +37,7 @@ SMALL = {
     "c5": dict(batch=10, ctx_range=(60, 2500)),
     "c6": dict(batch=2, ctx=[3001, 129]),
     "c6_r4": dict(batch=3, ctx=[2100, 700, 4]),
+    "c6_f8": dict(batch=2, ctx=[3001, 129]),
 }
 
 
@@ -68,7 +69,7 @@ def test_parity_fp32_out(name):
         assert np.max(np.abs(got - ref_lse[rows])) <= 1e-3 * max(1.0, np.max(np.abs(ref_lse)))
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c2_ph", "c3", "c4", "c4_i8", "c5", "c6"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c2_ph", "c3", "c4", "c4_i8", "c5", "c6", "c6_f8"])
 def test_parity_bf16_out(name):
     print(f"[parity-bf16] {name}", flush=True)
     w = make_workload(name, **SMALL[name], out_dtype="bf16")
@@ -250,10 +251,11 @@ def test_gather_bit_exact(name):
 # changes with the splits: per-tensor FP8 V requantises P to two e4m3 terms (about
 # 1e-3 here), per-token-head FP8 KV carries P as one bf16 term (relative rounding
 # <= 2^-9 per probability; 4 x 2^-9 bounds the difference of two such sums).
-SPLIT_TOL = {"c3": 2e-5, "c4": 4 * 2.0 ** -9, "c4_i8": 4 * 2.0 ** -9, "c2": 3e-3, "c2_ph": 3e-3, "c6": 2e-5}
+SPLIT_TOL = {"c3": 2e-5, "c4": 4 * 2.0 ** -9, "c4_i8": 4 * 2.0 ** -9, "c2": 3e-3, "c2_ph": 3e-3, "c6": 2e-5,
+             "c6_f8": 4 * 2.0 ** -9}
 
 
-@pytest.mark.parametrize("name", ["c3", "c4", "c4_i8", "c2", "c2_ph", "c6"])
+@pytest.mark.parametrize("name", ["c3", "c4", "c4_i8", "c2", "c2_ph", "c6", "c6_f8"])
 def test_split_count_invariance(name):
     w = make_workload(name, **SMALL[name], out_dtype="fp32")
     di = to_device(w)
