@@ -85,9 +85,9 @@ typedef struct {
   int32_t page_size;           /* tokens per page: a power of two in [16, 1024]             */
   int32_t num_q_heads;         /* Hq                                                        */
   int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0                                        */
-  int32_t head_dim;            /* 128 or 256; 512 with bf16 queries, bf16 or PER_TOKEN_HEAD */
-                               /*   FP8 KV and at most 64 query rows x heads per KV head    */
-                               /*   (max_q_len * Hq / Hkv <= 64)                            */
+  int32_t head_dim;            /* 128 or 256; 512 with bf16 queries and bf16 or            */
+                               /*   PER_TOKEN_HEAD FP8 KV (a request's rows x heads per KV  */
+                               /*   head run in work items of at most 64)                   */
   pa_dtype q_dtype;            /* BF16, or FP8_E4M3 (then kv must be FP8 as well)           */
   pa_dtype kv_dtype;           /* BF16, FP8_E4M3 or INT8 (INT8: PER_TENSOR or PER_TOKEN_HEAD */
                                /*   scales, bf16 queries)                                   */

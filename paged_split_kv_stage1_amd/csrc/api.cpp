@@ -60,12 +60,26 @@ bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
   c->pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD || c->i8;
   // head_dim 256 with one query block: 64-token tiles (two token groups of two waves)
   // keep two LDS stages; 128-token tiles of d256 would fit only one
-  if (c->dh == 512) { c->wq = 4; c->nqb = nqb <= 4 ? 1 : (nqb + 3) / 4; }   // one block per wave
+  // head_dim 512 runs one 16-row block per wave; a request with more than four blocks
+  // per KV head is cut into groups of four, one work item per (group, KV split).  (For
+  // head_dim 128 and 256 the waves take several blocks each instead: groups measured
+  // slower on the ragged group-24 workload, 124 -> 132 us, since every group re-reads
+  // the split's K and V.)
+  if (c->dh == 512) { c->wq = 4; c->nqb = 1; }
   else if (nqb <= 1) { c->wq = c->dh == 256 ? 2 : 1; c->nqb = 1; }
   else if (nqb == 2) { c->wq = 2; c->nqb = 1; }
   else if (nqb <= 4) { c->wq = 4; c->nqb = 1; }
   else { c->wq = 4; c->nqb = (nqb + 3) / 4; }
   return stage1_cfg_supported(*c);
+}
+
+// Query-block groups of request b: its rows x heads in 16-row blocks, cut into runs of
+// the blocks one workgroup covers (waves x blocks per wave).
+int query_groups(const pa_plan_args& a, const KernelCfg& cfg, int b) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int nb16 = ((a.qo_indptr[b + 1] - a.qo_indptr[b]) * G + 15) / 16;
+  const int per = cfg.wq * cfg.nqb;
+  return (nb16 + per - 1) / per;
 }
 
 // ---- split-count cost model --------------------------------------------------------
@@ -107,10 +121,13 @@ void choose_splits(const pa_plan_args& a, const KernelCfg& cfg, const std::vecto
   const double bw_slot = kHbmBytesPerS / slots;
   const int wt = 4 / cfg.wq;                     // waves sharing the tokens of a tile
   const double comp_blk = compute_s_per_token_block(a);
-  std::vector<double> comp_tok(B);               // compute seconds per token, per request
+  std::vector<double> comp_tok(B);               // compute seconds per token, per item of request b
+  std::vector<int> ngrp(B);                      // query-block groups (items per split and KV head)
   for (int b = 0; b < B; ++b) {
     const int nb16 = ((a.qo_indptr[b + 1] - a.qo_indptr[b]) * G + 15) / 16;
-    const int rounds = (nb16 + cfg.wq - 1) / cfg.wq;
+    ngrp[b] = query_groups(a, cfg, b);
+    const int per_item = std::min(nb16, cfg.wq * cfg.nqb);
+    const int rounds = (per_item + cfg.wq - 1) / cfg.wq;
     comp_tok[b] = comp_blk * rounds / wt;
   }
   int max_blk = 1;
@@ -143,10 +160,11 @@ void choose_splits(const pa_plan_args& a, const KernelCfg& cfg, const std::vecto
       const int n = a.qo_indptr[b + 1] - a.qo_indptr[b];
       const double part = sb > 1 ? (double)n * G * (a.head_dim + 1) * 4.0 : 0.0;
       const double tok = (double)span[b] / sb;
-      const double cost = std::max(tok * kv_tok / bw_slot, tok * comp_tok[b]) + part / bw_slot + kItemOverheadS;
-      groups.push_back({cost, sb * a.num_kv_heads});
+      const double cost =
+          std::max(tok * kv_tok / bw_slot, tok * comp_tok[b]) + part / ngrp[b] / bw_slot + kItemOverheadS;
+      groups.push_back({cost, sb * a.num_kv_heads * ngrp[b]});
       merge_bytes += part * sb * a.num_kv_heads;
-      total += cost * sb * a.num_kv_heads;
+      total += cost * sb * a.num_kv_heads * ngrp[b];
       longest = std::max(longest, cost);
     }
     const double merge_t = merge_bytes > 0 ? merge_bytes / kMergeBytesPerS + kMergeLaunchS : 0.0;
@@ -272,7 +290,7 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   int64_t n_items = 0;
   for (int b = 0; b < B; ++b) {
     s_max = std::max(s_max, nsp[b]);
-    n_items += (int64_t)nsp[b] * Hkv;
+    n_items += (int64_t)nsp[b] * Hkv * query_groups(*a, cfg, b);
   }
   if (n_items > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "too many work items (%lld)", (long long)n_items);
   const int64_t th_count = (int64_t)T * a->num_q_heads;
@@ -308,33 +326,40 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
     const int n = a->qo_indptr[b + 1] - a->qo_indptr[b];
     const int L = a->kv_len[b];
     const int nblk = (span[b] + kSplitAlign - 1) / kSplitAlign;
+    const int ng = query_groups(*a, cfg, b);
     for (int g = 0; g < Hkv; ++g) {
       for (int s = 0; s < nsp[b]; ++s) {
-        PaItem it;
-        memset(&it, 0, sizeof it);
-        it.row0 = a->qo_indptr[b];
-        it.nrows = n;
-        it.kv_len = L;
-        it.page_base = a->kv_indptr[b];
-        it.window = a->window ? a->window[b] : 0;
-        it.kvh = g;
-        it.split = s;
-        it.nsplit = nsp[b];
-        const int64_t blk0 = (int64_t)s * nblk / nsp[b];
-        const int64_t blk1 = (int64_t)(s + 1) * nblk / nsp[b];
-        it.tok_begin = (int)std::min<int64_t>(begin[b] + blk0 * kSplitAlign, L);
-        it.tok_end = (int)std::min<int64_t>(begin[b] + blk1 * kSplitAlign, L);
-        it.req = b;
-        items.push_back(it);
+        for (int qg = 0; qg < ng; ++qg) {
+          PaItem it;
+          memset(&it, 0, sizeof it);
+          it.row0 = a->qo_indptr[b];
+          it.nrows = n;
+          it.kv_len = L;
+          it.page_base = a->kv_indptr[b];
+          it.window = a->window ? a->window[b] : 0;
+          it.kvh = g;
+          it.split = s;
+          it.nsplit = nsp[b];
+          const int64_t blk0 = (int64_t)s * nblk / nsp[b];
+          const int64_t blk1 = (int64_t)(s + 1) * nblk / nsp[b];
+          it.tok_begin = (int)std::min<int64_t>(begin[b] + blk0 * kSplitAlign, L);
+          it.tok_end = (int)std::min<int64_t>(begin[b] + blk1 * kSplitAlign, L);
+          it.req = b;
+          it.qblk0 = qg * cfg.wq * cfg.nqb;
+          items.push_back(it);
+        }
       }
     }
   }
   const int G = a->num_q_heads / Hkv;
-  std::stable_sort(items.begin(), items.end(), [G](const PaItem& x, const PaItem& y) {
-    const int64_t cx = (int64_t)(x.tok_end - x.tok_begin) * (64 + x.nrows * G);
-    const int64_t cy = (int64_t)(y.tok_end - y.tok_begin) * (64 + y.nrows * G);
-    return cx > cy;
-  });
+  const int rows_per_item = 16 * cfg.wq * cfg.nqb;
+  // heaviest first: tokens x (a fixed cost + the item's own rows x heads)
+  auto weight = [G, rows_per_item](const PaItem& x) {
+    const int m = std::min(x.nrows * G - 16 * x.qblk0, rows_per_item);
+    return (int64_t)(x.tok_end - x.tok_begin) * (64 + m);
+  };
+  std::stable_sort(items.begin(), items.end(),
+                   [&weight](const PaItem& x, const PaItem& y) { return weight(x) > weight(y); });
   uint8_t* out = static_cast<uint8_t*>(plan_host);
   memcpy(out, items.data(), items.size() * sizeof(PaItem));
   int32_t* row_ns = reinterpret_cast<int32_t*>(out + items.size() * sizeof(PaItem));

@@ -6,7 +6,7 @@ namespace pa {
 
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const PaItem it = a.items[blockIdx.x];
-  if (it.kvh != 0) return;
+  if (it.kvh != 0 || it.qblk0 != 0) return;     // one item per token range
   const int64_t base = a.kv_tok_offset[it.req];
   const int P = 1 << a.page_shift;
   for (int j = it.tok_begin + (int)threadIdx.x; j < it.tok_end; j += 256) {

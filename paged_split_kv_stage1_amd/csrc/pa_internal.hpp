@@ -17,7 +17,8 @@ struct PaItem {
   int32_t tok_begin;  // token range [tok_begin, tok_end) of this split
   int32_t tok_end;
   int32_t req;        // request index
-  int32_t pad[5];
+  int32_t qblk0;      // first 16-row query block (of the request's rows x heads) this item runs
+  int32_t pad[4];
 };
 static_assert(sizeof(PaItem) == 64, "PaItem must be 64 bytes");
 

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
   const int hstep = a.scale_per_head; // 1: scales indexed by head, 0: one scale
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
-    const int qb = wq + WQ * i;
+    const int qb = it.qblk0 + wq + WQ * i;
     qvalid[i] = 16 * qb < Mq;
     const int m = 16 * qb + L16;
     const int mr = m < Mq ? m : Mq - 1;
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
   // outstanding tile loads before its first MFMA.
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
-    const int m = 16 * (wq + WQ * i) + L16;
+    const int m = 16 * (it.qblk0 + wq + WQ * i) + L16;
     const int mr = m < Mq ? m : Mq - 1;                // rows past Mq repeat the last real row
     const int r = mr / G;
     const int hl = mr - r * G;
@@ -681,7 +681,7 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
     if (!qvalid[i]) continue;
-    const int m = 16 * (wq + WQ * i) + L16;
+    const int m = 16 * (it.qblk0 + wq + WQ * i) + L16;
     if (m >= Mq) continue;
     const int r = m / G;
     const int hl = m - r * G;
@@ -730,8 +730,9 @@ struct Pipe {
   static constexpr int NS = 2 * stage <= LDS_CAP ? 2 : 1;
   static constexpr int CPT = BN * DH * (KVF8 ? 1 : 2) / 16 / 256;
   // tiles in flight in registers (8 VGPRs per 16-byte chunk of K and V).  A third tile
-  // measured slower on the d256 per-token-head shape (register pressure), so at most two;
-  // head_dim 512 runs one wave per SIMD, whose register file holds two of its 64 KB tiles.
+  // measured slower on the d256 per-token-head shape (register pressure; also without
+  // spills once K stays FP8), so at most two; head_dim 512 runs one wave per SIMD, whose
+  // register file holds two of its 64 KB tiles (four FP8 tiles measured slower too).
   static constexpr int PD = (CPT <= 4 || DH == 512) ? 2 : 1;
 };
 

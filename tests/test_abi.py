@@ -41,7 +41,9 @@ def _items(info, plan):
     return plan[: n * 64].view(np.int32).reshape(n, 16), plan[n * 64:].view(np.int32)
 
 
-def _check_cover(info, plan, rows, kv, window, Hkv):
+def _check_cover(info, plan, rows, kv, window, Hkv, G=8, d=128):
+    # every (request, KV head, query-block group) has splits 0..S-1 covering the visible
+    # range once; the groups (runs of four 16-row blocks) cover the request's rows x heads
     it, row_ns = _items(info, plan)
     qo = np.concatenate([[0], np.cumsum(rows)])
     for b in range(len(kv)):
@@ -51,15 +53,19 @@ def _check_cover(info, plan, rows, kv, window, Hkv):
         sel_b = it[it[:, 10] == b]
         assert np.all(sel_b[:, 7] == sel_b[0, 7])                  # same nsplit for the request
         assert np.all(row_ns[qo[b]:qo[b + 1]] == sel_b[0, 7])
+        nb16 = -(-n * G // 16)
+        per = 4 if (d == 512 and nb16 > 4) else max(nb16, 1)       # blocks one item covers
+        assert sorted(set(sel_b[:, 11].tolist())) == list(range(0, nb16, per))
         for g in range(Hkv):
-            sel = sel_b[sel_b[:, 5] == g]
-            sel = sel[np.argsort(sel[:, 6])]
-            assert sel[:, 6].tolist() == list(range(len(sel)))
-            assert sel[0, 8] <= lo and sel[0, 8] % 64 == 0
-            assert np.all(sel[:-1, 9] == sel[1:, 8])                 # contiguous, no overlap
-            assert sel[-1, 9] == L
-            assert np.all(sel[:, 9] >= sel[:, 8])
-            assert np.all(sel[:, 0] == qo[b]) and np.all(sel[:, 1] == n) and np.all(sel[:, 2] == L)
+            for q0 in range(0, nb16, per):
+                sel = sel_b[(sel_b[:, 5] == g) & (sel_b[:, 11] == q0)]
+                sel = sel[np.argsort(sel[:, 6])]
+                assert sel[:, 6].tolist() == list(range(len(sel)))
+                assert sel[0, 8] <= lo and sel[0, 8] % 64 == 0
+                assert np.all(sel[:-1, 9] == sel[1:, 8])             # contiguous, no overlap
+                assert sel[-1, 9] == L
+                assert np.all(sel[:, 9] >= sel[:, 8])
+                assert np.all(sel[:, 0] == qo[b]) and np.all(sel[:, 1] == n) and np.all(sel[:, 2] == L)
 
 
 def test_plan_covers_visible_tokens_exactly_once():
@@ -85,12 +91,16 @@ def test_plan_properties(data):
     cus = data.draw(st.sampled_from([1, 8, 256, 304]))
     cap = data.draw(st.sampled_from([0, 1, 3, 64]))
     Hkv = data.draw(st.sampled_from([1, 2, 8]))
-    info, plan = _plan(B=B, rows=rows, kv=kv, window=win, cus=cus, max_splits=cap, Hq=Hkv * 8, Hkv=Hkv, d=128)
-    _check_cover(info, plan, rows, kv, win, Hkv)
+    G = data.draw(st.sampled_from([1, 8, 24]))
+    d = data.draw(st.sampled_from([128, 512])) if G * 8 <= 192 else 128
+    info, plan = _plan(B=B, rows=rows, kv=kv, window=win, cus=cus, max_splits=cap, Hq=Hkv * G, Hkv=Hkv, d=d)
+    _check_cover(info, plan, rows, kv, win, Hkv, G, d)
     if cap:
         assert info.max_splits <= cap
     it, _ = _items(info, plan)
-    cost = (it[:, 9] - it[:, 8]).astype(np.int64) * (64 + it[:, 1] * 8)
+    wq_nqb = 4 if d == 512 else {1: 1, 8: 4, 24: 12}[G]                # blocks one item covers
+    m = np.minimum(it[:, 1] * G - 16 * it[:, 11], 16 * wq_nqb)          # rows x heads of the item
+    cost = (it[:, 9] - it[:, 8]).astype(np.int64) * (64 + m)
     assert np.all(cost[:-1] >= cost[1:])                               # heaviest first
 
 
@@ -120,7 +130,6 @@ def test_single_split_plan_needs_no_merge():
     (dict(kvd="fp8"), PA_ERR_INVALID_ARGUMENT),
     (dict(P=24), PA_ERR_UNSUPPORTED),
     (dict(P=8), PA_ERR_UNSUPPORTED),
-    (dict(Hq=128, Hkv=1), PA_ERR_UNSUPPORTED),              # 8 rows x group 128 exceeds one tile
     (dict(force=5, max_splits=4), PA_ERR_INVALID_ARGUMENT),
 ])
 def test_plan_errors(kw, status):
@@ -273,16 +282,32 @@ def test_merge_without_splits_is_a_noop():
 
 
 def test_head_dim_512_plans_and_round_trips_its_variant():
-    # head_dim 512 (bf16 KV or per-token-head FP8 KV, <= 64 rows x heads per KV head) plans
-    # one item per CU slot and its tile variant names head_dim 512; more rows, a per-tensor
-    # FP8 cache, INT8 or FP8 queries are refused
+    # head_dim 512 (bf16 KV or per-token-head FP8 KV) plans one item per CU slot and query
+    # block group, each wave one 16-row block, and its tile variant names head_dim 512; a
+    # per-tensor FP8 cache, INT8 or FP8 queries are refused
     for kw in (dict(), dict(kvd="fp8", mode="per_token_head")):
         info, _ = _plan(B=1, rows=[8], kv=[131072], R=8, P=16, Hq=8, Hkv=1, d=512, **kw)
         assert info.head_dim == 512 and (info.variant >> 13) & 1 and info.num_items == 256
-    for kw in (dict(Hq=16), dict(kvd="fp8", mode="per_tensor"), dict(kvd="int8", mode="per_token_head"),
+    info, plan = _plan(B=1, rows=[8], kv=[131072], R=8, P=16, Hq=16, Hkv=1, d=512)   # 128 rows x heads
+    it, _ = _items(info, plan)
+    assert sorted(set(it[:, 11].tolist())) == [0, 4] and info.num_items % 2 == 0
+    for kw in (dict(kvd="fp8", mode="per_tensor"), dict(kvd="int8", mode="per_token_head"),
                dict(kvd="fp8", mode="per_token_head", q="fp8")):
         args = dict(B=1, rows=[8], kv=[131072], R=8, P=16, Hq=8, Hkv=1, d=512)
         args.update(kw)
         with pytest.raises(PaError) as e:
             _plan(**args)
         assert e.value.status == PA_ERR_UNSUPPORTED
+
+
+def test_query_block_groups_cover_rows_x_heads():
+    # head_dim 512 with more than four 16-row blocks per KV head (8 rows x group 24 = 12
+    # blocks; group 128 = 64 blocks): one item per run of four blocks and split
+    for Hq, Hkv, ngrp in ((48, 2, 3), (128, 1, 16)):
+        rows, kv = np.array([8, 3, 1]), np.array([5000, 900, 64])
+        info, plan = _plan(B=3, rows=rows, kv=kv, Hq=Hq, Hkv=Hkv, d=512)
+        G = Hq // Hkv
+        _check_cover(info, plan, rows, kv, None, Hkv, G, 512)
+        assert ((info.variant >> 4) & 15, (info.variant >> 8) & 15) == (4, 1)
+        it, _ = _items(info, plan)
+        assert it[it[:, 10] == 0][:, 11].max() == 4 * (ngrp - 1)
