@@ -10,25 +10,40 @@
 //   WPU = 1 (few splits): every wave merges a unit of its own, with its splits in
 //     flight together, so that short merges do not pay one workgroup each.
 // The partials were written just before by stage 1 and mostly come back from L2/MALL,
-// so the loop is bound by load latency: the point of both shapes is loads in flight.
+// so the loop is bound by load latency: the point of both shapes is loads in flight,
+// and of the single pass (online maximum) that no load waits for another.
 // Rows whose request has a single split were written by stage 1 directly and are
 // skipped.
 #include "common.hpp"
 
 namespace pa {
 
-// Largest LSE over the row-head's ns splits; every lane of the wave gets it.
-__device__ __forceinline__ float lse_max(const float* lse, int ns, int lane) {
-  float mx = -INFINITY;
-  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, lse[s]);
+// Weighted sums over splits s0, s0 + STEP, ... < ns of one lane's d element, in one
+// pass: each batch's LSE and partial loads are issued together, and the running maximum
+// m rescales the sums when a batch raises it (no separate pass for the maximum, whose
+// loads would have to come back before the first partial is requested).
+template <int B>
+__device__ __forceinline__ void merge_batch(const float (&l)[B], const float (&o)[B], float& m, float& num,
+                                            float& den) {
+  float bm = l[0];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  return mx;
+  for (int u = 1; u < B; ++u) bm = fmaxf(bm, l[u]);
+  if (bm > m) {                                   // (false while every LSE so far is -inf)
+    const float f = __expf(m - bm);               // 0 when m is still -inf
+    num *= f;
+    den *= f;
+    m = bm;
+  }
+#pragma unroll
+  for (int u = 0; u < B; ++u) {
+    const float wgt = (l[u] == -INFINITY) ? 0.f : __expf(l[u] - m);
+    den += wgt;
+    num += wgt * o[u];
+  }
 }
 
-// Weighted sums over splits s0, s0 + STEP, ... < ns of one lane's d element.
 template <int STEP>
-__device__ __forceinline__ void accumulate(const float* lse, const float* po, int dh, int s0, int ns, float muse,
+__device__ __forceinline__ void accumulate(const float* lse, const float* po, int dh, int s0, int ns, float& m,
                                            float& num, float& den) {
   int s = s0;
   for (; s + 15 * STEP < ns; s += 16 * STEP) {
@@ -38,12 +53,7 @@ __device__ __forceinline__ void accumulate(const float* lse, const float* po, in
       l[u] = lse[s + STEP * u];
       o[u] = po[(int64_t)(s + STEP * u) * dh];
     }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const float wgt = (l[u] == -INFINITY) ? 0.f : __expf(l[u] - muse);
-      den += wgt;
-      num += wgt * o[u];
-    }
+    merge_batch(l, o, m, num, den);
   }
   for (; s + 3 * STEP < ns; s += 4 * STEP) {
     float l[4], o[4];
@@ -52,29 +62,22 @@ __device__ __forceinline__ void accumulate(const float* lse, const float* po, in
       l[u] = lse[s + STEP * u];
       o[u] = po[(int64_t)(s + STEP * u) * dh];
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wgt = (l[u] == -INFINITY) ? 0.f : __expf(l[u] - muse);
-      den += wgt;
-      num += wgt * o[u];
-    }
+    merge_batch(l, o, m, num, den);
   }
   for (; s < ns; s += STEP) {
-    const float l = lse[s];
-    const float wgt = (l == -INFINITY) ? 0.f : __expf(l - muse);
-    den += wgt;
-    num += wgt * po[(int64_t)s * dh];
+    float l[1] = {lse[s]}, o[1] = {po[(int64_t)s * dh]};
+    merge_batch(l, o, m, num, den);
   }
 }
 
-__device__ __forceinline__ void store_merged(const MergeArgs& a, int th, int d, float num, float den, float muse,
+__device__ __forceinline__ void store_merged(const MergeArgs& a, int th, int d, float num, float den, float m,
                                              bool write_lse) {
   const float o = den > 0.f ? num / den : 0.f;
   if (a.out_bf16)
     static_cast<__bf16*>(a.out)[(int64_t)th * a.dh + d] = (__bf16)o;
   else
     static_cast<float*>(a.out)[(int64_t)th * a.dh + d] = o;
-  if (a.out_lse && write_lse) a.out_lse[th] = den > 0.f ? muse + __logf(den) : -INFINITY;
+  if (a.out_lse && write_lse) a.out_lse[th] = den > 0.f ? m + __logf(den) : -INFINITY;
 }
 
 template <int WPU>
@@ -92,23 +95,31 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int d = slice * 64 + lane;
   const float* lse = a.partial_lse + (int64_t)th * a.s_max;
   const float* po = a.partial_o + (int64_t)th * a.s_max * a.dh + d;
-  const float mx = lse_max(lse, ns, lane);
-  const float muse = (mx == -INFINITY) ? 0.f : mx;
-  float num = 0.f, den = 0.f;
+  float m = -INFINITY, num = 0.f, den = 0.f;
   if constexpr (WPU == 1) {
-    accumulate<1>(lse, po, a.dh, 0, ns, muse, num, den);
-    store_merged(a, th, d, num, den, muse, slice == 0 && lane == 0);
+    accumulate<1>(lse, po, a.dh, 0, ns, m, num, den);
+    store_merged(a, th, d, num, den, m, slice == 0 && lane == 0);
   } else {
     __shared__ float num_s[4][64];
-    __shared__ float den_s[4];
-    accumulate<4>(lse, po, a.dh, wave, ns, muse, num, den);
+    __shared__ float den_s[4], m_s[4];
+    accumulate<4>(lse, po, a.dh, wave, ns, m, num, den);
     num_s[wave][lane] = num;
-    if (lane == 0) den_s[wave] = den;
+    if (lane == 0) {
+      den_s[wave] = den;
+      m_s[wave] = m;
+    }
     __syncthreads();
     if (wave != 0) return;
-    num = (num_s[0][lane] + num_s[1][lane]) + (num_s[2][lane] + num_s[3][lane]);
-    den = (den_s[0] + den_s[1]) + (den_s[2] + den_s[3]);
-    store_merged(a, th, d, num, den, muse, slice == 0 && lane == 0);
+    const float mall = fmaxf(fmaxf(m_s[0], m_s[1]), fmaxf(m_s[2], m_s[3]));
+    num = 0.f;
+    den = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = m_s[w] == -INFINITY ? 0.f : __expf(m_s[w] - mall);
+      num += num_s[w][lane] * f;
+      den += den_s[w] * f;
+    }
+    store_merged(a, th, d, num, den, mall, slice == 0 && lane == 0);
   }
 }
 
