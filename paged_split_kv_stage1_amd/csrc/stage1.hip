@@ -64,7 +64,11 @@ struct S1Cfg {
   // or two query-block waves (K upconverted as it is read) and with three blocks per
   // wave it measured 2-5% slower, so those keep bf16 MFMA on upconverted K.
   static constexpr bool QX2 = KV == 1 && !QF8 && PT && WQ == 4 && NQB == 1;
-  static constexpr bool LBF = !KVF8 || I8 || (PT && !QF8 && WQ == 4 && !QX2);   // K tile in bf16
+  // The INT8 counterpart: two int8 query terms (q ~ s_r (hi + lo / 254), s_r =
+  // amax_row / 127) on the 16x16x64 integer MFMA against the raw K codes, exact int32
+  // sums, K kept in INT8 in LDS.
+  static constexpr bool QI2 = I8 && !QF8 && PT && WQ == 4 && NQB == 1;
+  static constexpr bool LBF = !KVF8 || (I8 && !QI2) || (PT && !QF8 && WQ == 4 && !QX2 && !I8);   // K tile in bf16
   static constexpr bool LBFV = !KVF8 || I8;                               // V tile in bf16
   static constexpr int LKB = LBF ? 2 : 1;           // bytes per K element in LDS
   static constexpr int LVB = LBFV ? 2 : 1;          // bytes per V element in LDS
@@ -82,6 +86,7 @@ struct S1Cfg {
   static constexpr int NPMAX = BN / 16 + 1;         // pages a tile can touch (page size >= 16)
   static constexpr int KC = DH / 32;                // K-steps of q.k (16x16x32 MFMA)
   static constexpr int KC2 = DH / 128;              // K-steps of q.k (16x16x128 FP8 MFMA, QX2)
+  static constexpr int KC4 = DH / 64;               // K-steps of q.k (16x16x64 INT8 MFMA, QI2)
   static constexpr int DB = DH / 16;                // 16-wide d blocks of P.V
   static constexpr bool PV_FP8 = KVF8 && !PT;       // per-tensor FP8 V: fp8 MFMA for P.V
   static constexpr int EPIB = (WT > 1) ? (4 * NQB * DB * 256 * 4 + 4 * NQB * 64 * 2 * 4) : 0;
@@ -335,6 +340,15 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
         const int t = tk0 + 16 * tb;
         kro2[tb][ks][h] = t * (C::LCPR * 16) + (((8 * ks + 2 * g + h) ^ swz_k<C::LCPR>(t)) << 4);
       }
+  // QI2: lane group g reads 16-byte chunk 4*ks + g of tokens tk0, tk0 + 16.
+  uint32_t kro4[2][C::KC4];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int ks = 0; ks < C::KC4; ++ks) {
+      const int t = tk0 + 16 * tb;
+      kro4[tb][ks] = t * (C::LCPR * 16) + (((4 * ks + g) ^ swz_k<C::LCPR>(t)) << 4);
+    }
   // V rows read transposed: bf16 -> two 4-token reads (tokens 4g+j and 16+4g+j);
   // fp8 -> one 8-token read (tokens {4g..4g+3, 16+4g..16+4g+3}).
   auto vaddr = [&](int db, int half) __attribute__((always_inline)) -> uint32_t {
@@ -399,8 +413,27 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
           s1 = mfma_fp8_k128<123>(k1, ql, s1);
         }
       }
+      if constexpr (C::QI2) {
+        i32x4 h0 = {0, 0, 0, 0}, l0 = {0, 0, 0, 0}, h1 = {0, 0, 0, 0}, l1 = {0, 0, 0, 0};
 #pragma unroll
-      for (int kc = 0; kc < (C::QX2 ? 0 : C::KC); ++kc) {
+        for (int ks = 0; ks < C::KC4; ++ks) {
+          const i32x4 k0 = *reinterpret_cast<const i32x4*>(Kl + kro4[0][ks]);
+          const i32x4 k1 = *reinterpret_cast<const i32x4*>(Kl + kro4[1][ks]);
+          const i32x4 qh = __builtin_bit_cast(i32x4, qget(i, 2 * ks));
+          const i32x4 ql = __builtin_bit_cast(i32x4, qget(i, 2 * ks + 1));
+          h0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(k0, qh, h0, 0, 0, 0);
+          h1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, qh, h1, 0, 0, 0);
+          l0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(k0, ql, l0, 0, 0, 0);
+          l1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, ql, l1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {        // exact int32 sums (|sum| < 2^24) -> fp32
+          s0[k] = fmaf((float)l0[k], 1.f / 254.f, (float)h0[k]);
+          s1[k] = fmaf((float)l1[k], 1.f / 254.f, (float)h1[k]);
+        }
+      }
+#pragma unroll
+      for (int kc = 0; kc < ((C::QX2 || C::QI2) ? 0 : C::KC); ++kc) {
         if constexpr (C::LBF) {
           const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Kl + kro[0][kc]);
           const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Kl + kro[1][kc]);
@@ -550,7 +583,7 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
     const int64_t qrow = ((int64_t)(it.row0 + r) * Hq + (int64_t)it.kvh * G + hl) * DH;
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
-      if constexpr (C::QX2) break;
+      if constexpr (C::QX2 || C::QI2) break;
       QT v;
       if constexpr (QF8)
         v = *reinterpret_cast<const long*>(static_cast<const uint8_t*>(a.q) + qrow + kc * 32 + 8 * g);
@@ -558,6 +591,50 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
         v = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + qrow + kc * 32 + 8 * g);
       if (i < C::QREG) qop[i][kc] = v;
       else *reinterpret_cast<QT*>(qlds + ((i - C::QREG) * C::KC + kc) * 1024) = v;   // read back by this lane only
+    }
+    if constexpr (C::QI2) {
+      // Lane group g holds d = 64*ks + 16*g .. +15 of its row for every K-step ks.  The
+      // row is scaled so that its largest magnitude maps to 127 and rounded to integers
+      // (hi); the residual in [-1/2, 1/2], x254, is rounded again (lo): q = s_r (hi +
+      // lo/254) to ~2^-16 of amax.  16-byte unit 2*ks + term holds 16 codes of term.
+      const __bf16* qp = static_cast<const __bf16*>(a.q) + qrow;
+      bf16x8 raw[C::KC4][2];
+      float amax = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KC4; ++ks)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          raw[ks][j] = *reinterpret_cast<const bf16x8*>(qp + 64 * ks + 16 * g + 8 * j);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)raw[ks][j][e]));
+        }
+      amax = wave_max_xor_16_32(amax);
+      const float inv = amax > 0.f ? 127.f / amax : 1.f;
+      xsb[i] *= amax > 0.f ? amax * (1.f / 127.f) : 1.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KC4; ++ks) {
+        u32x4 hi, lo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t h = 0, l = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = fminf(fmaxf((float)raw[ks][w >> 1][4 * (w & 1) + e] * inv, -127.f), 127.f);
+            const float xh = __builtin_rintf(x);
+            const float xl = fminf(fmaxf(__builtin_rintf((x - xh) * 254.f), -127.f), 127.f);
+            h |= ((uint32_t)(int)xh & 0xFFu) << (8 * e);
+            l |= ((uint32_t)(int)xl & 0xFFu) << (8 * e);
+          }
+          hi[w] = h;
+          lo[w] = l;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const QT v = __builtin_bit_cast(QT, u == 0 ? hi : lo);
+          if (i < C::QREG) qop[i][2 * ks + u] = v;
+          else *reinterpret_cast<QT*>(qlds + ((i - C::QREG) * C::KC + 2 * ks + u) * 1024) = v;
+        }
+      }
     }
     if constexpr (C::QX2) {
       // Lane group g holds d = 128*ks + 32*g .. +31 of its row for every K-step ks.  The
@@ -722,7 +799,8 @@ struct Pipe {
   static constexpr bool KVF8 = KV != 0;
   static constexpr int BN = 32 * (4 / WQ);
   static constexpr bool QX2 = KV == 1 && !QF8 && PT && WQ == 4 && NQB == 1;   // as S1Cfg::QX2
-  static constexpr bool LBF = !KVF8 || KV == 2 || (PT && !QF8 && WQ == 4 && !QX2);   // as S1Cfg::LBF
+  static constexpr bool QI2 = KV == 2 && !QF8 && PT && WQ == 4 && NQB == 1;   // as S1Cfg::QI2
+  static constexpr bool LBF = !KVF8 || (KV == 2 && !QI2) || (PT && !QF8 && WQ == 4 && !QX2 && KV != 2);
   static constexpr bool LBFV = !KVF8 || KV == 2;                              // as S1Cfg::LBFV
   static constexpr int stage = BN * DH * ((LBF ? 2 : 1) + (LBFV ? 2 : 1)) + (PT ? 2 * BN * 4 : 0);
   // LDS per workgroup: 80 KB (two workgroups per CU), 160 KB for head_dim 512 (one)
