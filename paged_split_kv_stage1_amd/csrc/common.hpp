@@ -16,8 +16,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((vector_size(8)));
 typedef int i32x2 __attribute__((vector_size(8)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define PA_LDS __attribute__((address_space(3)))
 
@@ -38,14 +36,6 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 mfma_fp8(long a, long b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
-}
-
-// 16x16x128 with e4m3 A and B (32 bytes per lane): A lane l holds row l%16 and
-// B lane l column l%16, both over the same 32 K positions of lane group l/16; C as
-// above.  scale_b is an E8M0 exponent (127 = x1) applied to B.
-template <int SCALE_B>
-__device__ __forceinline__ f32x4 mfma_fp8_k128(i32x8 a, i32x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, SCALE_B);
 }
 
 // ---- conversions ------------------------------------------------------------------

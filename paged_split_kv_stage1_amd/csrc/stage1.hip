@@ -39,6 +39,17 @@
 
 namespace pa {
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 16x16x128 with e4m3 A and B (32 bytes per lane): A lane l holds row l%16 and B lane l
+// column l%16, both over the same 32 K positions of lane group l/16; C as for 16x16x32.
+// SCALE_B is an E8M0 exponent (127 = x1) applied to B.
+template <int SCALE_B>
+__device__ __forceinline__ f32x4 mfma_fp8_k128(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, SCALE_B);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
