@@ -422,3 +422,26 @@ def test_graph_capture_replay():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy().astype(np.float64), o_eager)
+
+
+@pytest.mark.parametrize("name", ["c4", "c4_i8", "c6_f8"])
+def test_query_rows_with_outliers_tiny_tails_and_zeros(name):
+    # The four-wave kernels of these shapes carry each bf16 query row as two 8-bit terms
+    # under the row's own scale (amax/448 for e4m3, amax/127 for int8).  Rows dominated by
+    # one element, rows with a tail of elements a thousand times smaller, and all-zero rows
+    # (scale 1, every code 0: uniform weights) must still meet the bar.
+    print(f"[query-outliers] {name}", flush=True)
+    w = make_workload(name, **SMALL[name], out_dtype="fp32")
+    q = w.q.float()
+    q[:, :, 7] *= 40.0
+    q[-1, :, 100:] *= 1e-3
+    q[0] = 0.0
+    q[1, 3] = 0.0
+    w.q = q.to(torch.bfloat16)
+    di = to_device(w)
+    o, pd, _ = run_decode(w, di)
+    ref, _ = _oracle(w)
+    err = max_rel_err(o, ref)
+    print(f"  items={pd.num_items} maxrel={err:.3e}", flush=True)
+    assert not np.isnan(o).any()
+    assert err <= _bar(w), err
