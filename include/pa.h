@@ -144,7 +144,14 @@ pa_status pa_plan_splits(const pa_plan_args* args, void* plan_host, size_t plan_
  *   partial_o    device float32 [T, Hq, S_max, d] (unused if !info->needs_merge)
  *   partial_lse  device float32 [T, Hq, S_max]
  *   out          device [T, Hq, d] in out_dtype (BF16 or FP32)
- * Tokens past kv_len (the tail of the last page) are never read. */
+ * Tokens past kv_len (the tail of the last page) are never read.
+ * Accuracy (softmax(s q.k) v over the same quantised K/V): bf16 KV keeps P in two bf16
+ * terms (~2^-16 relative); per-tensor FP8 V carries P as two e4m3 terms; per-token-head
+ * FP8 and INT8 V carry P as one bf16 term with v_scale folded in.  With FP8 or INT8 K
+ * and four one-block waves per work item, bf16 queries are carried as two 8-bit terms
+ * under a per-row scale (~2^-8 relative for e4m3, ~2^-16 of the row's largest element
+ * for int8).  Measured against an fp64 evaluation: <= 2e-3 (bf16 KV) and <= 2e-2
+ * (FP8 / INT8 KV) max relative error per (row, head). */
 pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev,
                            const void* q, const float* q_scale,
                            const void* k_cache, const void* v_cache, const pa_kv_layout* kv,
