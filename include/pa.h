@@ -110,7 +110,7 @@ typedef struct {
   int32_t variant;             /* kernel tile configuration (library internal)              */
   int32_t reserved0;
   int64_t plan_bytes;          /* bytes of the plan buffer (host copy and device copy)       */
-  int64_t partial_o_bytes;     /* float32 [T, Hq, S_max, d]                                 */
+  int64_t partial_o_bytes;     /* [T, Hq, S_max, d]: float32 (bf16 KV) or bf16 (FP8/INT8 KV) */
   int64_t partial_lse_bytes;   /* float32 [T, Hq, S_max]                                    */
   int64_t reserved[4];
 } pa_plan_info;
@@ -141,7 +141,8 @@ pa_status pa_plan_splits(const pa_plan_args* args, void* plan_host, size_t plan_
  *                per-token-head array with strides sc (PER_TOKEN_HEAD); NULL for bf16 KV
  *   page_indices device int32, indexed through kv_indptr
  *   sm_scale     softmax scale applied to q.k (typically 1/sqrt(d) in float32)
- *   partial_o    device float32 [T, Hq, S_max, d] (unused if !info->needs_merge)
+ *   partial_o    device [T, Hq, S_max, d], info->partial_o_bytes: float32 for bf16 KV,
+ *                bf16 for FP8 / INT8 KV (unused if !info->needs_merge)
  *   partial_lse  device float32 [T, Hq, S_max]
  *   out          device [T, Hq, d] in out_dtype (BF16 or FP32)
  * Tokens past kv_len (the tail of the last page) are never read.
@@ -157,7 +158,7 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev,
                            const void* k_cache, const void* v_cache, const pa_kv_layout* kv,
                            const float* k_scale, const float* v_scale, const pa_scale_layout* sc,
                            const int32_t* page_indices, float sm_scale,
-                           float* partial_o, float* partial_lse,
+                           void* partial_o, float* partial_lse,
                            void* out, pa_dtype out_dtype, void* stream);
 
 /* Stage 2 (device): per (row, query head) with more than one split,
@@ -166,7 +167,7 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev,
  * natural-log LSE of those rows.  A no-op launch-free success when
  * info->needs_merge == 0. */
 pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev,
-                          const float* partial_o, const float* partial_lse,
+                          const void* partial_o, const float* partial_lse,
                           void* out, pa_dtype out_dtype, float* out_lse, void* stream);
 
 /* FP8 quantiser (device): src holds n_rows rows of head_dim contiguous values

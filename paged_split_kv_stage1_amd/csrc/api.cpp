@@ -46,6 +46,11 @@ int ilog2_exact(int v) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Partial outputs of split requests: float32, except with one-byte KV codes (FP8, INT8),
+// whose bar (2e-2) leaves room for bf16 partials (2^-9 relative) and half the bytes
+// written by stage 1 and read back by the merge.
+int partial_o_elem_bytes(int kv_dtype) { return kv_dtype == PA_DTYPE_BF16 ? 4 : 2; }
+
 // Tile configuration for the planned shape.
 bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -312,7 +317,7 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   info->num_cus = num_cus;
   info->variant = pack_cfg(cfg);
   info->plan_bytes = plan_bytes_for(n_items, T);
-  info->partial_o_bytes = s_max > 1 ? th_count * s_max * a->head_dim * 4 : 0;
+  info->partial_o_bytes = s_max > 1 ? th_count * s_max * a->head_dim * partial_o_elem_bytes(a->kv_dtype) : 0;
   info->partial_lse_bytes = s_max > 1 ? th_count * s_max * 4 : 0;
   if (!plan_host) return ok();
   if ((int64_t)plan_capacity < info->plan_bytes)
@@ -371,7 +376,7 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
 pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const void* q, const float* q_scale,
                            const void* k_cache, const void* v_cache, const pa_kv_layout* kv, const float* k_scale,
                            const float* v_scale, const pa_scale_layout* sc, const int32_t* page_indices,
-                           float sm_scale, float* partial_o, float* partial_lse, void* out, pa_dtype out_dtype,
+                           float sm_scale, void* partial_o, float* partial_lse, void* out, pa_dtype out_dtype,
                            void* stream) {
   if (!info || !plan_dev || !q || !k_cache || !v_cache || !kv || !page_indices || !out)
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_stage1: a required pointer is NULL");
@@ -418,6 +423,7 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const
   s.sm_scale = sm_scale;
   s.partial_o = partial_o;
   s.partial_lse = partial_lse;
+  s.part_bf16 = partial_o_elem_bytes(info->kv_dtype) == 2;
   s.out = out;
   s.out_bf16 = out_dtype == PA_DTYPE_BF16;
   s.hq = info->num_q_heads;
@@ -429,7 +435,7 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const
   return ok();
 }
 
-pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev, const float* partial_o,
+pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev, const void* partial_o,
                           const float* partial_lse, void* out, pa_dtype out_dtype, float* out_lse, void* stream) {
   if (!info || !plan_dev || !out) return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_merge: a required pointer is NULL");
   if (out_dtype != PA_DTYPE_BF16 && out_dtype != PA_DTYPE_FP32)
@@ -441,6 +447,7 @@ pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev, const 
                                                   (int64_t)info->num_items * sizeof(PaItem));
   m.partial_o = partial_o;
   m.partial_lse = partial_lse;
+  m.part_bf16 = partial_o_elem_bytes(info->kv_dtype) == 2;
   m.out = out;
   m.out_bf16 = out_dtype == PA_DTYPE_BF16;
   m.out_lse = out_lse;

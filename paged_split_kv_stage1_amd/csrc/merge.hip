@@ -42,8 +42,8 @@ __device__ __forceinline__ void merge_batch(const float (&l)[B], const float (&o
   }
 }
 
-template <int STEP>
-__device__ __forceinline__ void accumulate(const float* lse, const float* po, int dh, int s0, int ns, float& m,
+template <int STEP, typename T>
+__device__ __forceinline__ void accumulate(const float* lse, const T* po, int dh, int s0, int ns, float& m,
                                            float& num, float& den) {
   int s = s0;
   for (; s + 15 * STEP < ns; s += 16 * STEP) {
@@ -51,7 +51,7 @@ __device__ __forceinline__ void accumulate(const float* lse, const float* po, in
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       l[u] = lse[s + STEP * u];
-      o[u] = po[(int64_t)(s + STEP * u) * dh];
+      o[u] = (float)po[(int64_t)(s + STEP * u) * dh];
     }
     merge_batch(l, o, m, num, den);
   }
@@ -60,12 +60,12 @@ __device__ __forceinline__ void accumulate(const float* lse, const float* po, in
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       l[u] = lse[s + STEP * u];
-      o[u] = po[(int64_t)(s + STEP * u) * dh];
+      o[u] = (float)po[(int64_t)(s + STEP * u) * dh];
     }
     merge_batch(l, o, m, num, den);
   }
   for (; s < ns; s += STEP) {
-    float l[1] = {lse[s]}, o[1] = {po[(int64_t)s * dh]};
+    float l[1] = {lse[s]}, o[1] = {(float)po[(int64_t)s * dh]};
     merge_batch(l, o, m, num, den);
   }
 }
@@ -80,7 +80,7 @@ __device__ __forceinline__ void store_merged(const MergeArgs& a, int th, int d, 
   if (a.out_lse && write_lse) a.out_lse[th] = den > 0.f ? m + __logf(den) : -INFINITY;
 }
 
-template <int WPU>
+template <int WPU, typename T>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (ns <= 1) return;
   const int d = slice * 64 + lane;
   const float* lse = a.partial_lse + (int64_t)th * a.s_max;
-  const float* po = a.partial_o + (int64_t)th * a.s_max * a.dh + d;
+  const T* po = static_cast<const T*>(a.partial_o) + (int64_t)th * a.s_max * a.dh + d;
   float m = -INFINITY, num = 0.f, den = 0.f;
   if constexpr (WPU == 1) {
     accumulate<1>(lse, po, a.dh, 0, ns, m, num, den);
@@ -126,10 +126,13 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 int launch_merge(const MergeArgs& a, void* stream) {
   if (a.total_rows <= 0) return 0;
   const int64_t units = (int64_t)a.total_rows * a.hq * (a.dh / 64);
+  const dim3 g4((unsigned)units), g1((unsigned)((units + 3) / 4));
   if (a.s_max >= 64) {
-    hipLaunchKernelGGL(merge_kernel<4>, dim3((unsigned)units), dim3(256), 0, (hipStream_t)stream, a);
+    if (a.part_bf16) hipLaunchKernelGGL((merge_kernel<4, __bf16>), g4, dim3(256), 0, (hipStream_t)stream, a);
+    else hipLaunchKernelGGL((merge_kernel<4, float>), g4, dim3(256), 0, (hipStream_t)stream, a);
   } else {
-    hipLaunchKernelGGL(merge_kernel<1>, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, (hipStream_t)stream, a);
+    if (a.part_bf16) hipLaunchKernelGGL((merge_kernel<1, __bf16>), g1, dim3(256), 0, (hipStream_t)stream, a);
+    else hipLaunchKernelGGL((merge_kernel<1, float>), g1, dim3(256), 0, (hipStream_t)stream, a);
   }
   return (int)hipGetLastError();
 }

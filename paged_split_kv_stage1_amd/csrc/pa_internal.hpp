@@ -59,16 +59,18 @@ struct Stage1Args {
   int scale_per_head;                   // 1: k/v_scale[Hkv] and, for FP8 Q, q_scale[Hq]; 0: scalars
   const int32_t* page_indices;
   float sm_scale;
-  float* partial_o; float* partial_lse;
+  void* partial_o; float* partial_lse;  // partial O: float32, or bf16 when part_bf16
   void* out; int out_bf16;
   int hq, group, page_shift, s_max;
+  int part_bf16;
 };
 
 struct MergeArgs {
   const int32_t* row_nsplit;
-  const float* partial_o; const float* partial_lse;
+  const void* partial_o; const float* partial_lse;   // partial O: float32, or bf16 when part_bf16
   void* out; int out_bf16; float* out_lse;
   int total_rows, hq, dh, s_max;
+  int part_bf16;
 };
 
 struct GatherArgs {

@@ -792,8 +792,20 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = o[i][db] * sc;
       }
+    } else if (a.part_bf16) {
+      __bf16* dst = static_cast<__bf16*>(a.partial_o) + (th * a.s_max + it.split) * DH;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = (__bf16)(o[i][db][k] * sc);
+        *reinterpret_cast<bf16x4*>(dst + 16 * db + 4 * g) = v;
+      }
+      if (g == 0)
+        a.partial_lse[th * a.s_max + it.split] = empty ? -INFINITY : (mrun[i] + __log2f(ltot[i]) - kPoff) * kLn2;
     } else {
-      float* dst = a.partial_o + (th * a.s_max + it.split) * DH;
+      float* dst = static_cast<float*>(a.partial_o) + (th * a.s_max + it.split) * DH;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = o[i][db] * sc;
       if (g == 0)

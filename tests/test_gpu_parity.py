@@ -250,9 +250,11 @@ def test_gather_bit_exact(name):
 # is rounded relative to each split's running maximum the rounding of P itself
 # changes with the splits: per-tensor FP8 V requantises P to two e4m3 terms (about
 # 1e-3 here), per-token-head FP8 KV carries P as one bf16 term (relative rounding
-# <= 2^-9 per probability; 4 x 2^-9 bounds the difference of two such sums).
-SPLIT_TOL = {"c3": 2e-5, "c4": 4 * 2.0 ** -9, "c4_i8": 4 * 2.0 ** -9, "c2": 3e-3, "c2_ph": 3e-3, "c6": 2e-5,
-             "c6_f8": 4 * 2.0 ** -9}
+# <= 2^-9 per probability; 4 x 2^-9 bounds the difference of two such sums).  With
+# one-byte KV codes the split partials are stored in bf16 (2^-9 relative each, so the
+# merged row moves by at most 2^-9 more).
+SPLIT_TOL = {"c3": 2e-5, "c4": 5 * 2.0 ** -9, "c4_i8": 5 * 2.0 ** -9, "c2": 3e-3 + 2.0 ** -9,
+             "c2_ph": 3e-3 + 2.0 ** -9, "c6": 2e-5, "c6_f8": 5 * 2.0 ** -9}
 
 
 @pytest.mark.parametrize("name", ["c3", "c4", "c4_i8", "c2", "c2_ph", "c6", "c6_f8"])
@@ -350,17 +352,19 @@ def test_window_edges(window):
     assert max_rel_err(o, ref) <= BAR["fp8"]
 
 
+@pytest.mark.parametrize("name", ["c3", "c4"])
 @pytest.mark.parametrize("fs", [64, 81])
-def test_many_splits_workgroup_merge(fs):
+def test_many_splits_workgroup_merge(fs, name):
     # 64 or more splits take the merge shape in which four waves share one
-    # (row, head, d slice); fewer take the one-wave-per-slice shape
-    print(f"[many-splits] {fs}", flush=True)
-    w = make_workload("c3", batch=2, ctx=[5300, 4100], out_dtype="fp32")
+    # (row, head, d slice); fewer take the one-wave-per-slice shape.  bf16 KV merges
+    # float32 partials, FP8 KV bf16 partials.
+    print(f"[many-splits] {name} {fs}", flush=True)
+    w = make_workload(name, batch=2, ctx=[5300, 4100], out_dtype="fp32")
     di = to_device(w)
     o, pd, lse = run_decode(w, di, force_splits=fs, out_lse=True)
     assert pd.max_splits >= 64
     ref, ref_lse = _oracle(w)
-    assert max_rel_err(o, ref) <= BAR["bf16"]
+    assert max_rel_err(o, ref) <= _bar(w)
     assert np.max(np.abs(lse - ref_lse)) <= 1e-3 * max(1.0, np.max(np.abs(ref_lse)))
 
 
