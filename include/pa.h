@@ -165,7 +165,7 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev,
  * out = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M}, M = max_s lse_s, written
  * in out_dtype; out_lse (device float32 [T, Hq], nullable) receives the merged
  * natural-log LSE of those rows.  A no-op launch-free success when
- * info->needs_merge == 0. */
+ * info->needs_merge == 0.  out and partial_o must be 16-byte aligned (as for stage 1). */
 pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev,
                           const void* partial_o, const float* partial_lse,
                           void* out, pa_dtype out_dtype, float* out_lse, void* stream);

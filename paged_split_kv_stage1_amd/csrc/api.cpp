@@ -445,6 +445,8 @@ pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev, const 
     return fail(PA_ERR_INVALID_ARGUMENT, "out_dtype must be BF16 or FP32");
   if (!info->needs_merge) return ok();
   if (!partial_o || !partial_lse) return fail(PA_ERR_INVALID_ARGUMENT, "partial_o and partial_lse are required");
+  if (!aligned16(out) || !aligned16(partial_o))
+    return fail(PA_ERR_INVALID_ARGUMENT, "out and partial_o must be 16-byte aligned");
   MergeArgs m;
   m.row_nsplit = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(plan_dev) +
                                                   (int64_t)info->num_items * sizeof(PaItem));

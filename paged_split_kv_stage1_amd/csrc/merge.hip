@@ -14,6 +14,8 @@
 // and of the single pass (online maximum) that no load waits for another.
 // Rows whose request has a single split were written by stage 1 directly and are
 // skipped.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace pa {
@@ -42,8 +44,8 @@ __device__ __forceinline__ void merge_batch(const float (&l)[B], const float (&o
   }
 }
 
-template <int STEP, typename T>
-__device__ __forceinline__ void accumulate(const float* lse, const T* po, int dh, int s0, int ns, float& m,
+template <int STEP>
+__device__ __forceinline__ void accumulate(const float* lse, const float* po, int dh, int s0, int ns, float& m,
                                            float& num, float& den) {
   int s = s0;
   for (; s + 15 * STEP < ns; s += 16 * STEP) {
@@ -51,7 +53,7 @@ __device__ __forceinline__ void accumulate(const float* lse, const T* po, int dh
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       l[u] = lse[s + STEP * u];
-      o[u] = (float)po[(int64_t)(s + STEP * u) * dh];
+      o[u] = po[(int64_t)(s + STEP * u) * dh];
     }
     merge_batch(l, o, m, num, den);
   }
@@ -60,14 +62,97 @@ __device__ __forceinline__ void accumulate(const float* lse, const T* po, int dh
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       l[u] = lse[s + STEP * u];
-      o[u] = (float)po[(int64_t)(s + STEP * u) * dh];
+      o[u] = po[(int64_t)(s + STEP * u) * dh];
     }
     merge_batch(l, o, m, num, den);
   }
   for (; s < ns; s += STEP) {
-    float l[1] = {lse[s]}, o[1] = {(float)po[(int64_t)s * dh]};
+    float l[1] = {lse[s]}, o[1] = {po[(int64_t)s * dh]};
     merge_batch(l, o, m, num, den);
   }
+}
+
+// The same for bf16 partials, two adjacent d elements per lane (4-byte loads).
+template <int B>
+__device__ __forceinline__ void merge_batch2(const float (&l)[B], const f32x2 (&o)[B], float& m, f32x2& num,
+                                             float& den) {
+  float bm = l[0];
+#pragma unroll
+  for (int u = 1; u < B; ++u) bm = fmaxf(bm, l[u]);
+  if (bm > m) {
+    const float f = __expf(m - bm);
+    num *= f;
+    den *= f;
+    m = bm;
+  }
+#pragma unroll
+  for (int u = 0; u < B; ++u) {
+    const float wgt = (l[u] == -INFINITY) ? 0.f : __expf(l[u] - m);
+    den += wgt;
+    num += wgt * o[u];
+  }
+}
+
+__device__ __forceinline__ f32x2 load_bf16x2(const __bf16* p) {
+  const bf16x2 v = *reinterpret_cast<const bf16x2*>(p);
+  return f32x2{(float)v[0], (float)v[1]};
+}
+
+template <int STEP>
+__device__ __forceinline__ void accumulate2(const float* lse, const __bf16* po, int dh, int s0, int ns, float& m,
+                                            f32x2& num, float& den) {
+  int s = s0;
+  for (; s + 15 * STEP < ns; s += 16 * STEP) {
+    float l[16];
+    f32x2 o[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      l[u] = lse[s + STEP * u];
+      o[u] = load_bf16x2(po + (int64_t)(s + STEP * u) * dh);
+    }
+    merge_batch2(l, o, m, num, den);
+  }
+  for (; s + 3 * STEP < ns; s += 4 * STEP) {
+    float l[4];
+    f32x2 o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      l[u] = lse[s + STEP * u];
+      o[u] = load_bf16x2(po + (int64_t)(s + STEP * u) * dh);
+    }
+    merge_batch2(l, o, m, num, den);
+  }
+  for (; s < ns; s += STEP) {
+    float l[1] = {lse[s]};
+    f32x2 o[1] = {load_bf16x2(po + (int64_t)s * dh)};
+    merge_batch2(l, o, m, num, den);
+  }
+}
+
+// Lanes l and l ^ 32 hold the same two d elements over interleaved splits: combine them
+// (every lane of the pair gets the result).
+__device__ __forceinline__ void combine_halves(float& m, f32x2& num, float& den) {
+  auto sw = [](float x) __attribute__((always_inline)) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+  };
+  const f32x2 mm = sw(m), dd = sw(den), n0 = sw(num[0]), n1 = sw(num[1]);
+  const float mx = fmaxf(mm[0], mm[1]);
+  const float f0 = mm[0] == -INFINITY ? 0.f : __expf(mm[0] - mx);
+  const float f1 = mm[1] == -INFINITY ? 0.f : __expf(mm[1] - mx);
+  m = mx;
+  den = dd[0] * f0 + dd[1] * f1;
+  num = f32x2{n0[0] * f0 + n0[1] * f1, n1[0] * f0 + n1[1] * f1};
+}
+
+__device__ __forceinline__ void store_merged2(const MergeArgs& a, int th, int d, f32x2 num, float den, float m,
+                                              bool write_lse) {
+  const f32x2 o = den > 0.f ? num * (1.f / den) : f32x2{0.f, 0.f};
+  if (a.out_bf16)
+    *reinterpret_cast<bf16x2*>(static_cast<__bf16*>(a.out) + (int64_t)th * a.dh + d) = bf16x2{(__bf16)o[0], (__bf16)o[1]};
+  else
+    *reinterpret_cast<f32x2*>(static_cast<float*>(a.out) + (int64_t)th * a.dh + d) = o;
+  if (a.out_lse && write_lse) a.out_lse[th] = den > 0.f ? m + __logf(den) : -INFINITY;
 }
 
 __device__ __forceinline__ void store_merged(const MergeArgs& a, int th, int d, float num, float den, float m,
@@ -92,9 +177,45 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int t = th / a.hq;
   const int ns = a.row_nsplit[t];
   if (ns <= 1) return;
-  const int d = slice * 64 + lane;
   const float* lse = a.partial_lse + (int64_t)th * a.s_max;
-  const T* po = static_cast<const T*>(a.partial_o) + (int64_t)th * a.s_max * a.dh + d;
+  if constexpr (std::is_same<T, __bf16>::value) {
+    // lane pair (j, j + 32) owns d = 64 * slice + 2j, +1; half h takes every other split
+    const int h = lane >> 5, j = lane & 31;
+    const int d = slice * 64 + 2 * j;
+    const __bf16* po = static_cast<const __bf16*>(a.partial_o) + (int64_t)th * a.s_max * a.dh + d;
+    float m = -INFINITY, den = 0.f;
+    f32x2 num = {0.f, 0.f};
+    if constexpr (WPU == 1) {
+      accumulate2<2>(lse, po, a.dh, h, ns, m, num, den);
+      combine_halves(m, num, den);
+      if (h == 0) store_merged2(a, th, d, num, den, m, slice == 0 && j == 0);
+    } else {
+      __shared__ f32x2 num_s[4][32];
+      __shared__ float den_s[4], m_s[4];
+      accumulate2<8>(lse, po, a.dh, 2 * wave + h, ns, m, num, den);
+      combine_halves(m, num, den);
+      if (h == 0) num_s[wave][j] = num;
+      if (lane == 0) {
+        den_s[wave] = den;
+        m_s[wave] = m;
+      }
+      __syncthreads();
+      if (wave != 0 || h != 0) return;
+      const float mall = fmaxf(fmaxf(m_s[0], m_s[1]), fmaxf(m_s[2], m_s[3]));
+      num = f32x2{0.f, 0.f};
+      den = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = m_s[w] == -INFINITY ? 0.f : __expf(m_s[w] - mall);
+        num += num_s[w][j] * f;
+        den += den_s[w] * f;
+      }
+      store_merged2(a, th, d, num, den, mall, slice == 0 && j == 0);
+    }
+    return;
+  }
+  const int d = slice * 64 + lane;
+  const float* po = static_cast<const float*>(a.partial_o) + (int64_t)th * a.s_max * a.dh + d;
   float m = -INFINITY, num = 0.f, den = 0.f;
   if constexpr (WPU == 1) {
     accumulate<1>(lse, po, a.dh, 0, ns, m, num, den);
