@@ -333,7 +333,7 @@ def main():
                     help="run one 256 MiB device-to-device copy first, as a known-size reference for HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "the library and this benchmark run on one GPU; run with --gpus 1"}))
         sys.exit(2)
     if args.calibrate_copy:
         _calibrate_copy()
