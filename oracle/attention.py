@@ -5,8 +5,8 @@ the paged, block-size-64 FP8 decode it extends):
   * a request b owns n_b = qo_indptr[b+1] - qo_indptr[b] query rows (at most 8)
     and kv_len[b] cached tokens, the last n_b of which are the new rows' own keys;
   * each row is limited to its own position and to its window;
-  * query head h reads KV head h // G with G = Hq / Hkv (grouped-query attention,
-    "a program's query heads now divide the GQA group");
+  * query head h reads KV head h // G with G = Hq / Hkv (grouped-query attention; the
+    same PR makes the query heads of one program lie inside a single GQA group);
   * the output is softmax(sm_scale * q K^T) V over the visible tokens, with the
     K/V values dequantised first (FP8 dequantisation folded into the scores and
     into the final normaliser is the same arithmetic, FlashInfer PR #869 item 3);

@@ -7,8 +7,8 @@ from decimal import Decimal, getcontext
 import numpy as np
 import pytest
 
-from oracle.attention import (PagedKV, attend, decode_attention, gather_slots, merge_partials,
-                              split_partials, visible_range)
+from oracle.attention import (PagedKV, attend, decode_attention, decode_attention_one, gather_slots,
+                              merge_partials, split_partials, visible_range)
 from oracle.formats import bf16_bits_to_f64
 from tests.oracle_cases import bf16_bits, tiny_problem
 
@@ -261,3 +261,26 @@ def test_layouts_agree():
     oa, la = _run(a)
     ob, lb = _run(b)
     assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("layout", ["HPD", "PHD"])
+def test_single_vector_oracle_equals_full_oracle_and_brute_force(layout):
+    # decode_attention_one (the checker of the full-size sampled GPU tests) must give, for
+    # every (row, head) of a ragged, windowed, multi-row GQA problem, the full oracle's
+    # vector and LSE (up to the BLAS summation order: one row against a group of rows)
+    # and agree with the decimal brute force
+    pb = tiny_problem(17, B=3, rows=(3, 1, 4), kv_len=(9, 14, 22), window=(0, 4, 6), P=4, Hq=6, Hkv=2, d=8,
+                      layout=layout)
+    q64 = bf16_bits_to_f64(pb["q"])
+    full, lse = _run(pb)
+    bf = _brute_force(pb) if layout == "HPD" else None
+    for t in range(q64.shape[0]):
+        for h in range(pb["Hq"]):
+            o, l = decode_attention_one(q64[t, h], pb["k"], pb["v"], pb["page_indices"], pb["kv_indptr"],
+                                        pb["kv_len"], pb["qo_indptr"], pb["window"], pb["sm_scale"], t, h,
+                                        pb["Hkv"], pb["Hq"])
+            assert np.max(np.abs(o - full[t, h])) <= 1e-14 * np.max(np.abs(full[t, h]))
+            assert abs(l - lse[t, h]) <= 1e-14 * max(1.0, abs(lse[t, h]))
+            if bf is not None:
+                assert np.max(np.abs(o - bf[(t, h)][0])) <= 1e-13 * np.max(np.abs(bf[(t, h)][0]))
+                assert abs(l - bf[(t, h)][1]) <= 1e-13 * max(1.0, abs(bf[(t, h)][1]))

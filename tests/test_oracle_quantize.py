@@ -160,3 +160,38 @@ def test_oracle_inputs_use_each_workloads_own_format():
         if cfg["scale"] == "per_tensor":
             amax = np.float32(w.k.float().abs().max().item())
             assert np.float32(k.scale) == np.float32(amax / np.float32(127.0 if cfg["kv"] == "int8" else 448.0)), name
+
+
+def test_per_tensor_dequantisation_in_the_attention_inputs():
+    # PagedKV with one per-tensor scale multiplies every decoded code by that float32
+    # scale (FlashMLA PR #54, "Functionality": symmetric per-tensor K/V scales), checked
+    # against torch's own float8 decode in both cache layouts; INT8 codes likewise
+    from oracle.attention import PagedKV
+    rng = np.random.default_rng(12)
+    codes = rng.integers(0, 256, (3, 2, 4, 16)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x31             # no NaN codes
+    sc = np.float32(0.0172119140625 * 1.1)           # not a power of two: a divide would differ
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    slots = np.array([0, 3, 5, 9, 11])               # (page, slot) = (0,0) (0,3) (1,1) (2,1) (2,3)
+    for layout in ("HPD", "PHD"):
+        data = codes if layout == "HPD" else np.ascontiguousarray(codes.transpose(0, 2, 1, 3))
+        kv = PagedKV(data, "fp8", layout, "per_tensor", sc)
+        for g in range(2):
+            ref = dec[slots // 4, g, slots % 4] * np.float64(sc)
+            assert np.array_equal(kv.tokens(slots, g), ref)
+    i8 = rng.integers(-127, 128, (3, 2, 4, 16)).astype(np.int8)
+    kv = PagedKV(i8.view(np.uint8), "int8", "HPD", "per_tensor", sc)
+    ref = torch.from_numpy(i8).double().numpy()[slots // 4, 1, slots % 4] * np.float64(sc)
+    assert np.array_equal(kv.tokens(slots, 1), ref)
+
+
+def test_scalar_q_scale_dequantisation():
+    # FP8 queries with one per-tensor scale: every code decoded by torch times the scale
+    from oracle.attention import dequant_q
+    rng = np.random.default_rng(13)
+    q = rng.integers(0, 256, (5, 4, 32)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x44
+    qs = np.float32(0.0059814453125 * 3)
+    ref = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy() * np.float64(qs)
+    assert np.array_equal(dequant_q(q, "fp8", qs), ref)
+    assert np.array_equal(dequant_q(q, "fp8", np.array(qs)), ref)      # 0-d array form
