@@ -112,10 +112,16 @@ typedef struct {
   int64_t plan_bytes;          /* bytes of the plan buffer (host copy and device copy)       */
   int64_t partial_o_bytes;     /* [T, Hq, S_max, d]: float32 (bf16 KV) or bf16 (FP8/INT8 KV) */
   int64_t partial_lse_bytes;   /* float32 [T, Hq, S_max]                                    */
-  int64_t reserved[4];
+  int64_t max_item_tokens;     /* longest KV token range of one work item                   */
+  int64_t reserved[3];
 } pa_plan_info;
 
 /* Split planner (host only; no device work, no allocation).
+ * Defined by: FreeToken PR #900, "Changes" (the kernel takes qo_indptr and max_q_len,
+ * keeps the split-KV grid for multi-row requests, and sizes per-row scratch so that a
+ * captured graph keeps working) and its motivation section (one program per whole
+ * context is many times slower than splitting the KV sequence); hpc-ops issue #4, request
+ * section (unsupported query lengths are refused with an error).
  * Reads the host index arrays, validates them, chooses the number of KV splits of
  * every request for the device's compute units, and writes the work list into
  * plan_host (plan_capacity bytes).  With plan_host == NULL only *info is filled,
@@ -128,7 +134,12 @@ typedef struct {
 pa_status pa_plan_splits(const pa_plan_args* args, void* plan_host, size_t plan_capacity,
                          pa_plan_info* info);
 
-/* Stage 1 (device): for every work item (request, KV head, split) stream the split's
+/* Stage 1 (device).  Defined by: FreeToken PR #900, "Changes" (rows x GQA heads of one KV
+ * head share one tile, each row limited to its own position, partial output and LSE per
+ * split); FlashInfer PR #869, summary items 1-3 (V transposed for FP8 operands, P
+ * requantised for the FP8 P.V product, dequantisation folded into sm_scale and the
+ * final normaliser); hpc-ops issue #4, "why K x Q^T" question (the swapped product).
+ * For every work item (request, KV head, split) stream the split's
  * pages and write, for each of its query rows x heads, the split's normalised
  * partial output and natural-log LSE; requests planned with a single split write
  * the final output directly.
@@ -145,6 +156,9 @@ pa_status pa_plan_splits(const pa_plan_args* args, void* plan_host, size_t plan_
  *                bf16 for FP8 / INT8 KV (unused if !info->needs_merge)
  *   partial_lse  device float32 [T, Hq, S_max]
  *   out          device [T, Hq, d] in out_dtype (BF16 or FP32)
+ *   out_lse      device float32 [T, Hq] or NULL: rows of requests planned with a single
+ *                split receive their natural-log LSE here (pa_decode_merge writes the
+ *                rows of split requests, so the two together fill every row)
  * Tokens past kv_len (the tail of the last page) are never read.
  * Accuracy (softmax(s q.k) v over the same quantised K/V): bf16 KV keeps P in two bf16
  * terms (~2^-16 relative); per-tensor FP8 V carries P as two e4m3 terms; per-token-head
@@ -159,18 +173,23 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev,
                            const float* k_scale, const float* v_scale, const pa_scale_layout* sc,
                            const int32_t* page_indices, float sm_scale,
                            void* partial_o, float* partial_lse,
-                           void* out, pa_dtype out_dtype, void* stream);
+                           void* out, pa_dtype out_dtype, float* out_lse, void* stream);
 
-/* Stage 2 (device): per (row, query head) with more than one split,
+/* Stage 2 (device).  Defined by: FreeToken PR #900, "Changes" (stage 2 merges the splits
+ * of each row).  Per (row, query head) with more than one split,
  * out = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M}, M = max_s lse_s, written
  * in out_dtype; out_lse (device float32 [T, Hq], nullable) receives the merged
- * natural-log LSE of those rows.  A no-op launch-free success when
+ * natural-log LSE of those rows (stage 1 writes the LSE of single-split rows).  A no-op launch-free success when
  * info->needs_merge == 0.  out and partial_o must be 16-byte aligned (as for stage 1). */
 pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev,
                           const void* partial_o, const float* partial_lse,
                           void* out, pa_dtype out_dtype, float* out_lse, void* stream);
 
-/* FP8 quantiser (device): src holds n_rows rows of head_dim contiguous values
+/* FP8 quantiser (device).  Defined by: FlashMLA PR #54, "Functionality" (symmetric
+ * per-tensor FP8 scales for the KV cache); FreeToken PR #900, end-to-end A/B section (the
+ * fp8_per_token_head KV cache: one scale per token and KV head); the scale amax / 448 is
+ * the FP8 maximum FlashInfer PR #869 (summary item 2) scales by.
+ * src holds n_rows rows of head_dim contiguous values
  * (bf16 or float32; e.g. a [pages, Hkv, P, d] cache is pages*Hkv*P rows).
  *   PER_TOKEN_HEAD: scale[i] = amax_i / 448 (1 if amax_i == 0) per row i;
  *   PER_TENSOR:     one scale = amax / 448 over all rows, written to scale[0].
@@ -232,13 +251,23 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, pa_dtype src_dtype,
                        const pa_kv_layout* kv, float* k_scale, float* v_scale, const pa_scale_layout* sc,
                        void* stream);
 
-/* Test hook (device): for every work item of KV head 0 and every token t of its
- * split, writes the physical slot page*P + slot that stage 1 reads for token t of
- * its request to phys_out[kv_tok_offset[b] + t] (int64), where kv_tok_offset[b] =
- * sum of kv_len over requests < b.  Uses the same address code as stage 1.
- * Entries of tokens no split covers are left untouched. */
+/* Test hook (device), for the bit-exact page-gather check: runs stage 1's KV address code
+ * (the same device functions stage 1 loads through, with the tile geometry of the plan's
+ * kernel configuration) over every tile of every work item and records what it returns:
+ *   kv_off_out[(i * M + (t - b_i)) * C + c] = byte offset from the K (and V) cache base of
+ *     16-byte chunk c of token t of item i's KV head, for every token t of the item's range
+ *     [b_i, e_i), with M = info->max_item_tokens and C = head_dim * element size / 16
+ *     (device int64, caller-filled beforehand; entries past e_i - b_i stay untouched);
+ *   scale_off_out[(i * M + (t - b_i)) * 2 + {0: k, 1: v}] = element offset of that token's
+ *     per-token-head scale (device int64; required for PER_TOKEN_HEAD and INT8 KV, else
+ *     ignored and may be NULL; INT8 with a PER_TENSOR scale reads it through zero strides,
+ *     so its offsets are 0 and sc may be NULL).
+ * Item i is the i-th 64-byte record of the plan (fields in the library's plan layout).
+ * Errors: INVALID_ARGUMENT (NULL pointer, plan info not from pa_plan_splits, missing
+ * scale arguments). */
 pa_status pa_debug_gather(const pa_plan_info* info, const void* plan_dev, const int32_t* page_indices,
-                          int64_t* phys_out, const int64_t* kv_tok_offset, void* stream);
+                          const pa_kv_layout* kv, const pa_scale_layout* sc, int64_t* kv_off_out,
+                          int64_t* scale_off_out, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* pa_last_error(void);

@@ -42,7 +42,8 @@ class PlanInfo(ctypes.Structure):
                  "q_dtype", "kv_dtype", "kv_scale_mode", "num_items", "max_splits", "needs_merge", "num_cus",
                  "variant", "reserved0")] + \
                [("plan_bytes", ctypes.c_int64), ("partial_o_bytes", ctypes.c_int64),
-                ("partial_lse_bytes", ctypes.c_int64), ("reserved", ctypes.c_int64 * 4)]
+                ("partial_lse_bytes", ctypes.c_int64), ("max_item_tokens", ctypes.c_int64),
+                ("reserved", ctypes.c_int64 * 3)]
 
 
 class KVLayout(ctypes.Structure):
@@ -71,7 +72,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.pa_plan_splits.argtypes = [ctypes.POINTER(PlanArgs), _p, ctypes.c_size_t, ctypes.POINTER(PlanInfo)]
         L.pa_decode_stage1.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, _p, ctypes.POINTER(KVLayout), _p, _p,
-                                       ctypes.POINTER(ScaleLayout), _p, ctypes.c_float, _p, _p, _p, ctypes.c_int, _p]
+                                       ctypes.POINTER(ScaleLayout), _p, ctypes.c_float, _p, _p, _p, ctypes.c_int, _p,
+                                       _p]
         L.pa_decode_merge.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, ctypes.c_int, _p, _p]
         L.pa_kv_quantize_fp8.argtypes = [_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, _p, _p, _p]
         L.pa_kv_quantize_int8.argtypes = [_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, _p, _p, _p]
@@ -80,7 +82,8 @@ def lib() -> ctypes.CDLL:
         L.pa_kv_append.argtypes = [_p, _p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int32, _p, _p, _p, ctypes.c_int, ctypes.c_int, ctypes.POINTER(KVLayout),
                                    _p, _p, ctypes.POINTER(ScaleLayout), _p]
-        L.pa_debug_gather.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, _p]
+        L.pa_debug_gather.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, ctypes.POINTER(KVLayout),
+                                      ctypes.POINTER(ScaleLayout), _p, _p, _p]
         for f in ("pa_plan_splits", "pa_decode_stage1", "pa_decode_merge", "pa_kv_quantize_fp8",
                   "pa_kv_quantize_fp8_per_head", "pa_kv_quantize_int8", "pa_kv_append", "pa_debug_gather"):
             getattr(L, f).restype = ctypes.c_int
@@ -144,14 +147,14 @@ def pa_plan_splits(qo_indptr, kv_indptr, kv_len, window, max_q_len, page_size, n
 
 
 def pa_decode_stage1(info, plan_dev, q, q_scale, k_cache, v_cache, kv_layout, k_scale, v_scale, scale_layout,
-                     page_indices, sm_scale, partial_o, partial_lse, out, out_dtype, stream=None):
+                     page_indices, sm_scale, partial_o, partial_lse, out, out_dtype, out_lse=None, stream=None):
     kvl = KVLayout(*kv_layout)
     scl = None if scale_layout is None else ScaleLayout(*scale_layout)
     _check(lib().pa_decode_stage1(ctypes.byref(info), _ptr(plan_dev), _ptr(q), _ptr(q_scale), _ptr(k_cache),
                                   _ptr(v_cache), ctypes.byref(kvl), _ptr(k_scale), _ptr(v_scale),
                                   None if scl is None else ctypes.byref(scl), _ptr(page_indices),
                                   ctypes.c_float(sm_scale), _ptr(partial_o), _ptr(partial_lse), _ptr(out),
-                                  _dt(out_dtype), _stream(stream)))
+                                  _dt(out_dtype), _ptr(out_lse), _stream(stream)))
 
 
 def pa_decode_merge(info, plan_dev, partial_o, partial_lse, out, out_dtype, out_lse=None, stream=None):
@@ -184,6 +187,10 @@ def pa_kv_append(k_new, v_new, src_dtype, n_tokens, num_kv_heads, head_dim, page
                               _ptr(v_scale), None if scl is None else ctypes.byref(scl), _stream(stream)))
 
 
-def pa_debug_gather(info, plan_dev, page_indices, phys_out, kv_tok_offset, stream=None):
-    _check(lib().pa_debug_gather(ctypes.byref(info), _ptr(plan_dev), _ptr(page_indices), _ptr(phys_out),
-                                 _ptr(kv_tok_offset), _stream(stream)))
+def pa_debug_gather(info, plan_dev, page_indices, kv_layout, scale_layout, kv_off_out, scale_off_out=None,
+                    stream=None):
+    kvl = KVLayout(*kv_layout)
+    scl = None if scale_layout is None else ScaleLayout(*scale_layout)
+    _check(lib().pa_debug_gather(ctypes.byref(info), _ptr(plan_dev), _ptr(page_indices), ctypes.byref(kvl),
+                                 None if scl is None else ctypes.byref(scl), _ptr(kv_off_out), _ptr(scale_off_out),
+                                 _stream(stream)))

@@ -1,8 +1,13 @@
-"""Builds the gfx950 shared library libpa_gfx950.so in place (hipcc, no JIT cache)."""
+"""Builds the gfx950 shared library libpa_gfx950.so in place (hipcc, no JIT cache).
+
+Every HIP source is compiled with the compiler's per-kernel resource report
+(-Rpass-analysis=kernel-resource-usage); the build fails if any kernel uses scratch
+memory (register spills), and writes the report to _build/resource_usage.txt."""
 from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -21,21 +26,55 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # them in place instead of copying AGPR <-> VGPR every tile
          "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
+RESOURCE_FLAG = "-Rpass-analysis=kernel-resource-usage"
 
 
-def _compile(src: str) -> str:
+def parse_resource_usage(text: str) -> dict:
+    """Per-kernel fields of the compiler's resource-usage remarks:
+    {mangled name: {"VGPRs": int, "AGPRs": int, "ScratchSize": int, "Occupancy": int, ...}}."""
+    kernels, cur = {}, None
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = kernels.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+) \[-Rpass-analysis", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = int(m.group(2))
+    return kernels
+
+
+def spilling(kernels: dict) -> list:
+    return sorted(k for k, v in kernels.items()
+                  if v.get("ScratchSize", 0) > 0 or v.get("VGPRs Spill", 0) > 0 or v.get("SGPRs Spill", 0) > 0)
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    flags = FLAGS + ([RESOURCE_FLAG] if src.endswith(".hip") else [])
+    cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
-    return obj
+    return obj, parse_resource_usage(r.stderr)
 
 
 def build(jobs: int = 8, verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(_compile, SOURCES))
+    objs = [o for o, _ in results]
+    kernels = {}
+    for _, k in results:
+        kernels.update(k)
+    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+        for name in sorted(kernels):
+            v = kernels[name]
+            f.write(f"{name} VGPRs={v.get('VGPRs')} AGPRs={v.get('AGPRs')} ScratchSize={v.get('ScratchSize')} "
+                    f"Occupancy={v.get('Occupancy')} LDS={v.get('LDS Size')}\n")
+    bad = spilling(kernels)
+    if bad:
+        raise RuntimeError("kernels with register spills (scratch memory):\n  " + "\n  ".join(bad))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,7 +82,7 @@ def build(jobs: int = 8, verbose: bool = True) -> str:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} ({len(kernels)} kernels, none with scratch)")
     return LIB
 
 

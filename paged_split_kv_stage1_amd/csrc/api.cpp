@@ -3,6 +3,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cmath>
 #include <functional>
 #include <cstdarg>
 #include <cstdio>
@@ -65,14 +66,16 @@ bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
   c->pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD || c->i8;
   // head_dim 256 with one query block: 64-token tiles (two token groups of two waves)
   // keep two LDS stages; 128-token tiles of d256 would fit only one
-  // head_dim 512 runs one 16-row block per wave; a request with more than four blocks
-  // per KV head is cut into groups of four, one work item per (group, KV split).  (For
-  // head_dim 128 and 256 the waves take several blocks each instead: groups measured
-  // slower on the ragged group-24 workload, 124 -> 132 us, since every group re-reads
-  // the split's K and V.)
-  if (c->dh == 512) { c->wq = 4; c->nqb = 1; }
-  else if (nqb <= 1) { c->wq = c->dh == 256 ? 2 : 1; c->nqb = 1; }
-  else if (nqb == 2) { c->wq = 2; c->nqb = 1; }
+  // head_dim 512 and 256 run one 16-row block per wave; a request with more than four
+  // blocks per KV head is cut into groups of four, one work item per (group, KV split)
+  // (at head_dim 256 two blocks per wave would need more than the 256 registers a wave
+  // has at two workgroups per CU).  For head_dim 128 the waves take several blocks each
+  // instead: groups measured slower on the ragged group-24 workload, 124 -> 132 us,
+  // since every group re-reads the split's K and V.
+  const bool d256_bf16q_pt8 = c->dh == 256 && c->kvf8 && !c->pt && !c->qf8;   // no two-wave variant
+  if (c->dh == 512 || (c->dh == 256 && nqb > 4)) { c->wq = 4; c->nqb = 1; }
+  else if (nqb <= 1) { c->wq = c->dh == 256 ? (d256_bf16q_pt8 ? 4 : 2) : 1; c->nqb = 1; }
+  else if (nqb == 2) { c->wq = d256_bf16q_pt8 ? 4 : 2; c->nqb = 1; }
   else if (nqb <= 4) { c->wq = 4; c->nqb = 1; }
   else { c->wq = 4; c->nqb = (nqb + 3) / 4; }
   return stage1_cfg_supported(*c);
@@ -95,8 +98,8 @@ int query_groups(const pa_plan_args& a, const KernelCfg& cfg, int b) {
 // streaming time and its compute time (which grows with the number of 16-row query
 // blocks each wave runs per token), plus its partial-output write when the request is
 // split, plus a fixed prologue.  Items are placed longest-first on the least loaded
-// slot; the merge reads every partial back.  The candidate split length with the
-// smallest estimated step time wins (ties go to fewer, longer splits).
+// slot; the merge reads every partial back.  The candidate split plan with the smallest
+// estimated step time wins (ties go to fewer, longer splits).
 constexpr double kHbmBytesPerS = 6.5e12;     // MI355X HBM3E, sustained streaming rate
 constexpr int kSlotsPerCu = 2;
 constexpr double kItemOverheadS = 1.5e-6;    // item prologue + pipeline fill
@@ -135,33 +138,46 @@ void choose_splits(const pa_plan_args& a, const KernelCfg& cfg, const std::vecto
     const int rounds = (per_item + cfg.wq - 1) / cfg.wq;
     comp_tok[b] = comp_blk * rounds / wt;
   }
-  int max_blk = 1;
-  for (int b = 0; b < B; ++b) max_blk = std::max(max_blk, (span[b] + kSplitAlign - 1) / kSplitAlign);
-  // candidate split lengths in 64-token blocks: every distinct ceil(max_blk / S), so
-  // that each split count of the longest request is reachable (about 2 sqrt(max_blk)
-  // values), in increasing order
-  std::vector<int> cand;
-  for (int sc = std::min(max_blk, split_cap); sc >= 1; --sc) {
-    const int c = (max_blk + sc - 1) / sc;
-    if (cand.empty() || cand.back() != c) cand.push_back(c);
+  // Split counts: every request's items should cost about the same, so a request whose
+  // tokens are more expensive (more 16-row query blocks per wave: compute-bound) is cut
+  // into shorter splits than a memory-bound one.  The candidates are the item costs
+  // C = W_max / S, S = 1, 2, ..., where W_max is the cost of the heaviest request's whole
+  // range; request b then gets ceil(W_b / C) splits (at most its 64-token blocks and the
+  // cap).  On uniform batches this is the same as cutting every request into equal runs.
+  std::vector<int> nblk(B);
+  std::vector<double> ctok(B);                   // seconds per token of request b's items
+  double heavy = 0;
+  int heavy_b = 0;
+  for (int b = 0; b < B; ++b) {
+    nblk[b] = std::max(1, (span[b] + kSplitAlign - 1) / kSplitAlign);
+    ctok[b] = std::max(kv_tok / bw_slot, comp_tok[b]);
+    const double wb = (double)span[b] * ctok[b] * ngrp[b];
+    if (wb > heavy) {
+      heavy = wb;
+      heavy_b = b;
+    }
   }
-  std::vector<int> best(B, 1), cur(B);
+  const int s_heavy = std::max(1, std::min(split_cap, nblk[heavy_b]));
+  std::vector<int> best(B, 1), cur(B), prev;
   double best_t = 1e30;
   std::vector<std::pair<double, int>> groups;       // (item cost, item count)
   std::vector<double> heap;
-  // Longest split length (fewest splits) first, so that an equal estimate keeps the
-  // plan with fewer splits.  A candidate whose lower bound -- its work spread evenly
-  // over the CUs, or its longest item, plus its merge -- cannot beat the best estimate
-  // so far is not scheduled at all.
-  for (auto ci = cand.rbegin(); ci != cand.rend(); ++ci) {
-    const int c = *ci;
+  // Fewest splits first, so that an equal estimate keeps the plan with fewer splits.  A
+  // candidate whose lower bound -- its work spread evenly over the CUs, or its longest
+  // item, plus its merge -- cannot beat the best estimate so far is not scheduled at all.
+  for (int S = 1; S <= s_heavy; ++S) {
+    const double target = heavy / S;
+    for (int b = 0; b < B; ++b) {
+      const double wb = (double)span[b] * ctok[b] * ngrp[b];
+      const int sb = (int)std::ceil(wb / target * (1 - 1e-12));
+      cur[b] = std::max(1, std::min(sb, std::min(split_cap, nblk[b])));
+    }
+    if (cur == prev) continue;
+    prev = cur;
     groups.clear();
     double merge_bytes = 0, total = 0, longest = 0;
     for (int b = 0; b < B; ++b) {
-      const int nblk = (span[b] + kSplitAlign - 1) / kSplitAlign;
-      int sb = (nblk + c - 1) / c;
-      sb = std::max(1, std::min(sb, split_cap));
-      cur[b] = sb;
+      const int sb = cur[b];
       const int n = a.qo_indptr[b + 1] - a.qo_indptr[b];
       // partial bytes at 4 per element even where they are stored in bf16: with the
       // bf16 size the model picks 1082 items for the ragged group-24 mix instead of 704,
@@ -301,6 +317,22 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
     n_items += (int64_t)nsp[b] * Hkv * query_groups(*a, cfg, b);
   }
   if (n_items > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "too many work items (%lld)", (long long)n_items);
+  // split s of request b covers 64-token blocks [s * nblk / S, (s + 1) * nblk / S) from begin[b]
+  auto split_range = [&](int b, int s, int* t0, int* t1) {
+    const int L = a->kv_len[b];
+    const int nblk = (span[b] + kSplitAlign - 1) / kSplitAlign;
+    const int64_t blk0 = (int64_t)s * nblk / nsp[b];
+    const int64_t blk1 = (int64_t)(s + 1) * nblk / nsp[b];
+    *t0 = (int)std::min<int64_t>(begin[b] + blk0 * kSplitAlign, L);
+    *t1 = (int)std::min<int64_t>(begin[b] + blk1 * kSplitAlign, L);
+  };
+  int64_t max_item_tokens = 0;
+  for (int b = 0; b < B; ++b)
+    for (int s = 0; s < nsp[b]; ++s) {
+      int t0, t1;
+      split_range(b, s, &t0, &t1);
+      max_item_tokens = std::max<int64_t>(max_item_tokens, t1 - t0);
+    }
   const int64_t th_count = (int64_t)T * a->num_q_heads;
 
   memset(info, 0, sizeof *info);
@@ -322,6 +354,7 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   info->plan_bytes = plan_bytes_for(n_items, T);
   info->partial_o_bytes = s_max > 1 ? th_count * s_max * a->head_dim * partial_o_elem_bytes(a->kv_dtype) : 0;
   info->partial_lse_bytes = s_max > 1 ? th_count * s_max * 4 : 0;
+  info->max_item_tokens = max_item_tokens;
   if (!plan_host) return ok();
   if ((int64_t)plan_capacity < info->plan_bytes)
     return fail(PA_ERR_INSUFFICIENT_WORKSPACE, "plan buffer holds %zu bytes, %lld needed", plan_capacity,
@@ -333,7 +366,6 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   for (int b = 0; b < B; ++b) {
     const int n = a->qo_indptr[b + 1] - a->qo_indptr[b];
     const int L = a->kv_len[b];
-    const int nblk = (span[b] + kSplitAlign - 1) / kSplitAlign;
     const int ng = query_groups(*a, cfg, b);
     for (int g = 0; g < Hkv; ++g) {
       for (int s = 0; s < nsp[b]; ++s) {
@@ -348,10 +380,7 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
           it.kvh = g;
           it.split = s;
           it.nsplit = nsp[b];
-          const int64_t blk0 = (int64_t)s * nblk / nsp[b];
-          const int64_t blk1 = (int64_t)(s + 1) * nblk / nsp[b];
-          it.tok_begin = (int)std::min<int64_t>(begin[b] + blk0 * kSplitAlign, L);
-          it.tok_end = (int)std::min<int64_t>(begin[b] + blk1 * kSplitAlign, L);
+          split_range(b, s, &it.tok_begin, &it.tok_end);
           it.req = b;
           it.qblk0 = qg * cfg.wq * cfg.nqb;
           items.push_back(it);
@@ -380,7 +409,7 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const
                            const void* k_cache, const void* v_cache, const pa_kv_layout* kv, const float* k_scale,
                            const float* v_scale, const pa_scale_layout* sc, const int32_t* page_indices,
                            float sm_scale, void* partial_o, float* partial_lse, void* out, pa_dtype out_dtype,
-                           void* stream) {
+                           float* out_lse, void* stream) {
   if (!info || !plan_dev || !q || !k_cache || !v_cache || !kv || !page_indices || !out)
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_stage1: a required pointer is NULL");
   if (out_dtype != PA_DTYPE_BF16 && out_dtype != PA_DTYPE_FP32)
@@ -429,6 +458,7 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const
   s.part_bf16 = partial_o_elem_bytes(info->kv_dtype) == 2;
   s.out = out;
   s.out_bf16 = out_dtype == PA_DTYPE_BF16;
+  s.out_lse = out_lse;
   s.hq = info->num_q_heads;
   s.group = info->num_q_heads / info->num_kv_heads;
   s.page_shift = ps;
@@ -566,16 +596,36 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, pa_dtype src_dtype,
 }
 
 pa_status pa_debug_gather(const pa_plan_info* info, const void* plan_dev, const int32_t* page_indices,
-                          int64_t* phys_out, const int64_t* kv_tok_offset, void* stream) {
-  if (!info || !plan_dev || !page_indices || !phys_out || !kv_tok_offset)
+                          const pa_kv_layout* kv, const pa_scale_layout* sc, int64_t* kv_off_out,
+                          int64_t* scale_off_out, void* stream) {
+  if (!info || !plan_dev || !page_indices || !kv || !kv_off_out)
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_debug_gather: NULL pointer");
+  const KernelCfg cfg = unpack_cfg(info->variant);
+  if (!stage1_cfg_supported(cfg) || cfg.dh != info->head_dim)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_plan_info was not produced by pa_plan_splits");
+  // INT8 KV runs the per-token scale path for both scale modes (per tensor: zero strides)
+  const bool per_token = info->kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD || info->kv_dtype == PA_DTYPE_INT8;
+  if (per_token && !scale_off_out)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_debug_gather: per-token scales need scale_off_out");
+  if (info->kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD && !sc)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_debug_gather: per-token-head scales need a scale layout");
   GatherArgs g;
+  memset(&g, 0, sizeof g);
   g.items = static_cast<const PaItem*>(plan_dev);
   g.page_indices = page_indices;
-  g.phys_out = phys_out;
-  g.kv_tok_offset = kv_tok_offset;
+  g.kv_sp = kv->page;
+  g.kv_sh = kv->head;
+  g.kv_ss = kv->slot;
+  if (per_token && info->kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD) {
+    g.sc_sp = sc->page;
+    g.sc_sh = sc->head;
+    g.sc_ss = sc->slot;
+  }
+  g.kv_off = kv_off_out;
+  g.sc_off = per_token ? scale_off_out : nullptr;
+  g.max_tok = info->max_item_tokens;
   g.page_shift = ilog2_exact(info->page_size);
-  const int e = launch_gather(g, info->num_items, stream);
+  const int e = launch_gather(cfg, g, info->num_items, stream);
   if (e) return hip_fail(e, "pa_debug_gather launch");
   return ok();
 }

@@ -1,6 +1,5 @@
 // Device helpers for the gfx950 kernels: vector types, FP8/bf16 conversions, MFMA
-// wrappers, wave shuffles, and the page-gather address code shared by stage 1 and
-// the gather test hook.
+// wrappers and wave shuffles (the page-gather address code is in kv_addr.hpp).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -18,15 +17,6 @@ typedef short i16x4 __attribute__((vector_size(8)));
 typedef int i32x2 __attribute__((vector_size(8)));
 
 #define PA_LDS __attribute__((address_space(3)))
-
-// ---- page gather ---------------------------------------------------------------
-// Logical token j of a request lives in page page_indices[page_base + j / P] at
-// slot j % P (P = 1 << page_shift).
-__device__ __forceinline__ int32_t token_page(const int32_t* __restrict__ page_indices, int32_t page_base,
-                                              int32_t j, int page_shift) {
-  return page_indices[page_base + (j >> page_shift)];
-}
-__device__ __forceinline__ int32_t token_slot(int32_t j, int page_shift) { return j & ((1 << page_shift) - 1); }
 
 // ---- MFMA ----------------------------------------------------------------------
 // 16x16x32: A lane l holds row l%16, K = 8*(l/16)..+7; B lane l holds column l%16,

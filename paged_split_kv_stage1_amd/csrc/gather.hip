@@ -1,25 +1,68 @@
-// Test hook: writes the physical slot (page * P + slot) that stage 1 reads for each
-// token of each split, using the same page-gather code (token_page / token_slot).
+// Test hook: runs stage 1's KV address code (kv_addr.hpp) over every tile of every work
+// item, with stage 1's tile geometry for the plan's kernel configuration, and records
+// the byte offset of every 16-byte K/V chunk (and the element offset of every
+// per-token-head scale) that stage 1 loads, indexed by (item, token - tok_begin, chunk).
 #include "common.hpp"
+#include "kv_addr.hpp"
 
 namespace pa {
 
+template <int DH, int KVB, int WQ, bool PT>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+  constexpr int CPR = DH * KVB / 16;
+  constexpr int BN = 32 * (4 / WQ);                     // tokens per tile, as in stage 1
+  constexpr int NP = BN / 16 + 1;
+  using KA = KvTileAddr<CPR, BN, KVB>;
   const PaItem it = a.items[blockIdx.x];
-  if (it.kvh != 0 || it.qblk0 != 0) return;     // one item per token range
-  const int64_t base = a.kv_tok_offset[it.req];
-  const int P = 1 << a.page_shift;
-  for (int j = it.tok_begin + (int)threadIdx.x; j < it.tok_end; j += 256) {
-    const int32_t pg = token_page(a.page_indices, it.page_base, j, a.page_shift);
-    const int32_t sl = token_slot(j, a.page_shift);
-    a.phys_out[base + j] = (int64_t)pg * P + sl;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const KA ka(lane, a.kv_ss);
+  const cint32* pidx = (const cint32*)(a.page_indices) + it.page_base;
+  const int64_t head_off = (int64_t)it.kvh * a.kv_sh;
+  const int shift = a.page_shift;
+  const int pmask = (1 << shift) - 1;
+  const int tb0 = it.tok_begin, te = it.tok_end;
+  const int ntiles = te > tb0 ? (te - tb0 + BN - 1) / BN : 0;
+  const int64_t base = (int64_t)blockIdx.x * a.max_tok;
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int tile0 = tb0 + ti * BN;
+#pragma unroll
+    for (int i = 0; i < KA::CPT; ++i) {
+      const int jb = KA::group_token(tile0, wave, i, te);
+      const int32_t page = KA::group_page(pidx, jb, shift);
+      const int64_t off = KA::row_offset(page, jb, a.kv_sp, head_off, a.kv_ss, pmask) + ka.lane_offset(jb, te, a.kv_ss);
+      a.kv_off[(base + ka.lane_token(jb, te) - tb0) * CPR + ka.cpos] = off;
+    }
+    if constexpr (PT) {
+      if (tid < 2 * BN) {
+        const ScaleTileAddr<BN, NP> sa(pidx, tile0, te, shift, tid, it.kvh, a.sc_sp, a.sc_sh, a.sc_ss);
+        a.sc_off[(base + sa.token - tb0) * 2 + (sa.is_v ? 1 : 0)] = sa.off;
+      }
+    }
   }
 }
 
-int launch_gather(const GatherArgs& a, int num_items, void* stream) {
-  if (num_items <= 0) return 0;
-  hipLaunchKernelGGL(gather_kernel, dim3(num_items), dim3(256), 0, (hipStream_t)stream, a);
+template <int DH, int KVB>
+static int launch_dk(const KernelCfg& c, const GatherArgs& a, int n, hipStream_t s) {
+  if (c.wq == 1 && !c.pt) hipLaunchKernelGGL((gather_kernel<DH, KVB, 1, false>), dim3(n), dim3(256), 0, s, a);
+  else if (c.wq == 1) hipLaunchKernelGGL((gather_kernel<DH, KVB, 1, true>), dim3(n), dim3(256), 0, s, a);
+  else if (c.wq == 2 && !c.pt) hipLaunchKernelGGL((gather_kernel<DH, KVB, 2, false>), dim3(n), dim3(256), 0, s, a);
+  else if (c.wq == 2) hipLaunchKernelGGL((gather_kernel<DH, KVB, 2, true>), dim3(n), dim3(256), 0, s, a);
+  else if (c.wq == 4 && !c.pt) hipLaunchKernelGGL((gather_kernel<DH, KVB, 4, false>), dim3(n), dim3(256), 0, s, a);
+  else if (c.wq == 4) hipLaunchKernelGGL((gather_kernel<DH, KVB, 4, true>), dim3(n), dim3(256), 0, s, a);
+  else return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
+}
+
+int launch_gather(const KernelCfg& c, const GatherArgs& a, int num_items, void* stream) {
+  if (num_items <= 0) return 0;
+  const hipStream_t s = (hipStream_t)stream;
+  const int kvb = c.kvf8 ? 1 : 2;
+  if (c.dh == 128) return kvb == 1 ? launch_dk<128, 1>(c, a, num_items, s) : launch_dk<128, 2>(c, a, num_items, s);
+  if (c.dh == 256) return kvb == 1 ? launch_dk<256, 1>(c, a, num_items, s) : launch_dk<256, 2>(c, a, num_items, s);
+  if (c.dh == 512) return kvb == 1 ? launch_dk<512, 1>(c, a, num_items, s) : launch_dk<512, 2>(c, a, num_items, s);
+  return (int)hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -61,6 +61,7 @@ struct Stage1Args {
   float sm_scale;
   void* partial_o; float* partial_lse;  // partial O: float32, or bf16 when part_bf16
   void* out; int out_bf16;
+  float* out_lse;                       // LSE of rows whose request has one split, or NULL
   int hq, group, page_shift, s_max;
   int part_bf16;
 };
@@ -75,14 +76,18 @@ struct MergeArgs {
 
 struct GatherArgs {
   const PaItem* items; const int32_t* page_indices;
-  int64_t* phys_out; const int64_t* kv_tok_offset;
+  int64_t kv_sp, kv_sh, kv_ss;          // KV element strides (page, head, slot)
+  int64_t sc_sp, sc_sh, sc_ss;          // per-token-head scale strides
+  int64_t* kv_off;                      // [items, max_tok, chunks per token]: byte offsets
+  int64_t* sc_off;                      // [items, max_tok, 2]: k / v scale element offsets, or NULL
+  int64_t max_tok;                      // longest token range of an item
   int page_shift;
 };
 
 // Launchers (defined in the .hip files); return a hipError_t as int.
 int launch_stage1(const KernelCfg& cfg, const Stage1Args& a, int num_items, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
-int launch_gather(const GatherArgs& a, int num_items, void* stream);
+int launch_gather(const KernelCfg& cfg, const GatherArgs& a, int num_items, void* stream);
 int launch_quant(const void* src, int src_bf16, int64_t n_rows, int head_dim, int per_tensor, int i8,
                  uint8_t* dst, float* scale, void* stream);
 bool stage1_cfg_supported(const KernelCfg& cfg);

@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "kv_addr.hpp"
 
 namespace pa {
 
@@ -226,23 +227,18 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
   }
 
   // ---- KV tile loads: HBM -> registers -> LDS ------------------------------------------
-  // Thread chunk i of a tile is 16-byte chunk cpos of token tb_i + lt, where one wave's
-  // 64 lanes cover TPI = 64/CPR consecutive tokens.  Those never straddle a page (pages
-  // hold >= 16 tokens, tiles start on 32-token boundaries), so each load's page and
-  // slot are wave-uniform: a scalar base plus a per-lane offset that does not change
-  // between tiles.  In LDS, position p (16-byte unit) of a K tile holds chunk
-  // (p % CPR) ^ swz_k(t) of token t = p / CPR; V likewise with swz_v.  Tokens past the
-  // split end are clamped to the last valid token (finite data, masked later).
+  // Thread chunk i of a tile is 16-byte chunk cpos of token tb_i + lt (the page-gather
+  // addressing of kv_addr.hpp: wave-uniform page and row, loop-invariant lane offset).
+  // In LDS, position p (16-byte unit) of a K tile holds chunk (p % CPR) ^ swz_k(t) of
+  // token t = p / CPR; V likewise with swz_v.
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v);
-  // The page table is read-only for the kernel's lifetime: reading it through the
-  // constant address space lets the compiler use scalar loads.
-  typedef const int32_t __attribute__((address_space(4))) cint32;
+  using KA = KvTileAddr<C::CPR, C::BN, C::KVB>;
+  const KA ka(lane, a.kv_ss);
   const cint32* pidx = (const cint32*)(a.page_indices) + it.page_base;
   const int64_t head_off = (int64_t)it.kvh * a.kv_sh;
-  const int lt = lane / C::CPR;
-  const int cpos = lane % C::CPR;
-  const uint32_t goff = (uint32_t)(lt * a.kv_ss * C::KVB) + (cpos << 4);
+  const int lt = ka.lt;
+  const int cpos = ka.cpos;
   uint32_t kpos[C::CPT][C::XPC], vpos[C::CPT][C::VXPC];
 #pragma unroll
   for (int i = 0; i < C::CPT; ++i) {
@@ -269,16 +265,14 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
     int32_t pages[C::CPT];
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      jbs[i] = min(tile0 + (wave * 64 + 256 * i) / C::CPR, te - 1);   // first token of this load (uniform)
-      pages[i] = pidx[jbs[i] >> shift];
+      jbs[i] = KA::group_token(tile0, wave, i, te);   // first token of this load (uniform)
+      pages[i] = KA::group_page(pidx, jbs[i], shift);
     }
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int jb = jbs[i];
-      const int ltc = min(lt, te - 1 - jb);
-      const uint32_t off = goff - (uint32_t)((lt - ltc) * a.kv_ss * C::KVB);
-      const int32_t page = pages[i];
-      const int64_t row = ((int64_t)page * a.kv_sp + head_off + (int64_t)(jb & pmask) * a.kv_ss) * C::KVB;
+      const uint32_t off = ka.lane_offset(jb, te, a.kv_ss);
+      const int64_t row = KA::row_offset(pages[i], jb, a.kv_sp, head_off, a.kv_ss, pmask);
       // Streaming loads: every KV byte is read once, so keep it out of the caches;
       // normal loads must first evict (and write back) whatever dirty lines the
       // preceding kernels left in L2/MALL, which halves the achieved HBM rate.
@@ -287,19 +281,8 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
     }
     if constexpr (PT) {
       if (tid < 2 * C::BN) {
-        int pages[C::NPMAX];
-        const int pg0 = tile0 >> shift;
-        const int pgl = (te - 1) >> shift;
-#pragma unroll
-        for (int k = 0; k < C::NPMAX; ++k) pages[k] = pidx[min(pg0 + k, pgl)];
-        const bool is_v = tid >= C::BN;
-        const int j = min(tile0 + (is_v ? tid - C::BN : tid), te - 1);
-        const int sel = (j >> shift) - pg0;
-        int page = pages[0];
-#pragma unroll
-        for (int k = 1; k < C::NPMAX; ++k) page = sel == k ? pages[k] : page;
-        const int64_t so = (int64_t)page * a.sc_sp + (int64_t)it.kvh * a.sc_sh + (int64_t)(j & pmask) * a.sc_ss;
-        sreg[SL] = __builtin_nontemporal_load((is_v ? a.v_scale : a.k_scale) + so);
+        const ScaleTileAddr<C::BN, C::NPMAX> sa(pidx, tile0, te, shift, tid, it.kvh, a.sc_sp, a.sc_sh, a.sc_ss);
+        sreg[SL] = __builtin_nontemporal_load((sa.is_v ? a.v_scale : a.k_scale) + sa.off);
       }
     }
   };
@@ -776,7 +759,9 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
     const int64_t th = (int64_t)(it.row0 + r) * Hq + (int64_t)it.kvh * G + hl;
     const bool empty = !(ltot[i] > 0.f);
     const float sc = empty ? 0.f : out_scale / ltot[i];
+    const float lse = empty ? -INFINITY : (mrun[i] + __log2f(ltot[i]) - kPoff) * kLn2;
     if (it.nsplit == 1) {
+      if (a.out_lse && g == 0) a.out_lse[th] = lse;
       if (a.out_bf16) {
         __bf16* dst = static_cast<__bf16*>(a.out) + th * DH;
 #pragma unroll
@@ -802,14 +787,12 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
         for (int k = 0; k < 4; ++k) v[k] = (__bf16)(o[i][db][k] * sc);
         *reinterpret_cast<bf16x4*>(dst + 16 * db + 4 * g) = v;
       }
-      if (g == 0)
-        a.partial_lse[th * a.s_max + it.split] = empty ? -INFINITY : (mrun[i] + __log2f(ltot[i]) - kPoff) * kLn2;
+      if (g == 0) a.partial_lse[th * a.s_max + it.split] = lse;
     } else {
       float* dst = static_cast<float*>(a.partial_o) + (th * a.s_max + it.split) * DH;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = o[i][db] * sc;
-      if (g == 0)
-        a.partial_lse[th * a.s_max + it.split] = empty ? -INFINITY : (mrun[i] + __log2f(ltot[i]) - kPoff) * kLn2;
+      if (g == 0) a.partial_lse[th * a.s_max + it.split] = lse;
     }
   }
 }
@@ -834,7 +817,11 @@ struct Pipe {
   // measured slower on the d256 per-token-head shape (register pressure; also without
   // spills once K stays FP8), so at most two; head_dim 512 runs one wave per SIMD, whose
   // register file holds two of its 64 KB tiles (four FP8 tiles measured slower too).
-  static constexpr int PD = (CPT <= 4 || DH == 512) ? 2 : 1;
+  // head_dim 256 with per-tensor FP8 V (a second, lo-term accumulator) or with INT8 tiles
+  // split over two token groups keeps one tile in flight: two would not fit beside the
+  // accumulators in the 256 registers a wave has at two workgroups per CU.
+  static constexpr bool PV_FP8 = KV == 1 && !PT;
+  static constexpr int PD = DH == 512 ? 2 : (DH == 256 && (PV_FP8 || (KV == 2 && WQ == 2))) ? 1 : (CPT <= 4 ? 2 : 1);
 };
 
 template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB>
@@ -849,12 +836,14 @@ static int launch_one(const Stage1Args& a, int num_items, void* stream) {
 }
 
 // Largest query-block count per wave instantiated for a mode: per-tensor FP8 V keeps
-// a second (lo) accumulator, which does not fit in registers for more blocks.
+// a second (lo) accumulator, which does not fit in registers for more blocks; at head_dim
+// 256 a wave's accumulators for one block already take 64 registers, so more than four
+// blocks per KV head run as query-block groups (one work item per run of four blocks).
 template <int DH, int KV, bool PT>
 constexpr int max_nqb() {
   constexpr bool pv_fp8 = KV == 1 && !PT;
   if constexpr (DH == 128) return pv_fp8 ? 2 : 3;
-  else return pv_fp8 ? 1 : 2;
+  else return 1;
 }
 
 template <int DH, bool QF8, int KV, bool PT>
@@ -863,7 +852,12 @@ static int dispatch_tiles(const KernelCfg& c, const Stage1Args& a, int n, void* 
   if constexpr (DH == 128) {      // d256 always runs >= 2 query-block waves (64-token tiles)
     if (c.wq == 1 && c.nqb == 1) return launch_one<DH, QF8, KV, PT, 1, 1>(a, n, s);
   }
-  if (c.wq == 2 && c.nqb == 1) return launch_one<DH, QF8, KV, PT, 2, 1>(a, n, s);
+  // (head_dim 256, bf16 queries against per-tensor FP8: the upconverted query operand,
+  // two accumulator sets and a 64-token tile in flight exceed 256 registers with two
+  // query-block waves, so such requests run on four one-block waves)
+  if constexpr (!(DH == 256 && KV == 1 && !PT && !QF8)) {
+    if (c.wq == 2 && c.nqb == 1) return launch_one<DH, QF8, KV, PT, 2, 1>(a, n, s);
+  }
   if (c.wq == 4 && c.nqb == 1) return launch_one<DH, QF8, KV, PT, 4, 1>(a, n, s);
   if constexpr (NMAX >= 2) {
     if (c.wq == 4 && c.nqb == 2) return launch_one<DH, QF8, KV, PT, 4, 2>(a, n, s);
@@ -896,7 +890,8 @@ bool stage1_cfg_supported(const KernelCfg& c) {
   if (!c.kvf8 && c.pt) return false;
   if (c.i8 && (!c.kvf8 || !c.pt || c.qf8)) return false;    // INT8 KV: bf16 queries, per-token scale path
   const bool pv_fp8 = c.kvf8 && !c.pt;
-  const int nmax = c.dh == 128 ? (pv_fp8 ? 2 : 3) : (pv_fp8 ? 1 : 2);
+  if (c.dh == 256 && pv_fp8 && !c.qf8 && c.wq == 2) return false;
+  const int nmax = c.dh == 128 ? (pv_fp8 ? 2 : 3) : 1;
   if (c.nqb == 1) return (c.wq == 1 && c.dh == 128) || c.wq == 2 || c.wq == 4;
   return c.wq == 4 && c.nqb >= 2 && c.nqb <= nmax;
 }

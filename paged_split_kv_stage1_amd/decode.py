@@ -39,9 +39,9 @@ class PagedDecode:
 
     def stage1(self, q, q_scale, k_cache, v_cache, kv_layout: Sequence[int], k_scale, v_scale,
                scale_layout: Optional[Sequence[int]], page_indices, sm_scale: float, out, out_dtype: str,
-               stream=None):
+               out_lse=None, stream=None):
         pa_decode_stage1(self.info, self.plan, q, q_scale, k_cache, v_cache, kv_layout, k_scale, v_scale, scale_layout,
-                         page_indices, sm_scale, self.partial_o, self.partial_lse, out, out_dtype, stream)
+                         page_indices, sm_scale, self.partial_o, self.partial_lse, out, out_dtype, out_lse, stream)
 
     def merge(self, out, out_dtype: str, out_lse=None, stream=None):
         pa_decode_merge(self.info, self.plan, self.partial_o, self.partial_lse, out, out_dtype, out_lse, stream)
@@ -49,7 +49,7 @@ class PagedDecode:
     def run(self, q, q_scale, k_cache, v_cache, kv_layout, k_scale, v_scale, scale_layout, page_indices,
             sm_scale: float, out, out_dtype: str, out_lse=None, stream=None):
         self.stage1(q, q_scale, k_cache, v_cache, kv_layout, k_scale, v_scale, scale_layout, page_indices, sm_scale,
-                    out, out_dtype, stream)
+                    out, out_dtype, out_lse, stream)
         self.merge(out, out_dtype, out_lse, stream)
 
     def row_nsplit(self) -> np.ndarray:
