@@ -269,6 +269,24 @@ pa_status pa_debug_gather(const pa_plan_info* info, const void* plan_dev, const 
                           const pa_kv_layout* kv, const pa_scale_layout* sc, int64_t* kv_off_out,
                           int64_t* scale_off_out, void* stream);
 
+/* Allocation-free decode step (device), for callers that cannot allocate device memory:
+ * code under graph capture, tight serving loops, harnesses that forbid hipMalloc.  Runs
+ * pa_decode_stage1 followed by pa_decode_merge with the same arguments, except that the
+ * split partials live in a scratch array inside the library (128 MiB per GPU, held
+ * from the library's first use on that GPU until the process ends) instead of caller
+ * workspace.  The caller still passes every input and output.  Calls no allocating
+ * routine.  Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (two streams, or two threads) race and give wrong results; calls on one stream are
+ * ordered and safe.  Errors: those of stage 1 and the merge, and
+ * INSUFFICIENT_WORKSPACE when info->partial_o_bytes (rounded up to 256) plus
+ * info->partial_lse_bytes exceed the array (plan with a lower max_splits). */
+pa_status pa_decode_noalloc(const pa_plan_info* info, const void* plan_dev,
+                            const void* q, const float* q_scale,
+                            const void* k_cache, const void* v_cache, const pa_kv_layout* kv,
+                            const float* k_scale, const float* v_scale, const pa_scale_layout* sc,
+                            const int32_t* page_indices, float sm_scale,
+                            void* out, pa_dtype out_dtype, float* out_lse, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* pa_last_error(void);
 

@@ -84,7 +84,10 @@ def lib() -> ctypes.CDLL:
                                    _p, _p, ctypes.POINTER(ScaleLayout), _p]
         L.pa_debug_gather.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, ctypes.POINTER(KVLayout),
                                       ctypes.POINTER(ScaleLayout), _p, _p, _p]
-        for f in ("pa_plan_splits", "pa_decode_stage1", "pa_decode_merge", "pa_kv_quantize_fp8",
+        L.pa_decode_noalloc.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, _p, ctypes.POINTER(KVLayout), _p,
+                                        _p, ctypes.POINTER(ScaleLayout), _p, ctypes.c_float, _p, ctypes.c_int, _p,
+                                        _p]
+        for f in ("pa_plan_splits", "pa_decode_stage1", "pa_decode_merge", "pa_decode_noalloc", "pa_kv_quantize_fp8",
                   "pa_kv_quantize_fp8_per_head", "pa_kv_quantize_int8", "pa_kv_append", "pa_debug_gather"):
             getattr(L, f).restype = ctypes.c_int
         L.pa_last_error.restype = ctypes.c_char_p
@@ -155,6 +158,17 @@ def pa_decode_stage1(info, plan_dev, q, q_scale, k_cache, v_cache, kv_layout, k_
                                   None if scl is None else ctypes.byref(scl), _ptr(page_indices),
                                   ctypes.c_float(sm_scale), _ptr(partial_o), _ptr(partial_lse), _ptr(out),
                                   _dt(out_dtype), _ptr(out_lse), _stream(stream)))
+
+
+def pa_decode_noalloc(info, plan_dev, q, q_scale, k_cache, v_cache, kv_layout, k_scale, v_scale, scale_layout,
+                      page_indices, sm_scale, out, out_dtype, out_lse=None, stream=None):
+    kvl = KVLayout(*kv_layout)
+    scl = None if scale_layout is None else ScaleLayout(*scale_layout)
+    _check(lib().pa_decode_noalloc(ctypes.byref(info), _ptr(plan_dev), _ptr(q), _ptr(q_scale), _ptr(k_cache),
+                                   _ptr(v_cache), ctypes.byref(kvl), _ptr(k_scale), _ptr(v_scale),
+                                   None if scl is None else ctypes.byref(scl), _ptr(page_indices),
+                                   ctypes.c_float(sm_scale), _ptr(out), _dt(out_dtype), _ptr(out_lse),
+                                   _stream(stream)))
 
 
 def pa_decode_merge(info, plan_dev, partial_o, partial_lse, out, out_dtype, out_lse=None, stream=None):

@@ -213,6 +213,12 @@ void choose_splits(const pa_plan_args& a, const KernelCfg& cfg, const std::vecto
 
 }  // namespace
 
+namespace pa {
+// Error reporting for entry points defined in other source files (same message slot
+// that pa_last_error returns).
+int report_error(int st, const char* msg) { return (int)fail((pa_status)st, "%s", msg); }
+}  // namespace pa
+
 extern "C" {
 
 const char* pa_last_error(void) { return g_err.c_str(); }

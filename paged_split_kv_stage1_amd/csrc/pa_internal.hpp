@@ -84,6 +84,9 @@ struct GatherArgs {
   int page_shift;
 };
 
+// Sets the message pa_last_error returns and returns st (defined in api.cpp).
+int report_error(int st, const char* msg);
+
 // Launchers (defined in the .hip files); return a hipError_t as int.
 int launch_stage1(const KernelCfg& cfg, const Stage1Args& a, int num_items, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);

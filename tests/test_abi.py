@@ -311,3 +311,16 @@ def test_query_block_groups_cover_rows_x_heads():
         assert ((info.variant >> 4) & 15, (info.variant >> 8) & 15) == (4, 1)
         it, _ = _items(info, plan)
         assert it[it[:, 10] == 0][:, 11].max() == 4 * (ngrp - 1)
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    # 8 rows x 16 heads x 1024 splits x d 256 float32 partials = 128 MiB + LSE: above the
+    # allocation-free entry point's scratch array, refused before any device call
+    info, _ = _plan(B=1, rows=[8], kv=[131072], force=1024)
+    assert info.partial_o_bytes + info.partial_lse_bytes > 128 << 20
+    fake = 1 << 20
+    with pytest.raises(PaError) as e:
+        _lib.pa_decode_noalloc(info, fake, fake, None, fake, fake, (16 * 256 * 2, 16 * 256, 256), None, None, None,
+                               fake, 0.1, fake, "bf16")
+    assert e.value.status == PA_ERR_INSUFFICIENT_WORKSPACE
+    assert "scratch" in str(e.value)
