@@ -107,37 +107,66 @@ constexpr double kMergeBytesPerS = 4.0e12;   // partials are re-read from the la
 constexpr double kMergeLaunchS = 3.0e-6;
 
 // Seconds of compute per KV token for one 16-row query block per wave, one workgroup
-// in a slot, by head_dim and KV format (measured with the KV loads switched off).
+// in a slot, by head_dim and KV format (measured with the KV loads switched off; for
+// per-token scales the constant that planned the ragged group-24 mix fastest: 14, 18, 22
+// and 28 ns gave 128.5, 138.6, 119 and 118.5 us of stage 1 -- its three-block waves
+// cost more per block than the one-block shapes the first figure came from).
 double compute_s_per_token_block(const pa_plan_args& a) {
   const bool f8 = a.kv_dtype != PA_DTYPE_BF16;
   const bool pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD || a.kv_dtype == PA_DTYPE_INT8;
   const double d_scale = a.head_dim / 128.0;
   double ns;
   if (!f8) ns = 16.0;            // two-term bf16 P
-  else if (pt) ns = 14.0;        // fp8 -> bf16 upconversion of K and V
+  else if (pt) ns = 22.0;        // fp8 -> bf16 upconversion of K and V, per-token scales
   else ns = 8.0;                 // fp8 MFMA for both products
   return ns * d_scale * 1e-9;
 }
 
-void choose_splits(const pa_plan_args& a, const KernelCfg& cfg, const std::vector<int>& begin,
-                   const std::vector<int>& span, int num_cus, int split_cap, std::vector<int>* nsp) {
+// Per-request item costs of the split model.
+struct CostModel {
+  int slots = 0;
+  double bw_slot = 0, kv_tok = 0;
+  std::vector<double> comp_tok;                  // compute seconds per token of request b's items
+  std::vector<double> part;                      // partial-output bytes one item of b writes when split
+  std::vector<int> ngrp;                         // query-block groups (items per split and KV head)
+  // Seconds of one item of request b over tok tokens: its KV bytes (plus its partial
+  // output when the request is split) at the slot's share of HBM, or its compute,
+  // whichever is longer, plus a fixed prologue.
+  double item_cost(int b, double tok, bool split) const {
+    const double mem = (tok * kv_tok + (split ? part[b] : 0.0)) / bw_slot;
+    return std::max(mem, tok * comp_tok[b]) + kItemOverheadS;
+  }
+};
+
+CostModel cost_model(const pa_plan_args& a, const KernelCfg& cfg, int num_cus) {
+  CostModel m;
   const int B = a.batch;
   const int G = a.num_q_heads / a.num_kv_heads;
-  const double kv_tok = 2.0 * a.head_dim * (a.kv_dtype != PA_DTYPE_BF16 ? 1 : 2) +
-                        (a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD ? 8 : 0);
-  const int slots = (cfg.dh == 512 ? 1 : kSlotsPerCu) * num_cus;   // head_dim 512: one workgroup per CU
-  const double bw_slot = kHbmBytesPerS / slots;
+  m.kv_tok = 2.0 * a.head_dim * (a.kv_dtype != PA_DTYPE_BF16 ? 1 : 2) +
+             (a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD ? 8 : 0);
+  m.slots = (cfg.dh == 512 ? 1 : kSlotsPerCu) * num_cus;   // head_dim 512: one workgroup per CU
+  m.bw_slot = kHbmBytesPerS / m.slots;
   const int wt = 4 / cfg.wq;                     // waves sharing the tokens of a tile
   const double comp_blk = compute_s_per_token_block(a);
-  std::vector<double> comp_tok(B);               // compute seconds per token, per item of request b
-  std::vector<int> ngrp(B);                      // query-block groups (items per split and KV head)
+  m.comp_tok.resize(B);
+  m.part.resize(B);
+  m.ngrp.resize(B);
   for (int b = 0; b < B; ++b) {
-    const int nb16 = ((a.qo_indptr[b + 1] - a.qo_indptr[b]) * G + 15) / 16;
-    ngrp[b] = query_groups(a, cfg, b);
+    const int n = a.qo_indptr[b + 1] - a.qo_indptr[b];
+    const int nb16 = (n * G + 15) / 16;
+    m.ngrp[b] = query_groups(a, cfg, b);
     const int per_item = std::min(nb16, cfg.wq * cfg.nqb);
     const int rounds = (per_item + cfg.wq - 1) / cfg.wq;
-    comp_tok[b] = comp_blk * rounds / wt;
+    m.comp_tok[b] = comp_blk * rounds / wt;
+    m.part[b] = (double)std::min(n * G, 16 * per_item) * (a.head_dim * partial_o_elem_bytes(a.kv_dtype) + 4.0);
   }
+  return m;
+}
+
+void choose_splits(const pa_plan_args& a, const CostModel& cm, const std::vector<int>& span, int split_cap,
+                   std::vector<int>* nsp) {
+  const int B = a.batch;
+  const int slots = cm.slots;
   // Split counts: every request's items should cost about the same, so a request whose
   // tokens are more expensive (more 16-row query blocks per wave: compute-bound) is cut
   // into shorter splits than a memory-bound one.  The candidates are the item costs
@@ -150,8 +179,8 @@ void choose_splits(const pa_plan_args& a, const KernelCfg& cfg, const std::vecto
   int heavy_b = 0;
   for (int b = 0; b < B; ++b) {
     nblk[b] = std::max(1, (span[b] + kSplitAlign - 1) / kSplitAlign);
-    ctok[b] = std::max(kv_tok / bw_slot, comp_tok[b]);
-    const double wb = (double)span[b] * ctok[b] * ngrp[b];
+    ctok[b] = std::max(cm.kv_tok / cm.bw_slot, cm.comp_tok[b]);
+    const double wb = (double)span[b] * ctok[b] * cm.ngrp[b];
     if (wb > heavy) {
       heavy = wb;
       heavy_b = b;
@@ -168,7 +197,7 @@ void choose_splits(const pa_plan_args& a, const KernelCfg& cfg, const std::vecto
   for (int S = 1; S <= s_heavy; ++S) {
     const double target = heavy / S;
     for (int b = 0; b < B; ++b) {
-      const double wb = (double)span[b] * ctok[b] * ngrp[b];
+      const double wb = (double)span[b] * ctok[b] * cm.ngrp[b];
       const int sb = (int)std::ceil(wb / target * (1 - 1e-12));
       cur[b] = std::max(1, std::min(sb, std::min(split_cap, nblk[b])));
     }
@@ -178,17 +207,11 @@ void choose_splits(const pa_plan_args& a, const KernelCfg& cfg, const std::vecto
     double merge_bytes = 0, total = 0, longest = 0;
     for (int b = 0; b < B; ++b) {
       const int sb = cur[b];
-      const int n = a.qo_indptr[b + 1] - a.qo_indptr[b];
-      // partial bytes at 4 per element even where they are stored in bf16: with the
-      // bf16 size the model picks 1082 items for the ragged group-24 mix instead of 704,
-      // a plan that measured 148 against 140 us per step (both with float32 partials)
-      const double part = sb > 1 ? (double)n * G * (a.head_dim + 1) * 4.0 : 0.0;
-      const double tok = (double)span[b] / sb;
-      const double cost =
-          std::max(tok * kv_tok / bw_slot, tok * comp_tok[b]) + part / ngrp[b] / bw_slot + kItemOverheadS;
-      groups.push_back({cost, sb * a.num_kv_heads * ngrp[b]});
-      merge_bytes += part * sb * a.num_kv_heads;
-      total += cost * sb * a.num_kv_heads * ngrp[b];
+      const double cost = cm.item_cost(b, (double)span[b] / sb, sb > 1);
+      const int count = sb * a.num_kv_heads * cm.ngrp[b];
+      groups.push_back({cost, count});
+      if (sb > 1) merge_bytes += cm.part[b] * count;
+      total += cost * count;
       longest = std::max(longest, cost);
     }
     const double merge_t = merge_bytes > 0 ? merge_bytes / kMergeBytesPerS + kMergeLaunchS : 0.0;
@@ -311,10 +334,11 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
     span[b] = L - begin[b];
     total_tok += (int64_t)span[b] * Hkv;
   }
+  const CostModel cm = cost_model(*a, cfg, num_cus);
   if (a->force_splits > 0) {
     for (int b = 0; b < B; ++b) nsp[b] = a->force_splits;
   } else {
-    choose_splits(*a, cfg, begin, span, num_cus, split_cap, &nsp);
+    choose_splits(*a, cm, span, split_cap, &nsp);
   }
   int s_max = 1;
   int64_t n_items = 0;
@@ -394,13 +418,9 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
       }
     }
   }
-  const int G = a->num_q_heads / Hkv;
-  const int rows_per_item = 16 * cfg.wq * cfg.nqb;
-  // heaviest first: tokens x (a fixed cost + the item's own rows x heads)
-  auto weight = [G, rows_per_item](const PaItem& x) {
-    const int m = std::min(x.nrows * G - 16 * x.qblk0, rows_per_item);
-    return (int64_t)(x.tok_end - x.tok_begin) * (64 + m);
-  };
+  // heaviest first by the split model's item cost: workgroups are dispatched in order to
+  // whichever slot frees up first, which makes the launch a longest-first list schedule
+  auto weight = [&cm](const PaItem& x) { return cm.item_cost(x.req, x.tok_end - x.tok_begin, x.nsplit > 1); };
   std::stable_sort(items.begin(), items.end(),
                    [&weight](const PaItem& x, const PaItem& y) { return weight(x) > weight(y); });
   uint8_t* out = static_cast<uint8_t*>(plan_host);

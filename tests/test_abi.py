@@ -98,10 +98,12 @@ def test_plan_properties(data):
     if cap:
         assert info.max_splits <= cap
     it, _ = _items(info, plan)
-    wq_nqb = 4 if d == 512 else {1: 1, 8: 4, 24: 12}[G]                # blocks one item covers
-    m = np.minimum(it[:, 1] * G - 16 * it[:, 11], 16 * wq_nqb)          # rows x heads of the item
-    cost = (it[:, 9] - it[:, 8]).astype(np.int64) * (64 + m)
-    assert np.all(cost[:-1] >= cost[1:])                               # heaviest first
+    # heaviest first: within a request (same rows, same split status) longer items come first
+    for b in range(B):
+        for grp in np.unique(it[it[:, 10] == b, 11]):
+            sel = (it[:, 10] == b) & (it[:, 11] == grp)
+            tok = (it[sel, 9] - it[sel, 8]).astype(np.int64)
+            assert np.all(tok[:-1] >= tok[1:])
 
 
 def test_force_splits_gives_exact_count():
