@@ -35,6 +35,8 @@ WORKLOAD_NAMES = {
     "c3_b1": "MTP verify R4 B1 16/2 heads d256 ctx32768 P16 bf16 KV",
     "c3_r1": "single-row decode B16 16/2 heads d256 ctx32768 P16 bf16 KV",
     "c3_r8": "MTP verify R8 B16 16/2 heads d256 ctx32768 P16 bf16 KV",
+    "c3_b1_r1": "single-row decode B1 16/2 heads d256 ctx32768 P16 bf16 KV",
+    "c3_b1_r8": "MTP verify R8 B1 16/2 heads d256 ctx32768 P16 bf16 KV",
     "c4": "long-context R8 B16 16/2 heads d256 ctx131072 P16 e4m3 KV per-token-head",
     "c4_i8": "long-context R8 B16 16/2 heads d256 ctx131072 P16 int8 KV per-token-head",
     "c4_i8t": "long-context R8 B16 16/2 heads d256 ctx131072 P16 int8 KV per-tensor",
@@ -313,6 +315,125 @@ def _calibrate_copy():
     del src, dst
 
 
+def iqm(x):
+    x = np.sort(x)
+    n = len(x)
+    return float(np.mean(x[n // 4: n - n // 4])) if n >= 4 else float(np.mean(x))
+
+
+def time_steps(pd, step, merge, flush, stream, steps, warmup, do_flush):
+    """Warm-up steps, then ``steps`` timed steps, each after a cache-evicting write of the
+    flush buffer; HIP events on the launch stream bracket stage 1 and the merge.
+    Returns (stage-1 us per step, merge us per step, wall seconds of the timed loop)."""
+    import torch
+
+    for _ in range(warmup):
+        if do_flush:
+            flush.fill_(1.0)
+        step()
+        merge()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if do_flush:
+            flush.fill_(1.0)
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+        merge()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    s1 = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3      # us
+    if pd.info.needs_merge:
+        mg = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    else:                      # no merge launch: the second event pair brackets nothing
+        mg = np.zeros_like(s1)
+    return s1, mg, wall
+
+
+# Every configuration of the benchmark target, timed in the default run after the
+# headline: the five workloads, the batch-1 and row-count variants the R8/R1 bar compares.
+PER_CONFIG = ("c1", "c3", "c3_r1", "c3_r8", "c3_b1", "c3_b1_r1", "c3_b1_r8", "c4", "c4_r1", "c4_b1", "c4_b1_r1",
+              "c5")
+MEMORY_BOUND = {"c2", "c3", "c3_r1", "c3_r8", "c3_b1", "c3_b1_r1", "c3_b1_r8", "c4", "c4_r1", "c4_b1", "c4_b1_r1",
+                "c5"}
+R8_R1 = (("c3_r8", "c3_r1"), ("c3_b1_r8", "c3_b1_r1"), ("c4", "c4_r1"), ("c4_b1", "c4_b1_r1"))
+
+
+def arithmetic(w, variant: int) -> str:
+    """What the stage-1 kernel of this plan multiplies in, from the tile configuration."""
+    qf8, kvf8, pt = (variant >> 1) & 1, (variant >> 2) & 1, (variant >> 3) & 1
+    wq, nqb, i8 = (variant >> 4) & 15, (variant >> 8) & 15, (variant >> 12) & 1
+    one_block_waves = wq == 4 and nqb == 1
+    if not kvf8:
+        return "bf16 MFMA for q.k and P.V (P as two bf16 terms)"
+    if qf8:
+        return "e4m3 MFMA for q.k (exact products) and P.V (P as two e4m3 terms)"
+    if i8:
+        qk = ("int8 MFMA on the raw K codes, bf16 query as two int8 terms" if one_block_waves
+              else "bf16 MFMA on K converted to bf16")
+        return f"q.k: {qk}; P.V: bf16 MFMA on V converted to bf16 (P one bf16 term, v_scale folded)"
+    if pt and one_block_waves and w.head_dim in (256, 512):
+        qk = "e4m3 16x16x128 MFMA on the raw K codes, bf16 query as two e4m3 terms under a per-row scale"
+    else:
+        qk = "bf16 MFMA on K upconverted exactly from e4m3"
+    pv = ("bf16 MFMA on V upconverted exactly from e4m3 (P one bf16 term, v_scale folded)" if pt
+          else "e4m3 MFMA (P as two e4m3 terms)")
+    return f"q.k: {qk}; P.V: {pv}"
+
+
+def per_config(args, flush, stream):
+    """Stage-1 and merge times of every configuration in PER_CONFIG (same flush and events as
+    the headline; at least 20 timed and 50 warm-up steps each), with achieved GB/s against
+    8 TB/s and the R8/R1 ratios."""
+    import torch
+
+    from paged_split_kv_stage1_amd.accounting import workload_accounting
+    from paged_split_kv_stage1_amd.decode import PagedDecode
+    from paged_split_kv_stage1_amd.device_inputs import to_device
+    from paged_split_kv_stage1_amd.inputs import make_workload
+
+    res = {}
+    for name in PER_CONFIG:
+        w = make_workload(name)
+        di = to_device(w, "cuda:0")
+        acc = workload_accounting(w)
+        pd = PagedDecode(w.qo_indptr, w.kv_indptr, w.kv_len, w.window, w.max_q_len, w.page_size, w.num_q_heads,
+                         w.num_kv_heads, w.head_dim, w.q_dtype, w.kv_dtype, w.kv_scale_mode, di.q.device,
+                         force_splits=w.forced_splits)
+        out = torch.empty(w.total_rows, w.num_q_heads, w.head_dim,
+                          dtype=torch.float32 if w.out_dtype == "fp32" else torch.bfloat16, device=di.q.device)
+
+        def step():
+            pd.stage1(di.q, di.q_scale, di.k, di.v, di.kv_layout, di.k_scale, di.v_scale, di.scale_layout,
+                      di.page_indices, w.sm_scale, out, w.out_dtype, stream=stream)
+
+        def merge():
+            pd.merge(out, w.out_dtype, stream=stream)
+
+        # at least 50 warm-up steps: the compute-heavy shapes need that many back-to-back
+        # steps before the clocks settle, whatever the headline's own warm-up count is
+        s1, mg, _ = time_steps(pd, step, merge, flush, stream, max(args.steps, 20), max(args.warmup, 50),
+                               not args.no_flush)
+        tot = float(np.mean(s1 + mg))
+        gbps = acc["bytes"] / (tot * 1e-6) / 1e9
+        res[name] = {"workload": WORKLOAD_NAMES[name], "stage1_us": round(float(np.mean(s1)), 2),
+                     "merge_us": round(float(np.mean(mg)), 2), "us_per_step": round(tot, 2),
+                     "algorithmic_bytes": acc["bytes"], "gbps": round(gbps, 1),
+                     "frac_of_8tbs": round(gbps / HBM_PEAK_GBPS, 4), "work_items": pd.num_items,
+                     "max_splits": pd.max_splits, "arithmetic": arithmetic(w, int(pd.info.variant))}
+        if name in MEMORY_BOUND:
+            res[name]["meets_70pct"] = bool(gbps >= 0.7 * HBM_PEAK_GBPS)
+        del di, out, pd
+        torch.cuda.empty_cache()
+    ratios = {f"{r8}/{r1}": round(res[r8]["us_per_step"] / res[r1]["us_per_step"], 3)
+              for r8, r1 in R8_R1 if r8 in res and r1 in res}
+    return res, ratios
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,6 +450,8 @@ def main():
     ap.add_argument("--op", default="decode", choices=["decode", "kv_append", "kv_quantize"],
                     help="decode (stage 1 + merge), or the cache-side append / quantiser on the workload's geometry")
     ap.add_argument("--tokens", type=int, default=131072, help="tokens appended or quantised per step (cache ops)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the headline workload (skip the per_config object of every configuration)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first, as a known-size reference for HBM counters")
     args = ap.parse_args()
@@ -373,37 +496,8 @@ def main():
         pd.merge(out, w.out_dtype, stream=st)
 
     _spin_up(flush)
-    for _ in range(args.warmup):
-        if not args.no_flush:
-            flush.fill_(1.0)
-        step()
-        merge()
-    torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if not args.no_flush:
-            flush.fill_(1.0)
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-        merge()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    s1 = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3      # us
-    if pd.info.needs_merge:
-        mg = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
-    else:                      # no merge launch: the second event pair brackets nothing
-        mg = np.zeros_like(s1)
+    s1, mg, wall = time_steps(pd, step, merge, flush, stream, args.steps, args.warmup, not args.no_flush)
     tot = s1 + mg
-
-    def iqm(x):
-        x = np.sort(x)
-        n = len(x)
-        return float(np.mean(x[n // 4: n - n // 4])) if n >= 4 else float(np.mean(x))
 
     graph = None
     if args.graph_reps > 0:
@@ -439,8 +533,8 @@ def main():
     result = {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(us_step / 1e3, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": ("bf16" if w.kv_dtype == "bf16" else "int8 (bf16 MFMA)" if w.kv_dtype == "int8" else
-                  "fp8-e4m3 (bf16 MFMA)" if w.q_dtype != "fp8" else "fp8-e4m3"),
+        "vs_baseline": None, "dtype": ("bf16" if w.kv_dtype == "bf16" else "int8" if w.kv_dtype == "int8" else "fp8-e4m3"),
+        "arithmetic": arithmetic(w, int(pd.info.variant)),
         "data": "synthetic (seeded N(0,1), random page permutation)",
         "config": {"workload": WORKLOAD_NAMES[args.config], "name": args.config, "batch": w.batch,
                    "total_rows": w.total_rows, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
@@ -457,6 +551,8 @@ def main():
                      "frac": round(roof_achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(args.config),
                      "kernel": "stage1_kernel", "bytes_per_launch": s1_bytes},
     }
+    if not args.no_per_config and args.config == "c2":
+        result["per_config"], result["r8_over_r1"] = per_config(args, flush, stream)
     if not args.no_cpu_baseline:
         out_np = out.float().cpu().numpy().astype(np.float64)
         cb, err = cpu_baseline(w, out_np, args.cpu_budget)

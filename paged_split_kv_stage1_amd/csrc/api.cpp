@@ -418,9 +418,16 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
       }
     }
   }
-  // heaviest first by the split model's item cost: workgroups are dispatched in order to
-  // whichever slot frees up first, which makes the launch a longest-first list schedule
-  auto weight = [&cm](const PaItem& x) { return cm.item_cost(x.req, x.tok_end - x.tok_begin, x.nsplit > 1); };
+  // heaviest first: workgroups are dispatched in order to whichever slot frees up first,
+  // which makes the launch a longest-first list schedule.  The weight is tokens x (a fixed
+  // cost + the item's own rows x heads): on the ragged group-24 mix this order measured
+  // 119 us of stage 1 against 137 us when ordered by the split model's item cost.
+  const int G = a->num_q_heads / Hkv;
+  const int rows_per_item = 16 * cfg.wq * cfg.nqb;
+  auto weight = [G, rows_per_item](const PaItem& x) {
+    const int m = std::min(x.nrows * G - 16 * x.qblk0, rows_per_item);
+    return (int64_t)(x.tok_end - x.tok_begin) * (64 + m);
+  };
   std::stable_sort(items.begin(), items.end(),
                    [&weight](const PaItem& x, const PaItem& y) { return weight(x) > weight(y); });
   uint8_t* out = static_cast<uint8_t*>(plan_host);

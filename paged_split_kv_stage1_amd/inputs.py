@@ -86,6 +86,10 @@ CONFIGS = {
                   scale="none", out="bf16"),
     "c3_r1": dict(batch=16, rows=1, hq=16, hkv=2, d=256, ctx=32768, page=16, q="bf16", kv="bf16",
                   scale="none", out="bf16"),
+    "c3_b1_r1": dict(batch=1, rows=1, hq=16, hkv=2, d=256, ctx=32768, page=16, q="bf16", kv="bf16",
+                     scale="none", out="bf16"),
+    "c3_b1_r8": dict(batch=1, rows=8, hq=16, hkv=2, d=256, ctx=32768, page=16, q="bf16", kv="bf16",
+                     scale="none", out="bf16"),
     "c3_r8": dict(batch=16, rows=8, hq=16, hkv=2, d=256, ctx=32768, page=16, q="bf16", kv="bf16",
                   scale="none", out="bf16"),
     "c4": dict(batch=16, rows=8, hq=16, hkv=2, d=256, ctx=131072, page=16, q="bf16", kv="fp8",
