@@ -269,6 +269,17 @@ pa_status pa_debug_gather(const pa_plan_info* info, const void* plan_dev, const 
                           const pa_kv_layout* kv, const pa_scale_layout* sc, int64_t* kv_off_out,
                           int64_t* scale_off_out, void* stream);
 
+/* Debug check (device; synchronises the stream): every page-table entry that the plan's
+ * work items read (page_indices[kv_indptr[b] + t / P] for the tokens t of each item) must
+ * lie in [0, num_pages), num_pages being the number of pages the K and V caches hold.
+ * Stage 1 never checks page numbers, so an entry outside the caches would make it read
+ * outside them; run this check first where the page table is not trusted (the Python
+ * binding runs it before every stage 1 when the environment sets PA_VALIDATE=1).
+ * Returns INVALID_ARGUMENT naming the count and the first offending position, PA_OK
+ * otherwise, or PA_ERR_HIP.  Not graph-capturable (it waits for its result). */
+pa_status pa_validate_page_indices(const pa_plan_info* info, const void* plan_dev, const int32_t* page_indices,
+                                   int64_t num_pages, void* stream);
+
 /* Allocation-free decode step (device), for callers that cannot allocate device memory:
  * code under graph capture, tight serving loops, harnesses that forbid hipMalloc.  Runs
  * pa_decode_stage1 followed by pa_decode_merge with the same arguments, except that the

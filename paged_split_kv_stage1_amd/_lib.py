@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
                                    _p, _p, ctypes.POINTER(ScaleLayout), _p]
         L.pa_debug_gather.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, ctypes.POINTER(KVLayout),
                                       ctypes.POINTER(ScaleLayout), _p, _p, _p]
+        L.pa_validate_page_indices.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, ctypes.c_int64, _p]
+        L.pa_validate_page_indices.restype = ctypes.c_int
         L.pa_decode_noalloc.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, _p, ctypes.POINTER(KVLayout), _p,
                                         _p, ctypes.POINTER(ScaleLayout), _p, ctypes.c_float, _p, ctypes.c_int, _p,
                                         _p]
@@ -158,6 +160,11 @@ def pa_decode_stage1(info, plan_dev, q, q_scale, k_cache, v_cache, kv_layout, k_
                                   None if scl is None else ctypes.byref(scl), _ptr(page_indices),
                                   ctypes.c_float(sm_scale), _ptr(partial_o), _ptr(partial_lse), _ptr(out),
                                   _dt(out_dtype), _ptr(out_lse), _stream(stream)))
+
+
+def pa_validate_page_indices(info, plan_dev, page_indices, num_pages, stream=None):
+    _check(lib().pa_validate_page_indices(ctypes.byref(info), _ptr(plan_dev), _ptr(page_indices),
+                                          ctypes.c_int64(int(num_pages)), _stream(stream)))
 
 
 def pa_decode_noalloc(info, plan_dev, q, q_scale, k_cache, v_cache, kv_layout, k_scale, v_scale, scale_layout,

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa_gfx950.so")
-SOURCES = ["api.cpp", "stage1.hip", "merge.hip", "quant.hip", "gather.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "stage1.hip", "merge.hip", "quant.hip", "gather.hip", "noalloc.hip", "validate.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # keep hipcc from emitting packed fp32 ops (v_pk_*_f32)

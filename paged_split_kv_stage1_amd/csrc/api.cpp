@@ -47,10 +47,45 @@ int ilog2_exact(int v) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Enum arguments come from C callers and may hold any int: read them as their int bits
+// (loading an out-of-range value as a C++ enum is undefined), and validate before use.
+template <class E>
+int raw(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "enum arguments are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 // Partial outputs of split requests: float32, except with one-byte KV codes (FP8, INT8),
 // whose bar (2e-2) leaves room for bf16 partials (2^-9 relative) and half the bytes
 // written by stage 1 and read back by the merge.
 int partial_o_elem_bytes(int kv_dtype) { return kv_dtype == PA_DTYPE_BF16 ? 4 : 2; }
+
+}  // namespace
+
+namespace pa {
+// Tile configurations stage 1 is instantiated for (its dispatcher in stage1.hip uses the
+// same list).
+bool stage1_cfg_supported(const KernelCfg& c) {
+  // head_dim 512: bf16 KV, or per-token-head FP8 KV with bf16 queries; up to four 16-row
+  // query blocks (one per wave), one workgroup per CU (its accumulators and query
+  // operand need the whole register file of a SIMD)
+  if (c.dh == 512)
+    return !c.qf8 && !c.i8 && (c.kvf8 ? c.pt : !c.pt) && c.wq == 4 && c.nqb == 1;
+  if (c.dh != 128 && c.dh != 256) return false;
+  if (c.qf8 && !c.kvf8) return false;
+  if (!c.kvf8 && c.pt) return false;
+  if (c.i8 && (!c.kvf8 || !c.pt || c.qf8)) return false;    // INT8 KV: bf16 queries, per-token scale path
+  const bool pv_fp8 = c.kvf8 && !c.pt;
+  if (c.dh == 256 && pv_fp8 && !c.qf8 && c.wq == 2) return false;
+  const int nmax = c.dh == 128 ? (pv_fp8 ? 2 : 3) : 1;
+  if (c.nqb == 1) return (c.wq == 1 && c.dh == 128) || c.wq == 2 || c.wq == 4;
+  return c.wq == 4 && c.nqb >= 2 && c.nqb <= nmax;
+}
+}  // namespace pa
+
+namespace {
 
 // Tile configuration for the planned shape.
 bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
@@ -239,7 +274,10 @@ void choose_splits(const pa_plan_args& a, const CostModel& cm, const std::vector
 namespace pa {
 // Error reporting for entry points defined in other source files (same message slot
 // that pa_last_error returns).
-int report_error(int st, const char* msg) { return (int)fail((pa_status)st, "%s", msg); }
+int report_error(int st, const char* msg) {
+  if (st == PA_OK) return (int)ok();
+  return (int)fail((pa_status)st, "%s", msg);
+}
 }  // namespace pa
 
 extern "C" {
@@ -265,19 +303,20 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   const int page_shift = ilog2_exact(a->page_size);
   if (page_shift < 4 || a->page_size > 1024)
     return fail(PA_ERR_UNSUPPORTED, "page_size %d: must be a power of two in [16, 1024]", a->page_size);
-  if (a->q_dtype != PA_DTYPE_BF16 && a->q_dtype != PA_DTYPE_FP8_E4M3)
+  const int qd = raw(a->q_dtype), kd = raw(a->kv_dtype), sm = raw(a->kv_scale_mode);
+  if (qd != PA_DTYPE_BF16 && qd != PA_DTYPE_FP8_E4M3)
     return fail(PA_ERR_INVALID_ARGUMENT, "q_dtype must be BF16 or FP8_E4M3");
-  if (a->kv_dtype != PA_DTYPE_BF16 && a->kv_dtype != PA_DTYPE_FP8_E4M3 && a->kv_dtype != PA_DTYPE_INT8)
+  if (kd != PA_DTYPE_BF16 && kd != PA_DTYPE_FP8_E4M3 && kd != PA_DTYPE_INT8)
     return fail(PA_ERR_INVALID_ARGUMENT, "kv_dtype must be BF16, FP8_E4M3 or INT8");
-  if (a->kv_dtype == PA_DTYPE_BF16 && a->kv_scale_mode != PA_SCALE_NONE)
+  if (kd == PA_DTYPE_BF16 && sm != PA_SCALE_NONE)
     return fail(PA_ERR_INVALID_ARGUMENT, "bf16 KV takes kv_scale_mode NONE");
-  if (a->kv_dtype == PA_DTYPE_FP8_E4M3 && a->kv_scale_mode != PA_SCALE_PER_TENSOR &&
-      a->kv_scale_mode != PA_SCALE_PER_HEAD && a->kv_scale_mode != PA_SCALE_PER_TOKEN_HEAD)
+  if (kd == PA_DTYPE_FP8_E4M3 && sm != PA_SCALE_PER_TENSOR &&
+      sm != PA_SCALE_PER_HEAD && sm != PA_SCALE_PER_TOKEN_HEAD)
     return fail(PA_ERR_INVALID_ARGUMENT, "FP8 KV takes kv_scale_mode PER_TENSOR, PER_HEAD or PER_TOKEN_HEAD");
-  if (a->kv_dtype == PA_DTYPE_INT8 && a->kv_scale_mode != PA_SCALE_PER_TENSOR &&
-      a->kv_scale_mode != PA_SCALE_PER_TOKEN_HEAD)
+  if (kd == PA_DTYPE_INT8 && sm != PA_SCALE_PER_TENSOR &&
+      sm != PA_SCALE_PER_TOKEN_HEAD)
     return fail(PA_ERR_INVALID_ARGUMENT, "INT8 KV takes kv_scale_mode PER_TENSOR or PER_TOKEN_HEAD");
-  if (a->q_dtype == PA_DTYPE_FP8_E4M3 && a->kv_dtype != PA_DTYPE_FP8_E4M3)
+  if (qd == PA_DTYPE_FP8_E4M3 && kd != PA_DTYPE_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "FP8 queries need an FP8 KV cache");
   if (a->max_splits < 0 || a->force_splits < 0 || a->num_cus < 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "max_splits, force_splits and num_cus must be >= 0");
@@ -445,7 +484,7 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const
                            float* out_lse, void* stream) {
   if (!info || !plan_dev || !q || !k_cache || !v_cache || !kv || !page_indices || !out)
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_stage1: a required pointer is NULL");
-  if (out_dtype != PA_DTYPE_BF16 && out_dtype != PA_DTYPE_FP32)
+  if (raw(out_dtype) != PA_DTYPE_BF16 && raw(out_dtype) != PA_DTYPE_FP32)
     return fail(PA_ERR_INVALID_ARGUMENT, "out_dtype must be BF16 or FP32");
   const KernelCfg cfg = unpack_cfg(info->variant);
   if (!stage1_cfg_supported(cfg) || cfg.dh != info->head_dim)
@@ -504,7 +543,7 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const
 pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev, const void* partial_o,
                           const float* partial_lse, void* out, pa_dtype out_dtype, float* out_lse, void* stream) {
   if (!info || !plan_dev || !out) return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_merge: a required pointer is NULL");
-  if (out_dtype != PA_DTYPE_BF16 && out_dtype != PA_DTYPE_FP32)
+  if (raw(out_dtype) != PA_DTYPE_BF16 && raw(out_dtype) != PA_DTYPE_FP32)
     return fail(PA_ERR_INVALID_ARGUMENT, "out_dtype must be BF16 or FP32");
   if (!info->needs_merge) return ok();
   if (!partial_o || !partial_lse) return fail(PA_ERR_INVALID_ARGUMENT, "partial_o and partial_lse are required");
@@ -531,9 +570,9 @@ pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev, const 
 pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows, int32_t head_dim,
                              pa_scale_mode mode, uint8_t* dst, float* scale, void* stream) {
   if (!src || !dst || !scale) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_quantize_fp8: NULL pointer");
-  if (src_dtype != PA_DTYPE_BF16 && src_dtype != PA_DTYPE_FP32)
+  if (raw(src_dtype) != PA_DTYPE_BF16 && raw(src_dtype) != PA_DTYPE_FP32)
     return fail(PA_ERR_INVALID_ARGUMENT, "src_dtype must be BF16 or FP32");
-  if (mode != PA_SCALE_PER_TENSOR && mode != PA_SCALE_PER_TOKEN_HEAD)   // per-head: pa_kv_quantize_fp8_per_head
+  if (raw(mode) != PA_SCALE_PER_TENSOR && raw(mode) != PA_SCALE_PER_TOKEN_HEAD)   // per-head: pa_kv_quantize_fp8_per_head
     return fail(PA_ERR_INVALID_ARGUMENT, "mode must be PER_TENSOR or PER_TOKEN_HEAD");
   if (n_rows < 0) return fail(PA_ERR_INVALID_ARGUMENT, "n_rows must be >= 0");
   if (head_dim < 64 || head_dim > 1024 || ilog2_exact(head_dim / 64) < 0 || head_dim % 64)
@@ -549,9 +588,9 @@ pa_status pa_kv_quantize_fp8(const void* src, pa_dtype src_dtype, int64_t n_rows
 pa_status pa_kv_quantize_int8(const void* src, pa_dtype src_dtype, int64_t n_rows, int32_t head_dim,
                               pa_scale_mode mode, int8_t* dst, float* scale, void* stream) {
   if (!src || !dst || !scale) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_quantize_int8: NULL pointer");
-  if (src_dtype != PA_DTYPE_BF16 && src_dtype != PA_DTYPE_FP32)
+  if (raw(src_dtype) != PA_DTYPE_BF16 && raw(src_dtype) != PA_DTYPE_FP32)
     return fail(PA_ERR_INVALID_ARGUMENT, "src_dtype must be BF16 or FP32");
-  if (mode != PA_SCALE_PER_TENSOR && mode != PA_SCALE_PER_TOKEN_HEAD)
+  if (raw(mode) != PA_SCALE_PER_TENSOR && raw(mode) != PA_SCALE_PER_TOKEN_HEAD)
     return fail(PA_ERR_INVALID_ARGUMENT, "mode must be PER_TENSOR or PER_TOKEN_HEAD");
   if (n_rows < 0) return fail(PA_ERR_INVALID_ARGUMENT, "n_rows must be >= 0");
   if (head_dim < 64 || head_dim > 1024 || ilog2_exact(head_dim / 64) < 0 || head_dim % 64)
@@ -567,7 +606,7 @@ pa_status pa_kv_quantize_int8(const void* src, pa_dtype src_dtype, int64_t n_row
 pa_status pa_kv_quantize_fp8_per_head(const void* src, pa_dtype src_dtype, int64_t n_tokens, int32_t num_heads,
                                       int32_t head_dim, uint8_t* dst, float* scale, void* stream) {
   if (!src || !dst || !scale) return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_quantize_fp8_per_head: NULL pointer");
-  if (src_dtype != PA_DTYPE_BF16 && src_dtype != PA_DTYPE_FP32)
+  if (raw(src_dtype) != PA_DTYPE_BF16 && raw(src_dtype) != PA_DTYPE_FP32)
     return fail(PA_ERR_INVALID_ARGUMENT, "src_dtype must be BF16 or FP32");
   if (n_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "n_tokens must be >= 0");
   if (num_heads < 1 || num_heads > 1024)
@@ -588,14 +627,15 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, pa_dtype src_dtype,
                        void* stream) {
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !kv)
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: NULL pointer");
-  if (src_dtype != PA_DTYPE_BF16 && src_dtype != PA_DTYPE_FP32)
+  if (raw(src_dtype) != PA_DTYPE_BF16 && raw(src_dtype) != PA_DTYPE_FP32)
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_kv_append: src_dtype must be BF16 or FP32");
   int m;
-  if (kv_dtype == PA_DTYPE_BF16 && mode == PA_SCALE_NONE) m = 0;
-  else if (kv_dtype == PA_DTYPE_FP8_E4M3 && (mode == PA_SCALE_PER_TENSOR || mode == PA_SCALE_PER_HEAD)) m = 1;
-  else if (kv_dtype == PA_DTYPE_FP8_E4M3 && mode == PA_SCALE_PER_TOKEN_HEAD) m = 2;
-  else if (kv_dtype == PA_DTYPE_INT8 && mode == PA_SCALE_PER_TENSOR) m = 1;
-  else if (kv_dtype == PA_DTYPE_INT8 && mode == PA_SCALE_PER_TOKEN_HEAD) m = 2;
+  const int kd = raw(kv_dtype), md = raw(mode);
+  if (kd == PA_DTYPE_BF16 && md == PA_SCALE_NONE) m = 0;
+  else if (kd == PA_DTYPE_FP8_E4M3 && (md == PA_SCALE_PER_TENSOR || md == PA_SCALE_PER_HEAD)) m = 1;
+  else if (kd == PA_DTYPE_FP8_E4M3 && md == PA_SCALE_PER_TOKEN_HEAD) m = 2;
+  else if (kd == PA_DTYPE_INT8 && md == PA_SCALE_PER_TENSOR) m = 1;
+  else if (kd == PA_DTYPE_INT8 && md == PA_SCALE_PER_TOKEN_HEAD) m = 2;
   else return fail(PA_ERR_INVALID_ARGUMENT,
                    "pa_kv_append: kv_dtype/mode must be BF16/NONE, FP8 with PER_TENSOR, PER_HEAD or PER_TOKEN_HEAD, "
                    "or INT8 with PER_TENSOR or PER_TOKEN_HEAD");

@@ -879,23 +879,6 @@ static int dispatch_modes(const KernelCfg& c, const Stage1Args& a, int n, void* 
   return (int)hipErrorInvalidValue;
 }
 
-bool stage1_cfg_supported(const KernelCfg& c) {
-  // head_dim 512: bf16 KV, or per-token-head FP8 KV with bf16 queries; up to four 16-row
-  // query blocks (one per wave), one workgroup per CU (its accumulators and query
-  // operand need the whole register file of a SIMD)
-  if (c.dh == 512)
-    return !c.qf8 && !c.i8 && (c.kvf8 ? c.pt : !c.pt) && c.wq == 4 && c.nqb == 1;
-  if (c.dh != 128 && c.dh != 256) return false;
-  if (c.qf8 && !c.kvf8) return false;
-  if (!c.kvf8 && c.pt) return false;
-  if (c.i8 && (!c.kvf8 || !c.pt || c.qf8)) return false;    // INT8 KV: bf16 queries, per-token scale path
-  const bool pv_fp8 = c.kvf8 && !c.pt;
-  if (c.dh == 256 && pv_fp8 && !c.qf8 && c.wq == 2) return false;
-  const int nmax = c.dh == 128 ? (pv_fp8 ? 2 : 3) : 1;
-  if (c.nqb == 1) return (c.wq == 1 && c.dh == 128) || c.wq == 2 || c.wq == 4;
-  return c.wq == 4 && c.nqb >= 2 && c.nqb <= nmax;
-}
-
 int launch_stage1(const KernelCfg& c, const Stage1Args& a, int num_items, void* stream) {
   if (num_items <= 0) return 0;
   if (c.dh == 128) return dispatch_modes<128>(c, a, num_items, stream);

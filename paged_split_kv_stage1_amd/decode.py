@@ -1,12 +1,13 @@
 """One decode step = plan (host) + stage 1 + merge, with torch providing device memory."""
 from __future__ import annotations
 
+import os
 from typing import Optional, Sequence
 
 import numpy as np
 import torch
 
-from ._lib import pa_decode_merge, pa_decode_stage1, pa_plan_splits
+from ._lib import pa_decode_merge, pa_decode_stage1, pa_plan_splits, pa_validate_page_indices
 
 
 class PagedDecode:
@@ -40,6 +41,8 @@ class PagedDecode:
     def stage1(self, q, q_scale, k_cache, v_cache, kv_layout: Sequence[int], k_scale, v_scale,
                scale_layout: Optional[Sequence[int]], page_indices, sm_scale: float, out, out_dtype: str,
                out_lse=None, stream=None):
+        if os.environ.get("PA_VALIDATE") == "1":         # page numbers must lie inside the caches
+            pa_validate_page_indices(self.info, self.plan, page_indices, k_cache.shape[0], stream)
         pa_decode_stage1(self.info, self.plan, q, q_scale, k_cache, v_cache, kv_layout, k_scale, v_scale, scale_layout,
                          page_indices, sm_scale, self.partial_o, self.partial_lse, out, out_dtype, out_lse, stream)
 
