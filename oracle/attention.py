@@ -11,7 +11,10 @@ the paged, block-size-64 FP8 decode it extends):
     K/V values dequantised first (FP8 dequantisation folded into the scores and
     into the final normaliser is the same arithmetic, FlashInfer PR #869 item 3);
   * split-KV: stage 1 produces, per KV split, the normalised partial output and
-    its log-sum-exp; stage 2 merges the splits of each row.
+    its log-sum-exp; stage 2 merges the splits of each row;
+  * keys and values may have different widths (FlashInfer PR #869, "Remaining Work":
+    separate head_dim_qk and head_dim_v): the scores use the key width, the output has
+    the value width; the MLA-style latent cache (LatentKV) is one such case.
 
 Readings (where the pages are silent):
   * row r of request b sits at position p = kv_len - n_b + r;
@@ -96,6 +99,65 @@ class PagedKV:
         return val
 
 
+@dataclasses.dataclass
+class LatentKV:
+    """MLA-style paged cache (FlashMLA PR #54, review thread: the no-position ("nope")
+    part in 8 bits with one scale per token and 128 channels, the rotary part kept in
+    16 bits): per (page, KV head, slot) a latent row of e4m3 codes with one float32 scale
+    per 128 channels, plus a bf16 rotary row.  The key is [latent, rotary] and the value
+    is the latent alone (the absorbed form of multi-head latent attention).
+
+    codes: uint8 [pages, Hkv, P, dv]; scale: float32 [pages, Hkv, P, dv / 128];
+    rope: bf16 bits [pages, Hkv, P, dr]."""
+    codes: np.ndarray
+    scale: np.ndarray
+    rope: np.ndarray
+
+    def latent(self, slots: np.ndarray, g: int) -> np.ndarray:
+        """Dequantised float64 [len(slots), dv]: code times its 128-channel block's scale."""
+        P = self.codes.shape[2]
+        page, slot = slots // P, slots % P
+        codes = e4m3_code_to_f64(self.codes[page, g, slot, :])
+        sc = np.asarray(self.scale[page, g, slot, :], dtype=np.float32).astype(np.float64)
+        return (codes.reshape(len(slots), -1, 128) * sc[:, :, None]).reshape(len(slots), -1)
+
+    def key_view(self):
+        return _LatentView(self, with_rope=True)
+
+    def value_view(self):
+        return _LatentView(self, with_rope=False)
+
+
+class _LatentView:
+    """Key ([latent, rotary]) or value (latent) side of a LatentKV, with the interface of
+    PagedKV that decode_attention uses (tokens, data shape [pages, Hkv, P, ...], page_size)."""
+
+    def __init__(self, kv: LatentKV, with_rope: bool):
+        self.kv, self.with_rope = kv, with_rope
+        self.data, self.layout = kv.codes, "HPD"
+
+    @property
+    def page_size(self) -> int:
+        return self.kv.codes.shape[2]
+
+    def tokens(self, slots: np.ndarray, g: int) -> np.ndarray:
+        lat = self.kv.latent(slots, g)
+        if not self.with_rope:
+            return lat
+        P = self.page_size
+        rope = bf16_bits_to_f64(self.kv.rope[slots // P, g, slots % P, :])
+        return np.concatenate([lat, rope], axis=1)
+
+
+def dequant_q_latent(codes: np.ndarray, scale: np.ndarray, rope_bits: np.ndarray) -> np.ndarray:
+    """MLA query [T, Hq, dv + dr] in float64: e4m3 codes [T, Hq, dv] times the scale of
+    their 128-channel block ([T, Hq, dv / 128]), followed by the bf16 rotary part."""
+    T, H, dv = codes.shape
+    lat = e4m3_code_to_f64(codes).reshape(T, H, dv // 128, 128) * \
+        np.asarray(scale, dtype=np.float32).astype(np.float64)[..., None]
+    return np.concatenate([lat.reshape(T, H, dv), bf16_bits_to_f64(rope_bits)], axis=2)
+
+
 def dequant_q(q_raw: np.ndarray, q_dtype: str, q_scale=None) -> np.ndarray:
     """Query [T, Hq, d] -> float64: bf16 bits, or e4m3 codes times a per-tensor scale
     (a scalar) or per-query-head scales ([Hq])."""
@@ -128,7 +190,8 @@ def decode_attention(q64: np.ndarray, kc: PagedKV, vc: PagedKV, page_indices, kv
     Hkv = kc.data.shape[1] if kc.layout == "HPD" else kc.data.shape[2]
     G = Hq // Hkv
     P = kc.page_size
-    out = np.full((T, Hq, d), np.nan)
+    dv = vc.data.shape[-1]                     # value width (may differ from the key width d)
+    out = np.full((T, Hq, dv), np.nan)
     lse = np.full((T, Hq), np.nan)
     B = len(kv_len)
     window = np.zeros(B, dtype=np.int64) if window is None else window
@@ -173,7 +236,7 @@ def split_partials(q64: np.ndarray, kc: PagedKV, vc: PagedKV, page_indices, kv_i
     slots = gather_slots(kv_indptr, page_indices, kv_len, kc.page_size, b)
     t0, n = int(qo_indptr[b]), int(qo_indptr[b + 1] - qo_indptr[b])
     S = len(splits)
-    o_out = np.zeros((n, Hq, S, d))
+    o_out = np.zeros((n, Hq, S, vc.data.shape[-1]))
     l_out = np.full((n, Hq, S), -np.inf)
     w = 0 if window is None else int(window[b])
     for g in range(Hkv):

@@ -57,6 +57,12 @@ class Workload:
     out_dtype: str             # "fp32" | "bf16"
     sm_scale: float            # float32 value of 1/sqrt(d)
     forced_splits: int = 0     # 0 = planner decides
+    head_dim_v: int = 0        # value width when it differs from head_dim (the key width); 0 = same
+    latent: bool = False       # MLA-style cache: k holds [latent (head_dim_v), rotary]; v is the latent
+
+    @property
+    def dv(self) -> int:
+        return self.head_dim_v or self.head_dim
 
     @property
     def total_rows(self) -> int:
@@ -117,9 +123,23 @@ CONFIGS = {
                   scale="per_token_head", out="bf16"),
     "c5": dict(batch=64, rows="ragged", hq=48, hkv=2, d=128, ctx="loguniform", page=32, q="bf16",
                kv="fp8", scale="per_token_head", out="bf16", windowed=True, window=64),
+    # keys wider than values (FlashInfer PR #869, "Remaining Work"): 192-channel keys (128 +
+    # a 64-channel rotary part, the split the pages' MLA model family uses) and 128-channel
+    # values, bf16, grouped query heads
+    "f3": dict(batch=32, rows=1, hq=32, hkv=4, d=192, dv=128, ctx=8192, page=16, q="bf16", kv="bf16",
+               scale="none", out="bf16"),
+    "f3_r4": dict(batch=32, rows=4, hq=32, hkv=4, d=192, dv=128, ctx=8192, page=16, q="bf16", kv="bf16",
+                  scale="none", out="bf16"),
+    # MLA-style decode (FlashMLA PR #54): one latent KV head of 512 e4m3 channels with a scale
+    # per (token, 128 channels) plus 64 bf16 rotary channels; queries likewise (nope part
+    # e4m3 per 128 channels, rotary bf16); 16 query heads; block size 64; values = latent
+    "mla": dict(batch=64, rows=1, hq=16, hkv=1, d=576, dv=512, ctx=4096, page=64, q="fp8", kv="fp8",
+                scale="per_token_block128", out="bf16", latent=True),
+    "mla_r2": dict(batch=64, rows=2, hq=16, hkv=1, d=576, dv=512, ctx=4096, page=64, q="fp8", kv="fp8",
+                   scale="per_token_block128", out="bf16", latent=True),
 }
 
-SEEDS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "c6": 6}
+SEEDS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "c6": 6, "f3": 7, "mla": 8}
 
 
 def _seed_for(name: str) -> int:
@@ -189,9 +209,13 @@ def make_workload(name: str, seed: Optional[int] = None, *, batch: Optional[int]
     page_indices = perm.astype(np.int32)
 
     T = int(qo_indptr[-1])
+    dv = cfg.get("dv", d)
     q = torch.randn(T, hq, d, generator=gen, dtype=torch.float32).to(torch.bfloat16)
     k = torch.randn(num_pages, hkv, P, d, generator=gen, dtype=torch.float32).to(torch.bfloat16)
-    v = torch.randn(num_pages, hkv, P, d, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    if cfg.get("latent"):
+        v = k[..., :dv]                  # the value is the key's latent part
+    else:
+        v = torch.randn(num_pages, hkv, P, dv, generator=gen, dtype=torch.float32).to(torch.bfloat16)
 
     unused = np.zeros((num_pages, P), dtype=bool)
     for b in range(B):
@@ -208,7 +232,7 @@ def make_workload(name: str, seed: Optional[int] = None, *, batch: Optional[int]
         q_dtype=cfg["q"], kv_dtype=cfg["kv"], kv_scale_mode=cfg["scale"],
         out_dtype=cfg["out"] if out_dtype is None else out_dtype,
         sm_scale=float(np.float32(1.0) / np.sqrt(np.float32(d))),
-        forced_splits=cfg.get("splits", 0))
+        forced_splits=cfg.get("splits", 0), head_dim_v=dv if dv != d else 0, latent=bool(cfg.get("latent")))
 
 
 # Byte patterns used to poison slots that hold no token: a NaN in each format, and for

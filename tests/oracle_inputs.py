@@ -3,7 +3,7 @@ oracle's own quantiser and poisoned exactly like the device copy."""
 import numpy as np
 import torch
 
-from oracle.attention import PagedKV, dequant_q
+from oracle.attention import LatentKV, PagedKV, dequant_q, dequant_q_latent
 from oracle.quantize import (quantize_int8_per_row, quantize_int8_per_tensor, quantize_per_head, quantize_per_row,
                              quantize_per_tensor)
 from paged_split_kv_stage1_amd.inputs import BF16_NAN_BITS, E4M3_NAN_CODE, INT8_POISON_CODE
@@ -25,6 +25,26 @@ def oracle_inputs(w, layout="HPD", requests=None):
     m4 = unused[:, None, :, None] if layout == "HPD" else unused[:, :, None, None]
     m3 = unused[:, None, :] if layout == "HPD" else unused[:, :, None]
     out = {}
+    if w.latent:
+        # MLA-style latent cache: latent channels quantised per (token, 128 channels), the
+        # rotary channels kept in bf16; queries the same way
+        dv = w.dv
+        assert layout == "HPD"
+        lat = kb[..., :dv]
+        codes, scale = quantize_per_row(np.ascontiguousarray(lat).reshape(*lat.shape[:-1], dv // 128, 128), "bf16")
+        codes = codes.reshape(lat.shape)
+        rope = np.ascontiguousarray(kb[..., dv:])
+        codes = np.where(np.broadcast_to(m4, codes.shape), np.uint8(E4M3_NAN_CODE), codes)
+        scale = np.where(np.broadcast_to(m4, scale.shape), np.float32(np.nan), scale)
+        rope = np.where(np.broadcast_to(m4, rope.shape), np.uint16(BF16_NAN_BITS), rope)
+        lkv = LatentKV(codes, scale, rope)
+        out["latent"], out["k"], out["v"] = lkv, lkv.key_view(), lkv.value_view()
+        qb = _bits(w.q)
+        qn = np.ascontiguousarray(qb[..., :dv])
+        qc, qs = quantize_per_row(qn.reshape(*qn.shape[:-1], dv // 128, 128), "bf16")
+        out["q_codes"], out["q_scale"], out["q_rope"] = qc.reshape(qn.shape), qs, np.ascontiguousarray(qb[..., dv:])
+        out["q64"] = dequant_q_latent(out["q_codes"], qs, out["q_rope"])
+        return out
     if w.kv_dtype == "bf16":
         kb = np.where(np.broadcast_to(m4, kb.shape), np.uint16(BF16_NAN_BITS), kb)
         vb = np.where(np.broadcast_to(m4, vb.shape), np.uint16(BF16_NAN_BITS), vb)

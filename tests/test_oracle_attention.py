@@ -284,3 +284,101 @@ def test_single_vector_oracle_equals_full_oracle_and_brute_force(layout):
             if bf is not None:
                 assert np.max(np.abs(o - bf[(t, h)][0])) <= 1e-13 * np.max(np.abs(bf[(t, h)][0]))
                 assert abs(l - bf[(t, h)][1]) <= 1e-13 * max(1.0, abs(bf[(t, h)][1]))
+
+
+def _brute_force_kv(q, k_tok, v_tok, kv_len, qo_indptr, window, sm_scale, Hq, Hkv):
+    """Decimal (40 digits) attention with separate key and value widths: q [T, Hq, dk]
+    float64, k_tok / v_tok[b] = [kv_len[b], dk] / [kv_len[b], dv] float64 per (request,
+    KV head) in logical token order.  Returns {(t, h): (o, lse)}."""
+    getcontext().prec = 40
+    out = {}
+    for b in range(len(kv_len)):
+        n = qo_indptr[b + 1] - qo_indptr[b]
+        for r in range(n):
+            t = qo_indptr[b] + r
+            pos = kv_len[b] - n + r
+            W = window[b]
+            keys = [j for j in range(kv_len[b]) if j <= pos and (W == 0 or j > pos - W)]
+            for h in range(Hq):
+                g = h * Hkv // Hq
+                K, V = k_tok[b][g], v_tok[b][g]
+                s = [Decimal(sm_scale) * sum(Decimal(q[t, h, c]) * Decimal(K[j, c]) for c in range(K.shape[1]))
+                     for j in keys]
+                m = max(s)
+                e = [(x - m).exp() for x in s]
+                l = sum(e)
+                o = [sum(ej * Decimal(V[j, c]) for j, ej in zip(keys, e)) / l for c in range(V.shape[1])]
+                out[(t, h)] = (np.array([float(x) for x in o]), float(m + l.ln()))
+    return out
+
+
+def test_key_and_value_widths_differ_decimal_brute_force():
+    # 12-channel keys, 8-channel values (separate head_dim_qk and head_dim_v)
+    rng = np.random.default_rng(21)
+    B, P, Hq, Hkv, dk, dv = 2, 4, 4, 2, 12, 8
+    kv_len = np.array([9, 14]); rows = np.array([2, 3]); window = np.array([0, 5])
+    qo = np.concatenate([[0], np.cumsum(rows)])
+    pages_b = (kv_len + P - 1) // P
+    kvi = np.concatenate([[0], np.cumsum(pages_b)])
+    npages = int(pages_b.sum()) + 2
+    pidx = rng.permutation(npages)[: int(pages_b.sum())].astype(np.int32)
+    k = PagedKV(bf16_bits(rng.standard_normal((npages, Hkv, P, dk))), "bf16")
+    v = PagedKV(bf16_bits(rng.standard_normal((npages, Hkv, P, dv))), "bf16")
+    qb = bf16_bits(rng.standard_normal((int(qo[-1]), Hq, dk)))
+    q = bf16_bits_to_f64(qb)
+    sm = float(np.float32(1 / np.sqrt(dk)))
+    out, lse = decode_attention(q, k, v, pidx, kvi, kv_len, qo, window, sm)
+    assert out.shape == (int(qo[-1]), Hq, dv)
+    kt = [[bf16_bits_to_f64(k.data[pidx[kvi[b] + np.arange(kv_len[b]) // P], g, np.arange(kv_len[b]) % P])
+           for g in range(Hkv)] for b in range(B)]
+    vt = [[bf16_bits_to_f64(v.data[pidx[kvi[b] + np.arange(kv_len[b]) // P], g, np.arange(kv_len[b]) % P])
+           for g in range(Hkv)] for b in range(B)]
+    bf = _brute_force_kv(q, kt, vt, kv_len, qo, window, sm, Hq, Hkv)
+    for (t, h), (o, l) in bf.items():
+        assert np.max(np.abs(out[t, h] - o)) <= 1e-13 * np.max(np.abs(o)) and abs(lse[t, h] - l) <= 1e-13 * max(1, abs(l))
+
+
+def test_latent_cache_against_torch_decode_and_decimal_brute_force():
+    # MLA-style cache: key = [latent codes x per-(token, 128 channel) scale, bf16 rotary],
+    # value = the latent; the dequantisation against torch's own float8 decode, the
+    # attention against a decimal brute force built from those values
+    import torch
+    from oracle.attention import LatentKV, dequant_q_latent
+    rng = np.random.default_rng(22)
+    B, P, Hq, Hkv, dv, dr = 2, 4, 3, 1, 256, 8
+    kv_len = np.array([7, 11]); rows = np.array([1, 2]); window = np.array([0, 0])
+    qo = np.concatenate([[0], np.cumsum(rows)])
+    pages_b = (kv_len + P - 1) // P
+    kvi = np.concatenate([[0], np.cumsum(pages_b)])
+    npages = int(pages_b.sum())
+    pidx = rng.permutation(npages).astype(np.int32)
+    codes = rng.integers(0, 256, (npages, Hkv, P, dv)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x2A
+    scale = (rng.random((npages, Hkv, P, dv // 128)) * 0.05 + 0.001).astype(np.float32)
+    rope = bf16_bits(rng.standard_normal((npages, Hkv, P, dr)))
+    lkv = LatentKV(codes, scale, rope)
+    slots = np.array([0, 5, 13])
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    for s in slots:
+        pg, sl = s // P, s % P
+        ref = dec[pg, 0, sl] * np.repeat(scale[pg, 0, sl].astype(np.float64), 128)
+        assert np.array_equal(lkv.latent(np.array([s]), 0)[0], ref)
+        assert np.array_equal(lkv.key_view().tokens(np.array([s]), 0)[0],
+                              np.concatenate([ref, bf16_bits_to_f64(rope[pg, 0, sl])]))
+    T = int(qo[-1])
+    qc = rng.integers(0, 256, (T, Hq, dv)).astype(np.uint8)
+    qc[(qc & 0x7F) == 0x7F] = 0x33
+    qs = (rng.random((T, Hq, dv // 128)) + 0.5).astype(np.float32)
+    qr = bf16_bits(rng.standard_normal((T, Hq, dr)))
+    q = dequant_q_latent(qc, qs, qr)
+    qref = np.concatenate([torch.from_numpy(qc).view(torch.float8_e4m3fn).double().numpy() *
+                           np.repeat(qs.astype(np.float64), 128, axis=2), bf16_bits_to_f64(qr)], axis=2)
+    assert np.array_equal(q, qref)
+    sm = float(np.float32(1 / np.sqrt(dv + dr)))
+    out, lse = decode_attention(q, lkv.key_view(), lkv.value_view(), pidx, kvi, kv_len, qo, window, sm)
+    kt = [[lkv.key_view().tokens(pidx[kvi[b] + np.arange(kv_len[b]) // P] * P + np.arange(kv_len[b]) % P, 0)]
+          for b in range(B)]
+    vt = [[x[0][:, :dv]] for x in kt]
+    bf = _brute_force_kv(q, kt, vt, kv_len, qo, window, sm, Hq, Hkv)
+    for (t, h), (o, l) in bf.items():
+        assert np.max(np.abs(out[t, h] - o)) <= 1e-12 * np.max(np.abs(o)) and abs(lse[t, h] - l) <= 1e-12 * max(1, abs(l))

@@ -155,7 +155,14 @@ def test_oracle_inputs_use_each_workloads_own_format():
     from tests.oracle_inputs import oracle_inputs
     for name, cfg in CONFIGS.items():
         w = make_workload(name, batch=1, ctx=[40], rows=1)
-        k = oracle_inputs(w)["k"]
+        oi = oracle_inputs(w)
+        if cfg.get("latent"):            # per (token, 128 channels) scales: amax / 448 of each block
+            lat = w.k.float()[..., :w.dv].reshape(*w.k.shape[:-1], w.dv // 128, 128)
+            ref = (lat.abs().amax(-1) / 448.0).numpy()
+            used = ~w.unused_slots
+            assert np.array_equal(oi["latent"].scale[:, 0][used], ref[:, 0][used]), name
+            continue
+        k = oi["k"]
         assert k.dtype == cfg["kv"] and k.scale_mode == cfg["scale"], name
         if cfg["scale"] == "per_tensor":
             amax = np.float32(w.k.float().abs().max().item())
