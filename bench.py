@@ -47,6 +47,10 @@ WORKLOAD_NAMES = {
     "c6_r4": "head_dim 512 verify R4 B1 8/1 heads ctx131072 P16 bf16 KV",
     "c6_f8": "head_dim 512 verify R8 B1 8/1 heads ctx131072 P16 e4m3 KV per-token-head",
     "c5": "ragged R1..8 B64 48/2 heads (group 24) d128 ctx loguniform 1K-64K, half window 64, P32 e4m3 per-token-head",
+    "f3": "keys 192 / values 128, B32 R1 32/4 heads ctx8192 P16 bf16 KV",
+    "f3_r4": "keys 192 / values 128, B32 R4 32/4 heads ctx8192 P16 bf16 KV",
+    "mla": "MLA-style latent cache 576/512, B64 R1 16/1 heads ctx4096 P64, e4m3 latent per (token, 128 ch) + bf16 rope",
+    "mla_r2": "MLA-style latent cache 576/512, B64 R2 16/1 heads ctx4096 P64, e4m3 latent per (token, 128 ch) + bf16 rope",
 }
 
 
@@ -357,7 +361,7 @@ def time_steps(pd, step, merge, flush, stream, steps, warmup, do_flush):
 # Every configuration of the benchmark target, timed in the default run after the
 # headline: the five workloads, the batch-1 and row-count variants the R8/R1 bar compares.
 PER_CONFIG = ("c1", "c3", "c3_r1", "c3_r8", "c3_b1", "c3_b1_r1", "c3_b1_r8", "c4", "c4_r1", "c4_b1", "c4_b1_r1",
-              "c5")
+              "c5", "f3", "mla")
 MEMORY_BOUND = {"c2", "c3", "c3_r1", "c3_r8", "c3_b1", "c3_b1_r1", "c3_b1_r8", "c4", "c4_r1", "c4_b1", "c4_b1_r1",
                 "c5"}
 R8_R1 = (("c3_r8", "c3_r1"), ("c3_b1_r8", "c3_b1_r1"), ("c4", "c4_r1"), ("c4_b1", "c4_b1_r1"))
@@ -365,6 +369,11 @@ R8_R1 = (("c3_r8", "c3_r1"), ("c3_b1_r8", "c3_b1_r1"), ("c4", "c4_r1"), ("c4_b1"
 
 def arithmetic(w, variant: int) -> str:
     """What the stage-1 kernel of this plan multiplies in, from the tile configuration."""
+    if (variant >> 14) & 1:
+        if (variant >> 15) & 1:
+            return ("bf16 MFMA on the e4m3 latent codes upconverted exactly: q.k per 128-channel block times both "
+                    "scales plus the bf16 rotary part; P.V with P times the token's block scale (one bf16 term)")
+        return "bf16 MFMA for q.k (192 channels) and P.V (128 channels, P as two bf16 terms)"
     qf8, kvf8, pt = (variant >> 1) & 1, (variant >> 2) & 1, (variant >> 3) & 1
     wq, nqb, i8 = (variant >> 4) & 15, (variant >> 8) & 15, (variant >> 12) & 1
     one_block_waves = wq == 4 and nqb == 1
@@ -385,6 +394,15 @@ def arithmetic(w, variant: int) -> str:
     return f"q.k: {qk}; P.V: {pv}"
 
 
+def stage1_call(pd, di, w, out, stream):
+    """Stage 1 of the plan: the equal-width kernel, or the one for keys wider than values."""
+    if pd.rope:
+        pd.stage1_rope(di, w.sm_scale, out, w.out_dtype, stream=stream)
+    else:
+        pd.stage1(di.q, di.q_scale, di.k, di.v, di.kv_layout, di.k_scale, di.v_scale, di.scale_layout,
+                  di.page_indices, w.sm_scale, out, w.out_dtype, stream=stream)
+
+
 def per_config(args, flush, stream):
     """Stage-1 and merge times of every configuration in PER_CONFIG (same flush and events as
     the headline; at least 20 timed and 50 warm-up steps each), with achieved GB/s against
@@ -403,13 +421,12 @@ def per_config(args, flush, stream):
         acc = workload_accounting(w)
         pd = PagedDecode(w.qo_indptr, w.kv_indptr, w.kv_len, w.window, w.max_q_len, w.page_size, w.num_q_heads,
                          w.num_kv_heads, w.head_dim, w.q_dtype, w.kv_dtype, w.kv_scale_mode, di.q.device,
-                         force_splits=w.forced_splits)
-        out = torch.empty(w.total_rows, w.num_q_heads, w.head_dim,
+                         force_splits=w.forced_splits, head_dim_v=w.head_dim_v)
+        out = torch.empty(w.total_rows, w.num_q_heads, w.dv,
                           dtype=torch.float32 if w.out_dtype == "fp32" else torch.bfloat16, device=di.q.device)
 
         def step():
-            pd.stage1(di.q, di.q_scale, di.k, di.v, di.kv_layout, di.k_scale, di.v_scale, di.scale_layout,
-                      di.page_indices, w.sm_scale, out, w.out_dtype, stream=stream)
+            stage1_call(pd, di, w, out, stream)
 
         def merge():
             pd.merge(out, w.out_dtype, stream=stream)
@@ -477,22 +494,21 @@ def main():
     acc = workload_accounting(w)
     pd = PagedDecode(w.qo_indptr, w.kv_indptr, w.kv_len, w.window, w.max_q_len, w.page_size, w.num_q_heads,
                      w.num_kv_heads, w.head_dim, w.q_dtype, w.kv_dtype, w.kv_scale_mode, dev,
-                     force_splits=w.forced_splits if args.force_splits is None else args.force_splits)
-    out = torch.empty(w.total_rows, w.num_q_heads, w.head_dim,
+                     force_splits=w.forced_splits if args.force_splits is None else args.force_splits,
+                     head_dim_v=w.head_dim_v)
+    out = torch.empty(w.total_rows, w.num_q_heads, w.dv,
                       dtype=torch.float32 if w.out_dtype == "fp32" else torch.bfloat16, device=dev)
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
-        pd.stage1(di.q, di.q_scale, di.k, di.v, di.kv_layout, di.k_scale, di.v_scale, di.scale_layout,
-                  di.page_indices, w.sm_scale, out, w.out_dtype, stream=stream)
+        stage1_call(pd, di, w, out, stream)
 
     def merge():
         pd.merge(out, w.out_dtype, stream=stream)
 
     def step_on(st):
-        pd.stage1(di.q, di.q_scale, di.k, di.v, di.kv_layout, di.k_scale, di.v_scale, di.scale_layout,
-                  di.page_indices, w.sm_scale, out, w.out_dtype, stream=st)
+        stage1_call(pd, di, w, out, st)
         pd.merge(out, w.out_dtype, stream=st)
 
     _spin_up(flush)

@@ -59,9 +59,12 @@ typedef enum {
   PA_SCALE_NONE = 0,           /* bf16 KV                                               */
   PA_SCALE_PER_TENSOR = 1,     /* one float32 scale for the whole K (and one for V)     */
   PA_SCALE_PER_TOKEN_HEAD = 2, /* one float32 scale per (token slot, KV head)           */
-  PA_SCALE_PER_HEAD = 3        /* one float32 scale per KV head for K and for V, and per */
+  PA_SCALE_PER_HEAD = 3,       /* one float32 scale per KV head for K and for V, and per */
                                /* query head for FP8 Q (FlashInfer PR #869, title:       */
                                /* per-head quantization)                                 */
+  PA_SCALE_PER_TOKEN_BLOCK128 = 4 /* MLA-style latent cache: one float32 scale per        */
+                               /* (token, KV head, 128 latent channels) (FlashMLA PR #54, */
+                               /* review thread); see pa_decode_stage1_rope              */
 } pa_scale_mode;
 
 /* Element strides of a paged cache: element (page, kv_head, slot, c) lives at
@@ -97,6 +100,9 @@ typedef struct {
   int32_t max_splits;          /* cap on splits per request (fixes scratch size for graph   */
                                /*   capture); 0 = no cap beyond the library's limit (1024)  */
   int32_t force_splits;        /* > 0: every request gets exactly this many splits           */
+  int32_t head_dim_v;          /* value width when it differs from head_dim (0 = head_dim):   */
+                               /*   192/128 (bf16) or 576/512 (latent cache, PER_TOKEN_BLOCK128 */
+                               /*   scales, FP8 queries); such plans run pa_decode_stage1_rope */
 } pa_plan_args;
 
 /* Planner output, consumed by stage1/merge.  Sizes are in bytes. */
@@ -108,9 +114,9 @@ typedef struct {
   int32_t needs_merge;         /* 0 when every request has a single split                   */
   int32_t num_cus;
   int32_t variant;             /* kernel tile configuration (library internal)              */
-  int32_t reserved0;
+  int32_t head_dim_v;          /* value width (output and partial-O rows)                    */
   int64_t plan_bytes;          /* bytes of the plan buffer (host copy and device copy)       */
-  int64_t partial_o_bytes;     /* [T, Hq, S_max, d]: float32 (bf16 KV) or bf16 (FP8/INT8 KV) */
+  int64_t partial_o_bytes;     /* [T, Hq, S_max, dv]: float32 (bf16 KV) or bf16 (FP8/INT8 KV) */
   int64_t partial_lse_bytes;   /* float32 [T, Hq, S_max]                                    */
   int64_t max_item_tokens;     /* longest KV token range of one work item                   */
   int64_t reserved[3];
@@ -174,6 +180,40 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev,
                            const int32_t* page_indices, float sm_scale,
                            void* partial_o, float* partial_lse,
                            void* out, pa_dtype out_dtype, float* out_lse, void* stream);
+
+/* Stage 1 for keys wider than values (device; a plan with head_dim != head_dim_v).
+ * Defined by: FlashInfer PR #869, "Remaining Work" (separate head_dim_qk and head_dim_v);
+ * the latent form by FlashMLA PR #54, review thread (keys' and queries' no-position part in
+ * 8 bits with one scale per token and 128 channels, their 64 rotary channels in 16 bits).
+ * Keys have head_dim = head_dim_v + 64 channels, the last 64 of which are rotary; the
+ * output and the partials have head_dim_v channels.  Otherwise as pa_decode_stage1 (same
+ * plan items, partial layout, LSE, out_lse and merge).
+ *   192/128, bf16 (kv_scale_mode NONE):
+ *     q        device bf16 [T, Hq, 192];  q_scale, q_rope, k_rope, k_scale: NULL
+ *     k_cache  bf16 key rows of 192 channels, element strides k_layout
+ *     v_cache  bf16 value rows of 128 channels, element strides v_layout
+ *   576/512 latent cache (kv_scale_mode PER_TOKEN_BLOCK128, q_dtype and kv_dtype FP8):
+ *     q        device e4m3 codes [T, Hq, 512] of the queries' latent part
+ *     q_scale  device float32 [T, Hq, 4]: the scale of each 128-channel block
+ *     q_rope   device bf16 [T, Hq, 64]: the queries' rotary part
+ *     k_cache  e4m3 latent codes, 512 per (page, KV head, slot), element strides k_layout
+ *     k_scale  float32 latent scales, 4 consecutive per (page, KV head, slot) (one per 128
+ *              channels; k_scale_layout gives the strides of the first)
+ *     k_rope   bf16 rotary rows of 64 channels, element strides k_rope_layout
+ *     v_cache, v_layout: NULL (the value is the latent: code times its block's scale)
+ * Accuracy: bf16 MFMA throughout (e4m3 codes upconverted exactly); 192/128 keeps P in two
+ * bf16 terms, the latent form one bf16 term of P times the token's block scale.  Pointers
+ * 16-byte aligned, cache strides multiples of 16 bytes.  Errors: INVALID_ARGUMENT (a plan
+ * of equal widths, missing or misaligned arguments). */
+pa_status pa_decode_stage1_rope(const pa_plan_info* info, const void* plan_dev,
+                                const void* q, const float* q_scale, const void* q_rope,
+                                const void* k_cache, const pa_kv_layout* k_layout,
+                                const void* k_rope, const pa_kv_layout* k_rope_layout,
+                                const float* k_scale, const pa_kv_layout* k_scale_layout,
+                                const void* v_cache, const pa_kv_layout* v_layout,
+                                const int32_t* page_indices, float sm_scale,
+                                void* partial_o, float* partial_lse,
+                                void* out, pa_dtype out_dtype, float* out_lse, void* stream);
 
 /* Stage 2 (device).  Defined by: FreeToken PR #900, "Changes" (stage 2 merges the splits
  * of each row).  Per (row, query head) with more than one split,
@@ -275,7 +315,8 @@ pa_status pa_debug_gather(const pa_plan_info* info, const void* plan_dev, const 
  * Stage 1 never checks page numbers, so an entry outside the caches would make it read
  * outside them; run this check first where the page table is not trusted (the Python
  * binding runs it before every stage 1 when the environment sets PA_VALIDATE=1).
- * Returns INVALID_ARGUMENT naming the count and the first offending position, PA_OK
+ * Returns INVALID_ARGUMENT naming the count of offending reads (an entry read by the items
+ * of several KV heads or splits counts once per item) and the first offending position, PA_OK
  * otherwise, or PA_ERR_HIP.  Not graph-capturable (it waits for its result). */
 pa_status pa_validate_page_indices(const pa_plan_info* info, const void* plan_dev, const int32_t* page_indices,
                                    int64_t num_pages, void* stream);

@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(_HERE, "libpa_gfx950.so")
 
 PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_INSUFFICIENT_WORKSPACE, PA_ERR_HIP = range(5)
 PA_DTYPE_BF16, PA_DTYPE_FP32, PA_DTYPE_FP8_E4M3, PA_DTYPE_INT8 = 0, 1, 2, 3
-PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_TOKEN_HEAD, PA_SCALE_PER_HEAD = 0, 1, 2, 3
+PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_TOKEN_HEAD, PA_SCALE_PER_HEAD, PA_SCALE_PER_TOKEN_BLOCK128 = 0, 1, 2, 3, 4
 
 DTYPES = {"bf16": PA_DTYPE_BF16, "fp32": PA_DTYPE_FP32, "fp8": PA_DTYPE_FP8_E4M3, "int8": PA_DTYPE_INT8}
 SCALE_MODES = {"none": PA_SCALE_NONE, "per_tensor": PA_SCALE_PER_TENSOR, "per_token_head": PA_SCALE_PER_TOKEN_HEAD,
-               "per_head": PA_SCALE_PER_HEAD}
+               "per_head": PA_SCALE_PER_HEAD, "per_token_block128": PA_SCALE_PER_TOKEN_BLOCK128}
 
 _p = ctypes.c_void_p
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -33,14 +33,15 @@ class PlanArgs(ctypes.Structure):
                 ("window", _i32p), ("max_q_len", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int), ("kv_scale_mode", ctypes.c_int),
-                ("num_cus", ctypes.c_int32), ("max_splits", ctypes.c_int32), ("force_splits", ctypes.c_int32)]
+                ("num_cus", ctypes.c_int32), ("max_splits", ctypes.c_int32), ("force_splits", ctypes.c_int32),
+                ("head_dim_v", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "total_rows", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "max_q_len",
                  "q_dtype", "kv_dtype", "kv_scale_mode", "num_items", "max_splits", "needs_merge", "num_cus",
-                 "variant", "reserved0")] + \
+                 "variant", "head_dim_v")] + \
                [("plan_bytes", ctypes.c_int64), ("partial_o_bytes", ctypes.c_int64),
                 ("partial_lse_bytes", ctypes.c_int64), ("max_item_tokens", ctypes.c_int64),
                 ("reserved", ctypes.c_int64 * 3)]
@@ -74,6 +75,11 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_stage1.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, _p, ctypes.POINTER(KVLayout), _p, _p,
                                        ctypes.POINTER(ScaleLayout), _p, ctypes.c_float, _p, _p, _p, ctypes.c_int, _p,
                                        _p]
+        L.pa_decode_stage1_rope.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, _p, ctypes.POINTER(KVLayout),
+                                            _p, ctypes.POINTER(KVLayout), _p, ctypes.POINTER(KVLayout), _p,
+                                            ctypes.POINTER(KVLayout), _p, ctypes.c_float, _p, _p, _p, ctypes.c_int,
+                                            _p, _p]
+        L.pa_decode_stage1_rope.restype = ctypes.c_int
         L.pa_decode_merge.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, ctypes.c_int, _p, _p]
         L.pa_kv_quantize_fp8.argtypes = [_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, _p, _p, _p]
         L.pa_kv_quantize_int8.argtypes = [_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, _p, _p, _p]
@@ -133,7 +139,8 @@ def pa_version() -> str:
 
 
 def pa_plan_splits(qo_indptr, kv_indptr, kv_len, window, max_q_len, page_size, num_q_heads, num_kv_heads, head_dim,
-                   q_dtype, kv_dtype, kv_scale_mode, num_cus=0, max_splits=0, force_splits=0, query_only=False):
+                   q_dtype, kv_dtype, kv_scale_mode, num_cus=0, max_splits=0, force_splits=0, query_only=False,
+                   head_dim_v=0):
     """Returns (PlanInfo, plan bytes as a numpy uint8 array, or None with query_only)."""
     arrs = [np.ascontiguousarray(np.asarray(x, dtype=np.int32)) for x in (qo_indptr, kv_indptr, kv_len)]
     win = None if window is None else np.ascontiguousarray(np.asarray(window, dtype=np.int32))
@@ -141,7 +148,7 @@ def pa_plan_splits(qo_indptr, kv_indptr, kv_len, window, max_q_len, page_size, n
     a = PlanArgs(B, arrs[0].ctypes.data_as(_i32p), arrs[1].ctypes.data_as(_i32p), arrs[2].ctypes.data_as(_i32p),
                  None if win is None else win.ctypes.data_as(_i32p), int(max_q_len), int(page_size),
                  int(num_q_heads), int(num_kv_heads), int(head_dim), _dt(q_dtype), _dt(kv_dtype),
-                 _sm(kv_scale_mode), int(num_cus), int(max_splits), int(force_splits))
+                 _sm(kv_scale_mode), int(num_cus), int(max_splits), int(force_splits), int(head_dim_v))
     info = PlanInfo()
     _check(lib().pa_plan_splits(ctypes.byref(a), None, 0, ctypes.byref(info)))
     if query_only:
@@ -176,6 +183,20 @@ def pa_decode_noalloc(info, plan_dev, q, q_scale, k_cache, v_cache, kv_layout, k
                                    None if scl is None else ctypes.byref(scl), _ptr(page_indices),
                                    ctypes.c_float(sm_scale), _ptr(out), _dt(out_dtype), _ptr(out_lse),
                                    _stream(stream)))
+
+
+def _layout(x):
+    return None if x is None else ctypes.byref(KVLayout(*x))
+
+
+def pa_decode_stage1_rope(info, plan_dev, q, q_scale, q_rope, k_cache, k_layout, k_rope, k_rope_layout, k_scale,
+                          k_scale_layout, v_cache, v_layout, page_indices, sm_scale, partial_o, partial_lse, out,
+                          out_dtype, out_lse=None, stream=None):
+    _check(lib().pa_decode_stage1_rope(ctypes.byref(info), _ptr(plan_dev), _ptr(q), _ptr(q_scale), _ptr(q_rope),
+                                       _ptr(k_cache), _layout(k_layout), _ptr(k_rope), _layout(k_rope_layout),
+                                       _ptr(k_scale), _layout(k_scale_layout), _ptr(v_cache), _layout(v_layout),
+                                       _ptr(page_indices), ctypes.c_float(sm_scale), _ptr(partial_o),
+                                       _ptr(partial_lse), _ptr(out), _dt(out_dtype), _ptr(out_lse), _stream(stream)))
 
 
 def pa_decode_merge(info, plan_dev, partial_o, partial_lse, out, out_dtype, out_lse=None, stream=None):

@@ -20,7 +20,11 @@ _SIZE = {"bf16": 2, "fp8": 1, "int8": 1, "fp32": 4}
 
 
 def step_accounting(batch, qo_indptr, kv_len, window, page_size, num_q_heads, num_kv_heads,
-                    head_dim, q_dtype, kv_dtype, kv_scale_mode, out_dtype) -> dict:
+                    head_dim, q_dtype, kv_dtype, kv_scale_mode, out_dtype, head_dim_v=0, latent=False) -> dict:
+    """Keys of head_dim channels and values of head_dim_v (0 = head_dim); with ``latent``
+    (MLA-style cache) each (token, KV head) stores head_dim_v e4m3 latent codes, one
+    float32 scale per 128 of them and head_dim - head_dim_v bf16 rotary channels, read
+    once for both products, and the queries likewise (codes, scales, bf16 rotary part)."""
     qo_indptr = np.asarray(qo_indptr, dtype=np.int64)
     kv_len = np.asarray(kv_len, dtype=np.int64)
     window = np.zeros(batch, dtype=np.int64) if window is None else np.asarray(window, dtype=np.int64)
@@ -41,6 +45,20 @@ def step_accounting(batch, qo_indptr, kv_len, window, page_size, num_q_heads, nu
             lo = max(0, p - int(window[b]) + 1) if window[b] > 0 else 0
             row_tokens += p - lo + 1
     T = int(qo_indptr[batch])
+    dv = head_dim_v or d
+    if latent or dv != d:
+        dr = d - dv
+        if latent:
+            per_tok = dv + 4 * (dv // 128) + 2 * dr
+            q_bytes = T * num_q_heads * (dv + 4 * (dv // 128) + 2 * dr)
+        else:
+            per_tok = (d + dv) * _SIZE[kv_dtype]
+            q_bytes = T * num_q_heads * d * _SIZE[q_dtype]
+        out = {"kv": kv_tok * num_kv_heads * per_tok, "kv_scales": 0, "q": q_bytes,
+               "out": T * num_q_heads * dv * _SIZE[out_dtype], "page_table": pages * 4,
+               "flops": 2 * (d + dv) * row_tokens * G * num_kv_heads}
+        out["bytes"] = out["kv"] + out["q"] + out["out"] + out["page_table"]
+        return out
     out = {
         "kv": kv_tok * num_kv_heads * 2 * d * _SIZE[kv_dtype],
         "kv_scales": kv_tok * num_kv_heads * 8 if kv_scale_mode == "per_token_head" else
@@ -60,4 +78,4 @@ def workload_accounting(w) -> dict:
     """step_accounting for an inputs.Workload."""
     return step_accounting(w.batch, w.qo_indptr, w.kv_len, w.window, w.page_size, w.num_q_heads,
                            w.num_kv_heads, w.head_dim, w.q_dtype, w.kv_dtype, w.kv_scale_mode,
-                           w.out_dtype)
+                           w.out_dtype, head_dim_v=w.head_dim_v, latent=w.latent)

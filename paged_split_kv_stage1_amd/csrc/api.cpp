@@ -68,6 +68,13 @@ namespace pa {
 // Tile configurations stage 1 is instantiated for (its dispatcher in stage1.hip uses the
 // same list).
 bool stage1_cfg_supported(const KernelCfg& c) {
+  // keys with a rotary part (stage1_kr.hip): bf16 192/128, or the MLA latent cache 576/512
+  // with e4m3 latent codes and e4m3 latent queries; one 16-row block per wave
+  if (c.kr) {
+    if (c.wq != 4 || c.nqb != 1) return false;
+    if (c.mla) return c.dv == 512 && c.dh == 576 && c.qf8 && c.kvf8 && !c.i8;
+    return c.dv == 128 && c.dh == 192 && !c.qf8 && !c.kvf8 && !c.pt;
+  }
   // head_dim 512: bf16 KV, or per-token-head FP8 KV with bf16 queries; up to four 16-row
   // query blocks (one per wave), one workgroup per CU (its accumulators and query
   // operand need the whole register file of a SIMD)
@@ -93,6 +100,18 @@ bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
   const int mq = a.max_q_len * G;
   const int nqb = (mq + 15) / 16;
   c->dh = a.head_dim;
+  c->dv = a.head_dim_v > 0 ? a.head_dim_v : a.head_dim;
+  if (c->dv != c->dh) {               // keys with a rotary part: one block per wave, groups of four
+    c->kr = 1;
+    c->mla = a.kv_scale_mode == PA_SCALE_PER_TOKEN_BLOCK128;
+    c->qf8 = a.q_dtype == PA_DTYPE_FP8_E4M3;
+    c->kvf8 = a.kv_dtype != PA_DTYPE_BF16;
+    c->i8 = a.kv_dtype == PA_DTYPE_INT8;
+    c->pt = c->mla;
+    c->wq = 4;
+    c->nqb = 1;
+    return stage1_cfg_supported(*c);
+  }
   c->qf8 = a.q_dtype == PA_DTYPE_FP8_E4M3;
   c->kvf8 = a.kv_dtype != PA_DTYPE_BF16;            // one-byte codes
   c->i8 = a.kv_dtype == PA_DTYPE_INT8;
@@ -147,6 +166,8 @@ constexpr double kMergeLaunchS = 3.0e-6;
 // and 28 ns gave 128.5, 138.6, 119 and 118.5 us of stage 1 -- its three-block waves
 // cost more per block than the one-block shapes the first figure came from).
 double compute_s_per_token_block(const pa_plan_args& a) {
+  if (a.head_dim_v > 0 && a.head_dim_v != a.head_dim)      // keys with a rotary part
+    return (a.kv_scale_mode == PA_SCALE_PER_TOKEN_BLOCK128 ? 60.0 : 20.0) * 1e-9;
   const bool f8 = a.kv_dtype != PA_DTYPE_BF16;
   const bool pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD || a.kv_dtype == PA_DTYPE_INT8;
   const double d_scale = a.head_dim / 128.0;
@@ -179,6 +200,8 @@ CostModel cost_model(const pa_plan_args& a, const KernelCfg& cfg, int num_cus) {
   const int G = a.num_q_heads / a.num_kv_heads;
   m.kv_tok = 2.0 * a.head_dim * (a.kv_dtype != PA_DTYPE_BF16 ? 1 : 2) +
              (a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD ? 8 : 0);
+  if (cfg.kr)                           // key rows of dh channels, value rows of dv (MLA: shared)
+    m.kv_tok = cfg.mla ? cfg.dv + 2.0 * 64 + 4.0 * cfg.dv / 128 : 2.0 * (cfg.dh + cfg.dv);
   m.slots = (cfg.dh == 512 ? 1 : kSlotsPerCu) * num_cus;   // head_dim 512: one workgroup per CU
   m.bw_slot = kHbmBytesPerS / m.slots;
   const int wt = 4 / cfg.wq;                     // waves sharing the tokens of a tile
@@ -193,7 +216,7 @@ CostModel cost_model(const pa_plan_args& a, const KernelCfg& cfg, int num_cus) {
     const int per_item = std::min(nb16, cfg.wq * cfg.nqb);
     const int rounds = (per_item + cfg.wq - 1) / cfg.wq;
     m.comp_tok[b] = comp_blk * rounds / wt;
-    m.part[b] = (double)std::min(n * G, 16 * per_item) * (a.head_dim * partial_o_elem_bytes(a.kv_dtype) + 4.0);
+    m.part[b] = (double)std::min(n * G, 16 * per_item) * (cfg.dv * partial_o_elem_bytes(a.kv_dtype) + 4.0);
   }
   return m;
 }
@@ -298,8 +321,13 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   if (a->num_q_heads < 1 || a->num_kv_heads < 1 || a->num_q_heads % a->num_kv_heads != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 a->num_q_heads, a->num_kv_heads);
-  if (a->head_dim != 128 && a->head_dim != 256 && a->head_dim != 512)
+  const int dv = a->head_dim_v > 0 ? a->head_dim_v : a->head_dim;
+  if (a->head_dim_v < 0) return fail(PA_ERR_INVALID_ARGUMENT, "head_dim_v must be >= 0");
+  if (dv == a->head_dim && a->head_dim != 128 && a->head_dim != 256 && a->head_dim != 512)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d: only 128, 256 and 512 are supported", a->head_dim);
+  if (dv != a->head_dim && !((a->head_dim == 192 && dv == 128) || (a->head_dim == 576 && dv == 512)))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d with head_dim_v %d: separate key and value widths are supported "
+                                    "as 192/128 and 576/512 (keys with a 64-channel rotary part)", a->head_dim, dv);
   const int page_shift = ilog2_exact(a->page_size);
   if (page_shift < 4 || a->page_size > 1024)
     return fail(PA_ERR_UNSUPPORTED, "page_size %d: must be a power of two in [16, 1024]", a->page_size);
@@ -310,9 +338,17 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
     return fail(PA_ERR_INVALID_ARGUMENT, "kv_dtype must be BF16, FP8_E4M3 or INT8");
   if (kd == PA_DTYPE_BF16 && sm != PA_SCALE_NONE)
     return fail(PA_ERR_INVALID_ARGUMENT, "bf16 KV takes kv_scale_mode NONE");
-  if (kd == PA_DTYPE_FP8_E4M3 && sm != PA_SCALE_PER_TENSOR &&
-      sm != PA_SCALE_PER_HEAD && sm != PA_SCALE_PER_TOKEN_HEAD)
-    return fail(PA_ERR_INVALID_ARGUMENT, "FP8 KV takes kv_scale_mode PER_TENSOR, PER_HEAD or PER_TOKEN_HEAD");
+  if (kd == PA_DTYPE_FP8_E4M3 && sm != PA_SCALE_PER_TENSOR && sm != PA_SCALE_PER_HEAD &&
+      sm != PA_SCALE_PER_TOKEN_HEAD && sm != PA_SCALE_PER_TOKEN_BLOCK128)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "FP8 KV takes kv_scale_mode PER_TENSOR, PER_HEAD, PER_TOKEN_HEAD or PER_TOKEN_BLOCK128");
+  if ((sm == PA_SCALE_PER_TOKEN_BLOCK128) != (a->head_dim == 576 && dv == 512))
+    return fail(PA_ERR_UNSUPPORTED, "PER_TOKEN_BLOCK128 scales are the latent cache of 576/512 keys/values "
+                                    "(and that cache takes no other mode)");
+  if (dv != a->head_dim && dv == 128 && (qd != PA_DTYPE_BF16 || kd != PA_DTYPE_BF16))
+    return fail(PA_ERR_UNSUPPORTED, "192/128 keys/values take bf16 queries and a bf16 cache");
+  if (sm == PA_SCALE_PER_TOKEN_BLOCK128 && qd != PA_DTYPE_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "the latent cache takes e4m3 latent queries (with bf16 rotary parts)");
   if (kd == PA_DTYPE_INT8 && sm != PA_SCALE_PER_TENSOR &&
       sm != PA_SCALE_PER_TOKEN_HEAD)
     return fail(PA_ERR_INVALID_ARGUMENT, "INT8 KV takes kv_scale_mode PER_TENSOR or PER_TOKEN_HEAD");
@@ -410,6 +446,7 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   info->num_q_heads = a->num_q_heads;
   info->num_kv_heads = Hkv;
   info->head_dim = a->head_dim;
+  info->head_dim_v = dv;
   info->page_size = a->page_size;
   info->max_q_len = a->max_q_len;
   info->q_dtype = a->q_dtype;
@@ -421,7 +458,7 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   info->num_cus = num_cus;
   info->variant = pack_cfg(cfg);
   info->plan_bytes = plan_bytes_for(n_items, T);
-  info->partial_o_bytes = s_max > 1 ? th_count * s_max * a->head_dim * partial_o_elem_bytes(a->kv_dtype) : 0;
+  info->partial_o_bytes = s_max > 1 ? th_count * s_max * dv * partial_o_elem_bytes(a->kv_dtype) : 0;
   info->partial_lse_bytes = s_max > 1 ? th_count * s_max * 4 : 0;
   info->max_item_tokens = max_item_tokens;
   if (!plan_host) return ok();
@@ -489,6 +526,8 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const
   const KernelCfg cfg = unpack_cfg(info->variant);
   if (!stage1_cfg_supported(cfg) || cfg.dh != info->head_dim)
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_plan_info was not produced by pa_plan_splits");
+  if (cfg.kr)
+    return fail(PA_ERR_INVALID_ARGUMENT, "this plan has keys wider than values: use pa_decode_stage1_rope");
   if (info->needs_merge && (!partial_o || !partial_lse))
     return fail(PA_ERR_INVALID_ARGUMENT, "this plan has several splits: partial_o and partial_lse are required");
   if (cfg.qf8 && !q_scale) return fail(PA_ERR_INVALID_ARGUMENT, "FP8 queries need q_scale");
@@ -540,6 +579,74 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const
   return ok();
 }
 
+pa_status pa_decode_stage1_rope(const pa_plan_info* info, const void* plan_dev, const void* q, const float* q_scale,
+                                const void* q_rope, const void* k_cache, const pa_kv_layout* k_layout,
+                                const void* k_rope, const pa_kv_layout* k_rope_layout, const float* k_scale,
+                                const pa_kv_layout* k_scale_layout, const void* v_cache, const pa_kv_layout* v_layout,
+                                const int32_t* page_indices, float sm_scale, void* partial_o, float* partial_lse,
+                                void* out, pa_dtype out_dtype, float* out_lse, void* stream) {
+  if (!info || !plan_dev || !q || !k_cache || !k_layout || !page_indices || !out)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_stage1_rope: a required pointer is NULL");
+  if (raw(out_dtype) != PA_DTYPE_BF16 && raw(out_dtype) != PA_DTYPE_FP32)
+    return fail(PA_ERR_INVALID_ARGUMENT, "out_dtype must be BF16 or FP32");
+  const KernelCfg cfg = unpack_cfg(info->variant);
+  if (!stage1_cfg_supported(cfg) || !cfg.kr || cfg.dh != info->head_dim)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_stage1_rope needs a plan with keys wider than values");
+  if (info->needs_merge && (!partial_o || !partial_lse))
+    return fail(PA_ERR_INVALID_ARGUMENT, "this plan has several splits: partial_o and partial_lse are required");
+  if (cfg.mla && (!q_scale || !q_rope || !k_rope || !k_rope_layout || !k_scale || !k_scale_layout))
+    return fail(PA_ERR_INVALID_ARGUMENT, "the latent cache needs q_scale, q_rope, k_rope and k_scale with layouts");
+  if (!cfg.mla && (!v_cache || !v_layout))
+    return fail(PA_ERR_INVALID_ARGUMENT, "192/128 keys/values need v_cache and v_layout");
+  const bool ok_align = aligned16(q) && aligned16(k_cache) && aligned16(out) && (!q_rope || aligned16(q_rope)) &&
+                        (!k_rope || aligned16(k_rope)) && (!v_cache || aligned16(v_cache)) &&
+                        (!info->needs_merge || aligned16(partial_o));
+  if (!ok_align) return fail(PA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  auto strides_ok = [](const pa_kv_layout* l, int esz) {
+    return l->page >= 0 && l->head >= 0 && l->slot >= 0 && (l->page * esz) % 16 == 0 && (l->head * esz) % 16 == 0 &&
+           (l->slot * esz) % 16 == 0;
+  };
+  if (!strides_ok(k_layout, cfg.mla ? 1 : 2) || (cfg.mla && !strides_ok(k_rope_layout, 2)) ||
+      (!cfg.mla && !strides_ok(v_layout, 2)))
+    return fail(PA_ERR_INVALID_ARGUMENT, "cache strides must be non-negative multiples of 16 bytes");
+  if (cfg.mla && (k_scale_layout->page < 0 || k_scale_layout->head < 0 || k_scale_layout->slot < 0))
+    return fail(PA_ERR_INVALID_ARGUMENT, "scale strides must be non-negative");
+  KrArgs s;
+  memset(&s, 0, sizeof s);
+  s.items = static_cast<const PaItem*>(plan_dev);
+  s.q = q;
+  s.q_scale = q_scale;
+  s.q_rope = q_rope;
+  s.k_main = k_cache;
+  s.m_sp = k_layout->page; s.m_sh = k_layout->head; s.m_ss = k_layout->slot;
+  if (cfg.mla) {
+    s.k_rope = k_rope;
+    s.r_sp = k_rope_layout->page; s.r_sh = k_rope_layout->head; s.r_ss = k_rope_layout->slot;
+    s.k_scale = k_scale;
+    s.s_sp = k_scale_layout->page; s.s_sh = k_scale_layout->head; s.s_ss = k_scale_layout->slot;
+  } else {                            // the rotary channels are the last 64 of each key row
+    s.k_rope = static_cast<const uint8_t*>(k_cache) + 2 * cfg.dv;
+    s.r_sp = s.m_sp; s.r_sh = s.m_sh; s.r_ss = s.m_ss;
+    s.v = v_cache;
+    s.v_sp = v_layout->page; s.v_sh = v_layout->head; s.v_ss = v_layout->slot;
+  }
+  s.page_indices = page_indices;
+  s.sm_scale = sm_scale;
+  s.partial_o = partial_o;
+  s.partial_lse = partial_lse;
+  s.part_bf16 = partial_o_elem_bytes(info->kv_dtype) == 2;
+  s.out = out;
+  s.out_bf16 = raw(out_dtype) == PA_DTYPE_BF16;
+  s.out_lse = out_lse;
+  s.hq = info->num_q_heads;
+  s.group = info->num_q_heads / info->num_kv_heads;
+  s.page_shift = ilog2_exact(info->page_size);
+  s.s_max = info->max_splits;
+  const int e = launch_stage1_kr(cfg.dv, cfg.mla, s, info->num_items, stream);
+  if (e) return hip_fail(e, "pa_decode_stage1_rope launch");
+  return ok();
+}
+
 pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev, const void* partial_o,
                           const float* partial_lse, void* out, pa_dtype out_dtype, float* out_lse, void* stream) {
   if (!info || !plan_dev || !out) return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_merge: a required pointer is NULL");
@@ -560,7 +667,7 @@ pa_status pa_decode_merge(const pa_plan_info* info, const void* plan_dev, const 
   m.out_lse = out_lse;
   m.total_rows = info->total_rows;
   m.hq = info->num_q_heads;
-  m.dh = info->head_dim;
+  m.dh = info->head_dim_v > 0 ? info->head_dim_v : info->head_dim;
   m.s_max = info->max_splits;
   const int e = launch_merge(m, stream);
   if (e) return hip_fail(e, "pa_decode_merge launch");
@@ -676,6 +783,7 @@ pa_status pa_debug_gather(const pa_plan_info* info, const void* plan_dev, const 
   const KernelCfg cfg = unpack_cfg(info->variant);
   if (!stage1_cfg_supported(cfg) || cfg.dh != info->head_dim)
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_plan_info was not produced by pa_plan_splits");
+  if (cfg.kr) return fail(PA_ERR_UNSUPPORTED, "pa_debug_gather covers the equal-width stage-1 kernel only");
   // INT8 KV runs the per-token scale path for both scale modes (per tensor: zero strides)
   const bool per_token = info->kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD || info->kv_dtype == PA_DTYPE_INT8;
   if (per_token && !scale_off_out)

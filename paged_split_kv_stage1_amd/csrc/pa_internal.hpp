@@ -27,22 +27,31 @@ inline int64_t plan_bytes_for(int64_t items, int64_t rows) { return items * 64 +
 
 // Tile configuration of a stage-1 launch (packed into pa_plan_info.variant).
 struct KernelCfg {
-  int dh;        // 128, 256 or 512
+  int dh;        // key width: 128, 256 or 512; with kr, dv + 64
   int qf8;       // q is e4m3 (fp8 MFMA for q.k)
   int kvf8;      // KV holds one-byte codes (e4m3, or int8 with i8)
   int i8;        // KV codes are int8
   int pt;        // per-(token, KV head) scales
   int wq;        // waves splitting the 16-row query blocks (1, 2, 4); 4/wq waves split tokens
   int nqb;       // 16-row query blocks per wave
+  int kr = 0;    // keys of dv + 64 channels with a 64-channel rotary part (stage1_kr.hip)
+  int mla = 0;   // with kr: MLA-style latent cache (value = latent, e4m3 per 128 channels)
+  int dv = 0;    // value width (= dh unless kr)
 };
 inline int32_t pack_cfg(const KernelCfg& c) {
   return (c.dh == 256 ? 1 : 0) | (c.qf8 << 1) | (c.kvf8 << 2) | (c.pt << 3) | (c.wq << 4) | (c.nqb << 8) |
-         (c.i8 << 12) | ((c.dh == 512 ? 1 : 0) << 13);
+         (c.i8 << 12) | ((c.dh == 512 ? 1 : 0) << 13) | (c.kr << 14) | (c.mla << 15);
 }
 inline KernelCfg unpack_cfg(int32_t v) {
   KernelCfg c;
   c.dh = ((v >> 13) & 1) ? 512 : ((v & 1) ? 256 : 128); c.qf8 = (v >> 1) & 1; c.kvf8 = (v >> 2) & 1; c.pt = (v >> 3) & 1;
   c.wq = (v >> 4) & 15; c.nqb = (v >> 8) & 15; c.i8 = (v >> 12) & 1;
+  c.kr = (v >> 14) & 1; c.mla = (v >> 15) & 1;
+  c.dv = c.dh;
+  if (c.kr) {
+    c.dv = c.mla ? 512 : 128;
+    c.dh = c.dv + 64;
+  }
   return c;
 }
 
@@ -64,6 +73,28 @@ struct Stage1Args {
   float* out_lse;                       // LSE of rows whose request has one split, or NULL
   int hq, group, page_shift, s_max;
   int part_bf16;
+};
+
+// Stage 1 of keys with a 64-channel rotary part (stage1_kr.hip).
+struct KrArgs {
+  const PaItem* items;
+  const void* q;                        // bf16 [T, Hq, dv + 64]; MLA: e4m3 latent codes [T, Hq, dv]
+  const float* q_scale;                 // MLA: [T, Hq, dv / 128]
+  const void* q_rope;                   // MLA: bf16 [T, Hq, 64]
+  const void* k_main;                   // bf16 key rows (dv + 64 channels); MLA: latent codes
+  int64_t m_sp, m_sh, m_ss;             // element strides (page, head, slot) of k_main
+  const void* k_rope;                   // rotary channels: k_main + dv elements, or MLA's bf16 cache
+  int64_t r_sp, r_sh, r_ss;
+  const void* v;                        // bf16 value rows (dv channels); MLA: unused (value = latent)
+  int64_t v_sp, v_sh, v_ss;
+  const float* k_scale;                 // MLA: latent scales, dv / 128 per (page, head, slot)
+  int64_t s_sp, s_sh, s_ss;
+  const int32_t* page_indices;
+  float sm_scale;
+  void* partial_o; float* partial_lse;  // partial O: float32, or bf16 when part_bf16
+  void* out; float* out_lse;
+  int out_bf16, part_bf16;
+  int hq, group, page_shift, s_max;
 };
 
 struct MergeArgs {
@@ -94,5 +125,6 @@ int launch_gather(const KernelCfg& cfg, const GatherArgs& a, int num_items, void
 int launch_quant(const void* src, int src_bf16, int64_t n_rows, int head_dim, int per_tensor, int i8,
                  uint8_t* dst, float* scale, void* stream);
 bool stage1_cfg_supported(const KernelCfg& cfg);
+int launch_stage1_kr(int dv, bool mla, const KrArgs& a, int num_items, void* stream);
 
 }  // namespace pa

@@ -1,0 +1,397 @@
+// Stage 1 for keys that carry a 64-channel rotary part: keys of DV + 64 channels, values
+// of DV channels (FlashInfer PR #869, "Remaining Work": separate head_dim_qk and
+// head_dim_v), in two cache forms:
+//   SEP -- bf16 K rows of DV + 64 channels in one cache and bf16 V rows of DV channels in
+//          another (head_dim_qk 192, head_dim_v 128);
+//   MLA -- the latent cache of multi-head latent attention in its absorbed form (FlashMLA
+//          PR #54, review thread: the "nope" part in 8 bits with one scale per token and
+//          128 channels, the rotary part kept in 16 bits): the key is [latent, rotary] with
+//          the latent as e4m3 codes plus float32 scales per (token, 128 channels) and the
+//          rotary part a bf16 cache of its own, and the value is the latent itself.  The
+//          query's latent part is e4m3 with a scale per (row, head, 128 channels), its
+//          rotary part bf16.
+//
+// One workgroup (4 waves) per work item (request, KV head, split, group of four 16-row
+// query blocks); wave w runs block qblk0 + w.  Scores are computed transposed, S^T = K Q^T
+// (tokens on the MFMA M axis), so that their accumulator is the P^T operand of
+// O^T = V^T P^T, as in the main stage-1 kernel.  K/V tiles of 32 tokens stream HBM ->
+// registers -> LDS (two stages) with the page-gather address code of kv_addr.hpp.
+//   QK: bf16 MFMA 16x16x32; e4m3 latent codes are upconverted exactly.  With MLA the latent
+//       part accumulates per 128-channel block and each block's sum is scaled by the
+//       token's and the row's scale of that block before the rotary part is added.
+//   softmax: log2 domain, per-row causal / window masks, lazy rescale.
+//   PV: SEP -- P as two bf16 terms (hi + lo) against bf16 V; MLA -- P times the token's
+//       latent scale of each 128-channel block, one bf16 term, against the upconverted
+//       latent codes.
+#include "common.hpp"
+#include "kv_addr.hpp"
+
+namespace pa {
+
+namespace {
+
+constexpr float kLog2eKr = 1.4426950408889634f;
+constexpr float kLn2Kr = 0.6931471805599453f;
+
+// XOR swizzle of the 16-byte chunk index within a token row in LDS (row-wise reads of 16
+// tokens x one chunk, and transposing reads of 4 or 8 tokens x one chunk, spread over banks).
+template <int CPR>
+__device__ __forceinline__ int swz(int t) {
+  if constexpr (CPR >= 16) return t & 15;
+  else return (t >> 1) & (CPR - 1);
+}
+
+template <int DV, bool MLA>
+struct KrCfg {
+  static constexpr int BN = 32;                       // tokens per tile
+  static constexpr int DR = 64;                       // rotary channels
+  static constexpr int MB = MLA ? 1 : 2;              // bytes per main-part element
+  static constexpr int CPR_M = DV * MB / 16;          // 16-byte chunks per main-part row
+  static constexpr int CPR_R = DR * 2 / 16;           // ... per rotary row (bf16)
+  static constexpr int CPR_V = MLA ? 0 : DV * 2 / 16; // ... per value row (SEP, bf16)
+  static constexpr int CPT_M = BN * CPR_M / 256;      // chunks per thread per tile
+  static constexpr int CPT_R = BN * CPR_R / 256;
+  static constexpr int CPT_V = BN * CPR_V / 256;
+  static constexpr int NBLK = DV / 128;               // 128-channel blocks of the latent
+  static constexpr int MTB = BN * DV * MB;            // LDS bytes of the main tile
+  static constexpr int RTB = BN * DR * 2;
+  static constexpr int VTB = BN * DV * 2 * (MLA ? 0 : 1);
+  static constexpr int STB = MLA ? BN * NBLK * 4 : 0; // latent scales of the tile
+  static constexpr int STAGEB = MTB + RTB + VTB + STB;
+  static constexpr int KCM = DV / 32;                 // K-steps of q.k over the main part
+  static constexpr int KCR = DR / 32;                 // ... over the rotary part
+  static constexpr int DB = DV / 16;                  // 16-wide output blocks
+  static_assert(CPT_M >= 1 && CPT_R >= 1 && (MLA || CPT_V >= 1), "tile must split over 256 threads");
+  static_assert(!MLA || DV % 128 == 0, "latent scales cover 128 channels");
+};
+
+template <int DV, bool MLA>
+__global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
+  using C = KrCfg<DV, MLA>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGEB];
+
+  const PaItem it = a.items[blockIdx.x];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int L16 = lane & 15;
+  const int g = lane >> 4;
+  const int G = a.group;
+  const int Hq = a.hq;
+  const int Mq = it.nrows * G;
+  const int tb0 = it.tok_begin;
+  const int te = it.tok_end;
+  const int shift = a.page_shift;
+  const int pmask = (1 << shift) - 1;
+
+  // ---- this wave's query block: rows, limits, operand -------------------------------------
+  const int qb = it.qblk0 + wave;
+  const bool has_rows = 16 * qb < Mq;
+  const int m = 16 * qb + L16;
+  const int mr = m < Mq ? m : Mq - 1;                  // rows past Mq repeat the last real row
+  const int r = mr / G;
+  const int hl = mr - r * G;
+  const int p = it.kv_len - it.nrows + r;
+  const int lo = it.window > 0 ? max(0, p - it.window + 1) : 0;
+  const int lim_lo = max(lo, tb0);
+  const int lim_hi = min(p, te - 1);
+  const int p_first = it.kv_len - it.nrows;
+  const int lo_last = it.window > 0 ? max(0, it.kv_len - 1 - it.window + 1) : 0;
+  const int vis_lo_all = max(lo_last, tb0);
+  const int vis_hi_all = min(p_first, te - 1);
+  const int64_t th = (int64_t)(it.row0 + r) * Hq + (int64_t)it.kvh * G + hl;    // (row, query head)
+
+  bf16x8 qm[C::KCM], qr[C::KCR];
+  float qs[MLA ? C::NBLK : 1];
+  if constexpr (MLA) {
+    const uint8_t* qc = static_cast<const uint8_t*>(a.q) + th * DV;
+#pragma unroll
+    for (int kc = 0; kc < C::KCM; ++kc) {
+      const uint2 w = *reinterpret_cast<const uint2*>(qc + kc * 32 + 8 * g);
+      qm[kc] = fp8x8_to_bf16x8(w.x, w.y);              // exact
+    }
+    const __bf16* qrp = static_cast<const __bf16*>(a.q_rope) + th * C::DR;
+#pragma unroll
+    for (int kc = 0; kc < C::KCR; ++kc) qr[kc] = *reinterpret_cast<const bf16x8*>(qrp + kc * 32 + 8 * g);
+#pragma unroll
+    for (int b = 0; b < C::NBLK; ++b) qs[b] = a.q_scale[th * C::NBLK + b];
+  } else {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + th * (DV + C::DR);
+#pragma unroll
+    for (int kc = 0; kc < C::KCM; ++kc) qm[kc] = *reinterpret_cast<const bf16x8*>(qp + kc * 32 + 8 * g);
+#pragma unroll
+    for (int kc = 0; kc < C::KCR; ++kc) qr[kc] = *reinterpret_cast<const bf16x8*>(qp + DV + kc * 32 + 8 * g);
+    qs[0] = 1.f;
+  }
+  const float qk_scale = a.sm_scale * kLog2eKr;
+
+  f32x4 o[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;
+
+  // ---- tile loads: HBM -> registers -> LDS -------------------------------------------------
+  using AM = KvTileAddr<C::CPR_M, C::BN, C::MB>;
+  using AR = KvTileAddr<C::CPR_R, C::BN, 2>;
+  const AM am(lane, a.m_ss);
+  const AR ar(lane, a.r_ss);
+  const cint32* pidx = (const cint32*)(a.page_indices) + it.page_base;
+  const uint8_t* mbase = static_cast<const uint8_t*>(a.k_main);
+  const uint8_t* rbase = static_cast<const uint8_t*>(a.k_rope);
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v);
+  const int64_t mhead = (int64_t)it.kvh * a.m_sh, rhead = (int64_t)it.kvh * a.r_sh, vhead = (int64_t)it.kvh * a.v_sh;
+  u32x4 mreg[C::CPT_M], rreg[C::CPT_R], vreg[C::CPT_V > 0 ? C::CPT_V : 1];
+  float sreg = 0.f;
+  auto load_tile = [&](int tile0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::CPT_M; ++i) {
+      const int jb = AM::group_token(tile0, wave, i, te);
+      const int32_t pg = AM::group_page(pidx, jb, shift);
+      mreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          mbase + AM::row_offset(pg, jb, a.m_sp, mhead, a.m_ss, pmask) + am.lane_offset(jb, te, a.m_ss)));
+    }
+#pragma unroll
+    for (int i = 0; i < C::CPT_R; ++i) {
+      const int jb = AR::group_token(tile0, wave, i, te);
+      const int32_t pg = AR::group_page(pidx, jb, shift);
+      rreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          rbase + AR::row_offset(pg, jb, a.r_sp, rhead, a.r_ss, pmask) + ar.lane_offset(jb, te, a.r_ss)));
+    }
+    if constexpr (!MLA) {
+      using AV = KvTileAddr<C::CPR_V, C::BN, 2>;
+      const AV av(lane, a.v_ss);
+#pragma unroll
+      for (int i = 0; i < C::CPT_V; ++i) {
+        const int jb = AV::group_token(tile0, wave, i, te);
+        const int32_t pg = AV::group_page(pidx, jb, shift);
+        vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            vbase + AV::row_offset(pg, jb, a.v_sp, vhead, a.v_ss, pmask) + av.lane_offset(jb, te, a.v_ss)));
+      }
+    } else {
+      if (tid < C::BN * C::NBLK) {                 // one latent scale per thread
+        const int j = min(tile0 + tid / C::NBLK, te - 1);
+        const int32_t pg = pidx[j >> shift];
+        sreg = __builtin_nontemporal_load(a.k_scale + (int64_t)pg * a.s_sp + (int64_t)it.kvh * a.s_sh +
+                                          (int64_t)(j & pmask) * a.s_ss + tid % C::NBLK);
+      }
+    }
+  };
+  // LDS: chunk c of token t of a tile sits at 16-byte unit t * CPR + (c ^ swz(t)).
+  auto store_tile = [&](uint8_t* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::CPT_M; ++i) {
+      const int t = (wave * 64 + 256 * i) / C::CPR_M + am.lt;
+      *reinterpret_cast<u32x4*>(st + ((t * C::CPR_M + (am.cpos ^ swz<C::CPR_M>(t))) << 4)) = mreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::CPT_R; ++i) {
+      const int t = (wave * 64 + 256 * i) / C::CPR_R + ar.lt;
+      *reinterpret_cast<u32x4*>(st + C::MTB + ((t * C::CPR_R + (ar.cpos ^ swz<C::CPR_R>(t))) << 4)) = rreg[i];
+    }
+    if constexpr (!MLA) {
+      const int lt = lane / C::CPR_V, cp = lane % C::CPR_V;
+#pragma unroll
+      for (int i = 0; i < C::CPT_V; ++i) {
+        const int t = (wave * 64 + 256 * i) / C::CPR_V + lt;
+        *reinterpret_cast<u32x4*>(st + C::MTB + C::RTB + ((t * C::CPR_V + (cp ^ swz<C::CPR_V>(t))) << 4)) = vreg[i];
+      }
+    } else {
+      if (tid < C::BN * C::NBLK) reinterpret_cast<float*>(st + C::MTB + C::RTB)[tid] = sreg;
+    }
+  };
+
+  // ---- one tile: S^T, softmax, O^T += V^T P^T ------------------------------------------------
+  auto compute_tile = [&](int tile0, const uint8_t* st) __attribute__((always_inline)) {
+    if (!has_rows) return;
+    const uint8_t* Ml = st;
+    const uint8_t* Rl = st + C::MTB;
+    const int tk[2] = {L16, 16 + L16};               // K rows (tokens) of the two 16-token halves
+    float x[8];
+    const float* scl = reinterpret_cast<const float*>(st + C::MTB + C::RTB);   // MLA: [BN][NBLK]
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int t = tk[tb];
+      f32x4 rs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < C::KCR; ++kc) {
+        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Rl + ((t * C::CPR_R + ((4 * kc + g) ^ swz<C::CPR_R>(t))) << 4));
+        rs = mfma_bf16(kv, qr[kc], rs);
+      }
+      if constexpr (MLA) {
+        // per 128-channel block: sum_c qcode * kcode, then times the row's and the token's scale
+        f32x4 acc = rs;
+#pragma unroll
+        for (int b = 0; b < C::NBLK; ++b) {
+          f32x4 sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const int kc = 4 * b + kk;
+            const uint2 w = *reinterpret_cast<const uint2*>(
+                Ml + ((t * C::CPR_M + ((2 * kc + (g >> 1)) ^ swz<C::CPR_M>(t))) << 4) + 8 * (g & 1));
+            sb = mfma_bf16(fp8x8_to_bf16x8(w.x, w.y), qm[kc], sb);
+          }
+          // accumulator lane layout: rows (tokens) 4 * g + k of this half, column L16 (query row)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[k] = fmaf(sb[k], qs[b] * scl[(16 * tb + 4 * g + k) * C::NBLK + b], acc[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[4 * tb + k] = acc[k];
+      } else {
+        f32x4 acc = rs;
+#pragma unroll
+        for (int kc = 0; kc < C::KCM; ++kc) {
+          const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Ml + ((t * C::CPR_M + ((4 * kc + g) ^ swz<C::CPR_M>(t))) << 4));
+          acc = mfma_bf16(kv, qm[kc], acc);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[4 * tb + k] = acc[k];
+      }
+    }
+    // ---- scale, mask, online softmax
+    const bool need_mask = !(tile0 >= vis_lo_all && tile0 + 31 <= vis_hi_all);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x[k] *= qk_scale;
+      if (need_mask) {
+        const int j = tile0 + (k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4));
+        x[k] = (j >= lim_lo && j <= lim_hi) ? x[k] : -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mx = wave_max_xor_16_32(mx);
+    const float mnew = fmaxf(mrun, mx);
+    const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+    if (__builtin_amdgcn_ballot_w64(mnew != mrun) != 0) {
+      const float alpha = fast_exp2(mrun - muse);
+      lrun *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+      mrun = mnew;
+    }
+    float pv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      pv[k] = fast_exp2(x[k] - muse);
+      lrun += pv[k];
+    }
+    // ---- O^T += V^T P^T
+    if constexpr (MLA) {
+      // transposing read of 8 tokens x one 16-channel block of the latent codes
+      const int jr = L16 >> 1;
+      const int tv = jr < 4 ? 4 * g + jr : 16 + 4 * g + (jr - 4);
+#pragma unroll
+      for (int b = 0; b < C::NBLK; ++b) {
+        bf16x8 pb;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int tok = k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4);
+          pb[k] = (__bf16)(pv[k] * scl[tok * C::NBLK + b]);
+        }
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          const int db = 8 * b + dd;
+          const uint32_t addr = ((tv * C::CPR_M + (db ^ swz<C::CPR_M>(tv))) << 4) + 8 * (L16 & 1);
+          const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Ml + addr));
+          o[db] = mfma_bf16(fp8x8_to_bf16x8((uint32_t)w[0], (uint32_t)w[1]), pb, o[db]);
+        }
+      }
+    } else {
+      const uint8_t* Vl = st + C::MTB + C::RTB;
+      bf16x8 hv, lv;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const __bf16 h = (__bf16)pv[k];
+        hv[k] = h;
+        lv[k] = (__bf16)(pv[k] - (float)h);
+      }
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        bf16x8 va;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int t1 = 4 * g + (L16 >> 2) + 16 * half;
+          const int c = 2 * db + ((L16 & 3) >> 1);
+          const uint32_t addr = ((t1 * C::CPR_V + (c ^ swz<C::CPR_V>(t1))) << 4) + 8 * (L16 & 1);
+          const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + addr));
+          const __bf16* pvv = reinterpret_cast<const __bf16*>(&v);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) va[4 * half + k] = pvv[k];
+        }
+        o[db] = mfma_bf16(va, hv, o[db]);
+        o[db] = mfma_bf16(va, lv, o[db]);
+      }
+    }
+  };
+
+  const int ntiles = te > tb0 ? (te - tb0 + C::BN - 1) / C::BN : 0;
+  if (ntiles > 0) {
+    load_tile(tb0);
+    __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);      // vmcnt(0) lgkmcnt(0)
+    store_tile(smem);
+    __syncthreads();
+  }
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int tile0 = tb0 + ti * C::BN;
+    const bool more = ti + 1 < ntiles;
+    if (more) load_tile(tile0 + C::BN);                // next tile in flight during this one
+    compute_tile(tile0, smem + (ti & 1) * C::STAGEB);
+    if (more) {
+      store_tile(smem + ((ti + 1) & 1) * C::STAGEB);   // the other stage was last read a tile ago
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue -------------------------------------------------------------------------------
+  if (!has_rows || m >= Mq) return;
+  const float ltot = wave_sum_xor_16_32(lrun);
+  const bool empty = !(ltot > 0.f);
+  const float sc = empty ? 0.f : 1.f / ltot;
+  const float lse = empty ? -INFINITY : (mrun + __log2f(ltot)) * kLn2Kr;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  if (it.nsplit == 1) {
+    if (a.out_lse && g == 0) a.out_lse[th] = lse;
+    if (a.out_bf16) {
+      __bf16* dst = static_cast<__bf16*>(a.out) + th * DV;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        bf16x4 v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = (__bf16)(o[db][k] * sc);
+        *reinterpret_cast<bf16x4*>(dst + 16 * db + 4 * g) = v;
+      }
+    } else {
+      float* dst = static_cast<float*>(a.out) + th * DV;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = o[db] * sc;
+    }
+  } else {
+    if (g == 0) a.partial_lse[th * a.s_max + it.split] = lse;
+    if (a.part_bf16) {
+      __bf16* dst = static_cast<__bf16*>(a.partial_o) + (th * a.s_max + it.split) * DV;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        bf16x4 v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = (__bf16)(o[db][k] * sc);
+        *reinterpret_cast<bf16x4*>(dst + 16 * db + 4 * g) = v;
+      }
+    } else {
+      float* dst = static_cast<float*>(a.partial_o) + (th * a.s_max + it.split) * DV;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = o[db] * sc;
+    }
+  }
+}
+
+}  // namespace
+
+int launch_stage1_kr(int dv, bool mla, const KrArgs& a, int num_items, void* stream) {
+  if (num_items <= 0) return 0;
+  const hipStream_t s = (hipStream_t)stream;
+  if (!mla && dv == 128) hipLaunchKernelGGL((stage1_kr_kernel<128, false>), dim3(num_items), dim3(256), 0, s, a);
+  else if (mla && dv == 512) hipLaunchKernelGGL((stage1_kr_kernel<512, true>), dim3(num_items), dim3(256), 0, s, a);
+  else return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+}  // namespace pa

@@ -67,8 +67,8 @@ extern "C" pa_status pa_validate_page_indices(const pa_plan_info* info, const vo
   }
   if (count > 0) {
     char msg[200];
-    snprintf(msg, sizeof msg, "pa_validate_page_indices: %d page-table entries read by the plan lie outside "
-             "[0, %lld); the first is page_indices[%d]", count, (long long)num_pages, first);
+    snprintf(msg, sizeof msg, "pa_validate_page_indices: %d reads of page-table entries outside [0, %lld) by the "
+             "plan's work items; the first offending entry is page_indices[%d]", count, (long long)num_pages, first);
     return (pa_status)report_error(PA_ERR_INVALID_ARGUMENT, msg);
   }
   return (pa_status)report_error(PA_OK, "");

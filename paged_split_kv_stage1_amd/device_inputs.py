@@ -29,6 +29,10 @@ class DeviceInputs:
     layout: str
     kv_layout: tuple                 # element strides (page, head, slot)
     scale_layout: Optional[tuple]
+    v_layout: Optional[tuple] = None        # value strides when values are narrower than keys
+    k_rope: Optional[torch.Tensor] = None   # latent cache: bf16 rotary rows [pages, Hkv, P, 64]
+    rope_layout: Optional[tuple] = None
+    q_rope: Optional[torch.Tensor] = None   # latent cache: bf16 [T, Hq, 64]
 
 
 def _strides(layout: str, Hkv: int, P: int, d: int):
@@ -60,7 +64,45 @@ def _quantize(src_bf16: torch.Tensor, mode: str, d: int, device, int8: bool = Fa
     return codes, scale
 
 
+def _to_device_rope(w: Workload, device) -> DeviceInputs:
+    """Keys wider than values ([pages, Hkv, P, d] layout): bf16 192/128 caches, or the
+    MLA-style latent cache (latent codes with a scale per (token, 128 channels) from the
+    library's quantiser over 128-channel rows, bf16 rotary rows; queries likewise)."""
+    d, dv, P, Hkv = w.head_dim, w.dv, w.page_size, w.num_kv_heads
+    unused = torch.from_numpy(w.unused_slots).to(device)
+    m4 = unused[:, None, :, None]
+    if not w.latent:
+        k = w.k.to(device)
+        v = w.v.to(device)
+        k.view(torch.int16).masked_fill_(m4.expand(k.shape), BF16_NAN_BITS)
+        v.view(torch.int16).masked_fill_(m4.expand(v.shape), BF16_NAN_BITS)
+        return DeviceInputs(q=w.q.to(device), q_scale=None, k=k, v=v, k_scale=None, v_scale=None,
+                            page_indices=torch.from_numpy(np.ascontiguousarray(w.page_indices)).to(device),
+                            layout="HPD", kv_layout=(Hkv * P * d, P * d, d), scale_layout=None,
+                            v_layout=(Hkv * P * dv, P * dv, dv))
+    src = w.k.to(device)
+    lat = src[..., :dv].contiguous()
+    codes, scale = _quantize(lat.view(*lat.shape[:-1], dv // 128, 128), "per_token_head", 128, device)
+    codes = codes.view(lat.shape)
+    rope = src[..., dv:].contiguous()
+    codes.masked_fill_(m4.expand(codes.shape), E4M3_NAN_CODE)
+    scale.masked_fill_(m4.expand(scale.shape), float("nan"))
+    rope.view(torch.int16).masked_fill_(m4.expand(rope.shape), BF16_NAN_BITS)
+    qsrc = w.q.to(device)
+    qn = qsrc[..., :dv].contiguous()
+    qc, qs = _quantize(qn.view(*qn.shape[:-1], dv // 128, 128), "per_token_head", 128, device)
+    dr = d - dv
+    return DeviceInputs(q=qc.view(qn.shape), q_scale=qs, k=codes, v=None, k_scale=scale, v_scale=None,
+                        page_indices=torch.from_numpy(np.ascontiguousarray(w.page_indices)).to(device),
+                        layout="HPD", kv_layout=(Hkv * P * dv, P * dv, dv),
+                        scale_layout=(Hkv * P * (dv // 128), P * (dv // 128), dv // 128),
+                        k_rope=rope, rope_layout=(Hkv * P * dr, P * dr, dr), q_rope=qsrc[..., dv:].contiguous())
+
+
 def to_device(w: Workload, device="cuda", layout: str = "HPD") -> DeviceInputs:
+    if w.dv != w.head_dim:
+        assert layout == "HPD", "keys wider than values: [pages, Hkv, P, d] caches"
+        return _to_device_rope(w, device)
     d, P, Hkv = w.head_dim, w.page_size, w.num_kv_heads
     kv_layout, sc_layout = _strides(layout, Hkv, P, d)
     k_src, v_src = w.k, w.v

@@ -35,8 +35,8 @@ void one_case(int cs) {
   const int nb = B > 0 ? B : 1;
   const int psizes[] = {16, 32, 64, 1024, 8, 48, 2048};
   const int P = wild ? pick(psizes) : pick(psizes) % 2048 > 0 && pick(psizes) >= 16 ? 16 << uni(0, 6) : 16;
-  const int dims[] = {128, 256, 512, 64, 96};
-  const int d = wild ? pick(dims) : dims[uni(0, 2)];
+  const int dims[] = {128, 256, 512, 192, 576, 64, 96};
+  int d = wild ? pick(dims) : dims[uni(0, 4)];
   const int hkvs[] = {1, 2, 8};
   const int Hkv = pick(hkvs);
   const int gs[] = {1, 2, 8, 24, 3};
@@ -54,6 +54,9 @@ void one_case(int cs) {
     kvi[b + 1] = kvi[b] + (int32_t)pages + (wild && next() % 10 == 0 ? 1 : 0);
     win[b] = next() % 2 ? 0 : (wild && next() % 10 == 0 ? -3 : uni(1, 2000));
   }
+  // keys wider than values: 192/128 bf16 or the 576/512 latent cache; sometimes a wrong pair
+  const int dvs[] = {0, 128, 512, 100};
+  const int dv = d == 192 ? 128 : d == 576 ? 512 : (wild ? pick(dvs) : 0);
   const pa_dtype qd[] = {PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3};
   const pa_dtype kd[] = {PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3, PA_DTYPE_INT8};
   pa_plan_args a;
@@ -72,6 +75,16 @@ void one_case(int cs) {
   a.kv_dtype = pick(kd);
   a.kv_scale_mode = a.kv_dtype == PA_DTYPE_BF16 ? PA_SCALE_NONE
                     : (pa_scale_mode)(a.kv_dtype == PA_DTYPE_INT8 ? (next() % 2 ? 1 : 2) : uni(1, 3));
+  if (d == 576 && !wild) {
+    a.q_dtype = PA_DTYPE_FP8_E4M3;
+    a.kv_dtype = PA_DTYPE_FP8_E4M3;
+    a.kv_scale_mode = PA_SCALE_PER_TOKEN_BLOCK128;
+  } else if (d == 192 && !wild) {
+    a.q_dtype = PA_DTYPE_BF16;
+    a.kv_dtype = PA_DTYPE_BF16;
+    a.kv_scale_mode = PA_SCALE_NONE;
+  }
+  a.head_dim_v = dv;
   if (wild && next() % 6 == 0) a.kv_scale_mode = (pa_scale_mode)uni(0, 5);
   const int cus[] = {1, 8, 256, 304};
   a.num_cus = pick(cus);

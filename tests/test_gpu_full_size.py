@@ -30,7 +30,7 @@ def _samples(w, rng, n=6):
 
 
 @pytest.mark.parametrize("name", ["c2", "c2_ph", "c3", "c3_b1", "c3_r1", "c3_r8", "c4", "c4_r1", "c4_b1", "c4_b1_r1",
-                                  "c4_i8", "c5", "c6", "c6_f8"])
+                                  "c4_i8", "c5", "c6", "c6_f8", "f3", "f3_r4", "mla", "mla_r2"])
 def test_full_size_whole_request_and_samples(name):
     print(f"[full-size] {name}", flush=True)
     w = make_workload(name)

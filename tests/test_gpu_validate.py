@@ -32,7 +32,8 @@ def test_validate_accepts_a_good_table_and_reports_bad_entries():
     with pytest.raises(PaError) as e:
         pa_validate_page_indices(pd.info, pd.plan, bad, npages)
     assert e.value.status == PA_ERR_INVALID_ARGUMENT
-    assert "2 page-table entries" in str(e.value) and "page_indices[5]" in str(e.value)
+    # each entry is read by the items of both KV heads: 2 bad entries, 4 reads
+    assert "4 reads" in str(e.value) and "page_indices[5]" in str(e.value)
     with pytest.raises(PaError):        # one page fewer in the caches: the largest entry is out
         pa_validate_page_indices(pd.info, pd.plan, di.page_indices, int(di.page_indices.max().item()))
 
