@@ -64,7 +64,8 @@ def _cpu_model() -> str:
     return platform.processor()
 
 
-KERNEL_SOURCES = ("stage1.hip", "common.hpp", "pa_internal.hpp")
+KERNEL_SOURCES = ("stage1.hip", "common.hpp", "kv_addr.hpp", "pa_internal.hpp")
+KR_SOURCES = ("stage1_kr.hip", "common.hpp", "kv_addr.hpp", "pa_internal.hpp")
 
 
 def kernel_code(text: str) -> str:
@@ -96,7 +97,7 @@ def measured_traffic(config: str, kernel: str = "stage1_kernel", sources=KERNEL_
     import glob
 
     digest = source_digest(sources)
-    for path in glob.glob(os.path.join(ROOT, "profiles", f"{kernel}_{config}_*_hbm_traffic.txt")):
+    for path in glob.glob(os.path.join(ROOT, "profiles", f"{kernel}_{config}*_hbm_traffic.txt")):
         fields = {}
         for line in open(path):
             if ":" in line:
@@ -564,8 +565,10 @@ def main():
         "tflops": round(acc["flops"] / (us_step * 1e-6) / 1e12, 3),
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "roofline": {"bound": "hbm", "achieved": round(roof_achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(roof_achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(args.config),
-                     "kernel": "stage1_kernel", "bytes_per_launch": s1_bytes},
+                     "frac": round(roof_achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(args.config, *(("stage1_kr_kernel", KR_SOURCES) if pd.rope else
+                                                                ("stage1_kernel", KERNEL_SOURCES))),
+                     "kernel": "stage1_kr_kernel" if pd.rope else "stage1_kernel", "bytes_per_launch": s1_bytes},
     }
     if not args.no_per_config and args.config == "c2":
         result["per_config"], result["r8_over_r1"] = per_config(args, flush, stream)
