@@ -69,9 +69,10 @@ namespace pa {
 // same list).
 bool stage1_cfg_supported(const KernelCfg& c) {
   // keys with a rotary part (stage1_kr.hip): bf16 192/128, or the MLA latent cache 576/512
-  // with e4m3 latent codes and e4m3 latent queries; one 16-row block per wave
+  // with e4m3 latent codes and e4m3 latent queries; one, two or four 16-row blocks per
+  // item, the four waves splitting each tile's tokens between the blocks' teams
   if (c.kr) {
-    if (c.wq != 4 || c.nqb != 1) return false;
+    if ((c.wq != 1 && c.wq != 2 && c.wq != 4) || c.nqb != 1) return false;   // blocks per item
     if (c.mla) return c.dv == 512 && c.dh == 576 && c.qf8 && c.kvf8 && !c.i8;
     return c.dv == 128 && c.dh == 192 && !c.qf8 && !c.kvf8 && !c.pt;
   }
@@ -101,14 +102,14 @@ bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
   const int nqb = (mq + 15) / 16;
   c->dh = a.head_dim;
   c->dv = a.head_dim_v > 0 ? a.head_dim_v : a.head_dim;
-  if (c->dv != c->dh) {               // keys with a rotary part: one block per wave, groups of four
+  if (c->dv != c->dh) {               // keys with a rotary part: up to four blocks per item
     c->kr = 1;
     c->mla = a.kv_scale_mode == PA_SCALE_PER_TOKEN_BLOCK128;
     c->qf8 = a.q_dtype == PA_DTYPE_FP8_E4M3;
     c->kvf8 = a.kv_dtype != PA_DTYPE_BF16;
     c->i8 = a.kv_dtype == PA_DTYPE_INT8;
     c->pt = c->mla;
-    c->wq = 4;
+    c->wq = nqb <= 1 ? 1 : nqb == 2 ? 2 : 4;     // blocks per item; 4 / wq waves per block
     c->nqb = 1;
     return stage1_cfg_supported(*c);
   }
@@ -202,7 +203,8 @@ CostModel cost_model(const pa_plan_args& a, const KernelCfg& cfg, int num_cus) {
              (a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD ? 8 : 0);
   if (cfg.kr)                           // key rows of dh channels, value rows of dv (MLA: shared)
     m.kv_tok = cfg.mla ? cfg.dv + 2.0 * 64 + 4.0 * cfg.dv / 128 : 2.0 * (cfg.dh + cfg.dv);
-  m.slots = (cfg.dh == 512 ? 1 : kSlotsPerCu) * num_cus;   // head_dim 512: one workgroup per CU
+  // head_dim 512 and the latent cache: one workgroup per CU (registers, LDS)
+  m.slots = (cfg.dh == 512 || cfg.mla ? 1 : kSlotsPerCu) * num_cus;
   m.bw_slot = kHbmBytesPerS / m.slots;
   const int wt = 4 / cfg.wq;                     // waves sharing the tokens of a tile
   const double comp_blk = compute_s_per_token_block(a);
@@ -642,7 +644,7 @@ pa_status pa_decode_stage1_rope(const pa_plan_info* info, const void* plan_dev, 
   s.group = info->num_q_heads / info->num_kv_heads;
   s.page_shift = ilog2_exact(info->page_size);
   s.s_max = info->max_splits;
-  const int e = launch_stage1_kr(cfg.dv, cfg.mla, s, info->num_items, stream);
+  const int e = launch_stage1_kr(cfg.dv, cfg.mla, cfg.wq, s, info->num_items, stream);
   if (e) return hip_fail(e, "pa_decode_stage1_rope launch");
   return ok();
 }

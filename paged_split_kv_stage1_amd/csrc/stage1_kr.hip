@@ -11,14 +11,19 @@
 //          query's latent part is e4m3 with a scale per (row, head, 128 channels), its
 //          rotary part bf16.
 //
-// One workgroup (4 waves) per work item (request, KV head, split, group of four 16-row
-// query blocks); wave w runs block qblk0 + w.  Scores are computed transposed, S^T = K Q^T
-// (tokens on the MFMA M axis), so that their accumulator is the P^T operand of
-// O^T = V^T P^T, as in the main stage-1 kernel.  K/V tiles of 32 tokens stream HBM ->
-// registers -> LDS (two stages) with the page-gather address code of kv_addr.hpp.
-//   QK: bf16 MFMA 16x16x32; e4m3 latent codes are upconverted exactly.  With MLA the latent
-//       part accumulates per 128-channel block and each block's sum is scaled by the
-//       token's and the row's scale of that block before the rotary part is added.
+// One workgroup (4 waves) per work item (request, KV head, split, group of one, two or four
+// 16-row query blocks): the rows x heads of one KV head often fill a single block here
+// (16 query heads per latent head), so the waves split the tokens of each 128-token tile
+// between them as far as the blocks leave waves free, and combine their (max, sum, O) at
+// the end.  Scores are computed
+// transposed, S^T = K Q^T (tokens on the MFMA M axis), so that their accumulator is the P^T
+// operand of O^T = V^T P^T, as in the main stage-1 kernel.  K/V tiles stream HBM ->
+// registers -> LDS (one stage, the next tile's loads in flight in registers) with the
+// page-gather address code of kv_addr.hpp.
+//   QK: bf16 MFMA 16x16x32 on bf16 parts; with MLA each 128-channel block of the latent is
+//       one 16x16x128 e4m3 MFMA over the raw codes of keys and queries (exact products,
+//       fp32 sums), scaled by the token's and the row's scale of that block, and the bf16
+//       rotary part is added.
 //   softmax: log2 domain, per-row causal / window masks, lazy rescale.
 //   PV: SEP -- P as two bf16 terms (hi + lo) against bf16 V; MLA -- P times the token's
 //       latent scale of each 128-channel block, one bf16 term, against the upconverted
@@ -29,6 +34,9 @@
 namespace pa {
 
 namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2eKr = 1.4426950408889634f;
 constexpr float kLn2Kr = 0.6931471805599453f;
@@ -43,7 +51,7 @@ __device__ __forceinline__ int swz(int t) {
 
 template <int DV, bool MLA>
 struct KrCfg {
-  static constexpr int BN = 32;                       // tokens per tile
+  static constexpr int BN = 128;                      // tokens per tile: four 32-token quarters
   static constexpr int DR = 64;                       // rotary channels
   static constexpr int MB = MLA ? 1 : 2;              // bytes per main-part element
   static constexpr int CPR_M = DV * MB / 16;          // 16-byte chunks per main-part row
@@ -58,17 +66,32 @@ struct KrCfg {
   static constexpr int VTB = BN * DV * 2 * (MLA ? 0 : 1);
   static constexpr int STB = MLA ? BN * NBLK * 4 : 0; // latent scales of the tile
   static constexpr int STAGEB = MTB + RTB + VTB + STB;
-  static constexpr int KCM = DV / 32;                 // K-steps of q.k over the main part
+  static constexpr int SPT = MLA ? BN * NBLK / 256 : 0;   // latent scales loaded per thread
+  static constexpr int KCM = DV / 32;                 // K-steps of q.k over a bf16 main part
   static constexpr int KCR = DR / 32;                 // ... over the rotary part
   static constexpr int DB = DV / 16;                  // 16-wide output blocks
+  static constexpr int OWB = 64 * 4 * DB * 4;         // bytes of one wave's O in the combine
   static_assert(CPT_M >= 1 && CPT_R >= 1 && (MLA || CPT_V >= 1), "tile must split over 256 threads");
-  static_assert(!MLA || DV % 128 == 0, "latent scales cover 128 channels");
+  static_assert(!MLA || (DV % 128 == 0 && SPT >= 1), "latent scales cover 128 channels");
 };
 
-template <int DV, bool MLA>
+// 16x16x128 with e4m3 A and B (32 bytes per lane: A lane l holds row l%16, B lane l column
+// l%16, both over the same 32 K positions of lane group l/16); no extra scaling.
+__device__ __forceinline__ f32x4 mfma_fp8_k128_kr(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// One work item is (request, KV head, split, group of WQ 16-row query blocks).  The four
+// waves form WQ teams of WT = 4 / WQ waves, one team per block; the WT waves of a team
+// take every WT-th 32-token quarter of each 128-token tile, keep their own (max, sum, O)
+// and combine them through LDS at the end.  A tile is loaded once for all blocks.
+template <int DV, bool MLA, int WQ>
 __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
   using C = KrCfg<DV, MLA>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGEB];
+  constexpr int WT = 4 / WQ;
+  static_assert(WQ == 1 || WQ == 2 || WQ == 4, "one, two or four query blocks per item");
+  static_assert(WT == 1 || C::STAGEB >= WQ * (C::OWB + 2 * 64 * 4), "the combine reuses the tile's LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::STAGEB];
 
   const PaItem it = a.items[blockIdx.x];
   const int tid = threadIdx.x;
@@ -83,9 +106,11 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
   const int te = it.tok_end;
   const int shift = a.page_shift;
   const int pmask = (1 << shift) - 1;
+  const int team = wave / WT;                          // the query block this wave works on
+  const int wave_in = wave % WT;                       // its place among the team's waves
 
-  // ---- this wave's query block: rows, limits, operand -------------------------------------
-  const int qb = it.qblk0 + wave;
+  // ---- this team's query block: rows, limits, operand ------------------------------------
+  const int qb = it.qblk0 + team;
   const bool has_rows = 16 * qb < Mq;
   const int m = 16 * qb + L16;
   const int mr = m < Mq ? m : Mq - 1;                  // rows past Mq repeat the last real row
@@ -101,27 +126,28 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
   const int vis_hi_all = min(p_first, te - 1);
   const int64_t th = (int64_t)(it.row0 + r) * Hq + (int64_t)it.kvh * G + hl;    // (row, query head)
 
-  bf16x8 qm[C::KCM], qr[C::KCR];
+  bf16x8 qr[C::KCR];
+  bf16x8 qm[MLA ? 1 : C::KCM];                         // SEP: bf16 main part
+  i32x8 qc[MLA ? C::NBLK : 1];                          // MLA: e4m3 latent codes, 32 per lane and block
   float qs[MLA ? C::NBLK : 1];
   if constexpr (MLA) {
-    const uint8_t* qc = static_cast<const uint8_t*>(a.q) + th * DV;
+    const uint8_t* qp = static_cast<const uint8_t*>(a.q) + th * DV;
 #pragma unroll
-    for (int kc = 0; kc < C::KCM; ++kc) {
-      const uint2 w = *reinterpret_cast<const uint2*>(qc + kc * 32 + 8 * g);
-      qm[kc] = fp8x8_to_bf16x8(w.x, w.y);              // exact
+    for (int b = 0; b < C::NBLK; ++b) {
+      const i32x4 c0 = *reinterpret_cast<const i32x4*>(qp + 128 * b + 32 * g);
+      const i32x4 c1 = *reinterpret_cast<const i32x4*>(qp + 128 * b + 32 * g + 16);
+      qc[b] = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+      qs[b] = a.q_scale[th * C::NBLK + b];
     }
     const __bf16* qrp = static_cast<const __bf16*>(a.q_rope) + th * C::DR;
 #pragma unroll
     for (int kc = 0; kc < C::KCR; ++kc) qr[kc] = *reinterpret_cast<const bf16x8*>(qrp + kc * 32 + 8 * g);
-#pragma unroll
-    for (int b = 0; b < C::NBLK; ++b) qs[b] = a.q_scale[th * C::NBLK + b];
   } else {
     const __bf16* qp = static_cast<const __bf16*>(a.q) + th * (DV + C::DR);
 #pragma unroll
     for (int kc = 0; kc < C::KCM; ++kc) qm[kc] = *reinterpret_cast<const bf16x8*>(qp + kc * 32 + 8 * g);
 #pragma unroll
     for (int kc = 0; kc < C::KCR; ++kc) qr[kc] = *reinterpret_cast<const bf16x8*>(qp + DV + kc * 32 + 8 * g);
-    qs[0] = 1.f;
   }
   const float qk_scale = a.sm_scale * kLog2eKr;
 
@@ -141,7 +167,7 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v);
   const int64_t mhead = (int64_t)it.kvh * a.m_sh, rhead = (int64_t)it.kvh * a.r_sh, vhead = (int64_t)it.kvh * a.v_sh;
   u32x4 mreg[C::CPT_M], rreg[C::CPT_R], vreg[C::CPT_V > 0 ? C::CPT_V : 1];
-  float sreg = 0.f;
+  float sreg[C::SPT > 0 ? C::SPT : 1];
   auto load_tile = [&](int tile0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::CPT_M; ++i) {
@@ -168,92 +194,87 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
             vbase + AV::row_offset(pg, jb, a.v_sp, vhead, a.v_ss, pmask) + av.lane_offset(jb, te, a.v_ss)));
       }
     } else {
-      if (tid < C::BN * C::NBLK) {                 // one latent scale per thread
-        const int j = min(tile0 + tid / C::NBLK, te - 1);
+#pragma unroll
+      for (int i = 0; i < C::SPT; ++i) {           // entry e = token e / NBLK, block e % NBLK
+        const int e = tid + 256 * i;
+        const int j = min(tile0 + e / C::NBLK, te - 1);
         const int32_t pg = pidx[j >> shift];
-        sreg = __builtin_nontemporal_load(a.k_scale + (int64_t)pg * a.s_sp + (int64_t)it.kvh * a.s_sh +
-                                          (int64_t)(j & pmask) * a.s_ss + tid % C::NBLK);
+        sreg[i] = __builtin_nontemporal_load(a.k_scale + (int64_t)pg * a.s_sp + (int64_t)it.kvh * a.s_sh +
+                                             (int64_t)(j & pmask) * a.s_ss + e % C::NBLK);
       }
     }
   };
   // LDS: chunk c of token t of a tile sits at 16-byte unit t * CPR + (c ^ swz(t)).
-  auto store_tile = [&](uint8_t* st) __attribute__((always_inline)) {
+  auto store_tile = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::CPT_M; ++i) {
       const int t = (wave * 64 + 256 * i) / C::CPR_M + am.lt;
-      *reinterpret_cast<u32x4*>(st + ((t * C::CPR_M + (am.cpos ^ swz<C::CPR_M>(t))) << 4)) = mreg[i];
+      *reinterpret_cast<u32x4*>(smem + ((t * C::CPR_M + (am.cpos ^ swz<C::CPR_M>(t))) << 4)) = mreg[i];
     }
 #pragma unroll
     for (int i = 0; i < C::CPT_R; ++i) {
       const int t = (wave * 64 + 256 * i) / C::CPR_R + ar.lt;
-      *reinterpret_cast<u32x4*>(st + C::MTB + ((t * C::CPR_R + (ar.cpos ^ swz<C::CPR_R>(t))) << 4)) = rreg[i];
+      *reinterpret_cast<u32x4*>(smem + C::MTB + ((t * C::CPR_R + (ar.cpos ^ swz<C::CPR_R>(t))) << 4)) = rreg[i];
     }
     if constexpr (!MLA) {
       const int lt = lane / C::CPR_V, cp = lane % C::CPR_V;
 #pragma unroll
       for (int i = 0; i < C::CPT_V; ++i) {
         const int t = (wave * 64 + 256 * i) / C::CPR_V + lt;
-        *reinterpret_cast<u32x4*>(st + C::MTB + C::RTB + ((t * C::CPR_V + (cp ^ swz<C::CPR_V>(t))) << 4)) = vreg[i];
+        *reinterpret_cast<u32x4*>(smem + C::MTB + C::RTB + ((t * C::CPR_V + (cp ^ swz<C::CPR_V>(t))) << 4)) = vreg[i];
       }
     } else {
-      if (tid < C::BN * C::NBLK) reinterpret_cast<float*>(st + C::MTB + C::RTB)[tid] = sreg;
+#pragma unroll
+      for (int i = 0; i < C::SPT; ++i) reinterpret_cast<float*>(smem + C::MTB + C::RTB)[tid + 256 * i] = sreg[i];
     }
   };
 
-  // ---- one tile: S^T, softmax, O^T += V^T P^T ------------------------------------------------
-  auto compute_tile = [&](int tile0, const uint8_t* st) __attribute__((always_inline)) {
-    if (!has_rows) return;
-    const uint8_t* Ml = st;
-    const uint8_t* Rl = st + C::MTB;
-    const int tk[2] = {L16, 16 + L16};               // K rows (tokens) of the two 16-token halves
+  // ---- 32 tokens of a tile (from wt0 on): S^T, softmax, O^T += V^T P^T ------------------
+  auto compute_quarter = [&](int tile0, int wt0) __attribute__((always_inline)) {
+    const int c0 = tile0 + wt0;
+    if (c0 >= te) return;
+    const uint8_t* Ml = smem;
+    const uint8_t* Rl = smem + C::MTB;
+    const float* scl = reinterpret_cast<const float*>(smem + C::MTB + C::RTB);   // MLA: [BN][NBLK]
     float x[8];
-    const float* scl = reinterpret_cast<const float*>(st + C::MTB + C::RTB);   // MLA: [BN][NBLK]
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int t = tk[tb];
-      f32x4 rs = {0.f, 0.f, 0.f, 0.f};
+      const int t = wt0 + 16 * tb + L16;               // K row (token) of this lane in the tile
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < C::KCR; ++kc) {
         const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Rl + ((t * C::CPR_R + ((4 * kc + g) ^ swz<C::CPR_R>(t))) << 4));
-        rs = mfma_bf16(kv, qr[kc], rs);
+        acc = mfma_bf16(kv, qr[kc], acc);
       }
       if constexpr (MLA) {
-        // per 128-channel block: sum_c qcode * kcode, then times the row's and the token's scale
-        f32x4 acc = rs;
+        // per 128-channel block: one e4m3 MFMA over the raw codes, then the row's and the
+        // token's scale of that block (accumulator rows are tokens 4g + k of this half)
 #pragma unroll
         for (int b = 0; b < C::NBLK; ++b) {
-          f32x4 sb = {0.f, 0.f, 0.f, 0.f};
+          const i32x4 k0 = *reinterpret_cast<const i32x4*>(Ml + ((t * C::CPR_M + ((8 * b + 2 * g) ^ swz<C::CPR_M>(t))) << 4));
+          const i32x4 k1 = *reinterpret_cast<const i32x4*>(Ml + ((t * C::CPR_M + ((8 * b + 2 * g + 1) ^ swz<C::CPR_M>(t))) << 4));
+          const f32x4 sb = mfma_fp8_k128_kr(__builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7), qc[b],
+                                            f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int kc = 4 * b + kk;
-            const uint2 w = *reinterpret_cast<const uint2*>(
-                Ml + ((t * C::CPR_M + ((2 * kc + (g >> 1)) ^ swz<C::CPR_M>(t))) << 4) + 8 * (g & 1));
-            sb = mfma_bf16(fp8x8_to_bf16x8(w.x, w.y), qm[kc], sb);
-          }
-          // accumulator lane layout: rows (tokens) 4 * g + k of this half, column L16 (query row)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) acc[k] = fmaf(sb[k], qs[b] * scl[(16 * tb + 4 * g + k) * C::NBLK + b], acc[k]);
+          for (int k = 0; k < 4; ++k) acc[k] = fmaf(sb[k], qs[b] * scl[(wt0 + 16 * tb + 4 * g + k) * C::NBLK + b], acc[k]);
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x[4 * tb + k] = acc[k];
       } else {
-        f32x4 acc = rs;
 #pragma unroll
         for (int kc = 0; kc < C::KCM; ++kc) {
           const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Ml + ((t * C::CPR_M + ((4 * kc + g) ^ swz<C::CPR_M>(t))) << 4));
           acc = mfma_bf16(kv, qm[kc], acc);
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x[4 * tb + k] = acc[k];
       }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[4 * tb + k] = acc[k];
     }
     // ---- scale, mask, online softmax
-    const bool need_mask = !(tile0 >= vis_lo_all && tile0 + 31 <= vis_hi_all);
+    const bool need_mask = !(c0 >= vis_lo_all && c0 + 31 <= vis_hi_all);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       x[k] *= qk_scale;
       if (need_mask) {
-        const int j = tile0 + (k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4));
+        const int j = c0 + (k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4));
         x[k] = (j >= lim_lo && j <= lim_hi) ? x[k] : -INFINITY;
       }
     }
@@ -278,13 +299,13 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
     if constexpr (MLA) {
       // transposing read of 8 tokens x one 16-channel block of the latent codes
       const int jr = L16 >> 1;
-      const int tv = jr < 4 ? 4 * g + jr : 16 + 4 * g + (jr - 4);
+      const int tv = wt0 + (jr < 4 ? 4 * g + jr : 16 + 4 * g + (jr - 4));
 #pragma unroll
       for (int b = 0; b < C::NBLK; ++b) {
         bf16x8 pb;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const int tok = k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4);
+          const int tok = wt0 + (k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4));
           pb[k] = (__bf16)(pv[k] * scl[tok * C::NBLK + b]);
         }
 #pragma unroll
@@ -296,7 +317,7 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
         }
       }
     } else {
-      const uint8_t* Vl = st + C::MTB + C::RTB;
+      const uint8_t* Vl = smem + C::MTB + C::RTB;
       bf16x8 hv, lv;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -309,7 +330,7 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
         bf16x8 va;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int t1 = 4 * g + (L16 >> 2) + 16 * half;
+          const int t1 = wt0 + 4 * g + (L16 >> 2) + 16 * half;
           const int c = 2 * db + ((L16 & 3) >> 1);
           const uint32_t addr = ((t1 * C::CPR_V + (c ^ swz<C::CPR_V>(t1))) << 4) + 8 * (L16 & 1);
           const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + addr));
@@ -322,31 +343,65 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
       }
     }
   };
+  auto compute_tile = [&](int tile0) __attribute__((always_inline)) {
+    if (!has_rows) return;
+#pragma unroll
+    for (int k = 0; k < WQ; ++k) compute_quarter(tile0, 32 * (wave_in + WT * k));
+  };
 
+  // One LDS stage: the next tile's loads are in flight in registers while this one is
+  // computed, and are stored once every wave is done reading the stage.
   const int ntiles = te > tb0 ? (te - tb0 + C::BN - 1) / C::BN : 0;
   if (ntiles > 0) {
     load_tile(tb0);
     __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);      // vmcnt(0) lgkmcnt(0)
-    store_tile(smem);
+    store_tile();
     __syncthreads();
   }
   for (int ti = 0; ti < ntiles; ++ti) {
     const int tile0 = tb0 + ti * C::BN;
     const bool more = ti + 1 < ntiles;
-    if (more) load_tile(tile0 + C::BN);                // next tile in flight during this one
-    compute_tile(tile0, smem + (ti & 1) * C::STAGEB);
+    if (more) load_tile(tile0 + C::BN);
+    compute_tile(tile0);
+    __syncthreads();
     if (more) {
-      store_tile(smem + ((ti + 1) & 1) * C::STAGEB);   // the other stage was last read a tile ago
+      store_tile();
       __syncthreads();
     }
   }
 
-  // ---- epilogue -------------------------------------------------------------------------------
-  if (!has_rows || m >= Mq) return;
+  // ---- combine each team's (max, sum, O) through LDS, one wave at a time -------------------
   const float ltot = wave_sum_xor_16_32(lrun);
-  const bool empty = !(ltot > 0.f);
-  const float sc = empty ? 0.f : 1.f / ltot;
-  const float lse = empty ? -INFINITY : (mrun + __log2f(ltot)) * kLn2Kr;
+  float* eo = reinterpret_cast<float*>(smem + team * (C::OWB + 2 * 64 * 4));
+  float* em = eo + 64 * 4 * C::DB;
+  float* el = em + 64;
+  float mall = mrun, lsum = ltot;
+  for (int w2 = 1; w2 < WT; ++w2) {
+    if (wave_in == w2) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) *reinterpret_cast<f32x4*>(eo + (db * 64 + lane) * 4) = o[db];
+      em[lane] = mrun;
+      el[lane] = ltot;
+    }
+    __syncthreads();
+    if (wave_in == 0) {
+      const float m2 = em[lane];
+      const float mn = fmaxf(mall, m2);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float f0 = fast_exp2(mall - mu), f2 = fast_exp2(m2 - mu);
+      lsum = lsum * f0 + el[lane] * f2;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) o[db] = o[db] * f0 + *reinterpret_cast<const f32x4*>(eo + (db * 64 + lane) * 4) * f2;
+      mall = mn;
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue (the first wave of each team) ------------------------------------------------
+  if (wave_in != 0 || !has_rows || m >= Mq) return;
+  const bool empty = !(lsum > 0.f);
+  const float sc = empty ? 0.f : 1.f / lsum;
+  const float lse = empty ? -INFINITY : (mall + __log2f(lsum)) * kLn2Kr;
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   if (it.nsplit == 1) {
     if (a.out_lse && g == 0) a.out_lse[th] = lse;
@@ -385,12 +440,23 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
 
 }  // namespace
 
-int launch_stage1_kr(int dv, bool mla, const KrArgs& a, int num_items, void* stream) {
+int launch_stage1_kr(int dv, bool mla, int wq, const KrArgs& a, int num_items, void* stream) {
   if (num_items <= 0) return 0;
   const hipStream_t s = (hipStream_t)stream;
-  if (!mla && dv == 128) hipLaunchKernelGGL((stage1_kr_kernel<128, false>), dim3(num_items), dim3(256), 0, s, a);
-  else if (mla && dv == 512) hipLaunchKernelGGL((stage1_kr_kernel<512, true>), dim3(num_items), dim3(256), 0, s, a);
-  else return (int)hipErrorInvalidValue;
+  const dim3 grid(num_items), block(256);
+  if (!mla && dv == 128) {
+    if (wq == 1) hipLaunchKernelGGL((stage1_kr_kernel<128, false, 1>), grid, block, 0, s, a);
+    else if (wq == 2) hipLaunchKernelGGL((stage1_kr_kernel<128, false, 2>), grid, block, 0, s, a);
+    else if (wq == 4) hipLaunchKernelGGL((stage1_kr_kernel<128, false, 4>), grid, block, 0, s, a);
+    else return (int)hipErrorInvalidValue;
+  } else if (mla && dv == 512) {
+    if (wq == 1) hipLaunchKernelGGL((stage1_kr_kernel<512, true, 1>), grid, block, 0, s, a);
+    else if (wq == 2) hipLaunchKernelGGL((stage1_kr_kernel<512, true, 2>), grid, block, 0, s, a);
+    else if (wq == 4) hipLaunchKernelGGL((stage1_kr_kernel<512, true, 4>), grid, block, 0, s, a);
+    else return (int)hipErrorInvalidValue;
+  } else {
+    return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 
