@@ -157,48 +157,58 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
   float mrun = -INFINITY, lrun = 0.f;
 
   // ---- tile loads: HBM -> registers -> LDS -------------------------------------------------
-  using AM = KvTileAddr<C::CPR_M, C::BN, C::MB>;
-  using AR = KvTileAddr<C::CPR_R, C::BN, 2>;
+  // Wave w loads quarter w of every tile (tokens 32 w .. 32 w + 31): latent / main rows,
+  // rotary rows, value rows (SEP) or latent scales (MLA).
+  using AM = KvQuarterAddr<C::CPR_M, C::MB>;
+  using AR = KvQuarterAddr<C::CPR_R, 2>;
+  using AV = KvQuarterAddr<(C::CPR_V > 0 ? C::CPR_V : 2), 2>;
   const AM am(lane, a.m_ss);
   const AR ar(lane, a.r_ss);
+  const AV av(lane, a.v_ss);
   const cint32* pidx = (const cint32*)(a.page_indices) + it.page_base;
   const uint8_t* mbase = static_cast<const uint8_t*>(a.k_main);
   const uint8_t* rbase = static_cast<const uint8_t*>(a.k_rope);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v);
   const int64_t mhead = (int64_t)it.kvh * a.m_sh, rhead = (int64_t)it.kvh * a.r_sh, vhead = (int64_t)it.kvh * a.v_sh;
+  static_assert(C::CPT_M == AM::NG && C::CPT_R == AR::NG && (MLA || C::CPT_V == AV::NG), "one quarter per wave");
+  static_assert(!MLA || C::SPT == 2, "32 tokens x 4 scales per wave");
   u32x4 mreg[C::CPT_M], rreg[C::CPT_R], vreg[C::CPT_V > 0 ? C::CPT_V : 1];
   float sreg[C::SPT > 0 ? C::SPT : 1];
   auto load_tile = [&](int tile0) __attribute__((always_inline)) {
+    const int q0 = tile0 + 32 * wave;
+    const QuarterPages qp(pidx, q0, te, shift);
+    {
+      const int64_t bA = qp.base(false, a.m_sp, mhead, C::MB), bB = qp.base(true, a.m_sp, mhead, C::MB);
 #pragma unroll
-    for (int i = 0; i < C::CPT_M; ++i) {
-      const int jb = AM::group_token(tile0, wave, i, te);
-      const int32_t pg = AM::group_page(pidx, jb, shift);
-      mreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          mbase + AM::row_offset(pg, jb, a.m_sp, mhead, a.m_ss, pmask) + am.lane_offset(jb, te, a.m_ss)));
+      for (int i = 0; i < AM::NG; ++i) {
+        const int jb = AM::group_token(q0, i, te);
+        mreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            mbase + AM::row_offset(jb, qp.first, bA, bB, shift, a.m_ss) + am.lane_offset(jb, te, a.m_ss)));
+      }
     }
+    {
+      const int64_t bA = qp.base(false, a.r_sp, rhead, 2), bB = qp.base(true, a.r_sp, rhead, 2);
 #pragma unroll
-    for (int i = 0; i < C::CPT_R; ++i) {
-      const int jb = AR::group_token(tile0, wave, i, te);
-      const int32_t pg = AR::group_page(pidx, jb, shift);
-      rreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          rbase + AR::row_offset(pg, jb, a.r_sp, rhead, a.r_ss, pmask) + ar.lane_offset(jb, te, a.r_ss)));
+      for (int i = 0; i < AR::NG; ++i) {
+        const int jb = AR::group_token(q0, i, te);
+        rreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            rbase + AR::row_offset(jb, qp.first, bA, bB, shift, a.r_ss) + ar.lane_offset(jb, te, a.r_ss)));
+      }
     }
     if constexpr (!MLA) {
-      using AV = KvTileAddr<C::CPR_V, C::BN, 2>;
-      const AV av(lane, a.v_ss);
+      const int64_t bA = qp.base(false, a.v_sp, vhead, 2), bB = qp.base(true, a.v_sp, vhead, 2);
 #pragma unroll
-      for (int i = 0; i < C::CPT_V; ++i) {
-        const int jb = AV::group_token(tile0, wave, i, te);
-        const int32_t pg = AV::group_page(pidx, jb, shift);
+      for (int i = 0; i < AV::NG; ++i) {
+        const int jb = AV::group_token(q0, i, te);
         vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            vbase + AV::row_offset(pg, jb, a.v_sp, vhead, a.v_ss, pmask) + av.lane_offset(jb, te, a.v_ss)));
+            vbase + AV::row_offset(jb, qp.first, bA, bB, shift, a.v_ss) + av.lane_offset(jb, te, a.v_ss)));
       }
     } else {
 #pragma unroll
       for (int i = 0; i < C::SPT; ++i) {           // entry e = token e / NBLK, block e % NBLK
-        const int e = tid + 256 * i;
-        const int j = min(tile0 + e / C::NBLK, te - 1);
-        const int32_t pg = pidx[j >> shift];
+        const int e = lane + 64 * i;
+        const int j = min(q0 + e / C::NBLK, te - 1);
+        const int32_t pg = (j >> shift) == qp.first ? qp.pA : qp.pB;
         sreg[i] = __builtin_nontemporal_load(a.k_scale + (int64_t)pg * a.s_sp + (int64_t)it.kvh * a.s_sh +
                                              (int64_t)(j & pmask) * a.s_ss + e % C::NBLK);
       }
@@ -207,25 +217,25 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
   // LDS: chunk c of token t of a tile sits at 16-byte unit t * CPR + (c ^ swz(t)).
   auto store_tile = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < C::CPT_M; ++i) {
-      const int t = (wave * 64 + 256 * i) / C::CPR_M + am.lt;
+    for (int i = 0; i < AM::NG; ++i) {
+      const int t = 32 * wave + AM::GT * i + am.lt;
       *reinterpret_cast<u32x4*>(smem + ((t * C::CPR_M + (am.cpos ^ swz<C::CPR_M>(t))) << 4)) = mreg[i];
     }
 #pragma unroll
-    for (int i = 0; i < C::CPT_R; ++i) {
-      const int t = (wave * 64 + 256 * i) / C::CPR_R + ar.lt;
+    for (int i = 0; i < AR::NG; ++i) {
+      const int t = 32 * wave + AR::GT * i + ar.lt;
       *reinterpret_cast<u32x4*>(smem + C::MTB + ((t * C::CPR_R + (ar.cpos ^ swz<C::CPR_R>(t))) << 4)) = rreg[i];
     }
     if constexpr (!MLA) {
-      const int lt = lane / C::CPR_V, cp = lane % C::CPR_V;
 #pragma unroll
-      for (int i = 0; i < C::CPT_V; ++i) {
-        const int t = (wave * 64 + 256 * i) / C::CPR_V + lt;
-        *reinterpret_cast<u32x4*>(smem + C::MTB + C::RTB + ((t * C::CPR_V + (cp ^ swz<C::CPR_V>(t))) << 4)) = vreg[i];
+      for (int i = 0; i < AV::NG; ++i) {
+        const int t = 32 * wave + AV::GT * i + av.lt;
+        *reinterpret_cast<u32x4*>(smem + C::MTB + C::RTB + ((t * C::CPR_V + (av.cpos ^ swz<C::CPR_V>(t))) << 4)) = vreg[i];
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < C::SPT; ++i) reinterpret_cast<float*>(smem + C::MTB + C::RTB)[tid + 256 * i] = sreg[i];
+      for (int i = 0; i < C::SPT; ++i)
+        reinterpret_cast<float*>(smem + C::MTB + C::RTB)[32 * wave * C::NBLK + lane + 64 * i] = sreg[i];
     }
   };
 
