@@ -66,6 +66,17 @@ def _cpu_model() -> str:
 
 KERNEL_SOURCES = ("stage1.hip", "common.hpp", "kv_addr.hpp", "pa_internal.hpp")
 KR_SOURCES = ("stage1_kr.hip", "common.hpp", "kv_addr.hpp", "pa_internal.hpp")
+MLA_SOURCES = ("stage1_mla.hip", "common.hpp", "kv_addr.hpp", "pa_internal.hpp")
+
+
+def stage1_kernel_of(latent: bool, rope: bool):
+    """(kernel name, its source files) of the stage-1 kernel a workload runs: the latent-cache
+    kernel, the rotary-key kernel (keys wider than values) or the equal-width kernel."""
+    if latent:
+        return "stage1_mla_kernel", MLA_SOURCES
+    if rope:
+        return "stage1_kr_kernel", KR_SOURCES
+    return "stage1_kernel", KERNEL_SOURCES
 
 
 def kernel_code(text: str) -> str:
@@ -566,9 +577,8 @@ def main():
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "roofline": {"bound": "hbm", "achieved": round(roof_achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(roof_achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(args.config, *(("stage1_kr_kernel", KR_SOURCES) if pd.rope else
-                                                                ("stage1_kernel", KERNEL_SOURCES))),
-                     "kernel": "stage1_kr_kernel" if pd.rope else "stage1_kernel", "bytes_per_launch": s1_bytes},
+                     "traffic": measured_traffic(args.config, *stage1_kernel_of(w.latent, pd.rope)),
+                     "kernel": stage1_kernel_of(w.latent, pd.rope)[0], "bytes_per_launch": s1_bytes},
     }
     if not args.no_per_config and args.config == "c2":
         result["per_config"], result["r8_over_r1"] = per_config(args, flush, stream)

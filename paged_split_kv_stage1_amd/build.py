@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa_gfx950.so")
-SOURCES = ["api.cpp", "stage1.hip", "stage1_kr.hip", "merge.hip", "quant.hip", "gather.hip", "noalloc.hip",
+SOURCES = ["api.cpp", "stage1.hip", "stage1_kr.hip", "stage1_mla.hip", "merge.hip", "quant.hip", "gather.hip", "noalloc.hip",
            "validate.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -31,7 +31,8 @@ RESOURCE_FLAG = "-Rpass-analysis=kernel-resource-usage"
 # Stage 1 never produces or consumes a NaN on purpose (masked scores are -inf, tail slots
 # past kv_len are never loaded): without NaN semantics the compiler drops the
 # canonicalising moves it otherwise puts in front of every fmax of the softmax maxima.
-PER_SOURCE_FLAGS = {"stage1.hip": ["-fno-honor-nans"], "stage1_kr.hip": ["-fno-honor-nans"]}
+PER_SOURCE_FLAGS = {"stage1.hip": ["-fno-honor-nans"], "stage1_kr.hip": ["-fno-honor-nans"],
+                    "stage1_mla.hip": ["-fno-honor-nans"]}
 
 
 def parse_resource_usage(text: str) -> dict:

@@ -203,8 +203,9 @@ CostModel cost_model(const pa_plan_args& a, const KernelCfg& cfg, int num_cus) {
              (a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD ? 8 : 0);
   if (cfg.kr)                           // key rows of dh channels, value rows of dv (MLA: shared)
     m.kv_tok = cfg.mla ? cfg.dv + 2.0 * 64 + 4.0 * cfg.dv / 128 : 2.0 * (cfg.dh + cfg.dv);
-  // head_dim 512 and the latent cache: one workgroup per CU (registers, LDS)
-  m.slots = (cfg.dh == 512 || cfg.mla ? 1 : kSlotsPerCu) * num_cus;
+  // head_dim 512 and the latent cache with four query blocks per item: one workgroup per
+  // CU (registers, LDS)
+  m.slots = (cfg.dh == 512 || (cfg.mla && cfg.wq == 4) ? 1 : kSlotsPerCu) * num_cus;
   m.bw_slot = kHbmBytesPerS / m.slots;
   const int wt = 4 / cfg.wq;                     // waves sharing the tokens of a tile
   const double comp_blk = compute_s_per_token_block(a);
@@ -644,7 +645,8 @@ pa_status pa_decode_stage1_rope(const pa_plan_info* info, const void* plan_dev, 
   s.group = info->num_q_heads / info->num_kv_heads;
   s.page_shift = ilog2_exact(info->page_size);
   s.s_max = info->max_splits;
-  const int e = launch_stage1_kr(cfg.dv, cfg.mla, cfg.wq, s, info->num_items, stream);
+  const int e = cfg.mla ? launch_stage1_mla(cfg.wq, s, info->num_items, stream)
+                        : launch_stage1_kr(cfg.dv, cfg.mla, cfg.wq, s, info->num_items, stream);
   if (e) return hip_fail(e, "pa_decode_stage1_rope launch");
   return ok();
 }

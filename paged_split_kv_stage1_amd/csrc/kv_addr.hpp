@@ -83,23 +83,24 @@ struct ScaleTileAddr {
   }
 };
 
-// 32-token quarters of a tile, one per wave, for rows of CPR 16-byte chunks: load group i
-// (i < CPR / 2) covers the 64 / CPR tokens from T0 + i * 64 / CPR of the quarter starting
-// at T0 (lane = token lt, chunk cpos).  Quarters start on multiples of 32 tokens and pages
-// hold >= 16 tokens, so a quarter touches at most two pages: their two page-table entries
-// are the only scalar loads, and each group picks its row base from them.  Tokens past the
-// split's last one (te - 1) are clamped to it, as in KvTileAddr.
-template <int CPR, int KVB>
-struct KvQuarterAddr {
-  static constexpr int NG = CPR / 2;         // load groups per quarter
-  static constexpr int GT = 64 / CPR;        // tokens per group
+// Spans of SPAN consecutive tokens of a tile, one per wave, for rows of CPR 16-byte chunks:
+// load group i (i < SPAN * CPR / 64) covers the 64 / CPR tokens from q0 + i * 64 / CPR of the
+// span starting at q0 (lane = token lt, chunk cpos).  Spans start on multiples of SPAN
+// tokens (SPAN = 16 or 32) and pages hold >= 16 tokens, so a span touches at most two
+// pages: their two page-table entries are the only scalar loads, and each group picks its
+// row base from them.  Tokens past the split's last one (te - 1) are clamped to it, as in
+// KvTileAddr.
+template <int CPR, int KVB, int SPAN = 32>
+struct KvSpanAddr {
+  static constexpr int NG = SPAN * CPR / 64;  // load groups per span
+  static constexpr int GT = 64 / CPR;         // tokens per group
   int lt, cpos;
   uint32_t goff;
-  __device__ __forceinline__ KvQuarterAddr(int lane, int64_t kv_ss)
+  __device__ __forceinline__ KvSpanAddr(int lane, int64_t kv_ss)
       : lt(lane / CPR), cpos(lane % CPR), goff((uint32_t)(lane / CPR * kv_ss * KVB) + ((lane % CPR) << 4)) {}
   // First token of group i (wave-uniform).
   static __device__ __forceinline__ int group_token(int q0, int i, int te) { return min(q0 + GT * i, te - 1); }
-  // Byte offset of group i's first row: page base A (the page of the quarter's first
+  // Byte offset of group i's first row: page base A (the page of the span's first
   // clamped token) or B (that of its last), plus the slot.
   static __device__ __forceinline__ int64_t row_offset(int jb, int pgA_first, int64_t baseA, int64_t baseB,
                                                        int page_shift, int64_t kv_ss) {
@@ -112,14 +113,14 @@ struct KvQuarterAddr {
   }
 };
 
-// The two page-table entries a 32-token quarter from q0 can touch (see KvQuarterAddr).
-struct QuarterPages {
-  int first;       // logical page of the quarter's first clamped token
+// The two page-table entries a span of `span` tokens from q0 can touch (see KvSpanAddr).
+struct SpanPages {
+  int first;       // logical page of the span's first clamped token
   int32_t pA, pB;  // physical pages of its first and last clamped tokens
-  __device__ __forceinline__ QuarterPages(const cint32* pidx, int q0, int te, int page_shift) {
+  __device__ __forceinline__ SpanPages(const cint32* pidx, int q0, int span, int te, int page_shift) {
     first = min(q0, te - 1) >> page_shift;
     pA = pidx[first];
-    pB = pidx[min(q0 + 31, te - 1) >> page_shift];
+    pB = pidx[min(q0 + span - 1, te - 1) >> page_shift];
   }
   // Byte offset of the page's row block of one head, for pages A and B.
   __device__ __forceinline__ int64_t base(bool b, int64_t kv_sp, int64_t head_off, int kvb) const {

@@ -159,9 +159,9 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
   // ---- tile loads: HBM -> registers -> LDS -------------------------------------------------
   // Wave w loads quarter w of every tile (tokens 32 w .. 32 w + 31): latent / main rows,
   // rotary rows, value rows (SEP) or latent scales (MLA).
-  using AM = KvQuarterAddr<C::CPR_M, C::MB>;
-  using AR = KvQuarterAddr<C::CPR_R, 2>;
-  using AV = KvQuarterAddr<(C::CPR_V > 0 ? C::CPR_V : 2), 2>;
+  using AM = KvSpanAddr<C::CPR_M, C::MB>;
+  using AR = KvSpanAddr<C::CPR_R, 2>;
+  using AV = KvSpanAddr<(C::CPR_V > 0 ? C::CPR_V : 2), 2>;
   const AM am(lane, a.m_ss);
   const AR ar(lane, a.r_ss);
   const AV av(lane, a.v_ss);
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
   float sreg[C::SPT > 0 ? C::SPT : 1];
   auto load_tile = [&](int tile0) __attribute__((always_inline)) {
     const int q0 = tile0 + 32 * wave;
-    const QuarterPages qp(pidx, q0, te, shift);
+    const SpanPages qp(pidx, q0, 32, te, shift);
     {
       const int64_t bA = qp.base(false, a.m_sp, mhead, C::MB), bB = qp.base(true, a.m_sp, mhead, C::MB);
 #pragma unroll

@@ -39,7 +39,7 @@ def _kernel_of(cfg: str):
     import bench
     from paged_split_kv_stage1_amd.inputs import CONFIGS
     rope = CONFIGS[cfg].get("dv", CONFIGS[cfg]["d"]) != CONFIGS[cfg]["d"]
-    return ("stage1_kr_kernel", bench.KR_SOURCES) if rope else ("stage1_kernel", bench.KERNEL_SOURCES)
+    return bench.stage1_kernel_of(bool(CONFIGS[cfg].get("latent", False)), rope)
 
 
 def _run(cmd, log, timeout):
