@@ -646,7 +646,7 @@ pa_status pa_decode_stage1_rope(const pa_plan_info* info, const void* plan_dev, 
   s.page_shift = ilog2_exact(info->page_size);
   s.s_max = info->max_splits;
   const int e = cfg.mla ? launch_stage1_mla(cfg.wq, s, info->num_items, stream)
-                        : launch_stage1_kr(cfg.dv, cfg.mla, cfg.wq, s, info->num_items, stream);
+                        : launch_stage1_kr(cfg.dv, cfg.wq, s, info->num_items, stream);
   if (e) return hip_fail(e, "pa_decode_stage1_rope launch");
   return ok();
 }

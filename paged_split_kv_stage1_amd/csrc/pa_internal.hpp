@@ -125,7 +125,7 @@ int launch_gather(const KernelCfg& cfg, const GatherArgs& a, int num_items, void
 int launch_quant(const void* src, int src_bf16, int64_t n_rows, int head_dim, int per_tensor, int i8,
                  uint8_t* dst, float* scale, void* stream);
 bool stage1_cfg_supported(const KernelCfg& cfg);
-int launch_stage1_kr(int dv, bool mla, int wq, const KrArgs& a, int num_items, void* stream);
+int launch_stage1_kr(int dv, int wq, const KrArgs& a, int num_items, void* stream);
 int launch_stage1_mla(int wq, const KrArgs& a, int num_items, void* stream);
 
 }  // namespace pa

@@ -1,42 +1,25 @@
-// Stage 1 for keys that carry a 64-channel rotary part: keys of DV + 64 channels, values
-// of DV channels (FlashInfer PR #869, "Remaining Work": separate head_dim_qk and
-// head_dim_v), in two cache forms:
-//   SEP -- bf16 K rows of DV + 64 channels in one cache and bf16 V rows of DV channels in
-//          another (head_dim_qk 192, head_dim_v 128);
-//   MLA -- the latent cache of multi-head latent attention in its absorbed form (FlashMLA
-//          PR #54, review thread: the "nope" part in 8 bits with one scale per token and
-//          128 channels, the rotary part kept in 16 bits): the key is [latent, rotary] with
-//          the latent as e4m3 codes plus float32 scales per (token, 128 channels) and the
-//          rotary part a bf16 cache of its own, and the value is the latent itself.  The
-//          query's latent part is e4m3 with a scale per (row, head, 128 channels), its
-//          rotary part bf16.
+// Stage 1 for keys wider than values: bf16 K rows of DV + 64 channels (a 64-channel rotary
+// part after DV channels) in one cache and bf16 V rows of DV channels in another
+// (head_dim_qk 192, head_dim_v 128; FlashInfer PR #869, "Remaining Work": separate
+// head_dim_qk and head_dim_v).  The latent cache of multi-head latent attention, whose keys
+// are also wider than its values, has a kernel of its own (stage1_mla.hip).
 //
 // One workgroup (4 waves) per work item (request, KV head, split, group of one, two or four
-// 16-row query blocks): the rows x heads of one KV head often fill a single block here
-// (16 query heads per latent head), so the waves split the tokens of each 128-token tile
-// between them as far as the blocks leave waves free, and combine their (max, sum, O) at
-// the end.  Scores are computed
-// transposed, S^T = K Q^T (tokens on the MFMA M axis), so that their accumulator is the P^T
-// operand of O^T = V^T P^T, as in the main stage-1 kernel.  K/V tiles stream HBM ->
-// registers -> LDS (one stage, the next tile's loads in flight in registers) with the
-// page-gather address code of kv_addr.hpp.
-//   QK: bf16 MFMA 16x16x32 on bf16 parts; with MLA each 128-channel block of the latent is
-//       one 16x16x128 e4m3 MFMA over the raw codes of keys and queries (exact products,
-//       fp32 sums), scaled by the token's and the row's scale of that block, and the bf16
-//       rotary part is added.
+// 16-row query blocks): the waves split the tokens of each 128-token tile between them as
+// far as the blocks leave waves free, and combine their (max, sum, O) at the end.  Scores
+// are computed transposed, S^T = K Q^T (tokens on the MFMA M axis), so that their
+// accumulator is the P^T operand of O^T = V^T P^T, as in the main stage-1 kernel.  K/V
+// tiles stream HBM -> registers -> LDS (one stage, the next tile's loads in flight in
+// registers) with the page-gather address code of kv_addr.hpp.
+//   QK: bf16 MFMA 16x16x32 over the DV main channels and the rotary channels.
 //   softmax: log2 domain, per-row causal / window masks, lazy rescale.
-//   PV: SEP -- P as two bf16 terms (hi + lo) against bf16 V; MLA -- P times the token's
-//       latent scale of each 128-channel block, one bf16 term, against the upconverted
-//       latent codes.
+//   PV: P as two bf16 terms (hi + lo) against bf16 V.
 #include "common.hpp"
 #include "kv_addr.hpp"
 
 namespace pa {
 
 namespace {
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2eKr = 1.4426950408889634f;
 constexpr float kLn2Kr = 0.6931471805599453f;
@@ -49,45 +32,34 @@ __device__ __forceinline__ int swz(int t) {
   else return (t >> 1) & (CPR - 1);
 }
 
-template <int DV, bool MLA>
+template <int DV>
 struct KrCfg {
   static constexpr int BN = 128;                      // tokens per tile: four 32-token quarters
   static constexpr int DR = 64;                       // rotary channels
-  static constexpr int MB = MLA ? 1 : 2;              // bytes per main-part element
-  static constexpr int CPR_M = DV * MB / 16;          // 16-byte chunks per main-part row
-  static constexpr int CPR_R = DR * 2 / 16;           // ... per rotary row (bf16)
-  static constexpr int CPR_V = MLA ? 0 : DV * 2 / 16; // ... per value row (SEP, bf16)
+  static constexpr int CPR_M = DV * 2 / 16;           // 16-byte chunks per main-part row
+  static constexpr int CPR_R = DR * 2 / 16;           // ... per rotary row
+  static constexpr int CPR_V = DV * 2 / 16;           // ... per value row
   static constexpr int CPT_M = BN * CPR_M / 256;      // chunks per thread per tile
   static constexpr int CPT_R = BN * CPR_R / 256;
   static constexpr int CPT_V = BN * CPR_V / 256;
-  static constexpr int NBLK = DV / 128;               // 128-channel blocks of the latent
-  static constexpr int MTB = BN * DV * MB;            // LDS bytes of the main tile
+  static constexpr int MTB = BN * DV * 2;             // LDS bytes of the main tile
   static constexpr int RTB = BN * DR * 2;
-  static constexpr int VTB = BN * DV * 2 * (MLA ? 0 : 1);
-  static constexpr int STB = MLA ? BN * NBLK * 4 : 0; // latent scales of the tile
-  static constexpr int STAGEB = MTB + RTB + VTB + STB;
-  static constexpr int SPT = MLA ? BN * NBLK / 256 : 0;   // latent scales loaded per thread
-  static constexpr int KCM = DV / 32;                 // K-steps of q.k over a bf16 main part
+  static constexpr int VTB = BN * DV * 2;
+  static constexpr int STAGEB = MTB + RTB + VTB;
+  static constexpr int KCM = DV / 32;                 // K-steps of q.k over the main part
   static constexpr int KCR = DR / 32;                 // ... over the rotary part
   static constexpr int DB = DV / 16;                  // 16-wide output blocks
   static constexpr int OWB = 64 * 4 * DB * 4;         // bytes of one wave's O in the combine
-  static_assert(CPT_M >= 1 && CPT_R >= 1 && (MLA || CPT_V >= 1), "tile must split over 256 threads");
-  static_assert(!MLA || (DV % 128 == 0 && SPT >= 1), "latent scales cover 128 channels");
+  static_assert(CPT_M >= 1 && CPT_R >= 1 && CPT_V >= 1, "tile must split over 256 threads");
 };
-
-// 16x16x128 with e4m3 A and B (32 bytes per lane: A lane l holds row l%16, B lane l column
-// l%16, both over the same 32 K positions of lane group l/16); no extra scaling.
-__device__ __forceinline__ f32x4 mfma_fp8_k128_kr(i32x8 a, i32x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
 
 // One work item is (request, KV head, split, group of WQ 16-row query blocks).  The four
 // waves form WQ teams of WT = 4 / WQ waves, one team per block; the WT waves of a team
 // take every WT-th 32-token quarter of each 128-token tile, keep their own (max, sum, O)
 // and combine them through LDS at the end.  A tile is loaded once for all blocks.
-template <int DV, bool MLA, int WQ>
-__global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
-  using C = KrCfg<DV, MLA>;
+template <int DV, int WQ>
+__global__ __launch_bounds__(256, 2) void stage1_kr_kernel(KrArgs a) {
+  using C = KrCfg<DV>;
   constexpr int WT = 4 / WQ;
   static_assert(WQ == 1 || WQ == 2 || WQ == 4, "one, two or four query blocks per item");
   static_assert(WT == 1 || C::STAGEB >= WQ * (C::OWB + 2 * 64 * 4), "the combine reuses the tile's LDS");
@@ -126,23 +98,8 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
   const int vis_hi_all = min(p_first, te - 1);
   const int64_t th = (int64_t)(it.row0 + r) * Hq + (int64_t)it.kvh * G + hl;    // (row, query head)
 
-  bf16x8 qr[C::KCR];
-  bf16x8 qm[MLA ? 1 : C::KCM];                         // SEP: bf16 main part
-  i32x8 qc[MLA ? C::NBLK : 1];                          // MLA: e4m3 latent codes, 32 per lane and block
-  float qs[MLA ? C::NBLK : 1];
-  if constexpr (MLA) {
-    const uint8_t* qp = static_cast<const uint8_t*>(a.q) + th * DV;
-#pragma unroll
-    for (int b = 0; b < C::NBLK; ++b) {
-      const i32x4 c0 = *reinterpret_cast<const i32x4*>(qp + 128 * b + 32 * g);
-      const i32x4 c1 = *reinterpret_cast<const i32x4*>(qp + 128 * b + 32 * g + 16);
-      qc[b] = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
-      qs[b] = a.q_scale[th * C::NBLK + b];
-    }
-    const __bf16* qrp = static_cast<const __bf16*>(a.q_rope) + th * C::DR;
-#pragma unroll
-    for (int kc = 0; kc < C::KCR; ++kc) qr[kc] = *reinterpret_cast<const bf16x8*>(qrp + kc * 32 + 8 * g);
-  } else {
+  bf16x8 qm[C::KCM], qr[C::KCR];
+  {
     const __bf16* qp = static_cast<const __bf16*>(a.q) + th * (DV + C::DR);
 #pragma unroll
     for (int kc = 0; kc < C::KCM; ++kc) qm[kc] = *reinterpret_cast<const bf16x8*>(qp + kc * 32 + 8 * g);
@@ -157,11 +114,11 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
   float mrun = -INFINITY, lrun = 0.f;
 
   // ---- tile loads: HBM -> registers -> LDS -------------------------------------------------
-  // Wave w loads quarter w of every tile (tokens 32 w .. 32 w + 31): latent / main rows,
-  // rotary rows, value rows (SEP) or latent scales (MLA).
-  using AM = KvSpanAddr<C::CPR_M, C::MB>;
+  // Wave w loads quarter w of every tile (tokens 32 w .. 32 w + 31): main, rotary and
+  // value rows.
+  using AM = KvSpanAddr<C::CPR_M, 2>;
   using AR = KvSpanAddr<C::CPR_R, 2>;
-  using AV = KvSpanAddr<(C::CPR_V > 0 ? C::CPR_V : 2), 2>;
+  using AV = KvSpanAddr<C::CPR_V, 2>;
   const AM am(lane, a.m_ss);
   const AR ar(lane, a.r_ss);
   const AV av(lane, a.v_ss);
@@ -170,15 +127,13 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
   const uint8_t* rbase = static_cast<const uint8_t*>(a.k_rope);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v);
   const int64_t mhead = (int64_t)it.kvh * a.m_sh, rhead = (int64_t)it.kvh * a.r_sh, vhead = (int64_t)it.kvh * a.v_sh;
-  static_assert(C::CPT_M == AM::NG && C::CPT_R == AR::NG && (MLA || C::CPT_V == AV::NG), "one quarter per wave");
-  static_assert(!MLA || C::SPT == 2, "32 tokens x 4 scales per wave");
-  u32x4 mreg[C::CPT_M], rreg[C::CPT_R], vreg[C::CPT_V > 0 ? C::CPT_V : 1];
-  float sreg[C::SPT > 0 ? C::SPT : 1];
+  static_assert(C::CPT_M == AM::NG && C::CPT_R == AR::NG && C::CPT_V == AV::NG, "one quarter per wave");
+  u32x4 mreg[C::CPT_M], rreg[C::CPT_R], vreg[C::CPT_V];
   auto load_tile = [&](int tile0) __attribute__((always_inline)) {
     const int q0 = tile0 + 32 * wave;
     const SpanPages qp(pidx, q0, 32, te, shift);
     {
-      const int64_t bA = qp.base(false, a.m_sp, mhead, C::MB), bB = qp.base(true, a.m_sp, mhead, C::MB);
+      const int64_t bA = qp.base(false, a.m_sp, mhead, 2), bB = qp.base(true, a.m_sp, mhead, 2);
 #pragma unroll
       for (int i = 0; i < AM::NG; ++i) {
         const int jb = AM::group_token(q0, i, te);
@@ -195,22 +150,13 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
             rbase + AR::row_offset(jb, qp.first, bA, bB, shift, a.r_ss) + ar.lane_offset(jb, te, a.r_ss)));
       }
     }
-    if constexpr (!MLA) {
+    {
       const int64_t bA = qp.base(false, a.v_sp, vhead, 2), bB = qp.base(true, a.v_sp, vhead, 2);
 #pragma unroll
       for (int i = 0; i < AV::NG; ++i) {
         const int jb = AV::group_token(q0, i, te);
         vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
             vbase + AV::row_offset(jb, qp.first, bA, bB, shift, a.v_ss) + av.lane_offset(jb, te, a.v_ss)));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::SPT; ++i) {           // entry e = token e / NBLK, block e % NBLK
-        const int e = lane + 64 * i;
-        const int j = min(q0 + e / C::NBLK, te - 1);
-        const int32_t pg = (j >> shift) == qp.first ? qp.pA : qp.pB;
-        sreg[i] = __builtin_nontemporal_load(a.k_scale + (int64_t)pg * a.s_sp + (int64_t)it.kvh * a.s_sh +
-                                             (int64_t)(j & pmask) * a.s_ss + e % C::NBLK);
       }
     }
   };
@@ -226,16 +172,10 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
       const int t = 32 * wave + AR::GT * i + ar.lt;
       *reinterpret_cast<u32x4*>(smem + C::MTB + ((t * C::CPR_R + (ar.cpos ^ swz<C::CPR_R>(t))) << 4)) = rreg[i];
     }
-    if constexpr (!MLA) {
 #pragma unroll
-      for (int i = 0; i < AV::NG; ++i) {
-        const int t = 32 * wave + AV::GT * i + av.lt;
-        *reinterpret_cast<u32x4*>(smem + C::MTB + C::RTB + ((t * C::CPR_V + (av.cpos ^ swz<C::CPR_V>(t))) << 4)) = vreg[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::SPT; ++i)
-        reinterpret_cast<float*>(smem + C::MTB + C::RTB)[32 * wave * C::NBLK + lane + 64 * i] = sreg[i];
+    for (int i = 0; i < AV::NG; ++i) {
+      const int t = 32 * wave + AV::GT * i + av.lt;
+      *reinterpret_cast<u32x4*>(smem + C::MTB + C::RTB + ((t * C::CPR_V + (av.cpos ^ swz<C::CPR_V>(t))) << 4)) = vreg[i];
     }
   };
 
@@ -245,7 +185,6 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
     if (c0 >= te) return;
     const uint8_t* Ml = smem;
     const uint8_t* Rl = smem + C::MTB;
-    const float* scl = reinterpret_cast<const float*>(smem + C::MTB + C::RTB);   // MLA: [BN][NBLK]
     float x[8];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -256,24 +195,10 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
         const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Rl + ((t * C::CPR_R + ((4 * kc + g) ^ swz<C::CPR_R>(t))) << 4));
         acc = mfma_bf16(kv, qr[kc], acc);
       }
-      if constexpr (MLA) {
-        // per 128-channel block: one e4m3 MFMA over the raw codes, then the row's and the
-        // token's scale of that block (accumulator rows are tokens 4g + k of this half)
 #pragma unroll
-        for (int b = 0; b < C::NBLK; ++b) {
-          const i32x4 k0 = *reinterpret_cast<const i32x4*>(Ml + ((t * C::CPR_M + ((8 * b + 2 * g) ^ swz<C::CPR_M>(t))) << 4));
-          const i32x4 k1 = *reinterpret_cast<const i32x4*>(Ml + ((t * C::CPR_M + ((8 * b + 2 * g + 1) ^ swz<C::CPR_M>(t))) << 4));
-          const f32x4 sb = mfma_fp8_k128_kr(__builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7), qc[b],
-                                            f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int k = 0; k < 4; ++k) acc[k] = fmaf(sb[k], qs[b] * scl[(wt0 + 16 * tb + 4 * g + k) * C::NBLK + b], acc[k]);
-        }
-      } else {
-#pragma unroll
-        for (int kc = 0; kc < C::KCM; ++kc) {
-          const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Ml + ((t * C::CPR_M + ((4 * kc + g) ^ swz<C::CPR_M>(t))) << 4));
-          acc = mfma_bf16(kv, qm[kc], acc);
-        }
+      for (int kc = 0; kc < C::KCM; ++kc) {
+        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Ml + ((t * C::CPR_M + ((4 * kc + g) ^ swz<C::CPR_M>(t))) << 4));
+        acc = mfma_bf16(kv, qm[kc], acc);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[4 * tb + k] = acc[k];
@@ -306,51 +231,29 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
       lrun += pv[k];
     }
     // ---- O^T += V^T P^T
-    if constexpr (MLA) {
-      // transposing read of 8 tokens x one 16-channel block of the latent codes
-      const int jr = L16 >> 1;
-      const int tv = wt0 + (jr < 4 ? 4 * g + jr : 16 + 4 * g + (jr - 4));
+    const uint8_t* Vl = smem + C::MTB + C::RTB;
+    bf16x8 hv, lv;
 #pragma unroll
-      for (int b = 0; b < C::NBLK; ++b) {
-        bf16x8 pb;
+    for (int k = 0; k < 8; ++k) {
+      const __bf16 h = (__bf16)pv[k];
+      hv[k] = h;
+      lv[k] = (__bf16)(pv[k] - (float)h);
+    }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int tok = wt0 + (k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4));
-          pb[k] = (__bf16)(pv[k] * scl[tok * C::NBLK + b]);
-        }
+    for (int db = 0; db < C::DB; ++db) {
+      bf16x8 va;
 #pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const int db = 8 * b + dd;
-          const uint32_t addr = ((tv * C::CPR_M + (db ^ swz<C::CPR_M>(tv))) << 4) + 8 * (L16 & 1);
-          const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Ml + addr));
-          o[db] = mfma_bf16(fp8x8_to_bf16x8((uint32_t)w[0], (uint32_t)w[1]), pb, o[db]);
-        }
+      for (int half = 0; half < 2; ++half) {
+        const int t1 = wt0 + 4 * g + (L16 >> 2) + 16 * half;
+        const int c = 2 * db + ((L16 & 3) >> 1);
+        const uint32_t addr = ((t1 * C::CPR_V + (c ^ swz<C::CPR_V>(t1))) << 4) + 8 * (L16 & 1);
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + addr));
+        const __bf16* pvv = reinterpret_cast<const __bf16*>(&v);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) va[4 * half + k] = pvv[k];
       }
-    } else {
-      const uint8_t* Vl = smem + C::MTB + C::RTB;
-      bf16x8 hv, lv;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const __bf16 h = (__bf16)pv[k];
-        hv[k] = h;
-        lv[k] = (__bf16)(pv[k] - (float)h);
-      }
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        bf16x8 va;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int t1 = wt0 + 4 * g + (L16 >> 2) + 16 * half;
-          const int c = 2 * db + ((L16 & 3) >> 1);
-          const uint32_t addr = ((t1 * C::CPR_V + (c ^ swz<C::CPR_V>(t1))) << 4) + 8 * (L16 & 1);
-          const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + addr));
-          const __bf16* pvv = reinterpret_cast<const __bf16*>(&v);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) va[4 * half + k] = pvv[k];
-        }
-        o[db] = mfma_bf16(va, hv, o[db]);
-        o[db] = mfma_bf16(va, lv, o[db]);
-      }
+      o[db] = mfma_bf16(va, hv, o[db]);
+      o[db] = mfma_bf16(va, lv, o[db]);
     }
   };
   auto compute_tile = [&](int tile0) __attribute__((always_inline)) {
@@ -450,23 +353,15 @@ __global__ __launch_bounds__(256, MLA ? 1 : 2) void stage1_kr_kernel(KrArgs a) {
 
 }  // namespace
 
-int launch_stage1_kr(int dv, bool mla, int wq, const KrArgs& a, int num_items, void* stream) {
+int launch_stage1_kr(int dv, int wq, const KrArgs& a, int num_items, void* stream) {
   if (num_items <= 0) return 0;
   const hipStream_t s = (hipStream_t)stream;
   const dim3 grid(num_items), block(256);
-  if (!mla && dv == 128) {
-    if (wq == 1) hipLaunchKernelGGL((stage1_kr_kernel<128, false, 1>), grid, block, 0, s, a);
-    else if (wq == 2) hipLaunchKernelGGL((stage1_kr_kernel<128, false, 2>), grid, block, 0, s, a);
-    else if (wq == 4) hipLaunchKernelGGL((stage1_kr_kernel<128, false, 4>), grid, block, 0, s, a);
-    else return (int)hipErrorInvalidValue;
-  } else if (mla && dv == 512) {
-    if (wq == 1) hipLaunchKernelGGL((stage1_kr_kernel<512, true, 1>), grid, block, 0, s, a);
-    else if (wq == 2) hipLaunchKernelGGL((stage1_kr_kernel<512, true, 2>), grid, block, 0, s, a);
-    else if (wq == 4) hipLaunchKernelGGL((stage1_kr_kernel<512, true, 4>), grid, block, 0, s, a);
-    else return (int)hipErrorInvalidValue;
-  } else {
-    return (int)hipErrorInvalidValue;
-  }
+  if (dv != 128) return (int)hipErrorInvalidValue;
+  if (wq == 1) hipLaunchKernelGGL((stage1_kr_kernel<128, 1>), grid, block, 0, s, a);
+  else if (wq == 2) hipLaunchKernelGGL((stage1_kr_kernel<128, 2>), grid, block, 0, s, a);
+  else if (wq == 4) hipLaunchKernelGGL((stage1_kr_kernel<128, 4>), grid, block, 0, s, a);
+  else return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
 

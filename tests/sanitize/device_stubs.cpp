@@ -8,7 +8,7 @@
 
 namespace pa {
 int launch_stage1(const KernelCfg&, const Stage1Args&, int, void*) { return 1; }
-int launch_stage1_kr(int, bool, int, const KrArgs&, int, void*) { return 1; }
+int launch_stage1_kr(int, int, const KrArgs&, int, void*) { return 1; }
 int launch_stage1_mla(int, const KrArgs&, int, void*) { return 1; }
 int launch_merge(const MergeArgs&, void*) { return 1; }
 int launch_gather(const KernelCfg&, const GatherArgs&, int, void*) { return 1; }
