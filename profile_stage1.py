@@ -52,6 +52,21 @@ def _run(cmd, log, timeout):
         raise SystemExit(f"{cmd[0]} exited with {r.returncode}")
 
 
+def _trim(d, keep):
+    """Keep only the rows of the kernels the summary reads (the flush and set-up kernels
+    of a run add megabytes of counter rows), and drop the per-dispatch kernel trace
+    (the summary reads the per-kernel statistics)."""
+    for f in glob.glob(os.path.join(d, "**", "run_counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            rows = list(csv.reader(fh))
+        col = rows[0].index("Kernel_Name")
+        kept = [rows[0]] + [r for r in rows[1:] if any(k in r[col] for k in keep)]
+        with open(f, "w", newline="") as fh:
+            csv.writer(fh).writerows(kept)
+    for f in glob.glob(os.path.join(d, "**", "run_kernel_trace.csv"), recursive=True):
+        os.remove(f)
+
+
 def run(configs):
     import bench
     os.makedirs(PROF, exist_ok=True)
@@ -64,12 +79,14 @@ def run(configs):
         d = os.path.join(PROF, f"trace_{cfg}")
         _run(["rocprofv3", "--kernel-trace", "--stats", "-d", d, "-o", "run", "--output-format", "csv", "--",
               py, bench_py, "--config", cfg] + BENCH_TRACE_ARGS, d + ".log", 600)
+        _trim(d, (kernel, "merge_kernel", "copyBuffer"))
         for tag, counters in PMC_PASSES.items():
             d = os.path.join(PROF, f"pmc_{tag}_{cfg}")
             extra = ["--calibrate-copy"] if tag in ("FETCH_SIZE", "WRITE_SIZE") else []
             _run(["timeout", "-s", "KILL", "200", "rocprofv3", "--pmc"] + counters +
                  ["-d", d, "-o", "run", "--output-format", "csv", "--", py, bench_py, "--config", cfg] +
                  BENCH_PMC_ARGS + extra, d + ".log", 260)
+            _trim(d, (kernel, "merge_kernel", "copyBuffer"))
         print(f"profiled {cfg}", flush=True)
 
 
