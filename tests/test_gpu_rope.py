@@ -84,3 +84,38 @@ def test_keys_wider_than_values_masked_positions():
     o2, _, _ = run_decode(w, di, force_splits=3)
     n0 = int(w.qo_indptr[1])
     assert np.array_equal(o2[:n0], o[:n0])
+
+
+@pytest.mark.parametrize("page", [16, 128])
+@pytest.mark.parametrize("hq", [16, 48])
+def test_latent_windows_ragged_rows_and_page_sizes(page, hq):
+    # ragged rows (1-4 per request), sliding windows on half the requests, pages of 16 and
+    # 128 tokens (a 16-token load span then lies in one page either way), 16 or 48 heads
+    # (one block per item, or three blocks in a four-block item: the fourth team idle)
+    print(f"[rope] latent page={page} hq={hq}", flush=True)
+    w = make_workload("mla", batch=4, ctx=[900, 130, 2100, 47], rows=[1, 3, 4, 2], page=page, out_dtype="fp32",
+                      overrides={"hq": hq})
+    w.window[:] = [0, 20, 0, 5]
+    di = to_device(w)
+    for splits in (0, 3):
+        o, pd, lse = run_decode(w, di, force_splits=splits, out_lse=True)
+        ref, ref_lse = _oracle(w)
+        err = max_rel_err(o, ref)
+        print(f"  splits={splits} items={pd.num_items} maxrel={err:.3e}", flush=True)
+        assert err <= BAR["fp8"], err
+        assert np.max(np.abs(lse - ref_lse)) <= 1e-3 * max(1.0, np.max(np.abs(ref_lse)))
+
+
+def test_latent_masked_positions_do_not_change_output():
+    # keys before a row's window leave the latent kernel's output bit-identical
+    w = make_workload("mla_r2", batch=2, ctx=[700, 300], out_dtype="fp32")
+    w.window[:] = [64, 0]
+    di = to_device(w)
+    o, _, _ = run_decode(w, di, force_splits=3)
+    ref, _ = _oracle(w)
+    assert max_rel_err(o, ref) <= BAR["fp8"]
+    di.k[di.page_indices[0].item()].fill_(0x38)        # page 0 of request 0 (tokens 0..63): e4m3 1.0
+    di.k_rope[di.page_indices[0].item()].fill_(5.0)
+    o2, _, _ = run_decode(w, di, force_splits=3)
+    n0 = int(w.qo_indptr[1])
+    assert np.array_equal(o2[:n0], o[:n0])
