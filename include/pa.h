@@ -201,8 +201,10 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev,
  *              channels; k_scale_layout gives the strides of the first)
  *     k_rope   bf16 rotary rows of 64 channels, element strides k_rope_layout
  *     v_cache, v_layout: NULL (the value is the latent: code times its block's scale)
- * Accuracy: bf16 MFMA throughout (e4m3 codes upconverted exactly); 192/128 keeps P in two
- * bf16 terms, the latent form one bf16 term of P times the token's block scale.  Pointers
+ * Accuracy: 192/128 runs bf16 MFMA and keeps P in two bf16 terms.  The latent form computes
+ * the latent q.k on the FP8 MFMA over the raw e4m3 codes of keys and queries (exact
+ * products, fp32 sums, then the two block scales), the rotary part on bf16 MFMA, and P.V as
+ * one bf16 term of P times the token's block scale against exactly upconverted codes.  Pointers
  * 16-byte aligned, cache strides multiples of 16 bytes.  Errors: INVALID_ARGUMENT (a plan
  * of equal widths, missing or misaligned arguments). */
 pa_status pa_decode_stage1_rope(const pa_plan_info* info, const void* plan_dev,
