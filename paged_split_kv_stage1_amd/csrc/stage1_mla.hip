@@ -147,8 +147,29 @@ __global__ __launch_bounds__(256, WQ == 4 ? 1 : 2) void stage1_mla_kernel(KrArgs
   const int64_t lhead = (int64_t)it.kvh * a.m_sh, rhead = (int64_t)it.kvh * a.r_sh;
   u32x4 lreg[AL::NG], rreg[AR::NG];
   float sreg;
+  const int64_t sl_lane = (int64_t)(lane >> 2) * a.s_ss + (lane & 3);   // scale of (token lane/4, block lane%4)
+  // A span whose 16 tokens all precede te (every tile but a split's last) lies in one page
+  // and needs no clamp: its row offsets are scalar and each lane's offset is a constant.
+  // The last tile takes the general path (tokens past te - 1 read the last token).
   auto load_tile = [&](int tile0) __attribute__((always_inline)) {
     const int u0 = tile0 + 16 * wave;
+    if (u0 + 15 < te) {
+      const int32_t pg = pidx[u0 >> shift];
+      const int64_t slot0 = u0 & pmask;
+      const uint8_t* lrow = lbase + ((int64_t)pg * a.m_sp + lhead + slot0 * a.m_ss);
+      const uint8_t* rrow = rbase + ((int64_t)pg * a.r_sp + rhead + slot0 * a.r_ss) * 2;
+#pragma unroll
+      for (int i = 0; i < AL::NG; ++i)
+        lreg[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(lrow + (int64_t)AL::GT * i * a.m_ss + al.goff));
+#pragma unroll
+      for (int i = 0; i < AR::NG; ++i)
+        rreg[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(rrow + (int64_t)AR::GT * i * a.r_ss * 2 + ar.goff));
+      sreg = __builtin_nontemporal_load(a.k_scale + (int64_t)pg * a.s_sp + (int64_t)it.kvh * a.s_sh +
+                                        slot0 * a.s_ss + sl_lane);
+      return;
+    }
     const SpanPages sp(pidx, u0, 16, te, shift);
     {
       const int64_t bA = sp.base(false, a.m_sp, lhead, 1), bB = sp.base(true, a.m_sp, lhead, 1);
