@@ -311,6 +311,26 @@ pa_status pa_debug_gather(const pa_plan_info* info, const void* plan_dev, const 
                           const pa_kv_layout* kv, const pa_scale_layout* sc, int64_t* kv_off_out,
                           int64_t* scale_off_out, void* stream);
 
+/* Test hook (device), the same for plans whose keys are wider than their values: runs the
+ * load enumerators of the two wider-key stage-1 kernels (the 192/128 kernel's 32-token
+ * quarters, the latent kernel's 16-token spans, each with its own page lookup and clamp)
+ * over every tile of every work item and records
+ *   off_out[(i * M + (t - b_i)) * N + col] (device int64, caller-filled beforehand; entries
+ *   past e_i - b_i stay untouched), M = info->max_item_tokens, with columns
+ *   192/128 (N = 40): 0..15 byte offsets of the 16-byte chunks of token t's 128 main K
+ *     channels from the K cache base, 16..23 of its 64 rotary channels from the rotary
+ *     base (K base + 256 bytes, K strides), 24..39 of its V row from the V cache base;
+ *   latent (N = 44): 0..31 latent chunks from the latent base, 32..39 rotary chunks from the
+ *     rotary base, 40..43 element offsets of its four block scales from the scale base.
+ * Layouts: k_layout always; v_layout for 192/128; k_rope_layout and k_scale_layout for the
+ * latent cache (others may be NULL).  Errors: INVALID_ARGUMENT (NULL pointer, plan info not
+ * from pa_plan_splits, a layout the plan's form needs is missing), UNSUPPORTED (a plan of
+ * equal widths: pa_debug_gather covers it). */
+pa_status pa_debug_gather_rope(const pa_plan_info* info, const void* plan_dev, const int32_t* page_indices,
+                               const pa_kv_layout* k_layout, const pa_kv_layout* k_rope_layout,
+                               const pa_kv_layout* v_layout, const pa_scale_layout* k_scale_layout, int64_t* off_out,
+                               void* stream);
+
 /* Debug check (device; synchronises the stream): every page-table entry that the plan's
  * work items read (page_indices[kv_indptr[b] + t / P] for the tokens t of each item) must
  * lie in [0, num_pages), num_pages being the number of pages the K and V caches hold.

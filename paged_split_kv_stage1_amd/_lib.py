@@ -90,13 +90,17 @@ def lib() -> ctypes.CDLL:
                                    _p, _p, ctypes.POINTER(ScaleLayout), _p]
         L.pa_debug_gather.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, ctypes.POINTER(KVLayout),
                                       ctypes.POINTER(ScaleLayout), _p, _p, _p]
+        L.pa_debug_gather_rope.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, ctypes.POINTER(KVLayout),
+                                           ctypes.POINTER(KVLayout), ctypes.POINTER(KVLayout),
+                                           ctypes.POINTER(ScaleLayout), _p, _p]
         L.pa_validate_page_indices.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, ctypes.c_int64, _p]
         L.pa_validate_page_indices.restype = ctypes.c_int
         L.pa_decode_noalloc.argtypes = [ctypes.POINTER(PlanInfo), _p, _p, _p, _p, _p, ctypes.POINTER(KVLayout), _p,
                                         _p, ctypes.POINTER(ScaleLayout), _p, ctypes.c_float, _p, ctypes.c_int, _p,
                                         _p]
         for f in ("pa_plan_splits", "pa_decode_stage1", "pa_decode_merge", "pa_decode_noalloc", "pa_kv_quantize_fp8",
-                  "pa_kv_quantize_fp8_per_head", "pa_kv_quantize_int8", "pa_kv_append", "pa_debug_gather"):
+                  "pa_kv_quantize_fp8_per_head", "pa_kv_quantize_int8", "pa_kv_append", "pa_debug_gather",
+                  "pa_debug_gather_rope"):
             getattr(L, f).restype = ctypes.c_int
         L.pa_last_error.restype = ctypes.c_char_p
         L.pa_version.restype = ctypes.c_char_p
@@ -187,6 +191,14 @@ def pa_decode_noalloc(info, plan_dev, q, q_scale, k_cache, v_cache, kv_layout, k
 
 def _layout(x):
     return None if x is None else ctypes.byref(KVLayout(*x))
+
+
+def pa_debug_gather_rope(info, plan_dev, page_indices, k_layout, k_rope_layout, v_layout, k_scale_layout, off_out,
+                         stream=None):
+    scl = None if k_scale_layout is None else ctypes.byref(ScaleLayout(*k_scale_layout))
+    _check(lib().pa_debug_gather_rope(ctypes.byref(info), _ptr(plan_dev), _ptr(page_indices), _layout(k_layout),
+                                      _layout(k_rope_layout), _layout(v_layout), scl, _ptr(off_out),
+                                      _stream(stream)))
 
 
 def pa_decode_stage1_rope(info, plan_dev, q, q_scale, q_rope, k_cache, k_layout, k_rope, k_rope_layout, k_scale,

@@ -815,4 +815,45 @@ pa_status pa_debug_gather(const pa_plan_info* info, const void* plan_dev, const 
   return ok();
 }
 
+pa_status pa_debug_gather_rope(const pa_plan_info* info, const void* plan_dev, const int32_t* page_indices,
+                               const pa_kv_layout* k_layout, const pa_kv_layout* k_rope_layout,
+                               const pa_kv_layout* v_layout, const pa_scale_layout* k_scale_layout, int64_t* off_out,
+                               void* stream) {
+  if (!info || !plan_dev || !page_indices || !k_layout || !off_out)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_debug_gather_rope: NULL pointer");
+  const KernelCfg cfg = unpack_cfg(info->variant);
+  if (!stage1_cfg_supported(cfg) || cfg.dh != info->head_dim)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_plan_info was not produced by pa_plan_splits");
+  if (!cfg.kr) return fail(PA_ERR_UNSUPPORTED, "equal key and value widths: use pa_debug_gather");
+  if (cfg.mla && (!k_rope_layout || !k_scale_layout))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_debug_gather_rope: the latent cache needs rotary and scale layouts");
+  if (!cfg.mla && !v_layout) return fail(PA_ERR_INVALID_ARGUMENT, "pa_debug_gather_rope: 192/128 needs v_layout");
+  GatherRopeArgs g;
+  memset(&g, 0, sizeof g);
+  g.items = static_cast<const PaItem*>(plan_dev);
+  g.page_indices = page_indices;
+  g.m_sp = k_layout->page;
+  g.m_sh = k_layout->head;
+  g.m_ss = k_layout->slot;
+  const pa_kv_layout* rl = cfg.mla ? k_rope_layout : k_layout;   // 192/128: rotary part of the K row
+  g.r_sp = rl->page;
+  g.r_sh = rl->head;
+  g.r_ss = rl->slot;
+  if (!cfg.mla) {
+    g.v_sp = v_layout->page;
+    g.v_sh = v_layout->head;
+    g.v_ss = v_layout->slot;
+  } else {
+    g.s_sp = k_scale_layout->page;
+    g.s_sh = k_scale_layout->head;
+    g.s_ss = k_scale_layout->slot;
+  }
+  g.off = off_out;
+  g.max_tok = info->max_item_tokens;
+  g.page_shift = ilog2_exact(info->page_size);
+  const int e = launch_gather_rope(cfg, g, info->num_items, stream);
+  if (e) return hip_fail(e, "pa_debug_gather_rope launch");
+  return ok();
+}
+
 }  // extern "C"

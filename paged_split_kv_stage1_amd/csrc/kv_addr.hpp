@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pa {
 
 // The page table is read-only while a kernel runs: reading it through the constant
@@ -111,6 +113,43 @@ struct KvSpanAddr {
     const int ltc = min(lt, te - 1 - jb);
     return goff - (uint32_t)((lt - ltc) * kv_ss * KVB);
   }
+  // Token whose chunk cpos this lane loads in group i (clamped like lane_offset).
+  __device__ __forceinline__ int lane_token(int jb, int te) const { return jb + min(lt, te - 1 - jb); }
+
+  // A span that lies wholly before te and starts on a multiple of 16 tokens sits in one
+  // page: its first row's byte offset is one scalar (span_row), group i adds a scalar
+  // step, and each lane adds its constant goff -- no clamp, no page choice.
+  static __device__ __forceinline__ bool span_full(int q0, int te) { return q0 + SPAN <= te; }
+  static __device__ __forceinline__ int64_t span_row(const cint32* pidx, int q0, int page_shift, int64_t kv_sp,
+                                                     int64_t head_off, int64_t kv_ss) {
+    return ((int64_t)pidx[q0 >> page_shift] * kv_sp + head_off +
+            (int64_t)(q0 & ((1 << page_shift) - 1)) * kv_ss) * KVB;
+  }
+  static __device__ __forceinline__ int64_t group_step(int i, int64_t kv_ss) { return (int64_t)GT * i * kv_ss * KVB; }
+};
+
+// Float32 scales of 128-channel blocks, four per (page, KV head, slot) with element strides
+// (sc_sp, sc_sh, sc_ss), for a 16-token span from u0: lane e reads the scale of block e % 4
+// of token u0 + e / 4 (clamped to te - 1), an element offset.
+struct BlockScaleAddr {
+  static __device__ __forceinline__ int64_t lane_term(int lane, int64_t sc_ss) {
+    return (int64_t)(lane >> 2) * sc_ss + (lane & 3);
+  }
+  // the span lies wholly before te: one page, lane_term precomputed
+  static __device__ __forceinline__ int64_t full(const cint32* pidx, int u0, int page_shift, int kvh, int64_t sc_sp,
+                                                 int64_t sc_sh, int64_t sc_ss, int64_t lane_term) {
+    return (int64_t)pidx[u0 >> page_shift] * sc_sp + (int64_t)kvh * sc_sh +
+           (int64_t)(u0 & ((1 << page_shift) - 1)) * sc_ss + lane_term;
+  }
+  // the last span of a split: clamped token, page A or B of the span
+  template <typename Pages>
+  static __device__ __forceinline__ int64_t clamped(const Pages& sp, int u0, int te, int page_shift, int lane, int kvh,
+                                                    int64_t sc_sp, int64_t sc_sh, int64_t sc_ss) {
+    const int j = min(u0 + (lane >> 2), te - 1);
+    const int32_t pg = (j >> page_shift) == sp.first ? sp.pA : sp.pB;
+    return (int64_t)pg * sc_sp + (int64_t)kvh * sc_sh + (int64_t)(j & ((1 << page_shift) - 1)) * sc_ss + (lane & 3);
+  }
+  static __device__ __forceinline__ int token(int u0, int te, int lane) { return min(u0 + (lane >> 2), te - 1); }
 };
 
 // The two page-table entries a span of `span` tokens from q0 can touch (see KvSpanAddr).
@@ -125,6 +164,119 @@ struct SpanPages {
   // Byte offset of the page's row block of one head, for pages A and B.
   __device__ __forceinline__ int64_t base(bool b, int64_t kv_sp, int64_t head_off, int kvb) const {
     return ((int64_t)(b ? pB : pA) * kv_sp + head_off) * kvb;
+  }
+};
+
+template <int V>
+using kv_part = std::integral_constant<int, V>;
+
+// Every load of one wave for one tile of the 192/128 kernel (stage1_kr.hip): the wave's
+// 32-token quarter from q0 of K main rows (DV bf16 channels), K rotary rows (64 bf16
+// channels at byte offset 2 DV of the K row) and V rows (DV bf16 channels).
+// emit(kv_part<p>, i, byte offset, token, chunk) once per 16-byte load, in load order:
+// part 0 K main (offset from the K base), 1 K rotary (from the K base + 2 DV bytes),
+// 2 V (from the V base); i the load group, token the (clamped) token, chunk the 16-byte
+// chunk of that part's row.  The gather test hook runs the same function.
+template <int DV>
+struct RopeQuarterLoads {
+  using AM = KvSpanAddr<DV * 2 / 16, 2>;
+  using AR = KvSpanAddr<8, 2>;
+  using AV = KvSpanAddr<DV * 2 / 16, 2>;
+  AM am; AR ar; AV av;
+  int64_t m_sp, m_ss, r_sp, r_ss, v_sp, v_ss, mhead, rhead, vhead;
+  __device__ __forceinline__ RopeQuarterLoads(int lane, int kvh, int64_t msp, int64_t msh, int64_t mss, int64_t rsp,
+                                              int64_t rsh, int64_t rss, int64_t vsp, int64_t vsh, int64_t vss)
+      : am(lane, mss), ar(lane, rss), av(lane, vss), m_sp(msp), m_ss(mss), r_sp(rsp), r_ss(rss), v_sp(vsp), v_ss(vss),
+        mhead((int64_t)kvh * msh), rhead((int64_t)kvh * rsh), vhead((int64_t)kvh * vsh) {}
+  template <class Emit>
+  __device__ __forceinline__ void tile(const cint32* pidx, int q0, int te, int shift, Emit&& emit) const {
+    const SpanPages qp(pidx, q0, 32, te, shift);
+    {
+      const int64_t bA = qp.base(false, m_sp, mhead, 2), bB = qp.base(true, m_sp, mhead, 2);
+#pragma unroll
+      for (int i = 0; i < AM::NG; ++i) {
+        const int jb = AM::group_token(q0, i, te);
+        emit(kv_part<0>{}, i, AM::row_offset(jb, qp.first, bA, bB, shift, m_ss) + am.lane_offset(jb, te, m_ss),
+             am.lane_token(jb, te), am.cpos);
+      }
+    }
+    {
+      const int64_t bA = qp.base(false, r_sp, rhead, 2), bB = qp.base(true, r_sp, rhead, 2);
+#pragma unroll
+      for (int i = 0; i < AR::NG; ++i) {
+        const int jb = AR::group_token(q0, i, te);
+        emit(kv_part<1>{}, i, AR::row_offset(jb, qp.first, bA, bB, shift, r_ss) + ar.lane_offset(jb, te, r_ss),
+             ar.lane_token(jb, te), ar.cpos);
+      }
+    }
+    {
+      const int64_t bA = qp.base(false, v_sp, vhead, 2), bB = qp.base(true, v_sp, vhead, 2);
+#pragma unroll
+      for (int i = 0; i < AV::NG; ++i) {
+        const int jb = AV::group_token(q0, i, te);
+        emit(kv_part<2>{}, i, AV::row_offset(jb, qp.first, bA, bB, shift, v_ss) + av.lane_offset(jb, te, v_ss),
+             av.lane_token(jb, te), av.cpos);
+      }
+    }
+  }
+};
+
+// Every load of one wave for one tile of the latent-cache kernel (stage1_mla.hip): the
+// wave's 16-token span from u0 of latent codes (DV bytes per row), bf16 rotary rows (64
+// channels) and the DV / 128 = 4 block scales per token.  emit(kv_part<p>, i, offset,
+// token, chunk) per load: part 0 latent (byte offset), 1 rotary (byte offset), 2 scale
+// (element offset; chunk = the 128-channel block).  Spans wholly before te take one page
+// and no clamp (scalar rows, constant lane offsets); the split's last span clamps tokens
+// past te - 1 to it.  The gather test hook runs the same function.
+template <int DV>
+struct LatentSpanLoads {
+  using AL = KvSpanAddr<DV / 16, 1, 16>;
+  using AR = KvSpanAddr<8, 2, 16>;
+  static_assert(DV == 512, "four 128-channel scale blocks per token: one scale load per lane");
+  AL al; AR ar;
+  int lane, kvh;
+  int64_t m_sp, m_ss, r_sp, r_ss, s_sp, s_sh, s_ss, mhead, rhead, sl_lane;
+  __device__ __forceinline__ LatentSpanLoads(int ln, int kh, int64_t msp, int64_t msh, int64_t mss, int64_t rsp,
+                                             int64_t rsh, int64_t rss, int64_t ssp, int64_t ssh, int64_t sss)
+      : al(ln, mss), ar(ln, rss), lane(ln), kvh(kh), m_sp(msp), m_ss(mss), r_sp(rsp), r_ss(rss), s_sp(ssp),
+        s_sh(ssh), s_ss(sss), mhead((int64_t)kh * msh), rhead((int64_t)kh * rsh),
+        sl_lane(BlockScaleAddr::lane_term(ln, sss)) {}
+  template <class Emit>
+  __device__ __forceinline__ void tile(const cint32* pidx, int u0, int te, int shift, Emit&& emit) const {
+    if (AL::span_full(u0, te)) {
+      const int64_t lrow = AL::span_row(pidx, u0, shift, m_sp, mhead, m_ss);
+      const int64_t rrow = AR::span_row(pidx, u0, shift, r_sp, rhead, r_ss);
+#pragma unroll
+      for (int i = 0; i < AL::NG; ++i)
+        emit(kv_part<0>{}, i, lrow + AL::group_step(i, m_ss) + al.goff, u0 + AL::GT * i + al.lt, al.cpos);
+#pragma unroll
+      for (int i = 0; i < AR::NG; ++i)
+        emit(kv_part<1>{}, i, rrow + AR::group_step(i, r_ss) + ar.goff, u0 + AR::GT * i + ar.lt, ar.cpos);
+      emit(kv_part<2>{}, 0, BlockScaleAddr::full(pidx, u0, shift, kvh, s_sp, s_sh, s_ss, sl_lane),
+           u0 + (lane >> 2), lane & 3);
+      return;
+    }
+    const SpanPages sp(pidx, u0, 16, te, shift);
+    {
+      const int64_t bA = sp.base(false, m_sp, mhead, 1), bB = sp.base(true, m_sp, mhead, 1);
+#pragma unroll
+      for (int i = 0; i < AL::NG; ++i) {
+        const int jb = AL::group_token(u0, i, te);
+        emit(kv_part<0>{}, i, AL::row_offset(jb, sp.first, bA, bB, shift, m_ss) + al.lane_offset(jb, te, m_ss),
+             al.lane_token(jb, te), al.cpos);
+      }
+    }
+    {
+      const int64_t bA = sp.base(false, r_sp, rhead, 2), bB = sp.base(true, r_sp, rhead, 2);
+#pragma unroll
+      for (int i = 0; i < AR::NG; ++i) {
+        const int jb = AR::group_token(u0, i, te);
+        emit(kv_part<1>{}, i, AR::row_offset(jb, sp.first, bA, bB, shift, r_ss) + ar.lane_offset(jb, te, r_ss),
+             ar.lane_token(jb, te), ar.cpos);
+      }
+    }
+    emit(kv_part<2>{}, 0, BlockScaleAddr::clamped(sp, u0, te, shift, lane, kvh, s_sp, s_sh, s_ss),
+         BlockScaleAddr::token(u0, te, lane), lane & 3);
   }
 };
 

@@ -115,6 +115,18 @@ struct GatherArgs {
   int page_shift;
 };
 
+struct GatherRopeArgs {
+  const PaItem* items; const int32_t* page_indices;
+  int64_t m_sp, m_sh, m_ss;             // K main rows / latent codes
+  int64_t r_sp, r_sh, r_ss;             // rotary rows
+  int64_t v_sp, v_sh, v_ss;             // V rows (192/128)
+  int64_t s_sp, s_sh, s_ss;             // latent block scales
+  int64_t* off;                         // [items, max_tok, columns]
+  int64_t max_tok;
+  int page_shift;
+};
+int launch_gather_rope(const KernelCfg& c, const GatherRopeArgs& a, int num_items, void* stream);
+
 // Sets the message pa_last_error returns and returns st (defined in api.cpp).
 int report_error(int st, const char* msg);
 

@@ -77,7 +77,6 @@ __global__ __launch_bounds__(256, 2) void stage1_kr_kernel(KrArgs a) {
   const int tb0 = it.tok_begin;
   const int te = it.tok_end;
   const int shift = a.page_shift;
-  const int pmask = (1 << shift) - 1;
   const int team = wave / WT;                          // the query block this wave works on
   const int wave_in = wave % WT;                       // its place among the team's waves
 
@@ -116,49 +115,29 @@ __global__ __launch_bounds__(256, 2) void stage1_kr_kernel(KrArgs a) {
   // ---- tile loads: HBM -> registers -> LDS -------------------------------------------------
   // Wave w loads quarter w of every tile (tokens 32 w .. 32 w + 31): main, rotary and
   // value rows.
-  using AM = KvSpanAddr<C::CPR_M, 2>;
-  using AR = KvSpanAddr<C::CPR_R, 2>;
-  using AV = KvSpanAddr<C::CPR_V, 2>;
-  const AM am(lane, a.m_ss);
-  const AR ar(lane, a.r_ss);
-  const AV av(lane, a.v_ss);
+  const RopeQuarterLoads<DV> ld(lane, it.kvh, a.m_sp, a.m_sh, a.m_ss, a.r_sp, a.r_sh, a.r_ss, a.v_sp, a.v_sh,
+                                a.v_ss);
+  using LD = RopeQuarterLoads<DV>;
+  const typename LD::AM& am = ld.am;
+  const typename LD::AR& ar = ld.ar;
+  const typename LD::AV& av = ld.av;
+  using AM = typename LD::AM;
+  using AR = typename LD::AR;
+  using AV = typename LD::AV;
   const cint32* pidx = (const cint32*)(a.page_indices) + it.page_base;
   const uint8_t* mbase = static_cast<const uint8_t*>(a.k_main);
   const uint8_t* rbase = static_cast<const uint8_t*>(a.k_rope);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v);
-  const int64_t mhead = (int64_t)it.kvh * a.m_sh, rhead = (int64_t)it.kvh * a.r_sh, vhead = (int64_t)it.kvh * a.v_sh;
   static_assert(C::CPT_M == AM::NG && C::CPT_R == AR::NG && C::CPT_V == AV::NG, "one quarter per wave");
   u32x4 mreg[C::CPT_M], rreg[C::CPT_R], vreg[C::CPT_V];
   auto load_tile = [&](int tile0) __attribute__((always_inline)) {
-    const int q0 = tile0 + 32 * wave;
-    const SpanPages qp(pidx, q0, 32, te, shift);
-    {
-      const int64_t bA = qp.base(false, a.m_sp, mhead, 2), bB = qp.base(true, a.m_sp, mhead, 2);
-#pragma unroll
-      for (int i = 0; i < AM::NG; ++i) {
-        const int jb = AM::group_token(q0, i, te);
-        mreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            mbase + AM::row_offset(jb, qp.first, bA, bB, shift, a.m_ss) + am.lane_offset(jb, te, a.m_ss)));
-      }
-    }
-    {
-      const int64_t bA = qp.base(false, a.r_sp, rhead, 2), bB = qp.base(true, a.r_sp, rhead, 2);
-#pragma unroll
-      for (int i = 0; i < AR::NG; ++i) {
-        const int jb = AR::group_token(q0, i, te);
-        rreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            rbase + AR::row_offset(jb, qp.first, bA, bB, shift, a.r_ss) + ar.lane_offset(jb, te, a.r_ss)));
-      }
-    }
-    {
-      const int64_t bA = qp.base(false, a.v_sp, vhead, 2), bB = qp.base(true, a.v_sp, vhead, 2);
-#pragma unroll
-      for (int i = 0; i < AV::NG; ++i) {
-        const int jb = AV::group_token(q0, i, te);
-        vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            vbase + AV::row_offset(jb, qp.first, bA, bB, shift, a.v_ss) + av.lane_offset(jb, te, a.v_ss)));
-      }
-    }
+    ld.tile(pidx, tile0 + 32 * wave, te, shift,
+            [&](auto part, int i, int64_t off, int, int) __attribute__((always_inline)) {
+              constexpr int PART = decltype(part)::value;
+              if constexpr (PART == 0) mreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(mbase + off));
+              else if constexpr (PART == 1) rreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rbase + off));
+              else vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off));
+            });
   };
   // LDS: chunk c of token t of a tile sits at 16-byte unit t * CPR + (c ^ swz(t)).
   auto store_tile = [&]() __attribute__((always_inline)) {

@@ -92,7 +92,6 @@ __global__ __launch_bounds__(256, WQ == 4 ? 1 : 2) void stage1_mla_kernel(KrArgs
   const int tb0 = it.tok_begin;
   const int te = it.tok_end;
   const int shift = a.page_shift;
-  const int pmask = (1 << shift) - 1;
 
   // ---- this team's query block: rows, limits, operands -----------------------------------
   const int qb = it.qblk0 + team;
@@ -136,65 +135,27 @@ __global__ __launch_bounds__(256, WQ == 4 ? 1 : 2) void stage1_mla_kernel(KrArgs
   float m_team = -INFINITY;                  // the team's common maximum O is scaled to
 
   // ---- tile loads: wave w fetches tokens 16 w .. 16 w + 15 --------------------------------
-  using AL = KvSpanAddr<C::CPR_L, 1, 16>;
-  using AR = KvSpanAddr<C::CPR_R, 2, 16>;
+  const LatentSpanLoads<C::DV> ld(lane, it.kvh, a.m_sp, a.m_sh, a.m_ss, a.r_sp, a.r_sh, a.r_ss, a.s_sp, a.s_sh,
+                                  a.s_ss);
+  using AL = LatentSpanLoads<C::DV>::AL;
+  using AR = LatentSpanLoads<C::DV>::AR;
   static_assert(AL::NG == 8 && AR::NG == 2, "16 tokens per wave");
-  const AL al(lane, a.m_ss);
-  const AR ar(lane, a.r_ss);
+  const AL& al = ld.al;
+  const AR& ar = ld.ar;
   const cint32* pidx = (const cint32*)(a.page_indices) + it.page_base;
   const uint8_t* lbase = static_cast<const uint8_t*>(a.k_main);
   const uint8_t* rbase = static_cast<const uint8_t*>(a.k_rope);
-  const int64_t lhead = (int64_t)it.kvh * a.m_sh, rhead = (int64_t)it.kvh * a.r_sh;
   u32x4 lreg[AL::NG], rreg[AR::NG];
   float sreg;
-  const int64_t sl_lane = (int64_t)(lane >> 2) * a.s_ss + (lane & 3);   // scale of (token lane/4, block lane%4)
-  // A span whose 16 tokens all precede te (every tile but a split's last) lies in one page
-  // and needs no clamp: its row offsets are scalar and each lane's offset is a constant.
-  // The last tile takes the general path (tokens past te - 1 read the last token).
+  // (spans wholly before the split's end take one page and no clamp; see LatentSpanLoads)
   auto load_tile = [&](int tile0) __attribute__((always_inline)) {
-    const int u0 = tile0 + 16 * wave;
-    if (u0 + 15 < te) {
-      const int32_t pg = pidx[u0 >> shift];
-      const int64_t slot0 = u0 & pmask;
-      const uint8_t* lrow = lbase + ((int64_t)pg * a.m_sp + lhead + slot0 * a.m_ss);
-      const uint8_t* rrow = rbase + ((int64_t)pg * a.r_sp + rhead + slot0 * a.r_ss) * 2;
-#pragma unroll
-      for (int i = 0; i < AL::NG; ++i)
-        lreg[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(lrow + (int64_t)AL::GT * i * a.m_ss + al.goff));
-#pragma unroll
-      for (int i = 0; i < AR::NG; ++i)
-        rreg[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(rrow + (int64_t)AR::GT * i * a.r_ss * 2 + ar.goff));
-      sreg = __builtin_nontemporal_load(a.k_scale + (int64_t)pg * a.s_sp + (int64_t)it.kvh * a.s_sh +
-                                        slot0 * a.s_ss + sl_lane);
-      return;
-    }
-    const SpanPages sp(pidx, u0, 16, te, shift);
-    {
-      const int64_t bA = sp.base(false, a.m_sp, lhead, 1), bB = sp.base(true, a.m_sp, lhead, 1);
-#pragma unroll
-      for (int i = 0; i < AL::NG; ++i) {
-        const int jb = AL::group_token(u0, i, te);
-        lreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            lbase + AL::row_offset(jb, sp.first, bA, bB, shift, a.m_ss) + al.lane_offset(jb, te, a.m_ss)));
-      }
-    }
-    {
-      const int64_t bA = sp.base(false, a.r_sp, rhead, 2), bB = sp.base(true, a.r_sp, rhead, 2);
-#pragma unroll
-      for (int i = 0; i < AR::NG; ++i) {
-        const int jb = AR::group_token(u0, i, te);
-        rreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            rbase + AR::row_offset(jb, sp.first, bA, bB, shift, a.r_ss) + ar.lane_offset(jb, te, a.r_ss)));
-      }
-    }
-    {                                        // lane e: token u0 + e / 4, block e % 4
-      const int j = min(u0 + (lane >> 2), te - 1);
-      const int32_t pg = (j >> shift) == sp.first ? sp.pA : sp.pB;
-      sreg = __builtin_nontemporal_load(a.k_scale + (int64_t)pg * a.s_sp + (int64_t)it.kvh * a.s_sh +
-                                        (int64_t)(j & pmask) * a.s_ss + (lane & 3));
-    }
+    ld.tile(pidx, tile0 + 16 * wave, te, shift,
+            [&](auto part, int i, int64_t off, int, int) __attribute__((always_inline)) {
+              constexpr int PART = decltype(part)::value;
+              if constexpr (PART == 0) lreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(lbase + off));
+              else if constexpr (PART == 1) rreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rbase + off));
+              else sreg = __builtin_nontemporal_load(a.k_scale + off);
+            });
   };
   // LDS: chunk c of token t sits at byte t * stride + 16 c.
   auto store_tile = [&]() __attribute__((always_inline)) {

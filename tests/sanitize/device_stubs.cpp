@@ -10,6 +10,7 @@ namespace pa {
 int launch_stage1(const KernelCfg&, const Stage1Args&, int, void*) { return 1; }
 int launch_stage1_kr(int, int, const KrArgs&, int, void*) { return 1; }
 int launch_stage1_mla(int, const KrArgs&, int, void*) { return 1; }
+int launch_gather_rope(const KernelCfg&, const GatherRopeArgs&, int, void*) { return 1; }
 int launch_merge(const MergeArgs&, void*) { return 1; }
 int launch_gather(const KernelCfg&, const GatherArgs&, int, void*) { return 1; }
 int launch_quant(const void*, int, int64_t, int, int, int, uint8_t*, float*, void*) { return 1; }

@@ -326,3 +326,21 @@ def test_noalloc_rejects_plans_beyond_its_scratch():
                                fake, 0.1, fake, "bf16")
     assert e.value.status == PA_ERR_INSUFFICIENT_WORKSPACE
     assert "scratch" in str(e.value)
+
+
+def test_gather_hooks_refuse_the_other_kernels_plans():
+    # each test hook covers its own kernel family; the check comes before any device call
+    fake = 1 << 20
+    lay = (16 * 256, 256, 256)
+    info, _ = _plan(rows=[1, 1], kv=[512, 70])
+    with pytest.raises(PaError) as e:
+        _lib.pa_debug_gather_rope(info, fake, fake, lay, None, lay, None, fake)
+    assert e.value.status == PA_ERR_UNSUPPORTED
+    qo, kvi, kv = [0, 1], [0, 5], [70]
+    info, _ = pa_plan_splits(qo, kvi, kv, None, 1, 16, 32, 4, 192, "bf16", "bf16", "none", num_cus=8, head_dim_v=128)
+    with pytest.raises(PaError) as e:
+        _lib.pa_debug_gather(info, fake, fake, lay, None, fake)
+    assert e.value.status == PA_ERR_UNSUPPORTED
+    with pytest.raises(PaError) as e:          # 192/128 needs the V layout
+        _lib.pa_debug_gather_rope(info, fake, fake, lay, None, None, None, fake)
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT

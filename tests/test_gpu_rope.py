@@ -119,3 +119,55 @@ def test_latent_masked_positions_do_not_change_output():
     o2, _, _ = run_decode(w, di, force_splits=3)
     n0 = int(w.qo_indptr[1])
     assert np.array_equal(o2[:n0], o[:n0])
+
+
+@pytest.mark.parametrize("name,window", [("f3", 0), ("f3_r4", 40), ("mla", 0), ("mla_r2", 30)])
+def test_wider_key_gather_bit_exact(name, window):
+    # the wider-key kernels' own load enumerators (run by the gather hook over every tile
+    # of every work item) against the oracle's page gather and the cache strides: byte
+    # offsets of every 16-byte chunk (K main / latent, rotary, V) and element offsets of
+    # every latent block scale, bit-exact, including each split's clamped last tile
+    import torch
+
+    from oracle.attention import gather_slots
+    from paged_split_kv_stage1_amd._lib import pa_debug_gather_rope
+    from paged_split_kv_stage1_amd.decode import PagedDecode
+
+    print(f"[gather-rope] {name} window={window}", flush=True)
+    w = make_workload(name, **SMALL[name])
+    w.window[:] = window
+    di = to_device(w)
+    pd = PagedDecode(w.qo_indptr, w.kv_indptr, w.kv_len, w.window, w.max_q_len, w.page_size, w.num_q_heads,
+                     w.num_kv_heads, w.head_dim, w.q_dtype, w.kv_dtype, w.kv_scale_mode, di.q.device,
+                     force_splits=3, head_dim_v=w.head_dim_v)
+    M = int(pd.info.max_item_tokens)
+    N = 44 if w.latent else 40
+    off = torch.full((pd.num_items, M, N), -1, dtype=torch.int64, device="cuda")
+    pa_debug_gather_rope(pd.info, pd.plan, di.page_indices, di.kv_layout, di.rope_layout, di.v_layout,
+                         di.scale_layout, off)
+    torch.cuda.synchronize()
+    got = off.cpu().numpy()
+    P = w.page_size
+    items = pd.items()
+    slots_of = {b: gather_slots(w.kv_indptr, w.page_indices, w.kv_len, P, b) for b in range(w.batch)}
+    ksp, ksh, kss = di.kv_layout
+    for i, it in enumerate(items):
+        b, kvh, t0, t1 = int(it[10]), int(it[5]), int(it[8]), int(it[9])
+        phys = slots_of[b][t0:t1]
+        page, slot = phys // P, phys % P
+        if w.latent:
+            rsp, rsh, rss = di.rope_layout
+            ssp, ssh, sss = di.scale_layout
+            exp = np.concatenate([
+                (page * ksp + kvh * ksh + slot * kss)[:, None] + 16 * np.arange(32)[None, :],
+                ((page * rsp + kvh * rsh + slot * rss) * 2)[:, None] + 16 * np.arange(8)[None, :],
+                (page * ssp + kvh * ssh + slot * sss)[:, None] + np.arange(4)[None, :]], axis=1)
+        else:
+            vsp, vsh, vss = di.v_layout
+            krow = (page * ksp + kvh * ksh + slot * kss) * 2
+            exp = np.concatenate([krow[:, None] + 16 * np.arange(16)[None, :],
+                                  krow[:, None] + 16 * np.arange(8)[None, :],
+                                  ((page * vsp + kvh * vsh + slot * vss) * 2)[:, None] + 16 * np.arange(16)[None, :]],
+                                 axis=1)
+        assert np.array_equal(got[i, :t1 - t0], exp), (i, b, kvh, t0, t1)
+        assert (got[i, t1 - t0:] == -1).all()
