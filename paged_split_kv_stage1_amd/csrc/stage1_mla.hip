@@ -15,8 +15,8 @@
 //   softmax: log2 domain, per-row causal / window masks.  Each wave keeps its own running
 //     maximum and sum over the units it scores, and writes p = 2^(s - m_wave) to LDS with
 //     its m_wave.
-//   PV: the team splits the 512 value channels (512 / WT per wave), so a wave's O^T
-//     accumulators are 32 / WT ... 128 registers instead of 128 for every wave.  For every
+//   PV: the team splits the 512 value channels (512 / WT per wave), so a wave holds 128 / WT
+//     O^T accumulator registers (32 at one block per item) instead of 128.  For every
 //     32-token step a wave rebuilds the P^T operand from LDS as
 //     bf16(p * 2^(m_src - m_team) * latent_scale[token][block]) and multiplies it with the
 //     transposed, exactly upconverted latent codes (ds_read_b64_tr_b8 + e4m3 -> bf16).
