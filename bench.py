@@ -339,8 +339,13 @@ def iqm(x):
 
 def time_steps(pd, step, merge, flush, stream, steps, warmup, do_flush):
     """Warm-up steps, then ``steps`` timed steps, each after a cache-evicting write of the
-    flush buffer; HIP events on the launch stream bracket stage 1 and the merge.
-    Returns (stage-1 us per step, merge us per step, wall seconds of the timed loop)."""
+    flush buffer, with HIP events on the launch stream around each step (stage 1 + merge
+    launched back to back, nothing between them).  When the plan has a merge, a second
+    pass of ``steps`` steps puts a third event between the two launches to split the time
+    into stage 1 and merge; that marker itself delays the merge launch by a few µs, so the
+    step time comes from the first pass.
+    Returns (step us, stage-1 us, merge us, wall seconds of the first timed pass); arrays
+    with one entry per step."""
     import torch
 
     for _ in range(warmup):
@@ -349,9 +354,22 @@ def time_steps(pd, step, merge, flush, stream, steps, warmup, do_flush):
         step()
         merge()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(steps):
+        if do_flush:
+            flush.fill_(1.0)
+        ev[i][0].record(stream)
+        step()
+        merge()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tot = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3      # us
+    if not pd.info.needs_merge:          # no merge launch: the step is stage 1
+        return tot, tot.copy(), np.zeros_like(tot), wall
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for i in range(steps):
         if do_flush:
             flush.fill_(1.0)
@@ -361,13 +379,9 @@ def time_steps(pd, step, merge, flush, stream, steps, warmup, do_flush):
         merge()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    s1 = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3      # us
-    if pd.info.needs_merge:
-        mg = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
-    else:                      # no merge launch: the second event pair brackets nothing
-        mg = np.zeros_like(s1)
-    return s1, mg, wall
+    s1 = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
+    mg = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    return tot, s1, mg, wall
 
 
 # Every configuration of the benchmark target, timed in the default run after the
@@ -445,9 +459,9 @@ def per_config(args, flush, stream):
 
         # at least 50 warm-up steps: the compute-heavy shapes need that many back-to-back
         # steps before the clocks settle, whatever the headline's own warm-up count is
-        s1, mg, _ = time_steps(pd, step, merge, flush, stream, max(args.steps, 20), max(args.warmup, 50),
-                               not args.no_flush)
-        tot = float(np.mean(s1 + mg))
+        st, s1, mg, _ = time_steps(pd, step, merge, flush, stream, max(args.steps, 20), max(args.warmup, 50),
+                                   not args.no_flush)
+        tot = float(np.mean(st))
         gbps = acc["bytes"] / (tot * 1e-6) / 1e9
         res[name] = {"workload": WORKLOAD_NAMES[name], "stage1_us": round(float(np.mean(s1)), 2),
                      "merge_us": round(float(np.mean(mg)), 2), "us_per_step": round(tot, 2),
@@ -524,8 +538,7 @@ def main():
         pd.merge(out, w.out_dtype, stream=st)
 
     _spin_up(flush)
-    s1, mg, wall = time_steps(pd, step, merge, flush, stream, args.steps, args.warmup, not args.no_flush)
-    tot = s1 + mg
+    tot, s1, mg, wall = time_steps(pd, step, merge, flush, stream, args.steps, args.warmup, not args.no_flush)
 
     graph = None
     if args.graph_reps > 0:
