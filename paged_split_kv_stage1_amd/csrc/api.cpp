@@ -166,9 +166,14 @@ constexpr double kMergeLaunchS = 3.0e-6;
 // per-token scales the constant that planned the ragged group-24 mix fastest: 14, 18, 22
 // and 28 ns gave 128.5, 138.6, 119 and 118.5 us of stage 1 -- its three-block waves
 // cost more per block than the one-block shapes the first figure came from).
+// Keys with a rotary part: the latent-cache kernel computes about 64 ns per token and
+// workgroup with its four waves on one block (all loads served from cache: 33 us for the
+// 512-token items of the latent workload), i.e. 256 ns per 16-row block for one wave; the
+// 192/128 kernel is bound by its loads (20 ns).  The planned split counts of both
+// workloads measured best in forced-split sweeps.
 double compute_s_per_token_block(const pa_plan_args& a) {
   if (a.head_dim_v > 0 && a.head_dim_v != a.head_dim)      // keys with a rotary part
-    return (a.kv_scale_mode == PA_SCALE_PER_TOKEN_BLOCK128 ? 60.0 : 20.0) * 1e-9;
+    return (a.kv_scale_mode == PA_SCALE_PER_TOKEN_BLOCK128 ? 256.0 : 20.0) * 1e-9;
   const bool f8 = a.kv_dtype != PA_DTYPE_BF16;
   const bool pt = a.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD || a.kv_dtype == PA_DTYPE_INT8;
   const double d_scale = a.head_dim / 128.0;
