@@ -395,6 +395,9 @@ R8_R1 = (("c3_r8", "c3_r1"), ("c3_b1_r8", "c3_b1_r1"), ("c4", "c4_r1"), ("c4_b1"
 
 def arithmetic(w, variant: int) -> str:
     """What the stage-1 kernel of this plan multiplies in, from the tile configuration."""
+    if (variant >> 16) & 1:
+        return arithmetic(w, variant & ~(1 << 16)) + "; query rows on the MFMA M axis (S = Q K^T, O = P V, P " \
+            "transposed through LDS)"
     if (variant >> 14) & 1:
         if (variant >> 15) & 1:
             return ("bf16 MFMA on the e4m3 latent codes upconverted exactly: q.k per 128-channel block times both "
@@ -411,7 +414,7 @@ def arithmetic(w, variant: int) -> str:
         qk = ("int8 MFMA on the raw K codes, bf16 query as two int8 terms" if one_block_waves
               else "bf16 MFMA on K converted to bf16")
         return f"q.k: {qk}; P.V: bf16 MFMA on V converted to bf16 (P one bf16 term, v_scale folded)"
-    if pt and one_block_waves and w.head_dim in (256, 512):
+    if pt and one_block_waves:
         qk = "e4m3 16x16x128 MFMA on the raw K codes, bf16 query as two e4m3 terms under a per-row scale"
     else:
         qk = "bf16 MFMA on K upconverted exactly from e4m3"
@@ -488,6 +491,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-splits", type=int, default=None)
+    ap.add_argument("--orientation", default="kv_on_m", choices=["kv_on_m", "q_on_m"],
+                    help="stage 1 with the key tokens (default) or the query rows on the MFMA M axis")
     ap.add_argument("--graph-reps", type=int, default=100,
                     help="also time this many replays of stage 1 + merge captured in one hipGraph (0: skip)")
     ap.add_argument("--op", default="decode", choices=["decode", "kv_append", "kv_quantize"],
@@ -521,7 +526,7 @@ def main():
     pd = PagedDecode(w.qo_indptr, w.kv_indptr, w.kv_len, w.window, w.max_q_len, w.page_size, w.num_q_heads,
                      w.num_kv_heads, w.head_dim, w.q_dtype, w.kv_dtype, w.kv_scale_mode, dev,
                      force_splits=w.forced_splits if args.force_splits is None else args.force_splits,
-                     head_dim_v=w.head_dim_v)
+                     head_dim_v=w.head_dim_v, orientation=args.orientation)
     out = torch.empty(w.total_rows, w.num_q_heads, w.dv,
                       dtype=torch.float32 if w.out_dtype == "fp32" else torch.bfloat16, device=dev)
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
@@ -581,7 +586,7 @@ def main():
                    "total_rows": w.total_rows, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "page_size": w.page_size, "kv_dtype": w.kv_dtype,
                    "kv_scale_mode": w.kv_scale_mode, "work_items": pd.num_items, "max_splits": pd.max_splits,
-                   "cache_flush_between_steps": not args.no_flush},
+                   "orientation": args.orientation, "cache_flush_between_steps": not args.no_flush},
         "us_per_step": round(us_step, 3), "us_per_step_iqm": round(iqm(tot), 3),
         "stage1_us": round(s1_us, 3), "merge_us": round(float(np.mean(mg)), 3), "graph_replay": graph,
         "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
@@ -590,10 +595,11 @@ def main():
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "roofline": {"bound": "hbm", "achieved": round(roof_achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(roof_achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(args.config, *stage1_kernel_of(w.latent, pd.rope)),
+                     "traffic": (measured_traffic(args.config, *stage1_kernel_of(w.latent, pd.rope))
+                                 if args.orientation == "kv_on_m" else None),
                      "kernel": stage1_kernel_of(w.latent, pd.rope)[0], "bytes_per_launch": s1_bytes},
     }
-    if not args.no_per_config and args.config == "c2":
+    if not args.no_per_config and args.config == "c2" and args.orientation == "kv_on_m":
         result["per_config"], result["r8_over_r1"] = per_config(args, flush, stream)
     if not args.no_cpu_baseline:
         out_np = out.float().cpu().numpy().astype(np.float64)

@@ -103,7 +103,18 @@ typedef struct {
   int32_t head_dim_v;          /* value width when it differs from head_dim (0 = head_dim):   */
                                /*   192/128 (bf16) or 576/512 (latent cache, PER_TOKEN_BLOCK128 */
                                /*   scales, FP8 queries); such plans run pa_decode_stage1_rope */
+  int32_t orientation;         /* pa_orientation of stage 1's matrix products (0 = default)  */
 } pa_plan_args;
+
+/* Which axis of stage 1's 16x16 MFMA tiles the key tokens take.  KV_ON_M (the default)
+ * computes S^T = K Q^T and O^T = V^T P^T: the score accumulator already has the layout
+ * of P^T as an operand, so P stays in registers.  Q_ON_M computes S = Q K^T and O = P V
+ * with the packed query rows on M (FreeToken PR #900, "Changes"), transposing P through
+ * LDS every tile; it is kept as the measured alternative (the swapped form is what
+ * hpc-ops issue #4 asks about) for bf16 KV and for PER_TOKEN_HEAD FP8 KV with bf16
+ * queries at head_dim 128 and 256, except bf16 KV at head_dim 256 with 9-16 query rows
+ * per KV head and bf16 KV at head_dim 128 with more than 128 (UNSUPPORTED there). */
+typedef enum { PA_ORIENT_KV_ON_M = 0, PA_ORIENT_Q_ON_M = 1 } pa_orientation;
 
 /* Planner output, consumed by stage1/merge.  Sizes are in bytes. */
 typedef struct {

@@ -34,7 +34,15 @@ class PlanArgs(ctypes.Structure):
                 ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int), ("kv_scale_mode", ctypes.c_int),
                 ("num_cus", ctypes.c_int32), ("max_splits", ctypes.c_int32), ("force_splits", ctypes.c_int32),
-                ("head_dim_v", ctypes.c_int32)]
+                ("head_dim_v", ctypes.c_int32), ("orientation", ctypes.c_int32)]
+
+
+PA_ORIENT_KV_ON_M, PA_ORIENT_Q_ON_M = 0, 1
+_ORIENT = {"kv_on_m": PA_ORIENT_KV_ON_M, "q_on_m": PA_ORIENT_Q_ON_M}
+
+
+def _orient(x) -> int:
+    return _ORIENT[x] if isinstance(x, str) else int(x)
 
 
 class PlanInfo(ctypes.Structure):
@@ -144,7 +152,7 @@ def pa_version() -> str:
 
 def pa_plan_splits(qo_indptr, kv_indptr, kv_len, window, max_q_len, page_size, num_q_heads, num_kv_heads, head_dim,
                    q_dtype, kv_dtype, kv_scale_mode, num_cus=0, max_splits=0, force_splits=0, query_only=False,
-                   head_dim_v=0):
+                   head_dim_v=0, orientation="kv_on_m"):
     """Returns (PlanInfo, plan bytes as a numpy uint8 array, or None with query_only)."""
     arrs = [np.ascontiguousarray(np.asarray(x, dtype=np.int32)) for x in (qo_indptr, kv_indptr, kv_len)]
     win = None if window is None else np.ascontiguousarray(np.asarray(window, dtype=np.int32))
@@ -152,7 +160,8 @@ def pa_plan_splits(qo_indptr, kv_indptr, kv_len, window, max_q_len, page_size, n
     a = PlanArgs(B, arrs[0].ctypes.data_as(_i32p), arrs[1].ctypes.data_as(_i32p), arrs[2].ctypes.data_as(_i32p),
                  None if win is None else win.ctypes.data_as(_i32p), int(max_q_len), int(page_size),
                  int(num_q_heads), int(num_kv_heads), int(head_dim), _dt(q_dtype), _dt(kv_dtype),
-                 _sm(kv_scale_mode), int(num_cus), int(max_splits), int(force_splits), int(head_dim_v))
+                 _sm(kv_scale_mode), int(num_cus), int(max_splits), int(force_splits), int(head_dim_v),
+                 _orient(orientation))
     info = PlanInfo()
     _check(lib().pa_plan_splits(ctypes.byref(a), None, 0, ctypes.byref(info)))
     if query_only:

@@ -68,6 +68,7 @@ namespace pa {
 // Tile configurations stage 1 is instantiated for (its dispatcher in stage1.hip uses the
 // same list).
 bool stage1_cfg_supported(const KernelCfg& c) {
+  if (c.qm && (c.kr || c.dh == 512)) return false;
   // keys with a rotary part (stage1_kr.hip): bf16 192/128, or the MLA latent cache 576/512
   // with e4m3 latent codes and e4m3 latent queries; one, two or four 16-row blocks per
   // item, the four waves splitting each tile's tokens between the blocks' teams
@@ -82,6 +83,18 @@ bool stage1_cfg_supported(const KernelCfg& c) {
   if (c.dh == 512)
     return !c.qf8 && !c.i8 && (c.kvf8 ? c.pt : !c.pt) && c.wq == 4 && c.nqb == 1;
   if (c.dh != 128 && c.dh != 256) return false;
+  if (c.qm) {
+    // query rows on the MFMA M axis (the alternative orientation): bf16 KV, or
+    // per-token-head FP8 KV with bf16 queries; not the two tile shapes whose registers
+    // would spill (bf16 KV with two query-block waves at head_dim 256, three blocks per
+    // wave at head_dim 128)
+    if (c.qf8 || c.i8 || (c.kvf8 != c.pt)) return false;
+    if (c.nqb == 1 && c.wq == 1) return c.dh == 128;
+    if (c.nqb == 1 && c.wq == 2) return c.dh == 128 || c.kvf8;
+    if (c.nqb == 1 && c.wq == 4) return true;
+    if (c.wq == 4 && c.nqb == 2) return c.dh == 128;
+    return c.wq == 4 && c.nqb == 3 && c.dh == 128 && c.kvf8;
+  }
   if (c.qf8 && !c.kvf8) return false;
   if (!c.kvf8 && c.pt) return false;
   if (c.i8 && (!c.kvf8 || !c.pt || c.qf8)) return false;    // INT8 KV: bf16 queries, per-token scale path
@@ -102,6 +115,7 @@ bool choose_cfg(const pa_plan_args& a, KernelCfg* c) {
   const int nqb = (mq + 15) / 16;
   c->dh = a.head_dim;
   c->dv = a.head_dim_v > 0 ? a.head_dim_v : a.head_dim;
+  c->qm = a.orientation == PA_ORIENT_Q_ON_M;
   if (c->dv != c->dh) {               // keys with a rotary part: up to four blocks per item
     c->kr = 1;
     c->mla = a.kv_scale_mode == PA_SCALE_PER_TOKEN_BLOCK128;
@@ -368,7 +382,14 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   if (a->force_splits > split_cap)
     return fail(PA_ERR_INVALID_ARGUMENT, "force_splits %d exceeds the split cap %d", a->force_splits, split_cap);
 
+  if (a->orientation != PA_ORIENT_KV_ON_M && a->orientation != PA_ORIENT_Q_ON_M)
+    return fail(PA_ERR_INVALID_ARGUMENT, "orientation must be PA_ORIENT_KV_ON_M or PA_ORIENT_Q_ON_M (got %d)",
+                a->orientation);
   KernelCfg cfg;
+  if (!choose_cfg(*a, &cfg) && cfg.qm)
+    return fail(PA_ERR_UNSUPPORTED, "query rows on the MFMA M axis are built for bf16 KV and per-token-head FP8 KV "
+                                    "with bf16 queries at head_dim 128/256, except bf16 KV at head_dim 256 with at "
+                                    "most 32 and at head_dim 128 with more than 128 query rows x heads per KV head");
   if (!choose_cfg(*a, &cfg))
     return fail(PA_ERR_UNSUPPORTED, "max_q_len x group = %d query rows per KV head is beyond the tile limit "
                                     "for head_dim %d and this dtype combination",

@@ -37,16 +37,17 @@ struct KernelCfg {
   int kr = 0;    // keys of dv + 64 channels with a 64-channel rotary part (stage1_kr.hip)
   int mla = 0;   // with kr: MLA-style latent cache (value = latent, e4m3 per 128 channels)
   int dv = 0;    // value width (= dh unless kr)
+  int qm = 0;    // query rows on the MFMA M axis (S = Q K^T) instead of the key tokens
 };
 inline int32_t pack_cfg(const KernelCfg& c) {
   return (c.dh == 256 ? 1 : 0) | (c.qf8 << 1) | (c.kvf8 << 2) | (c.pt << 3) | (c.wq << 4) | (c.nqb << 8) |
-         (c.i8 << 12) | ((c.dh == 512 ? 1 : 0) << 13) | (c.kr << 14) | (c.mla << 15);
+         (c.i8 << 12) | ((c.dh == 512 ? 1 : 0) << 13) | (c.kr << 14) | (c.mla << 15) | (c.qm << 16);
 }
 inline KernelCfg unpack_cfg(int32_t v) {
   KernelCfg c;
   c.dh = ((v >> 13) & 1) ? 512 : ((v & 1) ? 256 : 128); c.qf8 = (v >> 1) & 1; c.kvf8 = (v >> 2) & 1; c.pt = (v >> 3) & 1;
   c.wq = (v >> 4) & 15; c.nqb = (v >> 8) & 15; c.i8 = (v >> 12) & 1;
-  c.kr = (v >> 14) & 1; c.mla = (v >> 15) & 1;
+  c.kr = (v >> 14) & 1; c.mla = (v >> 15) & 1; c.qm = (v >> 16) & 1;
   c.dv = c.dh;
   if (c.kr) {
     c.dv = c.mla ? 512 : 128;

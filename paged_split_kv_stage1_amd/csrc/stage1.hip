@@ -50,12 +50,63 @@ template <int SCALE_B>
 __device__ __forceinline__ f32x4 mfma_fp8_k128(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, SCALE_B);
 }
+// The same with the E8M0 exponent applied to A.
+template <int SCALE_A>
+__device__ __forceinline__ f32x4 mfma_fp8_k128_sa(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, SCALE_A, 0, 127);
+}
+
+// q.k products with the key tokens on the MFMA M axis (S^T = K Q^T, QM false) or the
+// query rows on it (S = Q K^T, QM true): the A and B operands have the same per-lane
+// layout, so the orientation is the order of the two operands.
+template <bool QM>
+__device__ __forceinline__ f32x4 mfma_bf16_o(bf16x8 k, bf16x8 q, f32x4 c) {
+  return QM ? mfma_bf16(q, k, c) : mfma_bf16(k, q, c);
+}
+template <bool QM>
+__device__ __forceinline__ f32x4 mfma_fp8_o(long k, long q, f32x4 c) {
+  return QM ? mfma_fp8(q, k, c) : mfma_fp8(k, q, c);
+}
+template <bool QM>
+__device__ __forceinline__ i32x4 mfma_i8(i32x4 k, i32x4 q, i32x4 c) {
+  return QM ? __builtin_amdgcn_mfma_i32_16x16x64_i8(q, k, c, 0, 0, 0)
+            : __builtin_amdgcn_mfma_i32_16x16x64_i8(k, q, c, 0, 0, 0);
+}
+
+// Maximum and sum over the 16 lanes of each lane group (DPP within a row of 16 lanes:
+// swap neighbours, swap pairs, mirror halves of 8, mirror the 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));      // quad_perm 1,0,3,2
+  x = fmaxf(x, dpp_f<0x4E>(x));      // quad_perm 2,3,0,1
+  x = fmaxf(x, dpp_f<0x141>(x));     // row_half_mirror
+  return fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+}
+// Value of lane 4 (l / 4) + r (DPP quad_perm r,r,r,r); r must be a constant.
+__device__ __forceinline__ float quad_bcast(float x, int r) {
+  switch (r) {
+    case 0: return dpp_f<0x00>(x);
+    case 1: return dpp_f<0x55>(x);
+    case 2: return dpp_f<0xAA>(x);
+    default: return dpp_f<0xFF>(x);
+  }
+}
+__device__ __forceinline__ int quad_bcast_i(int x, int r) { return __float_as_int(quad_bcast(__int_as_float(x), r)); }
+__device__ __forceinline__ float lane16_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  return x + dpp_f<0x140>(x);
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // KV: 0 bf16 cache, 1 e4m3 codes, 2 int8 codes (both one byte per element).
-template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB, int NS, int PD>
+template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB, int NS, int PD, bool QM = false>
 struct S1Cfg {
   static constexpr bool KVF8 = KV != 0;             // one-byte codes (e4m3 or int8)
   static constexpr bool I8 = KV == 2;
@@ -109,13 +160,18 @@ struct S1Cfg {
   // every tile load still in flight, which undoes the prefetch.
   static constexpr int QREG = (NQB == 3 && KVF8 && PT && !QF8) ? 2 : NQB;
   static constexpr int QLB = (NQB - QREG) * KC * 1024;   // LDS bytes per wave
-  static constexpr int MAINB = NS * STAGEB + 4 * QLB;
+  // Query rows on the MFMA M axis (the alternative orientation): P is transposed through
+  // a per-wave LDS scratch of 32 tokens x 16 rows in bf16 (two terms for bf16 V), which
+  // also carries the final change of accumulator layout (1 KB per 16 x 16 block).
+  static constexpr int PSB = QM ? (KVF8 ? 1024 : 2048) : 0;
+  static constexpr int MAINB = NS * STAGEB + 4 * QLB + 4 * PSB;
   static constexpr int LDSB = MAINB > EPIB ? MAINB : EPIB;
   static_assert(CPT >= 1 && (BN * CPR) % 256 == 0, "tile must split evenly over 256 threads");
   static_assert(WT == 1 || NQB == 1, "query blocks per wave > 1 only without token split");
   static_assert(NS == 1 || NS == 2, "one or two LDS stages");
   static_assert(PD >= 1 && PD <= 3, "prefetch one to three tiles ahead");
   static_assert(2 * BN <= 256, "scale loads use one thread per token");
+  static_assert(!QM || (!PV_FP8 && DH <= 256), "query rows on M: bf16 P.V, head_dim <= 256");
 };
 
 // XOR swizzles of the 16-byte chunk index inside a token row, chosen so the MFMA
@@ -144,9 +200,9 @@ struct QOperand<true> { using T = long; };
 template <int V>
 using ic = std::integral_constant<int, V>;
 
-template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB, int NS, int PD>
+template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB, int NS, int PD, bool QM = false>
 __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Args a) {
-  using C = S1Cfg<DH, QF8, KV, PT, WQ, NQB, NS, PD>;
+  using C = S1Cfg<DH, QF8, KV, PT, WQ, NQB, NS, PD, QM>;
   constexpr bool KVF8 = C::KVF8;
   using QT = typename QOperand<QF8>::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDSB];
@@ -192,6 +248,12 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
     lim_hi[i] = min(p, te - 1);
     qsc[i] = QF8 ? a.q_scale[(it.kvh * G + hl) * hstep] : 1.0f;
   }
+  int qpos[NQB];                      // query rows on M: position of row 4g + (L16 & 3)
+  if constexpr (QM) {
+#pragma unroll
+    for (int i = 0; i < NQB; ++i)
+      qpos[i] = it.kv_len - it.nrows + min(16 * (it.qblk0 + wq + WQ * i) + 4 * g + (L16 & 3), Mq - 1) / G;
+  }
   // Tokens every real row of the item sees (fast path: no masking inside).
   const int p_first = it.kv_len - it.nrows;
   const int lo_last = it.window > 0 ? max(0, it.kv_len - 1 - it.window + 1) : 0;
@@ -212,13 +274,22 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
   f32x4 o[NQB][C::DB];
   f32x4 olo[C::PV_FP8 ? NQB : 1][C::PV_FP8 ? C::DB : 1];
   float mrun[NQB], lrun[NQB];
+  // With the query rows on M a lane holds rows 4g .. 4g+3 of each block: their partial
+  // sums (over the lane's tokens) and score scales, and, packed one row per lane (row
+  // 4g + (L16 & 3), read by the other lanes of the quad through DPP), their running
+  // maxima.
+  float lq[NQB][4], xq[NQB][4], mqp[NQB];
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
     mrun[i] = -INFINITY;
     lrun[i] = 0.f;
+    mqp[i] = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lq[i][r] = 0.f;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  uint8_t* const pscr = smem + NS * C::STAGEB + 4 * C::QLB + wave * C::PSB;   // P transpose (QM)
   if constexpr (C::PV_FP8) {
 #pragma unroll
     for (int i = 0; i < NQB; ++i)
@@ -356,6 +427,27 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
       return tv * (C::VCPR * 16) + ((db ^ swz_v<C::VCPR, true>(tv)) << 4) + 8 * (L16 & 1);
     }
   };
+  // V operand of one 16-channel block for 32 tokens, bf16 (k order {4g..4g+3,
+  // 16+4g..16+4g+3}; lane L16 = channel): A operand of O^T += V^T P^T, B operand of
+  // O += P V.
+  auto vfrag = [&](const uint8_t* Vl, int db) __attribute__((always_inline)) -> bf16x8 {
+    bf16x8 va;
+    if constexpr (C::LBFV) {
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 0)));
+      const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 1)));
+      const __bf16* p1 = reinterpret_cast<const __bf16*>(&v1);
+      const __bf16* p2 = reinterpret_cast<const __bf16*>(&v2);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        va[k] = p1[k];
+        va[4 + k] = p2[k];
+      }
+    } else {
+      const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
+      va = fp8x8_to_bf16x8((uint32_t)w[0], (uint32_t)w[1]);
+    }
+    return va;
+  };
   const bool wave_has_rows = qvalid[0];
   // exponent offset: per-tensor FP8 V scales P into [0, 448] inside exp2 (the final
   // normaliser divides the 448 out again because l accumulates the scaled P)
@@ -372,20 +464,31 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
     const int c0 = tile0 + wt * 32;          // first token of this wave's 32-token chunk
     if (!(c0 < te && wave_has_rows)) return;
     const bool need_mask = !(c0 >= vis_lo_all && c0 + 31 <= vis_hi_all);
-    float ks[8], vs[8];
+    // Per-token-head scales of the lane's tokens: with K on M, tokens {4g..4g+3,
+    // 16+4g..16+4g+3} of the chunk; with Q on M, tokens L16 and 16 + L16.
+    constexpr int NT = QM ? 2 : 8;
+    float ks[NT], vs[NT];
     if constexpr (PT) {
+      if constexpr (QM) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        ks[k] = ksl[wt * 32 + 4 * g + k] * qk_scale;
-        ks[4 + k] = ksl[wt * 32 + 16 + 4 * g + k] * qk_scale;
-        vs[k] = vsl[wt * 32 + 4 * g + k];
-        vs[4 + k] = vsl[wt * 32 + 16 + 4 * g + k];
+        for (int h = 0; h < 2; ++h) {
+          ks[h] = ksl[wt * 32 + 16 * h + L16] * qk_scale;
+          vs[h] = vsl[wt * 32 + 16 * h + L16];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          ks[k] = ksl[wt * 32 + 4 * g + k] * qk_scale;
+          ks[4 + k] = ksl[wt * 32 + 16 + 4 * g + k] * qk_scale;
+          vs[k] = vsl[wt * 32 + 4 * g + k];
+          vs[4 + k] = vsl[wt * 32 + 16 + 4 * g + k];
+        }
       }
     }
 #pragma unroll
     for (int i = 0; i < NQB; ++i) {
       if (!qvalid[i]) continue;
-      // ---- S^T = K Q^T for 2 x 16 tokens ----------------------------------------------
+      // ---- S^T = K Q^T (or S = Q K^T) for 2 x 16 tokens ---------------------------------
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
       if constexpr (C::QX2) {
 #pragma unroll
@@ -401,10 +504,17 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
           const i32x8 qh = __builtin_shufflevector(qld(0), qld(1), 0, 1, 2, 3, 4, 5, 6, 7);
           const i32x8 ql = __builtin_shufflevector(qld(2), qld(3), 0, 1, 2, 3, 4, 5, 6, 7);
           const i32x8 k0 = kld(0), k1 = kld(1);
-          s0 = mfma_fp8_k128<127>(k0, qh, s0);
-          s1 = mfma_fp8_k128<127>(k1, qh, s1);
-          s0 = mfma_fp8_k128<123>(k0, ql, s0);     // lo term carries x16: scale 2^-4
-          s1 = mfma_fp8_k128<123>(k1, ql, s1);
+          if constexpr (QM) {
+            s0 = mfma_fp8_k128_sa<127>(qh, k0, s0);
+            s1 = mfma_fp8_k128_sa<127>(qh, k1, s1);
+            s0 = mfma_fp8_k128_sa<123>(ql, k0, s0);
+            s1 = mfma_fp8_k128_sa<123>(ql, k1, s1);
+          } else {
+            s0 = mfma_fp8_k128<127>(k0, qh, s0);
+            s1 = mfma_fp8_k128<127>(k1, qh, s1);
+            s0 = mfma_fp8_k128<123>(k0, ql, s0);     // lo term carries x16: scale 2^-4
+            s1 = mfma_fp8_k128<123>(k1, ql, s1);
+          }
         }
       }
       if constexpr (C::QI2) {
@@ -415,10 +525,10 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
           const i32x4 k1 = *reinterpret_cast<const i32x4*>(Kl + kro4[1][ks]);
           const i32x4 qh = __builtin_bit_cast(i32x4, qget(i, 2 * ks));
           const i32x4 ql = __builtin_bit_cast(i32x4, qget(i, 2 * ks + 1));
-          h0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(k0, qh, h0, 0, 0, 0);
-          h1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, qh, h1, 0, 0, 0);
-          l0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(k0, ql, l0, 0, 0, 0);
-          l1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, ql, l1, 0, 0, 0);
+          h0 = mfma_i8<QM>(k0, qh, h0);
+          h1 = mfma_i8<QM>(k1, qh, h1);
+          l0 = mfma_i8<QM>(k0, ql, l0);
+          l1 = mfma_i8<QM>(k1, ql, l1);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {        // exact int32 sums (|sum| < 2^24) -> fp32
@@ -432,17 +542,17 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
           const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Kl + kro[0][kc]);
           const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Kl + kro[1][kc]);
           const QT qv = qget(i, kc);
-          s0 = mfma_bf16(k0, qv, s0);
-          s1 = mfma_bf16(k1, qv, s1);
+          s0 = mfma_bf16_o<QM>(k0, qv, s0);
+          s1 = mfma_bf16_o<QM>(k1, qv, s1);
         } else {
           const uint2 r0 = *reinterpret_cast<const uint2*>(Kl + kro[0][kc]);
           const uint2 r1 = *reinterpret_cast<const uint2*>(Kl + kro[1][kc]);
           if constexpr (QF8) {
-            s0 = mfma_fp8((long)r0.x | ((long)r0.y << 32), qop[i][kc], s0);
-            s1 = mfma_fp8((long)r1.x | ((long)r1.y << 32), qop[i][kc], s1);
+            s0 = mfma_fp8_o<QM>((long)r0.x | ((long)r0.y << 32), qop[i][kc], s0);
+            s1 = mfma_fp8_o<QM>((long)r1.x | ((long)r1.y << 32), qop[i][kc], s1);
           } else {
-            s0 = mfma_bf16(fp8x8_to_bf16x8(r0.x, r0.y), qop[i][kc], s0);
-            s1 = mfma_bf16(fp8x8_to_bf16x8(r1.x, r1.y), qop[i][kc], s1);
+            s0 = mfma_bf16_o<QM>(fp8x8_to_bf16x8(r0.x, r0.y), qop[i][kc], s0);
+            s1 = mfma_bf16_o<QM>(fp8x8_to_bf16x8(r1.x, r1.y), qop[i][kc], s1);
           }
         }
       }
@@ -452,6 +562,90 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
       for (int k = 0; k < 4; ++k) {
         x[k] = s0[k];
         x[4 + k] = s1[k];
+      }
+      if constexpr (QM) {
+        // Lane (L16, g) holds S[row 4g + r][token L16] in x[r] and S[row 4g + r][token
+        // 16 + L16] in x[4 + r]: four rows per lane, each row spread over 16 lanes.
+        if constexpr (PT) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[r] *= ks[0];
+            x[4 + r] *= ks[1];
+          }
+        }
+        if (need_mask) {
+          // visible range of row 4g + (L16 & 3) (as lim_lo / lim_hi), then of each row r
+          const int lop = max(it.window > 0 ? max(0, qpos[i] - it.window + 1) : 0, tb0);
+          const int hip = min(qpos[i], te - 1);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int lo = quad_bcast_i(lop, r), hi = quad_bcast_i(hip, r);
+            x[r] = (c0 + L16 >= lo && c0 + L16 <= hi) ? x[r] : -INFINITY;
+            x[4 + r] = (c0 + 16 + L16 >= lo && c0 + 16 + L16 <= hi) ? x[4 + r] : -INFINITY;
+          }
+        }
+        float mx[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx[r] = lane16_max(fmaxf(x[r], x[4 + r])) * xq[i][r];
+        const int sel = L16 & 3;
+        const float mxp = sel == 0 ? mx[0] : sel == 1 ? mx[1] : sel == 2 ? mx[2] : mx[3];
+        const float mnew = fmaxf(mqp[i], mxp);
+        const float musep = (mnew == -INFINITY) ? 0.f : mnew;
+        if (__builtin_amdgcn_ballot_w64(mnew != mqp[i]) != 0) {     // lazy rescale
+          const float alpha = fast_exp2(mqp[i] - musep);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float ar = quad_bcast(alpha, r);
+            lq[i][r] *= ar;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) o[i][db][r] *= ar;
+          }
+          mqp[i] = mnew;
+        }
+        // P, transposed through this wave's LDS scratch: P^T[token][row] (32 tokens x
+        // 16 rows, bf16), read back as the A operand P[row][tokens {4g..4g+3,
+        // 16+4g..16+4g+3}] with ds_read_b64_tr_b16 (the k order of the V operand below).
+        uint8_t* pw = pscr + L16 * 32 + 8 * g;
+        const uint8_t* pr = pscr + (4 * g + (L16 >> 2)) * 32 + 8 * (L16 & 3);
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x4 hv4, lv4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(fmaf(x[4 * h + r], xq[i][r], kPoff - quad_bcast(musep, r)));
+            lq[i][r] += p;
+            const float y = PT ? p * vs[h] : p;
+            const __bf16 hb = (__bf16)y;
+            hv4[r] = hb;
+            if constexpr (!KVF8) lv4[r] = (__bf16)(y - (float)hb);
+          }
+          *reinterpret_cast<bf16x4*>(pw + 512 * h) = hv4;
+          if constexpr (!KVF8) *reinterpret_cast<bf16x4*>(pw + 1024 + 512 * h) = lv4;
+        }
+        auto pread = [&](int term) __attribute__((always_inline)) -> bf16x8 {
+          const i16x4 u1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(pr + 1024 * term));
+          const i16x4 u2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(pr + 1024 * term + 512));
+          bf16x8 r8;
+          const __bf16* p1 = reinterpret_cast<const __bf16*>(&u1);
+          const __bf16* p2 = reinterpret_cast<const __bf16*>(&u2);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            r8[k] = p1[k];
+            r8[4 + k] = p2[k];
+          }
+          return r8;
+        };
+        const bf16x8 ph = pread(0);
+        bf16x8 pl;
+        if constexpr (!KVF8) pl = pread(1);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const bf16x8 vb = vfrag(Vl, db);
+          o[i][db] = mfma_bf16(ph, vb, o[i][db]);
+          if constexpr (!KVF8) o[i][db] = mfma_bf16(pl, vb, o[i][db]);
+        }
+        continue;
       }
       const float xs = xsb[i];               // score scale still to apply
       if constexpr (PT) {
@@ -517,21 +711,7 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
         }
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          bf16x8 va;
-          if constexpr (C::LBFV) {
-            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 0)));
-            const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db, 1)));
-            const __bf16* p1 = reinterpret_cast<const __bf16*>(&v1);
-            const __bf16* p2 = reinterpret_cast<const __bf16*>(&v2);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              va[k] = p1[k];
-              va[4 + k] = p2[k];
-            }
-          } else {
-            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
-            va = fp8x8_to_bf16x8((uint32_t)w[0], (uint32_t)w[1]);
-          }
+          const bf16x8 va = vfrag(Vl, db);
           o[i][db] = mfma_bf16(va, hv, o[i][db]);
           if constexpr (!KVF8) o[i][db] = mfma_bf16(va, lv, o[i][db]);
         }
@@ -676,6 +856,15 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
       }
     }
   }
+  if constexpr (QM) {
+    // score scale of row 4g + r: that of lane L16 = 4g + r (the same in every lane group;
+    // one value for all rows unless the query carries per-head or per-row scales)
+#pragma unroll
+    for (int i = 0; i < NQB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        xq[i][r] = (!QF8 && !C::QX2 && !C::QI2) ? xsb[i] : __shfl(xsb[i], 4 * g + r);
+  }
   __builtin_amdgcn_s_waitcnt(0xC07F & ~0xC00F);          // vmcnt(0) lgkmcnt(0)
   if (ntiles > 0) {
     store_tile(ic<0>{}, smem);
@@ -694,6 +883,30 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
     }
     if constexpr (PD >= 3) {
       if (ti + 2 < ntiles) step(ic<2>{}, ic<0>{}, ti + 2);
+    }
+  }
+  if constexpr (QM) {
+    // Back to the K-on-M accumulator layout the epilogue takes: lane (L16, g) gets row
+    // L16's maximum, its sum (in lane group 0; the epilogue sums the four groups) and
+    // O^T[16 db + 4g + r][row L16], through this wave's scratch.
+    float* pf = reinterpret_cast<float*>(pscr);
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) {
+      float lt[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lt[r] = lane16_sum(lq[i][r]);
+      if (L16 == 0) *reinterpret_cast<f32x4*>(pf + 4 * g) = f32x4{lt[0], lt[1], lt[2], lt[3]};
+      // row L16 = 4 (L16 >> 2) + (L16 & 3): packed in lane 16 (L16 >> 2) + (L16 & 3)
+      mrun[i] = __shfl(mqp[i], 16 * (L16 >> 2) + (L16 & 3));
+      lrun[i] = g == 0 ? pf[L16] : 0.f;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        *reinterpret_cast<f32x4*>(pf + L16 * 16 + 4 * g) = o[i][db];    // [channel][row]
+        f32x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = pf[(4 * g + r) * 16 + L16];
+        o[i][db] = v;
+      }
     }
   }
   __syncthreads();
@@ -824,15 +1037,38 @@ struct Pipe {
   static constexpr int PD = DH == 512 ? 2 : (DH == 256 && (PV_FP8 || (KV == 2 && WQ == 2))) ? 1 : (CPT <= 4 ? 2 : 1);
 };
 
-template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB>
+template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB, bool QM = false>
 static int launch_one(const Stage1Args& a, int num_items, void* stream) {
   using Pp = Pipe<DH, QF8, KV, PT, WQ, NQB>;
-  using C = S1Cfg<DH, QF8, KV, PT, WQ, NQB, Pp::NS, Pp::PD>;
+  using C = S1Cfg<DH, QF8, KV, PT, WQ, NQB, Pp::NS, Pp::PD, QM>;
   static_assert(Pp::stage == C::STAGEB, "host and kernel disagree on the LDS stage size");
   static_assert(C::LDSB <= Pp::LDS_CAP, "the workgroups of a CU must fit in its 160 KB of LDS");
-  hipLaunchKernelGGL((stage1_kernel<DH, QF8, KV, PT, WQ, NQB, Pp::NS, Pp::PD>), dim3(num_items), dim3(256), 0,
+  hipLaunchKernelGGL((stage1_kernel<DH, QF8, KV, PT, WQ, NQB, Pp::NS, Pp::PD, QM>), dim3(num_items), dim3(256), 0,
                      (hipStream_t)stream, a);
   return (int)hipGetLastError();
+}
+
+// The query-rows-on-M orientation, for bf16 KV and per-token-head FP8 KV with bf16
+// queries at head_dim 128 and 256, in the tile shapes listed by stage1_cfg_supported
+// (bf16 KV at head_dim 256 with two query-block waves and at head_dim 128 with three
+// blocks per wave would need more than 256 registers).
+template <int DH, int KV>
+static int dispatch_qm(const KernelCfg& c, const Stage1Args& a, int n, void* s) {
+  constexpr bool PT = KV == 1;
+  if constexpr (DH == 128) {
+    if (c.wq == 1 && c.nqb == 1) return launch_one<DH, false, KV, PT, 1, 1, true>(a, n, s);
+  }
+  if constexpr (DH == 128 || PT) {
+    if (c.wq == 2 && c.nqb == 1) return launch_one<DH, false, KV, PT, 2, 1, true>(a, n, s);
+  }
+  if (c.wq == 4 && c.nqb == 1) return launch_one<DH, false, KV, PT, 4, 1, true>(a, n, s);
+  if constexpr (DH == 128) {
+    if (c.wq == 4 && c.nqb == 2) return launch_one<DH, false, KV, PT, 4, 2, true>(a, n, s);
+  }
+  if constexpr (DH == 128 && PT) {
+    if (c.wq == 4 && c.nqb == 3) return launch_one<DH, false, KV, PT, 4, 3, true>(a, n, s);
+  }
+  return (int)hipErrorInvalidValue;
 }
 
 // Largest query-block count per wave instantiated for a mode: per-tensor FP8 V keeps
@@ -870,6 +1106,10 @@ static int dispatch_tiles(const KernelCfg& c, const Stage1Args& a, int n, void* 
 
 template <int DH>
 static int dispatch_modes(const KernelCfg& c, const Stage1Args& a, int n, void* s) {
+  if (c.qm) {
+    if (c.qf8 || c.i8 || c.kvf8 != c.pt) return (int)hipErrorInvalidValue;
+    return c.kvf8 ? dispatch_qm<DH, 1>(c, a, n, s) : dispatch_qm<DH, 0>(c, a, n, s);
+  }
   if (c.i8) return !c.qf8 && c.pt ? dispatch_tiles<DH, false, 2, true>(c, a, n, s) : (int)hipErrorInvalidValue;
   if (!c.qf8 && !c.kvf8) return dispatch_tiles<DH, false, 0, false>(c, a, n, s);
   if (c.qf8 && c.kvf8 && !c.pt) return dispatch_tiles<DH, true, 1, false>(c, a, n, s);

@@ -21,10 +21,11 @@ class PagedDecode:
     def __init__(self, qo_indptr, kv_indptr, kv_len, window, max_q_len: int, page_size: int, num_q_heads: int,
                  num_kv_heads: int, head_dim: int, q_dtype: str, kv_dtype: str, kv_scale_mode: str,
                  device: torch.device, num_cus: int = 0, max_splits: int = 0, force_splits: int = 0,
-                 head_dim_v: int = 0):
+                 head_dim_v: int = 0, orientation: str = "kv_on_m"):
         self.info, plan = pa_plan_splits(qo_indptr, kv_indptr, kv_len, window, max_q_len, page_size, num_q_heads,
                                          num_kv_heads, head_dim, q_dtype, kv_dtype, kv_scale_mode, num_cus=num_cus,
-                                         max_splits=max_splits, force_splits=force_splits, head_dim_v=head_dim_v)
+                                         max_splits=max_splits, force_splits=force_splits, head_dim_v=head_dim_v,
+                                         orientation=orientation)
         self.rope = head_dim_v not in (0, head_dim)
         self.plan_host = plan
         self.plan = torch.from_numpy(plan).to(device)

@@ -27,13 +27,13 @@ def test_library_exports_every_declared_symbol():
 
 
 def _plan(B=2, rows=(1, 4), kv=(100, 3000), window=None, R=8, P=16, Hq=16, Hkv=2, d=256, q="bf16", kvd="bf16",
-          mode="none", cus=256, max_splits=0, force=0):
+          mode="none", cus=256, max_splits=0, force=0, orientation="kv_on_m"):
     rows = np.asarray(rows)
     kv = np.asarray(kv)
     qo = np.concatenate([[0], np.cumsum(rows)])
     kvi = np.concatenate([[0], np.cumsum((kv + P - 1) // P)])
     return pa_plan_splits(qo, kvi, kv, window, R, P, Hq, Hkv, d, q, kvd, mode, num_cus=cus, max_splits=max_splits,
-                          force_splits=force)
+                          force_splits=force, orientation=orientation)
 
 
 def _items(info, plan):
@@ -343,4 +343,38 @@ def test_gather_hooks_refuse_the_other_kernels_plans():
     assert e.value.status == PA_ERR_UNSUPPORTED
     with pytest.raises(PaError) as e:          # 192/128 needs the V layout
         _lib.pa_debug_gather_rope(info, fake, fake, lay, None, None, None, fake)
+    assert e.value.status == PA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(kvd="fp8", mode="per_token_head"),
+                                dict(d=128, Hq=48, kvd="fp8", mode="per_token_head"),
+                                dict(d=128, Hq=32, R=4, rows=(3, 4))])
+def test_query_rows_on_m_plans_the_same_work(kw):
+    """The orientation changes only the kernel: the same work list, the variant with its bit."""
+    a_info, a_plan = _plan(**kw)
+    b_info, b_plan = _plan(orientation="q_on_m", **kw)
+    assert b_info.variant == a_info.variant | (1 << 16)
+    assert (a_info.num_items, a_info.max_splits, a_info.plan_bytes) == (b_info.num_items, b_info.max_splits,
+                                                                        b_info.plan_bytes)
+    assert np.array_equal(a_plan, b_plan)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q="fp8", kvd="fp8", mode="per_tensor"),             # e4m3 P.V
+    dict(kvd="fp8", mode="per_tensor"),
+    dict(kvd="int8", mode="per_token_head"),
+    dict(R=4, rows=(1, 4)),                                  # bf16, d256, 32 rows x heads: two-wave tiles
+    dict(d=128, Hq=48, R=8, rows=(8, 1)),                    # bf16, d128, 3 blocks per wave
+    dict(d=512, Hq=8, Hkv=1),
+])
+def test_query_rows_on_m_refuses_what_it_is_not_built_for(kw):
+    _plan(**kw)                                              # the default orientation plans it
+    with pytest.raises(PaError) as e:
+        _plan(orientation="q_on_m", **kw)
+    assert e.value.status == PA_ERR_UNSUPPORTED
+
+
+def test_orientation_value_is_checked():
+    with pytest.raises(PaError) as e:
+        _plan(orientation=2)
     assert e.value.status == PA_ERR_INVALID_ARGUMENT
