@@ -603,6 +603,7 @@ pa_status pa_decode_stage1(const pa_plan_info* info, const void* plan_dev, const
   s.group = info->num_q_heads / info->num_kv_heads;
   s.page_shift = ps;
   s.s_max = info->max_splits;
+  s.fair = info->num_items <= kSlotsPerCu * info->num_cus;
   const int e = launch_stage1(cfg, s, info->num_items, stream);
   if (e) return hip_fail(e, "pa_decode_stage1 launch");
   return ok();
@@ -671,6 +672,7 @@ pa_status pa_decode_stage1_rope(const pa_plan_info* info, const void* plan_dev, 
   s.group = info->num_q_heads / info->num_kv_heads;
   s.page_shift = ilog2_exact(info->page_size);
   s.s_max = info->max_splits;
+  s.fair = info->num_items <= kSlotsPerCu * info->num_cus;
   const int e = cfg.mla ? launch_stage1_mla(cfg.wq, s, info->num_items, stream)
                         : launch_stage1_kr(cfg.dv, cfg.wq, s, info->num_items, stream);
   if (e) return hip_fail(e, "pa_decode_stage1_rope launch");

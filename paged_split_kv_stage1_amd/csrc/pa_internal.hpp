@@ -74,6 +74,7 @@ struct Stage1Args {
   float* out_lse;                       // LSE of rows whose request has one split, or NULL
   int hq, group, page_shift, s_max;
   int part_bf16;
+  int fair;                             // every item runs at once (at most two per CU)
 };
 
 // Stage 1 of keys with a 64-channel rotary part (stage1_kr.hip).
@@ -96,6 +97,7 @@ struct KrArgs {
   void* out; float* out_lse;
   int out_bf16, part_bf16;
   int hq, group, page_shift, s_max;
+  int fair;                             // every item runs at once (at most two per CU)
 };
 
 struct MergeArgs {

@@ -871,7 +871,13 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
     __syncthreads();
   }
   int ti = 0;
+  // Issue-priority balance with the other workgroup of the CU (FairShare), for one-block
+  // waves: with several blocks per wave the added loop check measured 2% slower on the
+  // ragged mix, whose plans run in more than one round anyway.
+  constexpr bool FAIRK = !QM && NQB == 1;
+  const FairShare fs(FAIRK && a.fair, ntiles, PD);
   for (; ti + 2 * PD - 1 < ntiles; ti += PD) {         // steady state
+    if constexpr (FAIRK) fs.at(ti);
     step(ic<0>{}, ic<1>{}, ti);
     if constexpr (PD >= 2) step(ic<1>{}, ic<1>{}, ti + 1);
     if constexpr (PD >= 3) step(ic<2>{}, ic<1>{}, ti + 2);

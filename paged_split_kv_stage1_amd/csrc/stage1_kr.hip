@@ -250,7 +250,9 @@ __global__ __launch_bounds__(256, 2) void stage1_kr_kernel(KrArgs a) {
     store_tile();
     __syncthreads();
   }
+  const FairShare fs(a.fair != 0, ntiles);     // issue-priority balance within the CU
   for (int ti = 0; ti < ntiles; ++ti) {
+    fs.at(ti);
     const int tile0 = tb0 + ti * C::BN;
     const bool more = ti + 1 < ntiles;
     if (more) load_tile(tile0 + C::BN);

@@ -294,7 +294,10 @@ __global__ __launch_bounds__(256, WQ == 4 ? 1 : 2) void stage1_mla_kernel(KrArgs
     store_tile();
     __syncthreads();
   }
+  // issue-priority balance within the CU (not for one block per item: measured 3% slower)
+  const FairShare fs(WQ > 1 && a.fair != 0, ntiles);
   for (int ti = 0; ti < ntiles; ++ti) {
+    fs.at(ti);
     const int tile0 = tb0 + ti * C::BN;
     const bool more = ti + 1 < ntiles;
     if (more) load_tile(tile0 + C::BN);      // next tile in flight during this one
