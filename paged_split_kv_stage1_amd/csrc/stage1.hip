@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "fair_share.hpp"
 #include "kv_addr.hpp"
 
 namespace pa {

@@ -15,6 +15,7 @@
 //   softmax: log2 domain, per-row causal / window masks, lazy rescale.
 //   PV: P as two bf16 terms (hi + lo) against bf16 V.
 #include "common.hpp"
+#include "fair_share.hpp"
 #include "kv_addr.hpp"
 
 namespace pa {

@@ -23,6 +23,7 @@
 //   End: the team combines its waves' sums under the common maximum and writes O / l and
 //     the LSE for its channel slices.
 #include "common.hpp"
+#include "fair_share.hpp"
 #include "kv_addr.hpp"
 
 namespace pa {
