@@ -14,6 +14,12 @@ Two steps:
       profiles/<kernel>_<workload>_hbm_traffic.txt (the traffic file carries the digest that
       bench.py compares before it reports roofline.traffic).
 
+The cache operations (bench.py --op kv_append / kv_quantize) the same way, named op:workload:
+  python3 profile_stage1.py run-ops kv_append:c4 kv_quantize:c2 ...      (GPU machine)
+  python3 profile_stage1.py summarize-ops kv_append:c4 kv_quantize:c2 ...
+      writes profiles/<kernel>_<op>_<workload>_kernel_trace.txt and _hbm_traffic.txt (an
+      op's time and traffic are the sums over the library kernels it launches per step).
+
 This script itself never touches the GPU: rocprofv3 starts bench.py as its own child.
 """
 from __future__ import annotations
@@ -33,6 +39,8 @@ PMC_PASSES = {"FETCH_SIZE": ["FETCH_SIZE"], "WRITE_SIZE": ["WRITE_SIZE"],
 BENCH_TRACE_ARGS = ["--steps", "100", "--warmup", "100", "--graph-reps", "100", "--no-cpu-baseline",
                     "--no-per-config"]
 BENCH_PMC_ARGS = ["--steps", "2", "--warmup", "1", "--graph-reps", "0", "--no-cpu-baseline", "--no-per-config"]
+CACHE_TRACE_ARGS = ["--steps", "50", "--warmup", "20", "--no-cpu-baseline"]
+CACHE_PMC_ARGS = ["--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--calibrate-copy"]
 
 
 def _kernel_of(cfg: str):
@@ -198,7 +206,125 @@ def summarize(configs):
               f"({ab / tot / 1e3 / 80:.1f}%), MFMA {100 * util:.1f}%, traffic/alg {traffic / ab:.3f}")
 
 
+def _cache_kernel(op: str, cfg: str) -> str:
+    """The kernel an op's measurements are filed under (bench.py reports roofline.traffic for it)."""
+    from paged_split_kv_stage1_amd.inputs import CONFIGS
+    if op == "kv_append":
+        return "append_kernel"
+    return "quant_rows_kernel" if CONFIGS[cfg]["scale"] == "per_token_head" else "quant_tensor_kernel"
+
+
+def _op_specs(specs):
+    out = []
+    for spec in specs:
+        op, cfg = spec.split(":")
+        if op not in ("kv_append", "kv_quantize"):
+            raise SystemExit(f"unknown op {op}")
+        out.append((op, cfg))
+    return out
+
+
+def _library_kernel(name: str) -> bool:
+    return name.startswith("pa::") or name.startswith("void pa::")
+
+
+def run_ops(specs):
+    import bench
+    os.makedirs(PROF, exist_ok=True)
+    py = sys.executable
+    bench_py = os.path.join(ROOT, "bench.py")
+    for op, cfg in _op_specs(specs):
+        tag = f"{op}_{cfg}"
+        json.dump({"workload": tag, "kernel": _cache_kernel(op, cfg),
+                   "kernel_source_sha256": bench.source_digest(bench.CACHE_OP_SOURCES)},
+                  open(os.path.join(PROF, f"meta_{tag}.json"), "w"))
+        keep = ("pa::", "copyBuffer")
+        d = os.path.join(PROF, f"trace_{tag}")
+        _run(["rocprofv3", "--kernel-trace", "--stats", "-d", d, "-o", "run", "--output-format", "csv", "--",
+              py, bench_py, "--op", op, "--config", cfg] + CACHE_TRACE_ARGS, d + ".log", 600)
+        _trim(d, keep)
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            d = os.path.join(PROF, f"pmc_{counter}_{tag}")
+            _run(["timeout", "-s", "KILL", "200", "rocprofv3", "--pmc", counter, "-d", d, "-o", "run",
+                  "--output-format", "csv", "--", py, bench_py, "--op", op, "--config", cfg] + CACHE_PMC_ARGS,
+                 d + ".log", 260)
+            _trim(d, keep)
+        print(f"profiled {tag}", flush=True)
+
+
+def summarize_ops(specs):
+    repo = "$REPO"
+    for op, cfg in _op_specs(specs):
+        tag = f"{op}_{cfg}"
+        meta = json.load(open(os.path.join(PROF, f"meta_{tag}.json")))
+        kernel = meta["kernel"]
+        stats = [r for r in csv.DictReader(open(_one(f"{PROF}/trace_{tag}/**/run_kernel_stats.csv")))
+                 if _library_kernel(r["Name"])]
+        if not any(kernel in r["Name"] for r in stats):
+            raise SystemExit(f"{tag}: no {kernel} in the kernel statistics")
+        bj = _bench_json(os.path.join(PROF, f"trace_{tag}.log"))
+        us = sum(float(r["AverageNs"]) for r in stats) / 1e3
+        nbytes = bj["algorithmic_bytes_per_step"]
+        names = ", ".join(r["Name"].split("(")[0].replace("void ", "") for r in stats)
+        trace_cmd = (f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d {repo}/gpurun_out/prof/"
+                     f"trace_{tag} -o run --output-format csv -- python3 {repo}/bench.py --op {op} --config {cfg} " +
+                     " ".join(CACHE_TRACE_ARGS))
+        lines = [f"# {op} ({names}), workload: {bj['config']['workload']}",
+                 f"command: {trace_cmd}",
+                 f"written by: python3 profile_stage1.py run-ops {op}:{cfg} (GPU machine), then "
+                 f"python3 profile_stage1.py summarize-ops {op}:{cfg}",
+                 f"kernel sources: SHA-256 {meta['kernel_source_sha256']} (comment-free text, as bench.py computes it)",
+                 "", f"{'kernel':<72} {'calls':>6} {'avg_ns':>10} {'min_ns':>8} {'max_ns':>8}"]
+        for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+            name = r["Name"] if len(r["Name"]) <= 72 else r["Name"][:69] + "..."
+            lines.append(f"{name:<72} {int(r['Calls']):>6} {float(r['AverageNs']):>10.0f} "
+                         f"{float(r['MinNs']):>8.0f} {float(r['MaxNs']):>8.0f}")
+        lines += ["", f"op avg {us:.1f} us per step (kernel trace, sum over the kernels above); HIP events in the "
+                      f"same run {bj['us_per_step']:.1f} us",
+                  f"algorithmic bytes per step {nbytes} -> {nbytes / us / 1e3:.1f} GB/s = "
+                  f"{nbytes / us / 1e3 / 80:.1f}% of 8 TB/s"]
+        open(os.path.join(ROOT, "profiles", f"{kernel}_{tag}_kernel_trace.txt"), "w").write("\n".join(lines) + "\n")
+        fe, wr = _counters(tag, "FETCH_SIZE"), _counters(tag, "WRITE_SIZE")
+        fc = [v["FETCH_SIZE"] for k, v in fe if "copyBuffer" in k]
+        wc = [v["WRITE_SIZE"] for k, v in wr if "copyBuffer" in k]
+        if not fc or not wc:
+            raise SystemExit(f"{tag}: no calibration copy in the counter runs")
+        fs, ws = 262144.0 / fc[0], 262144.0 / wc[0]
+        per = []
+        traffic = 0.0
+        for r in stats:
+            base = r["Name"]
+            f1 = [v["FETCH_SIZE"] for k, v in fe if k == base]
+            w1 = [v["WRITE_SIZE"] for k, v in wr if k == base]
+            if f1 and w1:
+                traffic += (f1[-1] * fs + w1[-1] * ws) * 1024     # the last step's dispatch of each kernel
+                per.append(f"{base.split('(')[0].replace('void ', '')}: FETCH_SIZE "
+                           f"{', '.join(f'{x:.0f}' for x in f1)} KiB; WRITE_SIZE {', '.join(f'{x:.0f}' for x in w1)} KiB")
+        traffic = int(traffic)
+        pmc_cmd = (f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 200 rocprofv3 --pmc FETCH_SIZE -d "
+                   f"{repo}/gpurun_out/prof/pmc_FETCH_SIZE_{tag} -o run --output-format csv -- python3 "
+                   f"{repo}/bench.py --op {op} --config {cfg} " + " ".join(CACHE_PMC_ARGS))
+        t = [f"# {op} ({names}), workload: {bj['config']['workload']}: HBM traffic from FETCH_SIZE and "
+             f"WRITE_SIZE (two separate rocprofv3 --pmc runs)",
+             f"command (fetch): {pmc_cmd}",
+             f"command (write): the same with --pmc WRITE_SIZE -d {repo}/gpurun_out/prof/pmc_WRITE_SIZE_{tag}",
+             f"written by: python3 profile_stage1.py run-ops {op}:{cfg}, then python3 profile_stage1.py "
+             f"summarize-ops {op}:{cfg}", "",
+             f"calibration (256 MiB device copy): FETCH_SIZE {fc[0]:.0f} KiB -> scale {fs:.4f}; "
+             f"WRITE_SIZE {wc[0]:.0f} KiB -> scale {ws:.4f}"] + per + [
+             f"scaled traffic per step: {traffic / 1e6:.1f} MB (algorithmic {nbytes / 1e6:.1f} MB, ratio "
+             f"{traffic / nbytes:.4f})", "",
+             f"workload_name: {tag}",
+             "digest: SHA-256 of the quantiser / append kernel sources without comments and blank lines",
+             f"kernel_source_sha256: {meta['kernel_source_sha256']}",
+             f"traffic_bytes_per_launch: {traffic}"]
+        open(os.path.join(ROOT, "profiles", f"{kernel}_{tag}_hbm_traffic.txt"), "w").write("\n".join(t) + "\n")
+        print(f"{tag}: {us:.1f} us, {nbytes / us / 1e3:.0f} GB/s, traffic/alg {traffic / nbytes:.3f}")
+
+
+MODES = {"run": run, "summarize": summarize, "run-ops": run_ops, "summarize-ops": summarize_ops}
+
 if __name__ == "__main__":
-    if len(sys.argv) < 3 or sys.argv[1] not in ("run", "summarize"):
+    if len(sys.argv) < 3 or sys.argv[1] not in MODES:
         raise SystemExit(__doc__)
-    (run if sys.argv[1] == "run" else summarize)(sys.argv[2:])
+    MODES[sys.argv[1]](sys.argv[2:])
