@@ -737,6 +737,21 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
     }
   };
 
+  // Two-term FP8 query: the bf16 row is requested before the first tiles, so that its
+  // conversion below waits for it alone and runs while the tiles are in flight.
+  bf16x8 qraw[C::QX2 ? C::KC2 : 1][4];
+  if constexpr (C::QX2) {
+    static_assert(NQB == 1, "two-term query: one block per wave");
+    const int m = 16 * (it.qblk0 + wq) + L16;
+    const int mr = m < Mq ? m : Mq - 1;
+    const int r = mr / G;
+    const int hl = mr - r * G;
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + ((int64_t)(it.row0 + r) * Hq + (int64_t)it.kvh * G + hl) * DH;
+#pragma unroll
+    for (int ks = 0; ks < C::KC2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qraw[ks][j] = *reinterpret_cast<const bf16x8*>(qp + 128 * ks + 32 * g + 8 * j);
+  }
   if (ntiles > 0) {
     load_tile(ic<0>{}, tb0);
     if constexpr (PD >= 2) {
@@ -817,14 +832,12 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
       // and the residual, x16, rounded again (lo): q = s_r (hi + lo/16) to ~2^-8
       // relative, and s_r joins the row's score scale.  16-byte unit 4*ks + 2*term + half
       // of the operand store holds 16 codes of term (0 hi, 1 lo).
-      const __bf16* qp = static_cast<const __bf16*>(a.q) + qrow;
-      bf16x8 raw[C::KC2][4];
+      bf16x8 (&raw)[C::KC2][4] = qraw;
       float amax = 0.f;
 #pragma unroll
       for (int ks = 0; ks < C::KC2; ++ks)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          raw[ks][j] = *reinterpret_cast<const bf16x8*>(qp + 128 * ks + 32 * g + 8 * j);
 #pragma unroll
           for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)raw[ks][j][e]));
         }
