@@ -64,9 +64,9 @@ def _cpu_model() -> str:
     return platform.processor()
 
 
-KERNEL_SOURCES = ("stage1.hip", "common.hpp", "fair_share.hpp", "kv_addr.hpp", "pa_internal.hpp")
+KERNEL_SOURCES = ("stage1.hip", "common.hpp", "fair_share.hpp", "row_store.hpp", "kv_addr.hpp", "pa_internal.hpp")
 KR_SOURCES = ("stage1_kr.hip", "common.hpp", "fair_share.hpp", "kv_addr.hpp", "pa_internal.hpp")
-MLA_SOURCES = ("stage1_mla.hip", "common.hpp", "fair_share.hpp", "kv_addr.hpp", "pa_internal.hpp")
+MLA_SOURCES = ("stage1_mla.hip", "common.hpp", "fair_share.hpp", "row_store.hpp", "kv_addr.hpp", "pa_internal.hpp")
 
 
 def stage1_kernel_of(latent: bool, rope: bool):

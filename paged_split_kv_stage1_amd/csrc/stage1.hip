@@ -37,6 +37,7 @@
 
 #include "common.hpp"
 #include "fair_share.hpp"
+#include "row_store.hpp"
 #include "kv_addr.hpp"
 
 namespace pa {
@@ -982,33 +983,6 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
   }
   if (wt != 0) return;
 
-  // Row L16 of block i, scaled by sc, as bf16 at dst: lane group g holds channels
-  // 16 db + 4g .. +3 of every 16-channel block db; for each pair of blocks the lane
-  // groups 2h and 2h+1 exchange one half (v_permlane16_swap), so that each lane writes
-  // 8 contiguous channels -- one 16-byte store per pair instead of two 8-byte ones (the
-  // stores of the last tile queue behind the other workgroup's loads).
-  auto store_row_bf16 = [&](__bf16* dst, int i, float sc) __attribute__((always_inline)) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bool odd = (g & 1) != 0;
-    const int h = g >> 1;
-#pragma unroll
-    for (int db = 0; db < C::DB; db += 2) {
-      uint32_t keep[2], got[2];
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const bf16x2 pa = {(__bf16)(o[i][db][2 * w] * sc), (__bf16)(o[i][db][2 * w + 1] * sc)};
-        const bf16x2 pb = {(__bf16)(o[i][db + 1][2 * w] * sc), (__bf16)(o[i][db + 1][2 * w + 1] * sc)};
-        const uint32_t ua = __builtin_bit_cast(uint32_t, pa), ub = __builtin_bit_cast(uint32_t, pb);
-        const uint32_t send = odd ? ua : ub;
-        const auto r = __builtin_amdgcn_permlane16_swap(send, send, false, false);
-        got[w] = odd ? r[0] : r[1];       // odd: the even lane's block db+1 half; even: the odd lane's block db half
-        keep[w] = odd ? ub : ua;
-      }
-      const uint4 v = odd ? uint4{got[0], got[1], keep[0], keep[1]} : uint4{keep[0], keep[1], got[0], got[1]};
-      *reinterpret_cast<uint4*>(dst + 16 * (db + (odd ? 1 : 0)) + 8 * h) = v;
-    }
-  };
-
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
     if (!qvalid[i]) continue;
@@ -1023,14 +997,14 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
     if (it.nsplit == 1) {
       if (a.out_lse && g == 0) a.out_lse[th] = lse;
       if (a.out_bf16) {
-        store_row_bf16(static_cast<__bf16*>(a.out) + th * DH, i, sc);
+        store_row_bf16_x16(static_cast<__bf16*>(a.out) + th * DH, o[i], sc, g);
       } else {
         float* dst = static_cast<float*>(a.out) + th * DH;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = o[i][db] * sc;
       }
     } else if (a.part_bf16) {
-      store_row_bf16(static_cast<__bf16*>(a.partial_o) + (th * a.s_max + it.split) * DH, i, sc);
+      store_row_bf16_x16(static_cast<__bf16*>(a.partial_o) + (th * a.s_max + it.split) * DH, o[i], sc, g);
       if (g == 0) a.partial_lse[th * a.s_max + it.split] = lse;
     } else {
       float* dst = static_cast<float*>(a.partial_o) + (th * a.s_max + it.split) * DH;

@@ -24,6 +24,7 @@
 //     the LSE for its channel slices.
 #include "common.hpp"
 #include "fair_share.hpp"
+#include "row_store.hpp"
 #include "kv_addr.hpp"
 
 namespace pa {
@@ -333,7 +334,6 @@ __global__ __launch_bounds__(256, WQ == 4 ? 1 : 2) void stage1_mla_kernel(KrArgs
   const bool empty = !(lsum > 0.f);
   const float sc = empty ? 0.f : 1.f / lsum;
   const float lse = empty ? -INFINITY : (mall + __log2f(lsum)) * kLn2M;
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   const int ch0 = wave_in * CW;
   const bool final_out = it.nsplit == 1;
   if (g == 0 && wave_in == 0) {
@@ -347,14 +347,7 @@ __global__ __launch_bounds__(256, WQ == 4 ? 1 : 2) void stage1_mla_kernel(KrArgs
   const int64_t row = final_out ? th : th * a.s_max + it.split;
   const bool bf = final_out ? a.out_bf16 : a.part_bf16;
   if (bf) {
-    __bf16* dst = static_cast<__bf16*>(dstv) + row * C::DV + ch0;
-#pragma unroll
-    for (int d = 0; d < DBW; ++d) {
-      bf16x4 v;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) v[kk] = (__bf16)(o[d][kk] * sc);
-      *reinterpret_cast<bf16x4*>(dst + 16 * d + 4 * g) = v;
-    }
+    store_row_bf16_x16(static_cast<__bf16*>(dstv) + row * C::DV + ch0, o, sc, g);
   } else {
     float* dst = static_cast<float*>(dstv) + row * C::DV + ch0;
 #pragma unroll
