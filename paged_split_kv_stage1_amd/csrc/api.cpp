@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "pa.h"
@@ -512,13 +513,12 @@ pa_status pa_plan_splits(const pa_plan_args* a, void* plan_host, size_t plan_cap
   // kernel: c3 175 -> 172.5 us, c3 R1 171 -> 167.6, c4 R1 342.5 -> 338; the 192/128
   // kernel measured 0.6% slower with it and keeps equal splits).
   if (n_items <= cm.slots && cm.slots % (2 * kXcds) == 0 && a->force_splits == 0 && !cfg.kr) {
-    std::vector<std::vector<int>> pos;           // positions of the splits of (b, kvh, qblk0)
-    std::vector<int64_t> key;
-    std::vector<std::pair<int64_t, int>> keyed;
+    // item positions grouped by range (request, KV head, query-block group)
+    std::vector<std::pair<std::tuple<int, int, int>, int>> keyed;
     keyed.reserve(items.size());
     for (int p = 0; p < (int)items.size(); ++p) {
       const PaItem& x = items[p];
-      keyed.push_back({((int64_t)x.req * Hkv + x.kvh) * 4096 + x.qblk0, p});
+      keyed.push_back({std::make_tuple(x.req, x.kvh, x.qblk0), p});
     }
     std::stable_sort(keyed.begin(), keyed.end());
     for (size_t i = 0; i < keyed.size();) {
