@@ -33,6 +33,12 @@
 //        PR #869 item 2), as a hi term plus a lo term of the residual x16, with the
 //        per-tensor v_scale applied in the final normaliser.
 // Waves that split the tokens of a tile merge their (max, sum, O) in LDS at the end.
+//
+// The other orientation, S = Q K^T and O = P V with the query rows on the MFMA M axis,
+// is instantiated beside it (template flag QM, chosen per plan): the score accumulator
+// then holds four rows of one token per lane, so P goes through a per-wave LDS scratch
+// to become an A operand, and row maxima take DPP reductions across 16 lanes.  It is
+// the measured alternative, slower on the compute-bound shapes.
 #include <type_traits>
 
 #include "common.hpp"
