@@ -1046,10 +1046,12 @@ struct Pipe {
   // accumulators in the 256 registers a wave has at two workgroups per CU.  bf16 KV at
   // head_dim 256 with four row-block waves keeps one too: measured c3 R8 177 -> 175 us
   // and c3 B1 R8 26.4 -> 24.8 us (32 KB tiles: with two in flight, the first compute of
-  // a batch-1 launch waits for 32 MB requested by all workgroups at once); the FP8
-  // four-wave shape lost 4.5% with one and keeps two.
+  // a batch-1 launch waits for 32 MB requested by all workgroups at once); so does FP8
+  // KV with two row-block waves (c4 R1 331.5 -> 327.5 us, c4 B1 R1 30.4 -> 30.0).  The
+  // FP8 four-wave shape lost 4.5% with one and keeps two, as does head_dim 512 (c6 74.2
+  // -> 75.3 us with one).
   static constexpr bool PV_FP8 = KV == 1 && !PT;
-  static constexpr int PD = DH == 512 ? 2 : (DH == 256 && (PV_FP8 || (KV == 2 && WQ == 2) || (WQ == 4 && KV == 0))) ? 1 : (CPT <= 4 ? 2 : 1);
+  static constexpr int PD = DH == 512 ? 2 : (DH == 256 && (PV_FP8 || (KV == 2 && WQ == 2) || (WQ == 4 && KV == 0) || (WQ == 2 && KV == 1))) ? 1 : (CPT <= 4 ? 2 : 1);
 };
 
 template <int DH, bool QF8, int KV, bool PT, int WQ, int NQB, bool QM = false>
