@@ -120,6 +120,23 @@ def measured_traffic(config: str, kernel: str = "stage1_kernel", sources=KERNEL_
     return None
 
 
+def measured_mfma_util(config: str, kernel: str = "stage1_kernel", sources=KERNEL_SOURCES):
+    """MFMA utilisation of ``kernel`` on this workload (SQ_VALU_MFMA_BUSY_CYCLES over the
+    SIMDs' cycles, rocprofv3 counters) from the committed kernel-trace summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    import re
+
+    digest = source_digest(sources)
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_kernel_trace.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if f"SHA-256 {digest}" not in text:
+        return None
+    m = re.search(r"MFMA utilisation .*?= ([0-9.]+)%", text)
+    return round(float(m.group(1)) / 100, 4) if m else None
+
+
 def cpu_baseline(w, out_gpu: np.ndarray, budget_s: float, threads: int = 0):
     """Times the fp64 oracle on a bounded sample (whole requests, in order, until the
     time budget is spent) and compares the GPU output of those requests with it.
@@ -470,7 +487,8 @@ def per_config(args, flush, stream):
                      "merge_us": round(float(np.mean(mg)), 2), "us_per_step": round(tot, 2),
                      "algorithmic_bytes": acc["bytes"], "gbps": round(gbps, 1),
                      "frac_of_8tbs": round(gbps / HBM_PEAK_GBPS, 4), "work_items": pd.num_items,
-                     "max_splits": pd.max_splits, "arithmetic": arithmetic(w, int(pd.info.variant))}
+                     "max_splits": pd.max_splits, "arithmetic": arithmetic(w, int(pd.info.variant)),
+                     "mfma_util": measured_mfma_util(name, *stage1_kernel_of(w.latent, pd.rope))}
         if name in MEMORY_BOUND:
             res[name]["meets_70pct"] = bool(gbps >= 0.7 * HBM_PEAK_GBPS)
         del di, out, pd
@@ -597,7 +615,9 @@ def main():
                      "frac": round(roof_achieved / HBM_PEAK_GBPS, 4),
                      "traffic": (measured_traffic(args.config, *stage1_kernel_of(w.latent, pd.rope))
                                  if args.orientation == "kv_on_m" else None),
-                     "kernel": stage1_kernel_of(w.latent, pd.rope)[0], "bytes_per_launch": s1_bytes},
+                     "kernel": stage1_kernel_of(w.latent, pd.rope)[0], "bytes_per_launch": s1_bytes,
+                     "mfma_util": (measured_mfma_util(args.config, *stage1_kernel_of(w.latent, pd.rope))
+                                   if args.orientation == "kv_on_m" else None)},
     }
     if not args.no_per_config and args.config == "c2" and args.orientation == "kv_on_m":
         result["per_config"], result["r8_over_r1"] = per_config(args, flush, stream)
