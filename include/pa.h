@@ -144,6 +144,10 @@ typedef struct {
  * plan_host (plan_capacity bytes).  With plan_host == NULL only *info is filled,
  * which tells the caller how large the plan and scratch buffers must be.  The caller
  * copies plan_host to a device buffer of info->plan_bytes bytes before stage 1.
+ * Split boundaries are 64-token aligned but not necessarily equal: when every item gets
+ * its own workgroup slot, the splits of a memory-bound range are sized for the XCD their
+ * position in the work list runs on (workgroup p on XCD p mod 8; the odd XCDs were
+ * measured ~10% slower at streaming); info->max_item_tokens is the longest item.
  * Errors: INVALID_ARGUMENT (non-monotone CSR, n_b > kv_len, kv_indptr inconsistent
  * with kv_len, Hq % Hkv != 0, bad enum), UNSUPPORTED (max_q_len > 8, head_dim not
  * 128/256/512, page size not a power of two in [16, 1024], rows x group too large for one
