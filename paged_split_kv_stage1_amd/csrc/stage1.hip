@@ -139,6 +139,7 @@ struct S1Cfg {
   // amax_row / 127) on the 16x16x64 integer MFMA against the raw K codes, exact int32
   // sums, K kept in INT8 in LDS.
   static constexpr bool QI2 = I8 && !QF8 && PT && WQ == 4 && NQB == 1;
+  static constexpr bool VPRE = QX2 && !QM;          // V fragments read before the softmax
   static constexpr bool LBF = !KVF8 || (I8 && !QI2) || (PT && !QF8 && WQ == 4 && !QX2 && !I8);   // K tile in bf16
   static constexpr bool LBFV = !KVF8 || I8;                               // V tile in bf16
   static constexpr int LKB = LBF ? 2 : 1;           // bytes per K element in LDS
@@ -655,6 +656,15 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
         }
         continue;
       }
+      // Four one-block waves on FP8 V: the tile's V fragments are requested here, before
+      // the softmax, so that their LDS latency hides behind it (in the P.V loop each read
+      // would otherwise be waited for on its own).
+      i32x2 vraw[C::VPRE ? C::DB : 1];
+      if constexpr (C::VPRE) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+          vraw[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
+      }
       const float xs = xsb[i];               // score scale still to apply
       if constexpr (PT) {
 #pragma unroll
@@ -719,7 +729,9 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
         }
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 va = vfrag(Vl, db);
+          bf16x8 va;
+          if constexpr (C::VPRE) va = fp8x8_to_bf16x8((uint32_t)vraw[db][0], (uint32_t)vraw[db][1]);
+          else va = vfrag(Vl, db);
           o[i][db] = mfma_bf16(va, hv, o[i][db]);
           if constexpr (!KVF8) o[i][db] = mfma_bf16(va, lv, o[i][db]);
         }
