@@ -161,6 +161,10 @@ struct S1Cfg {
   static constexpr int KC4 = DH / 64;               // K-steps of q.k (16x16x64 INT8 MFMA, QI2)
   static constexpr int DB = DH / 16;                // 16-wide d blocks of P.V
   static constexpr bool PV_FP8 = KVF8 && !PT;       // per-tensor FP8 V: fp8 MFMA for P.V
+  // bf16 K and V operand fragments read this many steps ahead of their MFMAs (0: as the
+  // compiler schedules them, one step ahead).  With one wave per SIMD (head_dim 512)
+  // nothing else covers an LDS read's latency.
+  static constexpr int RA = (DH == 512 && !QM) ? 4 : 0;
   static constexpr int EPIB = (WT > 1) ? (4 * NQB * DB * 256 * 4 + 4 * NQB * 64 * 2 * 4) : 0;
   // Query blocks whose operand stays in registers.  Three blocks of bf16 queries against
   // per-token-head FP8 would need more than 256 VGPRs: the third block's operand lives in
@@ -545,8 +549,33 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
           s1[k] = fmaf((float)l1[k], 1.f / 254.f, (float)h1[k]);
         }
       }
+      if constexpr (C::LBF && C::RA > 0 && !C::QX2 && !C::QI2) {
+        // ring of RA K-step fragment pairs: the reads for step kc + RA go out before the
+        // MFMAs of step kc
+        bf16x8 kr[C::RA][2];
+        auto kread = [&](int kc, int tb) __attribute__((always_inline)) -> bf16x8 {
+          return *reinterpret_cast<const bf16x8*>(Kl + kro[tb][kc]);
+        };
 #pragma unroll
-      for (int kc = 0; kc < ((C::QX2 || C::QI2) ? 0 : C::KC); ++kc) {
+        for (int p = 0; p < C::RA; ++p) {
+          kr[p][0] = kread(p, 0);
+          kr[p][1] = kread(p, 1);
+        }
+#pragma unroll
+        for (int kc = 0; kc < C::KC; ++kc) {
+          const bf16x8 k0 = kr[kc % C::RA][0], k1 = kr[kc % C::RA][1];
+          if (kc + C::RA < C::KC) {
+            kr[kc % C::RA][0] = kread(kc + C::RA, 0);
+            kr[kc % C::RA][1] = kread(kc + C::RA, 1);
+          }
+          const QT qv = qget(i, kc);
+          s0 = mfma_bf16(k0, qv, s0);
+          s1 = mfma_bf16(k1, qv, s1);
+          __builtin_amdgcn_sched_barrier(0);   // keep the read-ahead in this step
+        }
+      }
+#pragma unroll
+      for (int kc = 0; kc < ((C::QX2 || C::QI2 || (C::LBF && C::RA > 0)) ? 0 : C::KC); ++kc) {
         if constexpr (C::LBF) {
           const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Kl + kro[0][kc]);
           const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Kl + kro[1][kc]);
@@ -727,13 +756,36 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
           hv[k] = h;
           if constexpr (!KVF8) lv[k] = (__bf16)(y - (float)h);
         }
+        if constexpr (C::LBFV && C::RA > 0) {
+          // ring of RA d-block fragments (two transposing reads each), as for K
+          i16x4 vr[C::RA][2];
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          bf16x8 va;
-          if constexpr (C::VPRE) va = fp8x8_to_bf16x8((uint32_t)vraw[db][0], (uint32_t)vraw[db][1]);
-          else va = vfrag(Vl, db);
-          o[i][db] = mfma_bf16(va, hv, o[i][db]);
-          if constexpr (!KVF8) o[i][db] = mfma_bf16(va, lv, o[i][db]);
+          for (int p = 0; p < C::RA; ++p) {
+            vr[p][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(p, 0)));
+            vr[p][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(p, 1)));
+          }
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            const i16x4 v1 = vr[db % C::RA][0], v2 = vr[db % C::RA][1];
+            if (db + C::RA < C::DB) {
+              vr[db % C::RA][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db + C::RA, 0)));
+              vr[db % C::RA][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS i16x4*)(Vl + vaddr(db + C::RA, 1)));
+            }
+            const auto w = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 va = __builtin_bit_cast(bf16x8, w);
+            o[i][db] = mfma_bf16(va, hv, o[i][db]);
+            if constexpr (!KVF8) o[i][db] = mfma_bf16(va, lv, o[i][db]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            bf16x8 va;
+            if constexpr (C::VPRE) va = fp8x8_to_bf16x8((uint32_t)vraw[db][0], (uint32_t)vraw[db][1]);
+            else va = vfrag(Vl, db);
+            o[i][db] = mfma_bf16(va, hv, o[i][db]);
+            if constexpr (!KVF8) o[i][db] = mfma_bf16(va, lv, o[i][db]);
+          }
         }
       }
     }
