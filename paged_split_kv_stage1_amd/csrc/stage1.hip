@@ -139,7 +139,12 @@ struct S1Cfg {
   // amax_row / 127) on the 16x16x64 integer MFMA against the raw K codes, exact int32
   // sums, K kept in INT8 in LDS.
   static constexpr bool QI2 = I8 && !QF8 && PT && WQ == 4 && NQB == 1;
-  static constexpr bool VPRE = QX2 && !QM;          // V fragments read before the softmax
+  // FP8 V of four one-block waves: the tile's V fragments are read before the softmax
+  // (VPRE, all of them), or at head_dim 512, where all of them would take 64 registers,
+  // the first VRA of them, the rest VRA steps ahead of their MFMAs (VRING).
+  static constexpr bool VPRE = QX2 && !QM && DH < 512;
+  static constexpr bool VRING = QX2 && !QM && DH == 512;
+  static constexpr int VRA = 4;
   static constexpr bool LBF = !KVF8 || (I8 && !QI2) || (PT && !QF8 && WQ == 4 && !QX2 && !I8);   // K tile in bf16
   static constexpr bool LBFV = !KVF8 || I8;                               // V tile in bf16
   static constexpr int LKB = LBF ? 2 : 1;           // bytes per K element in LDS
@@ -689,10 +694,10 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
       // Four one-block waves on FP8 V: the tile's V fragments are requested here, before
       // the softmax, so that their LDS latency hides behind it (in the P.V loop each read
       // would otherwise be waited for on its own).
-      i32x2 vraw[C::VPRE ? C::DB : 1];
-      if constexpr (C::VPRE) {
+      i32x2 vraw[C::VPRE ? C::DB : C::VRING ? C::VRA : 1];
+      if constexpr (C::VPRE || C::VRING) {
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < (C::VPRE ? C::DB : C::VRA); ++db)
           vraw[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
       }
       const float xs = xsb[i];               // score scale still to apply
@@ -776,6 +781,25 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
             const bf16x8 va = __builtin_bit_cast(bf16x8, w);
             o[i][db] = mfma_bf16(va, hv, o[i][db]);
             if constexpr (!KVF8) o[i][db] = mfma_bf16(va, lv, o[i][db]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else if constexpr (C::VRING) {
+          // fragment db + 1 is converted while the MFMA of db runs; slot r of vraw holds
+          // fragments r, r + VRA, ... in turn, each refilled when its fragment is converted
+          auto vread = [&](int db) __attribute__((always_inline)) -> i32x2 {
+            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2*)(Vl + vaddr(db, 0)));
+          };
+          bf16x8 vnext = fp8x8_to_bf16x8((uint32_t)vraw[0][0], (uint32_t)vraw[0][1]);
+          if (C::VRA < C::DB) vraw[0] = vread(C::VRA);
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            const bf16x8 va = vnext;
+            if (db + 1 < C::DB) {
+              const int r = (db + 1) % C::VRA;
+              vnext = fp8x8_to_bf16x8((uint32_t)vraw[r][0], (uint32_t)vraw[r][1]);
+              if (db + 1 + C::VRA < C::DB) vraw[r] = vread(db + 1 + C::VRA);
+            }
+            o[i][db] = mfma_bf16(va, hv, o[i][db]);
             __builtin_amdgcn_sched_barrier(0);
           }
         } else {
