@@ -169,8 +169,9 @@ struct S1Cfg {
   // bf16 K and V operand fragments read this many steps ahead of their MFMAs (0: as the
   // compiler schedules them, one step ahead).  With one wave per SIMD (head_dim 512)
   // nothing else covers an LDS read's latency; two steps measured slightly faster than
-  // four (eight spills), and with two waves per SIMD (head_dim 256) it gains nothing.
-  static constexpr int RA = (DH == 512 && !QM) ? 2 : 0;
+  // four (eight spills).  With two waves per SIMD it gains nothing on the bf16 head_dim
+  // 256 kernels and 1-2% on the compute-bound INT8 four-wave kernel (bf16 V in LDS).
+  static constexpr int RA = QM ? 0 : DH == 512 ? 2 : (DH == 256 && KV == 2 && WQ == 4) ? 4 : 0;
   static constexpr int EPIB = (WT > 1) ? (4 * NQB * DB * 256 * 4 + 4 * NQB * 64 * 2 * 4) : 0;
   // Query blocks whose operand stays in registers.  Three blocks of bf16 queries against
   // per-token-head FP8 would need more than 256 VGPRs: the third block's operand lives in
