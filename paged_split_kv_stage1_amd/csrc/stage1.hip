@@ -692,9 +692,9 @@ __global__ __launch_bounds__(256, DH == 512 ? 1 : 2) void stage1_kernel(Stage1Ar
         }
         continue;
       }
-      // Four one-block waves on FP8 V: the tile's V fragments are requested here, before
-      // the softmax, so that their LDS latency hides behind it (in the P.V loop each read
-      // would otherwise be waited for on its own).
+      // Four one-block waves on FP8 V: the tile's V fragments (at head_dim 512 the first
+      // VRA of them) are requested here, before the softmax, so that their LDS latency
+      // hides behind it (in the P.V loop each read would otherwise be waited for on its own).
       i32x2 vraw[C::VPRE ? C::DB : C::VRING ? C::VRA : 1];
       if constexpr (C::VPRE || C::VRING) {
 #pragma unroll
